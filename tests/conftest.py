@@ -1,0 +1,22 @@
+"""pytest configuration: the ``gpu`` marker and the oracle library."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    """Compile the oracle once if it is not built yet (test infrastructure)."""
+    import oracle
+    oracle.build(force=False)
+    yield
