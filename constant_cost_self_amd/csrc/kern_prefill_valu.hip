@@ -1,0 +1,145 @@
+// kern_prefill_valu.hip -- fp32 chunked prefill scan on the vector ALUs (gfx950).
+//
+// The inter-chunk half of the chunked prefill ([TA] "Feature maps and linear
+// attention": the state recurrence evaluated chunk by chunk).  A block owns one
+// slice of `SV` consecutive features of one head's state, S[f][0..d_V] (column
+// d_V is Z), keeps it in LDS for the whole segment and walks the chunks in order.
+// For chunk c with tokens t0..t0+L-1:
+//     readout   part[t][j] = sum_{f in slice} qw[f] phi_f(q_t) S[f][j]   (S before c)
+//     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
+// The readout of every slice is written as a partial sum; the finalize kernel adds
+// the partials of all slices to the intra-chunk part.  Arithmetic is fp32 on the
+// VALU: this is the path for fp32 inputs and for sizes the MFMA scan does not
+// cover.  Tokens past n in the last chunk get u = 0 and so never enter the state.
+#include "launch.h"
+#include "sata_common.h"
+
+namespace sata {
+
+namespace {
+
+__host__ __device__ inline int64_t valu_lds_floats(int SV, int d_K, int d_V, int L) {
+    const int cols = d_V + 1;
+    return (int64_t)SV * cols + 2LL * L * (d_K + 1) + (int64_t)L * cols + (int64_t)L * SV;
+}
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
+    using T = typename In::T;
+    extern __shared__ float lds[];
+    const int slice = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int SV = a.slice_feats, L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1;
+    const int nidx = a.P - 1;
+    const int64_t F0 = (int64_t)slice * SV;
+
+    float* Ssl = lds;                              // [SV][cols]
+    float* xq = Ssl + SV * cols;                   // [L][d_K+1], coordinate d_K == 1
+    float* xk = xq + L * (d_K + 1);                // [L][d_K+1]
+    float* us = xk + L * (d_K + 1);                // [L][cols]
+    float* hat = us + L * cols;                    // [L][SV]
+
+    const T* q = static_cast<const T*>(a.q) + bh * a.n * d_K;
+    const T* k = static_cast<const T*>(a.k) + bh * a.n * d_K;
+    const T* v = static_cast<const T*>(a.v) + bh * a.n * d_V;
+    float* state = a.state ? a.state + bh * (int64_t)cols * a.M_pad : nullptr;
+
+    for (int idx = tid; idx < SV * cols; idx += kThreads) {
+        const int f = idx / cols, j = idx % cols;
+        const int64_t F = F0 + f;
+        Ssl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
+    }
+
+    const int nch = a.c_end - a.c_begin;
+    for (int c = a.c_begin; c < a.c_end; ++c) {
+        const int64_t t0 = (int64_t)c * L;
+        const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
+        __syncthreads();
+        for (int idx = tid; idx < L * (d_K + 1); idx += kThreads) {
+            const int t = idx / (d_K + 1), i = idx % (d_K + 1);
+            float vq = 1.0f, vk = 1.0f;
+            if (i < d_K) {
+                vq = t < nvalid ? In::load(q, (t0 + t) * d_K + i) : 0.0f;
+                vk = t < nvalid ? In::load(k, (t0 + t) * d_K + i) : 0.0f;
+            }
+            xq[idx] = vq;
+            xk[idx] = vk;
+        }
+        for (int idx = tid; idx < L * cols; idx += kThreads) {
+            const int t = idx / cols, j = idx % cols;
+            float u = 0.0f;
+            if (t < nvalid) u = j < d_V ? In::load(v, (t0 + t) * d_V + j) : 1.0f;
+            us[idx] = u;
+        }
+        __syncthreads();
+        // weighted query features of the slice
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            hat[idx] = F < a.M ? a.qw[F] * feature_value(xq + t * (d_K + 1), a.fidx[F], nidx)
+                               : 0.0f;
+        }
+        __syncthreads();
+        // readout against the state of the chunks before c
+        float* part = a.partial +
+                      (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * cols;
+        for (int idx = tid; idx < L * cols; idx += kThreads) {
+            const int t = idx / cols, j = idx % cols;
+            const float* h = hat + t * SV;
+            float acc = 0.0f;
+            for (int f = 0; f < SV; ++f) acc = fmaf(h[f], Ssl[f * cols + j], acc);
+            part[idx] = acc;
+        }
+        __syncthreads();
+        // key features of the slice
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            hat[idx] = F < a.M ? feature_value(xk + t * (d_K + 1), a.fidx[F], nidx) : 0.0f;
+        }
+        __syncthreads();
+        // state update with the chunk
+        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+            const int f = idx / cols, j = idx % cols;
+            float s = 0.0f;
+            for (int t = 0; t < L; ++t) s = fmaf(hat[t * SV + f], us[t * cols + j], s);
+            Ssl[idx] += s;
+        }
+    }
+    __syncthreads();
+    if (a.store_state) {
+        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+            const int j = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            if (F < a.M_pad) state[(int64_t)j * a.M_pad + F] = Ssl[f * cols + j];
+        }
+    }
+}
+
+}  // namespace
+
+int valu_slice_feats(int d_K, int d_V, int L) {
+    for (int SV = 256; SV >= 16; SV >>= 1)
+        if (valu_lds_floats(SV, d_K, d_V, L) * 4 <= 96 * 1024) return SV;
+    return 0;
+}
+
+hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st) {
+    const size_t lds = (size_t)valu_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
+    dim3 grid(a.nslices, a.BH);
+    if (a.bf16) {
+        hipError_t e = hipFuncSetAttribute((const void*)scan_valu_kernel<InBF16>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(scan_valu_kernel<InBF16>, grid, dim3(kThreads), lds, st, a);
+    } else {
+        hipError_t e = hipFuncSetAttribute((const void*)scan_valu_kernel<InF32>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(scan_valu_kernel<InF32>, grid, dim3(kThreads), lds, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sata

@@ -1,0 +1,57 @@
+// launch.h -- host-side launchers of the SATA kernels (internal to libsata).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sata_common.h"
+
+namespace sata {
+
+struct DecodeArgs {
+    float* state;
+    const void* q;
+    const void* k;
+    const void* v;
+    float* y;
+    const uint32_t* fidx;
+    const float* qw;
+    float* partial;     // [BH][nblk][d_V+1] workspace
+    int64_t M, M_pad;
+    int BH, d_K, d_V, P, nblk;
+    bool bf16;
+};
+
+// Number of feature blocks per head of the decode kernel.
+int decode_blocks(int64_t M_pad);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// One segment [c_begin, c_end) of chunks of a chunked prefill.
+struct PrefillSegArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* y;
+    float* state;            // [BH][d_V+1][M_pad]; read if load_state, written if store_state
+    float* partial;          // [BH][c_end-c_begin][nslices][L][d_V+1] workspace
+    const uint32_t* fidx;    // packed feature indices [M_pad]
+    const float* qw;         // alpha_p C_p [M_pad]
+    const void* mfma_rows;   // slice tables of the MFMA scan (nullptr for the VALU scan)
+    Alpha alpha;
+    int64_t M, M_pad;
+    int BH, n, d_K, d_V, P, L;
+    int nslices, slice_feats; // slice decomposition of the feature axis
+    int c_begin, c_end;
+    int load_state, store_state;
+    bool bf16;
+};
+
+// VALU fp32 scan: slice_feats features per block, chosen by valu_slice_feats().
+int valu_slice_feats(int d_K, int d_V, int L);
+hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st);
+
+// Intra-chunk part + reduction of the slice partials + normalisation -> y.
+int64_t finalize_lds_bytes(int d_K, int d_V, int L);
+hipError_t launch_finalize(const PrefillSegArgs& a, hipStream_t st);
+
+}  // namespace sata

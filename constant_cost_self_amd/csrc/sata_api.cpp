@@ -1,0 +1,331 @@
+// sata_api.cpp -- the C ABI of libsata (include/sata.h): argument checks, the
+// tables handle and its workspace, and the launch sequence of each entry point.
+//
+// Prefill ([TA] "Feature maps and linear attention", evaluated by chunks):
+//   for each segment of whole chunks (one segment unless the slice partials of
+//   the whole sequence would exceed the workspace cap):
+//     scan      per (head, feature slice), sequential over the segment's chunks:
+//               partial readouts against the state, then the state update
+//     finalize  per (head, chunk): intra-chunk direct part + sum of partials, y
+//   The state of a slice is carried from one segment to the next through the
+//   caller's state buffer (or a workspace copy when the caller passed none).
+// Decode: one streaming read-modify-write kernel over the state, then a per-head
+//   reduction of the partial readouts.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/sata.h"
+#include "launch.h"
+#include "scan_mfma.h"
+#include "tables.h"
+
+struct sata_tables {
+    sata::HostTables h;
+    int device = -1;
+    uint32_t* d_fidx = nullptr;
+    float* d_qw = nullptr;
+    sata::MfmaTables mfma;            // slice tables of the MFMA scan (may be empty)
+    std::mutex mu;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    int64_t ws_limit = 16LL << 30;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_err() { g_err[0] = '\0'; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_device(const sata_tables* t) {
+    if (t->device < 0) return fail(SATA_ERR_ARG, "host-only handle: it has no device tables");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SATA_ERR_HIP, "hipGetDevice failed");
+    if (dev != t->device)
+        return fail(SATA_ERR_ARG, "handle was built on device %d but device %d is current",
+                    t->device, dev);
+    return SATA_OK;
+}
+
+// Grow the handle's workspace to at least `bytes`.  Growth waits for `st` (calls
+// on one handle are issued on one stream), frees the old buffer and allocates.
+int ensure_ws(sata_tables* t, size_t bytes, hipStream_t st) {
+    if (bytes <= t->ws_bytes) return SATA_OK;
+    if (t->ws) {
+        if (hipStreamSynchronize(st) != hipSuccess)
+            return fail(SATA_ERR_HIP, "hipStreamSynchronize failed while growing the workspace");
+        (void)hipFree(t->ws);
+        t->ws = nullptr;
+        t->ws_bytes = 0;
+    }
+    const size_t rounded = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    if (hipMalloc(&t->ws, rounded) != hipSuccess) {
+        (void)hipGetLastError();
+        t->ws = nullptr;
+        return fail(SATA_ERR_OOM, "cannot allocate a %zu-byte workspace", rounded);
+    }
+    t->ws_bytes = rounded;
+    return SATA_OK;
+}
+
+int check_sizes(int d_K, int d_V, int P) {
+    if (d_K < 1 || d_K > sata::kMaxD || d_V < 1 || d_V > sata::kMaxD || P < 1 || P > sata::kMaxP)
+        return fail(SATA_ERR_UNSUPPORTED,
+                    "unsupported sizes d_K=%d d_V=%d P=%d (need 1..128, 1..128, 1..5)", d_K,
+                    d_V, P);
+    return SATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sata_last_error(void) { return g_err; }
+
+int64_t sata_feature_dim(int d_K, int P) {
+    if (d_K < 1 || d_K > sata::kMaxD || P < 1 || P > sata::kMaxP) return -1;
+    return sata::feature_dim(d_K, P);
+}
+
+int64_t sata_state_stride(int d_K, int P) {
+    if (d_K < 1 || d_K > sata::kMaxD || P < 1 || P > sata::kMaxP) return -1;
+    return sata::state_stride(d_K, P);
+}
+
+int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P) {
+    if (B < 1 || H < 1 || d_V < 1 || d_V > sata::kMaxD) return -1;
+    const int64_t Mp = sata_state_stride(d_K, P);
+    if (Mp < 0) return -1;
+    return 4LL * B * H * (d_V + 1) * Mp;
+}
+
+int sata_tables_build(int d_K, int P, sata_tables** out) {
+    clear_err();
+    if (!out) return fail(SATA_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (d_K < 1 || d_K > sata::kMaxD || P < 1 || P > sata::kMaxP)
+        return fail(SATA_ERR_UNSUPPORTED, "unsupported d_K=%d P=%d", d_K, P);
+    sata_tables* t = new (std::nothrow) sata_tables();
+    if (!t) return fail(SATA_ERR_OOM, "host allocation failed");
+    if (!sata::build_host_tables(d_K, P, t->h)) {
+        delete t;
+        return fail(SATA_ERR_ARG, "table construction failed for d_K=%d P=%d", d_K, P);
+    }
+    if (hipGetDevice(&t->device) != hipSuccess) {
+        delete t;
+        return fail(SATA_ERR_HIP, "hipGetDevice failed");
+    }
+    const size_t n = (size_t)t->h.M_pad;
+    if (hipMalloc(&t->d_fidx, n * 4) != hipSuccess || hipMalloc(&t->d_qw, n * 4) != hipSuccess) {
+        (void)hipGetLastError();
+        sata_tables_free(t);
+        return fail(SATA_ERR_OOM, "device allocation of the tables failed");
+    }
+    if (hipMemcpy(t->d_fidx, t->h.fidx.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(t->d_qw, t->h.qw.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess) {
+        sata_tables_free(t);
+        return fail(SATA_ERR_HIP, "copy of the tables to the device failed");
+    }
+    int rc = sata::build_mfma_tables(t->h, t->mfma);
+    if (rc != SATA_OK) {
+        sata_tables_free(t);
+        return fail(rc, "MFMA slice tables failed");
+    }
+    *out = t;
+    return SATA_OK;
+}
+
+int sata_tables_build_host(int d_K, int P, sata_tables** out) {
+    clear_err();
+    if (!out) return fail(SATA_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (d_K < 1 || d_K > sata::kMaxD || P < 1 || P > sata::kMaxP)
+        return fail(SATA_ERR_UNSUPPORTED, "unsupported d_K=%d P=%d", d_K, P);
+    sata_tables* t = new (std::nothrow) sata_tables();
+    if (!t) return fail(SATA_ERR_OOM, "host allocation failed");
+    if (!sata::build_host_tables(d_K, P, t->h)) {
+        delete t;
+        return fail(SATA_ERR_ARG, "table construction failed for d_K=%d P=%d", d_K, P);
+    }
+    t->device = -1;
+    *out = t;
+    return SATA_OK;
+}
+
+int sata_tables_get(const sata_tables* t, int p, const int32_t** M_p, const int32_t** C_p,
+                    int64_t* m_p) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (p < 0 || p >= t->h.P) return fail(SATA_ERR_ARG, "p=%d outside 0..%d", p, t->h.P - 1);
+    if (M_p) *M_p = t->h.Mp[p].empty() ? nullptr : t->h.Mp[p].data();
+    if (C_p) *C_p = t->h.Cp[p].data();
+    if (m_p) *m_p = t->h.m[p];
+    return SATA_OK;
+}
+
+void sata_tables_free(sata_tables* t) {
+    if (!t) return;
+    if (t->d_fidx) (void)hipFree(t->d_fidx);
+    if (t->d_qw) (void)hipFree(t->d_qw);
+    sata::free_mfma_tables(t->mfma);
+    if (t->ws) (void)hipFree(t->ws);
+    delete t;
+}
+
+int sata_set_workspace_limit(sata_tables* t, int64_t bytes) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (bytes < 0) return fail(SATA_ERR_ARG, "negative limit");
+    std::lock_guard<std::mutex> lock(t->mu);
+    t->ws_limit = bytes == 0 ? (16LL << 30) : bytes;
+    return SATA_OK;
+}
+
+int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void* v, float* y,
+                 float* state, int B, int H, int n, int d_K, int d_V, int P, int chunk,
+                 sata_dtype in_dtype, int flags, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!q || !k || !v || !y) return fail(SATA_ERR_ARG, "q, k, v and y must be non-NULL");
+    if (B < 1 || H < 1 || n < 1) return fail(SATA_ERR_ARG, "need B, H, n >= 1 (got %d %d %d)", B, H, n);
+    int rc = check_sizes(d_K, d_V, P);
+    if (rc) return rc;
+    if (d_K != t->h.d_K || P != t->h.P)
+        return fail(SATA_ERR_ARG, "handle built for d_K=%d P=%d, call has d_K=%d P=%d",
+                    t->h.d_K, t->h.P, d_K, P);
+    if (in_dtype != SATA_F32 && in_dtype != SATA_BF16)
+        return fail(SATA_ERR_ARG, "unknown input dtype %d", (int)in_dtype);
+    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 16, 32, 64 or 128 (got %d)", chunk);
+    if (flags & ~SATA_PREFILL_CONTINUE) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
+    const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0;
+    if (cont && !state) return fail(SATA_ERR_ARG, "SATA_PREFILL_CONTINUE needs a state buffer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
+        (state && !aligned16(state)))
+        return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (sata::finalize_lds_bytes(d_K, d_V, chunk) > 160 * 1024)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk=%d is too large for d_K=%d, d_V=%d", chunk,
+                    d_K, d_V);
+    if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    rc = check_device(t);
+    if (rc) return rc;
+
+    const bool bf16 = in_dtype == SATA_BF16;
+    const int BH = B * H, L = chunk, cols = d_V + 1;
+    const int nchunks = (int)(((int64_t)n + L - 1) / L);
+
+    sata::PrefillSegArgs a{};
+    a.q = q; a.k = k; a.v = v; a.y = y;
+    a.fidx = t->d_fidx;
+    a.qw = t->d_qw;
+    for (int p = 0; p < P; ++p) a.alpha.a[p] = (float)t->h.alpha[p];
+    a.M = t->h.M;
+    a.M_pad = t->h.M_pad;
+    a.BH = BH; a.n = n; a.d_K = d_K; a.d_V = d_V; a.P = P; a.L = L;
+    a.bf16 = bf16;
+
+    const bool use_mfma = sata::mfma_supported(t->mfma, bf16, d_K, d_V, P, L);
+    if (use_mfma) {
+        a.nslices = t->mfma.nslices;
+        a.slice_feats = t->mfma.slice_feats;
+        a.mfma_rows = t->mfma.d_rows;
+    } else {
+        a.slice_feats = sata::valu_slice_feats(d_K, d_V, L);
+        if (a.slice_feats == 0) return fail(SATA_ERR_UNSUPPORTED, "no VALU slice fits LDS");
+        a.nslices = (int)((t->h.M + a.slice_feats - 1) / a.slice_feats);
+        a.mfma_rows = nullptr;
+    }
+
+    std::lock_guard<std::mutex> lock(t->mu);
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t per_chunk = (int64_t)BH * a.nslices * L * cols * 4;
+    const int64_t state_b = (int64_t)BH * cols * t->h.M_pad * 4;
+    int64_t seg = nchunks;
+    if (per_chunk * seg > t->ws_limit) {
+        seg = (t->ws_limit - (state ? 0 : state_b)) / per_chunk;
+        if (seg < 1) seg = 1;
+    }
+    const int nseg = (int)((nchunks + seg - 1) / seg);
+    float* carrier = state;
+    size_t need = (size_t)(per_chunk * seg);
+    if (!state && nseg > 1) need += (size_t)state_b;
+    rc = ensure_ws(t, need, st);
+    if (rc) return rc;
+    a.partial = (float*)t->ws;
+    if (!carrier && nseg > 1) carrier = (float*)((char*)t->ws + per_chunk * seg);
+    a.state = carrier;
+
+    for (int s = 0; s < nseg; ++s) {
+        a.c_begin = (int)(s * seg);
+        a.c_end = (int)((s + 1) * seg < nchunks ? (s + 1) * seg : nchunks);
+        a.load_state = (s > 0 || cont) ? 1 : 0;
+        a.store_state = (s < nseg - 1 || state) ? 1 : 0;
+        hipError_t e = use_mfma ? sata::launch_scan_mfma(a, t->mfma, st)
+                                : sata::launch_scan_valu(a, st);
+        if (e != hipSuccess)
+            return fail(SATA_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+        e = sata::launch_finalize(a, st);
+        if (e != hipSuccess)
+            return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
+    }
+    return SATA_OK;
+}
+
+int sata_decode_step(const sata_tables* tc, float* state, const void* q, const void* k,
+                     const void* v, float* y, int B, int H, int d_K, int d_V, int P,
+                     sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!state || !q || !k || !v || !y)
+        return fail(SATA_ERR_ARG, "state, q, k, v and y must be non-NULL");
+    if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
+    int rc = check_sizes(d_K, d_V, P);
+    if (rc) return rc;
+    if (d_K != t->h.d_K || P != t->h.P)
+        return fail(SATA_ERR_ARG, "handle built for d_K=%d P=%d, call has d_K=%d P=%d",
+                    t->h.d_K, t->h.P, d_K, P);
+    if (in_dtype != SATA_F32 && in_dtype != SATA_BF16)
+        return fail(SATA_ERR_ARG, "unknown input dtype %d", (int)in_dtype);
+    if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+        return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    rc = check_device(t);
+    if (rc) return rc;
+
+    sata::DecodeArgs a{};
+    a.state = state; a.q = q; a.k = k; a.v = v; a.y = y;
+    a.fidx = t->d_fidx;
+    a.qw = t->d_qw;
+    a.M = t->h.M;
+    a.M_pad = t->h.M_pad;
+    a.BH = B * H; a.d_K = d_K; a.d_V = d_V; a.P = P;
+    a.nblk = sata::decode_blocks(t->h.M_pad);
+    a.bf16 = in_dtype == SATA_BF16;
+
+    std::lock_guard<std::mutex> lock(t->mu);
+    hipStream_t st = (hipStream_t)stream;
+    rc = ensure_ws(t, (size_t)a.BH * a.nblk * (d_V + 1) * 4, st);
+    if (rc) return rc;
+    a.partial = (float*)t->ws;
+    hipError_t e = sata::launch_decode(a, st);
+    if (e != hipSuccess) return fail(SATA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return SATA_OK;
+}
+
+}  // extern "C"

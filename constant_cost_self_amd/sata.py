@@ -1,0 +1,219 @@
+"""Thin ctypes binding of libsata (include/sata.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind
+the C ABI.  PyTorch supplies device memory and the stream.  The functions keep
+the C names; tensors are passed as torch tensors (their data pointers) and the
+stream defaults to torch's current stream.  If the built library is missing the
+first call raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libsata.so")
+
+SATA_F32 = 0
+SATA_BF16 = 1
+SATA_PREFILL_CONTINUE = 1
+SATA_OK = 0
+SATA_ERR_ARG = -1
+SATA_ERR_UNSUPPORTED = -2
+SATA_ERR_ALIGN = -3
+SATA_ERR_HIP = -4
+SATA_ERR_OOM = -5
+
+EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "sata_tables_free", "sata_feature_dim",
+            "sata_state_stride", "sata_state_bytes", "sata_prefill", "sata_decode_step",
+            "sata_last_error", "sata_set_workspace_limit")
+
+_lib = None
+
+
+class SataError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("sata error %d: %s" % (code, msg))
+        self.code = code
+
+
+def load():
+    """Load libsata.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsata.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m constant_cost_self_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.sata_tables_build.restype = i32
+    lib.sata_tables_build.argtypes = [i32, i32, ctypes.POINTER(vp)]
+    lib.sata_tables_build_host.restype = i32
+    lib.sata_tables_build_host.argtypes = [i32, i32, ctypes.POINTER(vp)]
+    lib.sata_tables_get.restype = i32
+    lib.sata_tables_get.argtypes = [vp, i32, ctypes.POINTER(ctypes.POINTER(ctypes.c_int32)),
+                                    ctypes.POINTER(ctypes.POINTER(ctypes.c_int32)),
+                                    ctypes.POINTER(i64)]
+    lib.sata_tables_free.restype = None
+    lib.sata_tables_free.argtypes = [vp]
+    lib.sata_feature_dim.restype = i64
+    lib.sata_feature_dim.argtypes = [i32, i32]
+    lib.sata_state_stride.restype = i64
+    lib.sata_state_stride.argtypes = [i32, i32]
+    lib.sata_state_bytes.restype = i64
+    lib.sata_state_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.sata_prefill.restype = i32
+    lib.sata_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                 i32, i32, vp]
+    lib.sata_decode_step.restype = i32
+    lib.sata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.sata_last_error.restype = ctypes.c_char_p
+    lib.sata_last_error.argtypes = []
+    lib.sata_set_workspace_limit.restype = i32
+    lib.sata_set_workspace_limit.argtypes = [vp, i64]
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().sata_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != SATA_OK:
+        raise SataError(rc, last_error())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _need(*tensors):
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and not t.is_contiguous():
+            raise ValueError("tensors passed to libsata must be contiguous")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SATA_F32
+    if t.dtype == torch.bfloat16:
+        return SATA_BF16
+    raise TypeError("inputs must be float32 or bfloat16, got %s" % t.dtype)
+
+
+# --------------------------------------------------------------------------
+# Size helpers
+# --------------------------------------------------------------------------
+
+def sata_feature_dim(d_K: int, P: int) -> int:
+    return int(load().sata_feature_dim(d_K, P))
+
+
+def sata_state_stride(d_K: int, P: int) -> int:
+    return int(load().sata_state_stride(d_K, P))
+
+
+def sata_state_bytes(B: int, H: int, d_K: int, d_V: int, P: int) -> int:
+    return int(load().sata_state_bytes(B, H, d_K, d_V, P))
+
+
+# --------------------------------------------------------------------------
+# Tables
+# --------------------------------------------------------------------------
+
+class Tables:
+    """Owner of a sata_tables handle (freed on close() or garbage collection)."""
+
+    def __init__(self, handle: int, d_K: int, P: int):
+        self.handle = handle
+        self.d_K = d_K
+        self.P = P
+
+    def get(self, p: int):
+        """Host copies of (M_p [m_p, p] int32, C_p [m_p] int32) as numpy arrays."""
+        import numpy as np
+        M = ctypes.POINTER(ctypes.c_int32)()
+        C = ctypes.POINTER(ctypes.c_int32)()
+        m = ctypes.c_int64()
+        _check(load().sata_tables_get(self.handle, p, ctypes.byref(M), ctypes.byref(C),
+                                      ctypes.byref(m)))
+        mp = m.value
+        Mnp = (np.ctypeslib.as_array(M, shape=(mp * p,)).reshape(mp, p).copy()
+               if p > 0 else np.zeros((mp, 0), dtype=np.int32))
+        Cnp = np.ctypeslib.as_array(C, shape=(mp,)).copy()
+        return Mnp, Cnp
+
+    def set_workspace_limit(self, nbytes: int):
+        _check(load().sata_set_workspace_limit(self.handle, nbytes))
+
+    def close(self):
+        if self.handle:
+            load().sata_tables_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sata_tables_build(d_K: int, P: int) -> Tables:
+    h = ctypes.c_void_p()
+    _check(load().sata_tables_build(d_K, P, ctypes.byref(h)))
+    return Tables(h.value, d_K, P)
+
+
+def sata_tables_build_host(d_K: int, P: int) -> Tables:
+    """Host-only handle (no GPU needed): table inspection and argument checks."""
+    h = ctypes.c_void_p()
+    _check(load().sata_tables_build_host(d_K, P, ctypes.byref(h)))
+    return Tables(h.value, d_K, P)
+
+
+# --------------------------------------------------------------------------
+# Hot path
+# --------------------------------------------------------------------------
+
+def sata_prefill(t: Tables, q, k, v, y, state=None, *, chunk: int = 64,
+                 continue_state: bool = False, stream=None):
+    """Chunked causal prefill.  q, k: [B, H, n, d_K]; v: [B, H, n, d_V] (fp32 or
+    bf16, contiguous, on the GPU); y: fp32 [B, H, n, d_V]; state: optional fp32
+    [B, H, d_V + 1, M_pad]."""
+    _need(q, k, v, y, state)
+    B, H, n, d_K = q.shape
+    d_V = v.shape[-1]
+    flags = SATA_PREFILL_CONTINUE if continue_state else 0
+    _check(load().sata_prefill(t.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(state),
+                               B, H, n, d_K, d_V, t.P, chunk, _dtype_code(q), flags,
+                               _stream(stream)))
+
+
+def sata_decode_step(t: Tables, state, q, k, v, y, *, stream=None):
+    """One decode step.  q, k: [B, H, d_K]; v: [B, H, d_V]; y: fp32 [B, H, d_V];
+    state: fp32 [B, H, d_V + 1, M_pad], updated in place."""
+    _need(state, q, k, v, y)
+    B, H, d_K = q.shape
+    d_V = v.shape[-1]
+    _check(load().sata_decode_step(t.handle, _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(y),
+                                   B, H, d_K, d_V, t.P, _dtype_code(q), _stream(stream)))
+
+
+def sata_last_error() -> str:
+    return last_error()

@@ -1,0 +1,165 @@
+/*
+ * sata.h -- C ABI of the SATA causal self-attention hot path on MI355X (gfx950).
+ *
+ * Method: Heinsen & Kozachkov, "Self-Attention at Constant Cost per Token via
+ * Symmetry-Aware Taylor Approximation" (arXiv:2602.00294), as described on the
+ * blog.hotdry.top post "self-attention-constant-cost-taylor-approximation"
+ * ([TA], cited by section) and its companion "constant-cost-attention-hardware-
+ * optimization" ([HW]).
+ *
+ * What is computed.  For one head with queries q_t, keys k_t (d_K) and values
+ * v_t (d_V), the exponential kernel exp(q.k / c), c = sqrt(d_K), is truncated to
+ * its first P Taylor terms ([TA] "Feature maps and linear attention"):
+ *     w(q, k) = sum_{p=0}^{P-1} alpha_p (q.k)^p,   alpha_p = 1 / (p! c^p),
+ * and causal attention with it is
+ *     y_T = sum_{t<=T} w(q_T, k_t) v_t  /  sum_{t<=T} w(q_T, k_t).
+ * Each (q.k)^p is written over the unique monomials of the symmetric tensor
+ * q^{(x)p}: index tuples i1 <= ... <= ip (table M_p, m_p = binom(d_K+p-1, p)
+ * rows, [TA] "The mathematical breakthrough of the Taylor approximation"), with
+ * C_p the number of times each monomial occurs in the full expansion ([TA]
+ * "Feature maps and linear attention").  With phi_p(x)[r] = prod_{i in M_p[r]} x_i,
+ *     (q.k)^p = sum_r C_p[r] phi_p(q)[r] phi_p(k)[r],
+ * so attention becomes a scan over the fixed-size state ([TA] "Feature maps ...",
+ * "Hidden-state size and compute analysis")
+ *     S = sum_t phi(k_t) [v_t | 1]^T        ((d_V + 1) x M entries, M = sum_p m_p),
+ * read out by y_T = (q~_T^T S)[0:d_V] / (q~_T^T S)[d_V], q~[f] = alpha_p C_p[f] phi_p(q_T)[f].
+ *
+ * Conventions used by every entry point.
+ *   Feature order.  f runs over the concatenation p = 0, 1, ..., P-1 of the rows
+ *     of M_p, each M_p in lexicographic order of its (non-decreasing) tuples.
+ *     M = binom(d_K + P - 1, P - 1).  M_pad = M rounded up to a multiple of 64.
+ *   Tensors (row-major, contiguous, device memory, 16-byte aligned):
+ *     prefill  q, k : [B][H][n][d_K]     v : [B][H][n][d_V]     y : [B][H][n][d_V]
+ *     decode   q, k : [B][H][d_K]        v : [B][H][d_V]        y : [B][H][d_V]
+ *     state    fp32 [B][H][d_V + 1][M_pad]: entry [b][h][j][f] is S[f][j] of
+ *              head (b, h); column j = d_V is the normaliser Z = sum_t phi(k_t).
+ *              The state is unweighted (no alpha_p, no C_p).  Entries f >= M are
+ *              zero and stay zero.  An all-zero state is the empty prefix.
+ *   Input dtype.  q, k, v are fp32 (SATA_F32) or bfloat16 (SATA_BF16); y and the
+ *     state are always fp32.
+ *   Causality.  Row T attends to t <= T (inclusive); the decode step adds the new
+ *     token to the state before reading it out.
+ *   Streams.  Work is enqueued on `stream` (a hipStream_t, NULL = default stream)
+ *     and returns without waiting; no call synchronises the host.
+ *   Ownership.  The caller owns q, k, v, y and the state.  The library owns the
+ *     tables handle (host and device copies) and a scratch workspace held by the
+ *     handle, grown on demand and released by sata_tables_free.  Calls that share
+ *     one handle must not overlap in time (issue them on one stream, or use one
+ *     handle per stream): they share that workspace.
+ *   Errors.  Every int-returning call returns SATA_OK (0) or a negative code and
+ *     never aborts; sata_last_error() gives the calling thread's last message.
+ *     Arguments are checked before anything is enqueued, so on an argument error
+ *     no output and no state is touched.  A failed HIP launch returns SATA_ERR_HIP.
+ *   Supported sizes: 1 <= d_K <= 128, 1 <= d_V <= 128, 1 <= P <= 5,
+ *     chunk in {16, 32, 64, 128}, n >= 1, B, H >= 1.  n need not be a multiple of
+ *     chunk (the last chunk is masked).
+ */
+#ifndef SATA_H
+#define SATA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sata_tables sata_tables;
+
+typedef enum { SATA_F32 = 0, SATA_BF16 = 1 } sata_dtype;
+
+enum {
+    SATA_OK = 0,
+    SATA_ERR_ARG = -1,          /* null pointer, bad size, handle mismatch        */
+    SATA_ERR_UNSUPPORTED = -2,  /* size outside the supported set                  */
+    SATA_ERR_ALIGN = -3,        /* a tensor pointer is not 16-byte aligned          */
+    SATA_ERR_HIP = -4,          /* a HIP call or kernel launch failed              */
+    SATA_ERR_OOM = -5           /* device or host allocation failed                */
+};
+
+/* Prefill flag: `state` holds the prefix on entry and is advanced in place. */
+#define SATA_PREFILL_CONTINUE 1
+
+/*
+ * Build the tables M_p, C_p (p = 0..P-1) for key dimension d_K on the host, plus
+ * the device tables the kernels read, on the current HIP device.  The rows of
+ * M_p are the non-decreasing index tuples in lexicographic order; C_p[r] =
+ * p! / prod_i (count of i in row r)!  ([TA] "The mathematical breakthrough of the
+ * Taylor approximation", "Feature maps and linear attention").
+ * *out receives a new handle (free with sata_tables_free).  The handle is used on
+ * the device that was current when it was built.
+ */
+int sata_tables_build(int d_K, int P, sata_tables **out);
+
+/*
+ * Host-only handle: builds the same host tables as sata_tables_build but no
+ * device copies, so it needs no GPU.  It serves sata_tables_get (inspection,
+ * tests); sata_prefill and sata_decode_step reject it with SATA_ERR_ARG after
+ * checking their other arguments.
+ */
+int sata_tables_build_host(int d_K, int P, sata_tables **out);
+
+/*
+ * Host views of M_p ([m_p][p] int32, 0-based indices) and C_p ([m_p] int32) for
+ * 0 <= p < P.  The pointers stay valid until sata_tables_free.  For p = 0, M_0 is
+ * an empty row (*M_p may be NULL) and C_0 = {1}.
+ */
+int sata_tables_get(const sata_tables *t, int p, const int32_t **M_p,
+                    const int32_t **C_p, int64_t *m_p);
+
+/* Release a handle, its device tables and its workspace.  NULL-safe. */
+void sata_tables_free(sata_tables *t);
+
+/* M = binom(d_K + P - 1, P - 1) ([TA] "Hidden-state size and compute analysis"),
+ * or -1 outside the supported sizes. */
+int64_t sata_feature_dim(int d_K, int P);
+
+/* M_pad: M rounded up to a multiple of 64 (the feature stride of the state). */
+int64_t sata_state_stride(int d_K, int P);
+
+/* Bytes of the fp32 state of B x H heads: 4 B H (d_V + 1) M_pad. */
+int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
+
+/*
+ * Causal prefill of n tokens per head: y for every row, by a chunked scan
+ * ([TA] "Feature maps and linear attention": the state recurrence, evaluated by
+ * chunks).  Within a chunk of `chunk` tokens the weights w(q_T, k_t) are formed
+ * directly from q.k; earlier chunks enter through the state.
+ *
+ * t      handle built for (d_K, P) on the current device
+ * q,k,v  inputs, in_dtype, layouts above
+ * y      fp32 output [B][H][n][d_V]
+ * state  nullable.  If non-NULL the state after the n tokens is written to it.
+ *        With flags & SATA_PREFILL_CONTINUE it must be non-NULL and on entry holds
+ *        the state of a prefix that precedes these n tokens; y then attends to
+ *        that prefix too.  Without the flag the prefix is empty.
+ * stream hipStream_t (NULL = default stream)
+ */
+int sata_prefill(const sata_tables *t, const void *q, const void *k, const void *v,
+                 float *y, float *state, int B, int H, int n, int d_K, int d_V,
+                 int P, int chunk, sata_dtype in_dtype, int flags, void *stream);
+
+/*
+ * One decode step for B x H heads ([TA] "Feature maps and linear attention":
+ * S_T = S_{T-1} + phi(k_T) [v_T | 1]^T, then the readout of q_T).  The state is
+ * read, updated with the new token and written back in place; y receives the
+ * readout of q against the updated state.
+ */
+int sata_decode_step(const sata_tables *t, float *state, const void *q,
+                     const void *k, const void *v, float *y, int B, int H,
+                     int d_K, int d_V, int P, sata_dtype in_dtype, void *stream);
+
+/* The calling thread's last error message ("" if none). */
+const char *sata_last_error(void);
+
+/*
+ * Optional: cap (bytes) on the workspace a handle may hold; prefill splits the
+ * sequence into segments of whole chunks to stay under it.  0 restores the
+ * default (16 GiB).
+ */
+int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATA_H */

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars (written in each test): tables bit-exact; y within 2e-2 for bf16 inputs
+with an fp32 state and 1e-5 for the fp32 path, as max over rows of
+max_j |y - y_ref| / max_j |y_ref|; the final state by the same bound per column
+(normalised by the column's max |S_ref|).
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import (TOL_BF16, TOL_F32, inputs, max_row_err, new_state, oracle, prefill,
+                         say, sata, state_col_err, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _tables(d_K, P):
+    return sata.sata_tables_build(d_K, P)
+
+
+# --------------------------------------------------------------------------
+# Tiny: d = 8, P = 4, fp32, chunk 16
+# --------------------------------------------------------------------------
+
+def test_tiny_prefill_y_and_state(torch_cuda):
+    w = inputs.TINY
+    say("tiny prefill n=%d chunk=%d fp32" % (w.n, w.chunk))
+    x = inputs.prefill_inputs(w)
+    q, k, v = upload(x, w.dtype)
+    t = _tables(w.d_K, w.P)
+    S = new_state(1, 1, w.d_K, w.d_V, w.P)
+    y = prefill(t, q, k, v, w.chunk, S)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], w.P)
+    err = max_row_err(y[0, 0].cpu().numpy(), ref)
+    say("  y err %.3e" % err)
+    assert err <= TOL_F32
+    _, S_ref = oracle.feature_form(None, x["k"][0, 0], x["v"][0, 0], w.P, want_y=False)
+    M = S_ref.shape[1]
+    S_gpu = S[0, 0].cpu().numpy()
+    assert state_col_err(S_gpu[:, :M], S_ref) <= TOL_F32
+    assert np.all(S_gpu[:, M:] == 0.0), "padding of the state must stay zero"
+    assert S_gpu[w.d_V, 0] == w.n          # Z of the p = 0 feature counts the tokens
+    t.close()
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+def test_chunk_invariance_ragged(torch_cuda, chunk):
+    w = inputs.TINY
+    n = 300                                  # not a multiple of any chunk size
+    say("tiny ragged n=%d chunk=%d" % (n, chunk))
+    x = inputs.prefill_inputs(w, n=n, seed=3)
+    q, k, v = upload(x, "f32")
+    t = _tables(w.d_K, w.P)
+    y = prefill(t, q, k, v, chunk)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], w.P)
+    assert max_row_err(y[0, 0].cpu().numpy(), ref) <= TOL_F32
+    t.close()
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 47])
+def test_short_sequences(torch_cuda, n):
+    w = inputs.TINY
+    say("tiny short n=%d" % n)
+    x = inputs.prefill_inputs(w, n=n, B=2, H=3, seed=4)
+    q, k, v = upload(x, "f32")
+    t = _tables(w.d_K, w.P)
+    y = prefill(t, q, k, v, 16)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], w.P)
+    assert max_row_err(y.cpu().numpy(), ref) <= TOL_F32
+    if n == 1:
+        assert np.allclose(y.cpu().numpy(), x["v"], rtol=1e-6, atol=1e-6)
+    t.close()
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5])
+def test_other_term_counts(torch_cuda, P):
+    say("d=8 P=%d prefill" % P)
+    w = inputs.TINY
+    x = inputs.prefill_inputs(w, n=130, B=1, H=2, seed=5)
+    q, k, v = upload(x, "f32")
+    t = _tables(8, P)
+    y = prefill(t, q, k, v, 32)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], P)
+    assert max_row_err(y.cpu().numpy(), ref) <= TOL_F32
+    if P == 1:
+        cm = np.cumsum(x["v"], axis=2) / np.arange(1, 131)[None, None, :, None]
+        assert np.allclose(y.cpu().numpy(), cm, rtol=1e-5, atol=1e-6)
+    t.close()
+
+
+def test_unequal_key_value_dims(torch_cuda):
+    say("d_K=16 d_V=5 prefill and decode")
+    x = inputs.draw((1, 2, 90, 16), (1, 2, 90, 5), "f32", 0.6, 1.0, 6)
+    q, k, v = upload(x, "f32")
+    t = _tables(16, 4)
+    S = new_state(1, 2, 16, 5, 4)
+    y = prefill(t, q, k, v, 32, S)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    assert max_row_err(y.cpu().numpy(), ref) <= TOL_F32
+    t.close()
+
+
+# --------------------------------------------------------------------------
+# Decode: state recurrence one token at a time
+# --------------------------------------------------------------------------
+
+def test_decode_from_empty_state_tiny(torch_cuda):
+    w = inputs.TINY
+    n = 64
+    say("tiny decode from empty state, %d steps" % n)
+    x = inputs.prefill_inputs(w, n=n, B=2, H=2, seed=7)
+    t = _tables(w.d_K, w.P)
+    S = new_state(2, 2, w.d_K, w.d_V, w.P)
+    ys = []
+    torch = torch_cuda
+    for T in range(n):
+        q = torch.from_numpy(np.ascontiguousarray(x["q"][:, :, T])).cuda()
+        k = torch.from_numpy(np.ascontiguousarray(x["k"][:, :, T])).cuda()
+        v = torch.from_numpy(np.ascontiguousarray(x["v"][:, :, T])).cuda()
+        y = torch.empty((2, 2, w.d_V), device="cuda:0")
+        sata.sata_decode_step(t, S, q, k, v, y)
+        ys.append(y.cpu().numpy())
+    y = np.stack(ys, axis=2)
+    ref = oracle.direct(x["q"], x["k"], x["v"], w.P)
+    assert max_row_err(y, ref) <= TOL_F32
+    _, S_ref = oracle.feature_form(None, x["k"][1, 0], x["v"][1, 0], w.P, want_y=False)
+    M = S_ref.shape[1]
+    Sg = S[1, 0].cpu().numpy()
+    assert state_col_err(Sg[:, :M], S_ref) <= TOL_F32
+    assert np.all(Sg[:, M:] == 0.0)
+    t.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_then_decode_equals_longer_prefill(torch_cuda, dtype):
+    torch = torch_cuda
+    d, P, n1, steps = 16, 4, 77, 9
+    say("prefill(%d) + %d decode steps, d=%d %s" % (n1, steps, d, dtype))
+    x = inputs.draw((2, 3, n1 + steps, d), (2, 3, n1 + steps, d), dtype, 0.5, 1.0, 8)
+    t = _tables(d, P)
+    q, k, v = upload(x, dtype)
+    S = new_state(2, 3, d, d, P)
+    prefill(t, q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(),
+            32, S)
+    ys = []
+    for T in range(n1, n1 + steps):
+        y = torch.empty((2, 3, d), device="cuda:0")
+        sata.sata_decode_step(t, S, q[:, :, T].contiguous(), k[:, :, T].contiguous(),
+                              v[:, :, T].contiguous(), y)
+        ys.append(y.cpu().numpy())
+    S2 = new_state(2, 3, d, d, P)
+    yfull = prefill(t, q, k, v, 32, S2)
+    torch.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], P)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert max_row_err(np.stack(ys, axis=2), ref[:, :, n1:]) <= tol
+    assert max_row_err(yfull.cpu().numpy(), ref) <= tol
+    M = sata.sata_feature_dim(d, P)
+    Sa = S.cpu().numpy()[..., :M]
+    Sb = S2.cpu().numpy()[..., :M]
+    rel = np.max(np.abs(Sa - Sb)) / np.max(np.abs(Sb))
+    assert rel <= 1e-5
+    t.close()
+
+
+def test_prefill_continue_equals_one_prefill(torch_cuda):
+    say("prefill(n1) + prefill(n2, continue) == prefill(n1 + n2)")
+    d, P, n1, n2 = 8, 4, 96, 70
+    x = inputs.draw((1, 2, n1 + n2, d), (1, 2, n1 + n2, d), "f32", 1.0, 1.0, 9)
+    t = _tables(d, P)
+    q, k, v = upload(x, "f32")
+    S = new_state(1, 2, d, d, P)
+    prefill(t, q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(),
+            16, S)
+    y2 = prefill(t, q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(),
+                 v[:, :, n1:].contiguous(), 16, S, continue_state=True)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], P)
+    assert max_row_err(y2.cpu().numpy(), ref[:, :, n1:]) <= TOL_F32
+    _, S_ref = oracle.feature_form(None, x["k"][0, 1], x["v"][0, 1], P, want_y=False)
+    M = S_ref.shape[1]
+    assert state_col_err(S[0, 1].cpu().numpy()[:, :M], S_ref) <= TOL_F32
+    t.close()
+
+
+def test_segmented_prefill_is_bit_identical(torch_cuda):
+    """A workspace cap that forces many segments changes nothing in the result."""
+    say("segmented prefill vs one segment")
+    d, P, n = 8, 4, 500
+    x = inputs.draw((2, 2, n, d), (2, 2, n, d), "f32", 1.0, 1.0, 10)
+    q, k, v = upload(x, "f32")
+    t = _tables(d, P)
+    S1 = new_state(2, 2, d, d, P)
+    y1 = prefill(t, q, k, v, 16, S1)
+    t.set_workspace_limit(64 * 1024)
+    y2 = prefill(t, q, k, v, 16)            # no caller state: the library carries it
+    S3 = new_state(2, 2, d, d, P)
+    y3 = prefill(t, q, k, v, 16, S3)
+    torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(y1, y2) and torch_cuda.equal(y1, y3)
+    assert torch_cuda.equal(S1, S3)
+    t.close()
+
+
+# --------------------------------------------------------------------------
+# d = 64, P = 4 (the Mid workload: B=1, H=8, n=4096)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mid_parity(torch_cuda, dtype):
+    w = inputs.MID
+    say("mid prefill B=%d H=%d n=%d d=%d %s" % (w.B, w.H, w.n, w.d_K, dtype))
+    x = inputs.prefill_inputs(w)
+    q, k, v = upload(x, dtype)
+    t = _tables(w.d_K, w.P)
+    S = new_state(w.B, w.H, w.d_K, w.d_V, w.P)
+    y = prefill(t, q, k, v, w.chunk, S)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], w.P)
+    err = max_row_err(y.cpu().numpy(), ref)
+    say("  y err %.3e" % err)
+    assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    # final state of head (0, 3) against the literal feature sum
+    _, S_ref = oracle.feature_form(None, x["k"][0, 3], x["v"][0, 3], w.P, want_y=False)
+    M = S_ref.shape[1]
+    Sg = S[0, 3].cpu().numpy()
+    serr = state_col_err(Sg[:, :M], S_ref)
+    say("  state err %.3e" % serr)
+    assert serr <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    assert np.all(Sg[:, M:] == 0.0)
+    assert Sg[w.d_V, 0] == w.n
+    t.close()
