@@ -1,0 +1,250 @@
+"""Benchmark of the SATA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|mid|wide]
+
+One step = one chunked prefill (tables already built) of the workload with the
+final state written.  value = prefill tokens/s (B*n/t).  In the same run the
+batched decode step (16 sequences x 32 heads, d=64, P=4, fp32 states prefilled
+with 1024 tokens) is timed over 256 steps and reported as state GB/s.
+
+Rooflines come from HIP events recorded by libsata around each kernel launch on
+its own stream: achieved = algorithmic work per launch / mean launch time.
+  prefill scan: flops = B H n (4 d_V + 2 (P d_K + 1)/(d_K + 1) + 2) binom(d_K+P-1, P-1)
+                (the forward FLOPs/token closed form of the method), peak = bf16 MFMA
+                2.5 PFLOP/s.
+  decode:       bytes = 8 (d_V + 1) M per head (fp32 state read + write), peak 8 TB/s.
+cpu_baseline: the fp64 oracle's fixed-size-state form, timed on the host's cores
+on a bounded sample (one head, the first --cpu-tokens tokens).
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops_per_token(d_K, d_V, P):
+    return (4 * d_V + 2 * (P * d_K + 1) / (d_K + 1) + 2) * math.comb(d_K + P - 1, P - 1)
+
+
+def traffic_from_profiles(kernel_key):
+    """Measured HBM bytes per launch from profiles/traffic.json, if the kernel's
+    source has not changed since the counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def to_dev(a, dtype):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def bench_prefill(w, steps, warmup):
+    import torch
+    from constant_cost_self_amd import inputs, sata
+
+    log("prefill %s: generating inputs B=%d H=%d n=%d d=%d" % (w.name, w.B, w.H, w.n, w.d_K))
+    x = inputs.prefill_inputs(w)
+    q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
+    del x
+    t = sata.sata_tables_build(w.d_K, w.P)
+    Mp = sata.sata_state_stride(w.d_K, w.P)
+    y = torch.empty((w.B, w.H, w.n, w.d_V), device="cuda:0", dtype=torch.float32)
+    state = torch.empty((w.B, w.H, w.d_V + 1, Mp), device="cuda:0", dtype=torch.float32)
+    t.set_timing(True)
+    for i in range(warmup):
+        sata.sata_prefill(t, q, k, v, y, state, chunk=w.chunk)
+        log("  warmup %d done" % i)
+    torch.cuda.synchronize()
+    t.read_timing()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sata.sata_prefill(t, q, k, v, y, state, chunk=w.chunk)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tim = t.read_timing()
+    log("  timed %d steps: %.3f s; kernels %s" % (steps, wall, tim))
+    t.close()
+    return wall, tim
+
+
+def bench_decode(steps, warmup, prefill_chunk=64):
+    import torch
+    from constant_cost_self_amd import inputs, sata
+
+    w = inputs.DECODE
+    log("decode: prefilling %d tokens for %dx%d heads" % (w.n, w.B, w.H))
+    x = inputs.prefill_inputs(w)
+    q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
+    t = sata.sata_tables_build(w.d_K, w.P)
+    Mp = sata.sata_state_stride(w.d_K, w.P)
+    state = torch.zeros((w.B, w.H, w.d_V + 1, Mp), device="cuda:0", dtype=torch.float32)
+    y = torch.empty((w.B, w.H, w.n, w.d_V), device="cuda:0", dtype=torch.float32)
+    sata.sata_prefill(t, q, k, v, y, state, chunk=prefill_chunk)
+    del q, k, v, y, x
+    s = inputs.decode_inputs(w, warmup + steps, seed=1)
+    qs, ks, vs = (to_dev(s[c], w.dtype) for c in ("q", "k", "v"))
+    yd = torch.empty((w.B, w.H, w.d_V), device="cuda:0", dtype=torch.float32)
+    torch.cuda.synchronize()
+    t.set_timing(True)
+    for i in range(warmup):
+        sata.sata_decode_step(t, state, qs[i], ks[i], vs[i], yd)
+    torch.cuda.synchronize()
+    t.read_timing()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        sata.sata_decode_step(t, state, qs[i], ks[i], vs[i], yd)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tim = t.read_timing()
+    log("  decode %d steps: %.3f s; kernels %s" % (steps, wall, tim))
+    t.close()
+    M = math.comb(w.d_K + w.P - 1, w.P - 1)
+    bytes_per_step = 8.0 * (w.d_V + 1) * M * w.B * w.H
+    return wall, tim, bytes_per_step, w
+
+
+def cpu_baseline(w, ntok):
+    """The oracle's fixed-size-state form on head (0, 0), first ntok tokens."""
+    import oracle
+    from constant_cost_self_amd import inputs
+
+    x = inputs.prefill_inputs(w, n=ntok, B=1, H=1)
+    q, k, v = x["q"][0, 0], x["k"][0, 0], x["v"][0, 0]
+    oracle.feature_form(q[:4], k[:4], v[:4], w.P)         # load + warm the library
+    t0 = time.perf_counter()
+    oracle.feature_form(q, k, v, w.P)
+    dt = time.perf_counter() - t0
+    heads_per_token = w.H            # a token of the workload spans all H heads of a batch row
+    return {"value": ntok / dt / heads_per_token, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "fp64 oracle, fixed-size-state form (state update + readout per token), "
+                      "head (0,0) of the %s workload, first %d tokens, %.1f s; scaled to tokens "
+                      "of all %d heads" % (w.name, ntok, dt, w.H),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long", choices=["long", "mid", "wide"])
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the path is single-GPU (heads shard across GPUs "
+              "with no communication, so N GPUs run N independent copies); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from constant_cost_self_amd import inputs, sata
+
+    sata.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = inputs.WORKLOADS[args.workload]
+
+    wall, tim = bench_prefill(w, args.steps, args.warmup)
+    tokens = w.B * w.n
+    ms_per_step = wall / args.steps * 1e3
+    F = flops_per_token(w.d_K, w.d_V, w.P)
+    scan_ms, scan_n = tim["scan"]
+    alg_flops_total = F * w.B * w.H * w.n * args.steps
+    scan_tflops = alg_flops_total / scan_n / (scan_ms / scan_n * 1e-3) / 1e12
+    step_tflops = alg_flops_total / wall / 1e12
+    traffic = traffic_from_profiles("prefill_scan_" + w.name)
+    out = {
+        "metric": "prefill tokens/s (d=64,P=4) + decode state GB/s; % of MFMA/HBM peak",
+        "value": tokens / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded i.i.d. Gaussian q,k,v; no dataset, no weights)",
+        "config": {"workload": "%s prefill: B=%d H=%d n=%d d_K=%d d_V=%d P=%d chunk=%d %s inputs, "
+                               "fp32 state" % (w.name, w.B, w.H, w.n, w.d_K, w.d_V, w.P, w.chunk,
+                                                w.dtype),
+                   "B": w.B, "H": w.H, "n": w.n, "d_K": w.d_K, "d_V": w.d_V, "P": w.P,
+                   "chunk": w.chunk},
+        "roofline": {"bound": "mfma", "achieved": scan_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": scan_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic, "kernel": "prefill scan",
+                     "launches": scan_n, "ms_per_launch": scan_ms / scan_n,
+                     "algorithmic_flops_per_launch": alg_flops_total / scan_n},
+        "prefill_step": {"tflops": step_tflops, "frac_mfma": step_tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "token_heads_per_s": w.B * w.H * w.n / (wall / args.steps),
+                         "kernels_ms_per_step": {k: v[0] / args.steps for k, v in tim.items()}},
+    }
+
+    if not args.no_decode:
+        dwall, dtim, dbytes, dw = bench_decode(args.decode_steps, args.decode_warmup)
+        dk_ms, dk_n = dtim["decode"]
+        kern_gbs = dbytes / (dk_ms / dk_n * 1e-3) / 1e9
+        step_gbs = dbytes * args.decode_steps / dwall / 1e9
+        out["decode"] = {
+            "workload": "decode step: %d sequences x %d heads, d_K=d_V=%d, P=%d, fp32 states "
+                        "(%.3f GB) prefilled with %d tokens, %s q,k,v" %
+                        (dw.B, dw.H, dw.d_K, dw.P, dbytes / 2e9, dw.n, dw.dtype),
+            "value": step_gbs, "unit": "GB/s", "steps": args.decode_steps,
+            "ms_per_step": dwall / args.decode_steps * 1e3,
+            "seq_tokens_per_s": dw.B * args.decode_steps / dwall,
+            "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": kern_gbs / HBM_PEAK_GBS,
+                         "traffic": traffic_from_profiles("decode_step"),
+                         "kernel": "decode state read-modify-write",
+                         "ms_per_launch": dk_ms / dk_n,
+                         "algorithmic_bytes_per_launch": dbytes},
+            "reduce_ms_per_step": dtim["decode_reduce"][0] / max(dtim["decode_reduce"][1], 1),
+        }
+
+    if not args.no_cpu:
+        log("cpu baseline: oracle on %d tokens" % args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -134,10 +134,6 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
                        static_cast<const typename In::T*>(a.k),
                        static_cast<const typename In::T*>(a.v), a.fidx, a.qw, a.partial, a.M,
                        a.M_pad, a.d_K, a.d_V, a.P, a.nblk);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_finalize_kernel, dim3(a.BH), dim3(kThreads), 0, st, a.partial,
-                       a.y, a.d_V, a.nblk);
     return hipGetLastError();
 }
 
@@ -157,6 +153,12 @@ int decode_blocks(int64_t M_pad) { return (int)((M_pad + kDecFeatPerBlock - 1) /
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     return a.bf16 ? launch_decode_in<InBF16>(a, st) : launch_decode_in<InF32>(a, st);
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3(a.BH), dim3(kThreads), 0, st, a.partial,
+                       a.y, a.d_V, a.nblk);
+    return hipGetLastError();
 }
 
 }  // namespace sata

@@ -24,7 +24,8 @@ struct DecodeArgs {
 
 // Number of feature blocks per head of the decode kernel.
 int decode_blocks(int64_t M_pad);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);         // state RMW + partials
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);  // partials -> y
 
 // One segment [c_begin, c_end) of chunks of a chunked prefill.
 struct PrefillSegArgs {

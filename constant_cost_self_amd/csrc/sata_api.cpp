@@ -17,14 +17,70 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "../../include/sata.h"
 #include "launch.h"
 #include "scan_mfma.h"
 #include "tables.h"
 
+// Per-handle kernel timer: HIP event pairs recorded around launches on the
+// launch stream, resolved only by sata_read_timing.
+struct KernelTimer {
+    bool enabled = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[SATA_NUM_KERNELS];
+    std::vector<hipEvent_t> pool;
+
+    hipEvent_t take() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    // Returns the start event (or nullptr when timing is off or an event failed).
+    hipEvent_t begin(hipStream_t st) {
+        if (!enabled) return nullptr;
+        hipEvent_t e = take();
+        if (e && hipEventRecord(e, st) != hipSuccess) {
+            pool.push_back(e);
+            return nullptr;
+        }
+        return e;
+    }
+    void end(int kind, hipEvent_t start, hipStream_t st) {
+        if (!start) return;
+        hipEvent_t e = take();
+        if (!e || hipEventRecord(e, st) != hipSuccess) {
+            pool.push_back(start);
+            if (e) pool.push_back(e);
+            return;
+        }
+        pending[kind].emplace_back(start, e);
+    }
+    void recycle() {
+        for (auto& v : pending) {
+            for (auto& pr : v) {
+                pool.push_back(pr.first);
+                pool.push_back(pr.second);
+            }
+            v.clear();
+        }
+    }
+    void destroy() {
+        recycle();
+        for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+        pool.clear();
+    }
+};
+
 struct sata_tables {
     sata::HostTables h;
+    KernelTimer timer;
     int device = -1;
     uint32_t* d_fidx = nullptr;
     float* d_qw = nullptr;
@@ -183,7 +239,40 @@ void sata_tables_free(sata_tables* t) {
     if (t->d_qw) (void)hipFree(t->d_qw);
     sata::free_mfma_tables(t->mfma);
     if (t->ws) (void)hipFree(t->ws);
+    t->timer.destroy();
     delete t;
+}
+
+int sata_set_timing(sata_tables* t, int enable) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    std::lock_guard<std::mutex> lock(t->mu);
+    t->timer.recycle();
+    t->timer.enabled = enable != 0;
+    return SATA_OK;
+}
+
+int sata_read_timing(sata_tables* t, double* ms, int64_t* count) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    std::lock_guard<std::mutex> lock(t->mu);
+    int rc = SATA_OK;
+    for (int k = 0; k < SATA_NUM_KERNELS; ++k) {
+        double sum = 0.0;
+        for (auto& pr : t->timer.pending[k]) {
+            float e_ms = 0.0f;
+            if (hipEventSynchronize(pr.second) != hipSuccess ||
+                hipEventElapsedTime(&e_ms, pr.first, pr.second) != hipSuccess) {
+                rc = fail(SATA_ERR_HIP, "reading a timing event failed");
+                continue;
+            }
+            sum += e_ms;
+        }
+        if (ms) ms[k] = sum;
+        if (count) count[k] = (int64_t)t->timer.pending[k].size();
+    }
+    t->timer.recycle();
+    return rc;
 }
 
 int sata_set_workspace_limit(sata_tables* t, int64_t bytes) {
@@ -275,11 +364,15 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         a.c_end = (int)((s + 1) * seg < nchunks ? (s + 1) * seg : nchunks);
         a.load_state = (s > 0 || cont) ? 1 : 0;
         a.store_state = (s < nseg - 1 || state) ? 1 : 0;
+        hipEvent_t ev = t->timer.begin(st);
         hipError_t e = use_mfma ? sata::launch_scan_mfma(a, t->mfma, st)
                                 : sata::launch_scan_valu(a, st);
+        t->timer.end(SATA_KERNEL_SCAN, ev, st);
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+        ev = t->timer.begin(st);
         e = sata::launch_finalize(a, st);
+        t->timer.end(SATA_KERNEL_FINALIZE, ev, st);
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
     }
@@ -323,8 +416,15 @@ int sata_decode_step(const sata_tables* tc, float* state, const void* q, const v
     rc = ensure_ws(t, (size_t)a.BH * a.nblk * (d_V + 1) * 4, st);
     if (rc) return rc;
     a.partial = (float*)t->ws;
+    hipEvent_t ev = t->timer.begin(st);
     hipError_t e = sata::launch_decode(a, st);
+    t->timer.end(SATA_KERNEL_DECODE, ev, st);
     if (e != hipSuccess) return fail(SATA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    ev = t->timer.begin(st);
+    e = sata::launch_decode_reduce(a, st);
+    t->timer.end(SATA_KERNEL_DECODE_REDUCE, ev, st);
+    if (e != hipSuccess)
+        return fail(SATA_ERR_HIP, "decode reduction launch failed: %s", hipGetErrorString(e));
     return SATA_OK;
 }
 

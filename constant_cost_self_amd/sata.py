@@ -26,7 +26,9 @@ SATA_ERR_OOM = -5
 
 EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "sata_tables_free", "sata_feature_dim",
             "sata_state_stride", "sata_state_bytes", "sata_prefill", "sata_decode_step",
-            "sata_last_error", "sata_set_workspace_limit")
+            "sata_last_error", "sata_set_workspace_limit", "sata_set_timing",
+            "sata_read_timing")
+KERNELS = ("scan", "finalize", "decode", "decode_reduce")
 
 _lib = None
 
@@ -72,6 +74,11 @@ def load():
     lib.sata_last_error.argtypes = []
     lib.sata_set_workspace_limit.restype = i32
     lib.sata_set_workspace_limit.argtypes = [vp, i64]
+    lib.sata_set_timing.restype = i32
+    lib.sata_set_timing.argtypes = [vp, i32]
+    lib.sata_read_timing.restype = i32
+    lib.sata_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
     _lib = lib
     return lib
 
@@ -161,6 +168,17 @@ class Tables:
 
     def set_workspace_limit(self, nbytes: int):
         _check(load().sata_set_workspace_limit(self.handle, nbytes))
+
+    def set_timing(self, enable: bool):
+        _check(load().sata_set_timing(self.handle, 1 if enable else 0))
+
+    def read_timing(self):
+        """{kernel: (summed ms, launches)} since the previous read (waits for them)."""
+        n = len(KERNELS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        _check(load().sata_read_timing(self.handle, ms, cnt))
+        return {KERNELS[i]: (ms[i], cnt[i]) for i in range(n)}
 
     def close(self):
         if self.handle:

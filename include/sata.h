@@ -158,6 +158,25 @@ const char *sata_last_error(void);
  */
 int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
 
+/*
+ * Kernel timing.  With timing enabled, every kernel launch of the handle is
+ * bracketed by two HIP events recorded on the launch stream.  sata_read_timing
+ * waits for the recorded events, writes per kernel kind k (SATA_KERNEL_*) the
+ * summed elapsed milliseconds ms[k] and the number of launches count[k] since
+ * the previous read (either pointer may be NULL), and resets the record.
+ * Enabling or disabling also resets it.  Timing adds two event records per
+ * launch and no host synchronisation outside sata_read_timing.
+ */
+enum {
+    SATA_KERNEL_SCAN = 0,          /* inter-chunk scan (partials + state update) */
+    SATA_KERNEL_FINALIZE = 1,      /* intra-chunk part, reduction, y             */
+    SATA_KERNEL_DECODE = 2,        /* decode state read-modify-write             */
+    SATA_KERNEL_DECODE_REDUCE = 3, /* decode per-head reduction, y               */
+    SATA_NUM_KERNELS = 4
+};
+int sata_set_timing(sata_tables *t, int enable);
+int sata_read_timing(sata_tables *t, double *ms, int64_t *count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -242,3 +242,77 @@ def test_mid_parity(torch_cuda, dtype):
     assert np.all(Sg[:, M:] == 0.0)
     assert Sg[w.d_V, 0] == w.n
     t.close()
+
+
+# --------------------------------------------------------------------------
+# bf16 MFMA scan (d_K = d_V = 64, P = 4, chunk 64): ragged, continued, segmented
+# --------------------------------------------------------------------------
+
+def _bf16_64(n, B, H, seed):
+    return inputs.draw((B, H, n, 64), (B, H, n, 64), "bf16", 0.5, 1.0, seed)
+
+
+def test_mfma_ragged_and_short(torch_cuda):
+    for n in (1, 63, 64, 65, 1000):
+        say("mfma bf16 d=64 n=%d" % n)
+        x = _bf16_64(n, 1, 3, 20 + n)
+        q, k, v = upload(x, "bf16")
+        t = _tables(64, 4)
+        S = new_state(1, 3, 64, 64, 4)
+        y = prefill(t, q, k, v, 64, S)
+        torch_cuda.cuda.synchronize()
+        ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+        err = max_row_err(y.cpu().numpy(), ref)
+        say("  y err %.3e" % err)
+        assert err <= TOL_BF16
+        _, S_ref = oracle.feature_form(None, x["k"][0, 2], x["v"][0, 2], 4, want_y=False)
+        M = S_ref.shape[1]
+        Sg = S[0, 2].cpu().numpy()
+        assert state_col_err(Sg[:, :M], S_ref) <= TOL_BF16
+        assert np.all(Sg[:, M:] == 0.0)
+        t.close()
+
+
+def test_mfma_continue_from_state(torch_cuda):
+    say("mfma prefill(700) + prefill(500, continue) vs oracle")
+    n1, n2 = 700, 500
+    x = _bf16_64(n1 + n2, 1, 2, 30)
+    q, k, v = upload(x, "bf16")
+    t = _tables(64, 4)
+    S = new_state(1, 2, 64, 64, 4)
+    prefill(t, q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(),
+            64, S)
+    y2 = prefill(t, q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(),
+                 v[:, :, n1:].contiguous(), 64, S, continue_state=True)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    err = max_row_err(y2.cpu().numpy(), ref[:, :, n1:])
+    say("  y err %.3e" % err)
+    assert err <= TOL_BF16
+    _, S_ref = oracle.feature_form(None, x["k"][0, 1], x["v"][0, 1], 4, want_y=False)
+    M = S_ref.shape[1]
+    assert state_col_err(S[0, 1].cpu().numpy()[:, :M], S_ref) <= TOL_BF16
+    t.close()
+
+
+def test_mfma_segmented_matches_single_segment(torch_cuda):
+    """Segments carry the state through fp32 memory with the key-side factors
+    divided out and back in: equal to one segment to fp32 rounding."""
+    say("mfma segmented vs one segment")
+    n = 64 * 20 + 17
+    x = _bf16_64(n, 2, 2, 31)
+    q, k, v = upload(x, "bf16")
+    t = _tables(64, 4)
+    S1 = new_state(2, 2, 64, 64, 4)
+    y1 = prefill(t, q, k, v, 64, S1)
+    t.set_workspace_limit(4 << 20)
+    S2 = new_state(2, 2, 64, 64, 4)
+    y2 = prefill(t, q, k, v, 64, S2)
+    y3 = prefill(t, q, k, v, 64)
+    torch_cuda.cuda.synchronize()
+    d12 = float((y1 - y2).abs().max() / y1.abs().max())
+    d13 = float((y1 - y3).abs().max() / y1.abs().max())
+    dS = float((S1 - S2).abs().max() / S1.abs().max())
+    say("  rel diffs y %.2e %.2e state %.2e" % (d12, d13, dS))
+    assert d12 <= 1e-5 and d13 <= 1e-5 and dS <= 1e-5
+    t.close()
