@@ -72,12 +72,23 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
     __syncthreads();
     const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * L * cols;
     for (int idx = tid; idx < L * cols; idx += kThreads) {
-        const int T_ = idx / cols, j = idx % cols;
+        const int j = idx / L, T_ = idx % L;      // token fastest: coalesced partial reads
         const float* wr = W + T_ * (L + 1);
         float acc = 0.0f;
         for (int s = 0; s <= T_; ++s) acc = fmaf(wr[s], us[s * cols + j], acc);
-        for (int sl = 0; sl < a.nslices; ++sl) acc += part[(int64_t)sl * L * cols + idx];
-        num[idx] = acc;
+        // slice partials: read once, four independent sums to keep loads in flight
+        const float* p = part + j * L + T_;           // partials are [column][token]
+        const int64_t stride = (int64_t)L * cols;
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        int sl = 0;
+        for (; sl + 4 <= a.nslices; sl += 4) {
+            a0 += __builtin_nontemporal_load(p + (sl + 0) * stride);
+            a1 += __builtin_nontemporal_load(p + (sl + 1) * stride);
+            a2 += __builtin_nontemporal_load(p + (sl + 2) * stride);
+            a3 += __builtin_nontemporal_load(p + (sl + 3) * stride);
+        }
+        for (; sl < a.nslices; ++sl) a0 += __builtin_nontemporal_load(p + sl * stride);
+        num[T_ * cols + j] = acc + ((a0 + a1) + (a2 + a3));
     }
     __syncthreads();
     float* y = a.y + (bh * a.n + t0) * d_V;

@@ -7,7 +7,8 @@
 // For chunk c with tokens t0..t0+L-1:
 //     readout   part[t][j] = sum_{f in slice} qw[f] phi_f(q_t) S[f][j]   (S before c)
 //     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
-// The readout of every slice is written as a partial sum; the finalize kernel adds
+// The readout of every slice is written as a partial sum ([column][token] within
+// the chunk); the finalize kernel adds
 // the partials of all slices to the intra-chunk part.  Arithmetic is fp32 on the
 // VALU: this is the path for fp32 inputs and for sizes the MFMA scan does not
 // cover.  Tokens past n in the last chunk get u = 0 and so never enter the state.
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
             const float* h = hat + t * SV;
             float acc = 0.0f;
             for (int f = 0; f < SV; ++f) acc = fmaf(h[f], Ssl[f * cols + j], acc);
-            part[idx] = acc;
+            part[j * L + t] = acc;
         }
         __syncthreads();
         // key features of the slice

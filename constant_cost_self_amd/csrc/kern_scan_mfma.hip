@@ -43,20 +43,31 @@ constexpr int kL = 64;     // chunk length of the MFMA scan
 
 template <int D, int NCT>
 struct Layout {
-    static constexpr int QS = D + 12;        // qs row stride (floats): coords 0..D+7 + pad
-    static constexpr int KT = 68;            // kT / kpar row stride (floats): 64 tokens + pad
+    static constexpr int XR = D + 8;         // raw q/k row (bf16): D coords, 1, then 7 zeros
+    static constexpr int XSLOTS = XR / 8;    // 16-byte slots per raw row
+    static constexpr int KP = 68;            // kpar row stride (floats): 64 tokens + pad
     static constexpr int VT = 72;            // vT row stride (bf16): 64 tokens + pad
-    static constexpr int UR = NCT * 16 + 4;  // per-wave readout row stride (floats)
-    static constexpr int qs = 0;
-    static constexpr int kt = qs + kL * QS;
-    static constexpr int kp = kt + (D + 8) * KT;
-    static constexpr int ur = kp + kRowsPerSlice * KT;
-    static constexpr int vt_bytes = (ur + kWavesPerSlice * kL * UR) * 4;
-    static constexpr int bytes = vt_bytes + NCT * 16 * VT * 2;
+    static constexpr int UT = 68;            // readout region row stride (floats, rows = columns)
+    static constexpr int DV_MAX = NCT * 16;  // raw v row capacity (bf16)
+    static constexpr int rawq = 0;                                  // bytes
+    static constexpr int rawk = rawq + kL * XR * 2;
+    static constexpr int rawv = rawk + kL * XR * 2;
+    static constexpr int vt = rawv + kL * DV_MAX * 2;
+    static constexpr int kp = vt + NCT * 16 * VT * 2;
+    static constexpr int ur = kp + kRowsPerSlice * KP * 4;
+    static constexpr int rp = ur + kWavesPerSlice * NCT * 16 * UT * 4;
+    static constexpr int bytes = rp + kRowsPerSlice * 4;
+    // state load/store staging (outside the chunk loop) aliases the readout regions
+    static constexpr int IO = NCT * 16 + 4;                         // floats per feature row
+    static constexpr int io_rows = kWavesPerSlice * 32;             // 2 tiles per wave per phase
+    static_assert(io_rows * IO * 4 <= kWavesPerSlice * NCT * 16 * UT * 4, "state staging size");
+    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kp % 16 == 0 && ur % 16 == 0,
+                  "16-byte alignment of LDS regions");
 };
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline float bf16_at(const uint16_t* p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
 
 __device__ inline bf16x8 pack_bf16(const float* x) {
     bf16x8 r;
@@ -81,27 +92,65 @@ struct RowPtrs {
     const float* kscale;
     const int32_t* canon;
     const int32_t* wave_lblock;
+    const uint16_t* one_row;     // 8 bf16: 1, 0, ..., 0 (the constant coordinates d..d+7)
 };
 
+// Direct-to-LDS copies of one chunk.  A wave instruction moves 64 lanes x 16 bytes
+// into a contiguous 1 KiB block; lane i fills bytes [16 i, 16 i + 16).  q and k rows
+// get a ninth slot holding the constant coordinates (1, 0, ..., 0).  Rows past n
+// read row 0 of the chunk instead (masked later).
 template <int D, int NCT>
+__device__ inline void prefetch_x(const uint16_t* x, const uint16_t* one_row, int64_t t0, int nvalid,
+                                  unsigned char* dst, int w, int lane) {
+    using LY = Layout<D, NCT>;
+    constexpr int NBLK = kL * LY::XSLOTS / 64;
+#pragma unroll
+    for (int blk = w; blk < NBLK; blk += kWavesPerSlice) {
+        const int sl = blk * 64 + lane;
+        const int t = sl / LY::XSLOTS, cs = sl % LY::XSLOTS;
+        const void* src = cs == D / 8 ? (const void*)one_row
+                                      : (const void*)(x + (t0 + (t < nvalid ? t : 0)) * D + 8 * cs);
+        __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)(dst + blk * 1024),
+                                         16, 0, 0);
+    }
+}
+
+template <int D, int NCT>
+__device__ inline void prefetch_v(const uint16_t* v, int64_t t0, int nvalid, int d_V, unsigned char* dst,
+                                  int w, int lane) {
+    const int VB = kL * d_V * 2;
+    for (int blk = w; blk < (VB + 1023) / 1024; blk += kWavesPerSlice) {
+        int off = blk * 1024 + lane * 16;
+        if (off >= VB) off = 0;                        // lanes past the chunk reload its start
+        const int t = off / (d_V * 2);
+        const int src = t < nvalid ? off : off % (d_V * 2);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)(v + t0 * d_V) + src),
+                                         (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
+    }
+}
+
+template <int D, int DV, int NPC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
+    constexpr int NCT = (DV + 1 + 15) / 16;  // column tiles of [v | 1]
     using LY = Layout<D, NCT>;
     constexpr int KS = kRowsPerWave / 4;     // readout K-steps per wave (32 features each)
     constexpr int NT = 2 * KS;               // update tiles per wave (16 features each)
+    constexpr int XR = LY::XR;
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    float* lds = reinterpret_cast<float*>(lds_raw);
-    float* qs = lds + LY::qs;
-    float* kT = lds + LY::kt;
-    float* kpar = lds + LY::kp;
-    float* ured = lds + LY::ur;
-    __bf16* vT = reinterpret_cast<__bf16*>(lds_raw + LY::vt_bytes);
+    const uint16_t* rq = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawq);
+    const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
+    const uint16_t* rv = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawv);
+    uint16_t* vt16 = reinterpret_cast<uint16_t*>(lds_raw + LY::vt);
+    float* kpar = reinterpret_cast<float*>(lds_raw + LY::kp);
+    float* ured = reinterpret_cast<float*>(lds_raw + LY::ur);
+    uint32_t* rowpar = reinterpret_cast<uint32_t*>(lds_raw + LY::rp);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y;
-    const int d_V = a.d_V, cols = d_V + 1;
+    constexpr int d_V = DV, cols = DV + 1;
     const int nch = a.c_end - a.c_begin;
     const int row_wg = slice * kRowsPerSlice;               // first row of the workgroup
     const int row_w = row_wg + w * kRowsPerWave;            // first row of this wave
@@ -112,12 +161,28 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint16_t* v = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.n * d_V;
     float* state = a.state ? a.state + bh * (int64_t)cols * a.M_pad : nullptr;
 
-    // per-lane row constants
-    uint32_t pc[KS];
+    auto nvalid_of = [&](int c) {
+        const int64_t r = a.n - (int64_t)c * kL;
+        return (int)(r < kL ? r : kL);
+    };
+    {   // first chunk in flight while the state is being set up
+        const int64_t t0 = (int64_t)a.c_begin * kL;
+        const int nv = nvalid_of(a.c_begin);
+        prefetch_x<D, NCT>(q, rt.one_row, t0, nv, lds_raw + LY::rawq, w, lane);
+        prefetch_x<D, NCT>(k, rt.one_row, t0, nv, lds_raw + LY::rawk, w, lane);
+        prefetch_v<D, NCT>(v, t0, nv, d_V, lds_raw + LY::rawv, w, lane);
+    }
+
+    // per-lane row constants: query weight and LDS addresses of the parent coordinates
+    // of row 4 s + g in this lane's token row of the raw q buffer (m-tile 0)
+    uint32_t qoff[KS][NPC > 0 ? NPC : 1];
     float Wq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        pc[s] = rt.parent[row_w + 4 * s + g];
+        const uint32_t p3 = rt.parent[row_w + 4 * s + g];
+#pragma unroll
+        for (int e = 0; e < NPC; ++e)
+            qoff[s][e] = (uint32_t)(LY::rawq + (li * XR + ((p3 >> (10 * e)) & 1023u)) * 2);
         Wq[s] = rt.weight[row_w + 4 * s + g];
     }
     float cK[NT];
@@ -128,8 +193,9 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         cK[T] = rt.kscale[(row_w + 4 * s + (li >> 2)) * 8 + 4 * h + (li & 3)];
         ones[T] = __all(cK[T] == 1.0f);
     }
+    if (tid < kRowsPerSlice) rowpar[tid] = rt.parent[row_wg + tid];
 
-    // resident state slice, update-accumulator layout: lane (column 16 ct + li, g)
+    // Resident state slice, update-accumulator layout: lane (column 16 ct + li, g)
     // register r of tile T = 2 s + h holds kernel feature (row 4 s + g, element 4 h + r).
     f32x4v S[NT][NCT];
 #pragma unroll
@@ -137,206 +203,244 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[T][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
     if (a.load_state) {
-        // through LDS, half of the tiles at a time: plain gather loop, then a
-        // register fill with compile-time indices
+        // through LDS, 2 tiles per wave at a time: plain gather loop, then a register
+        // fill with compile-time indices (keeps the unrolled code free of table loads)
+        float* io = ured;
 #pragma unroll
-        for (int ph = 0; ph < 2; ++ph) {
+        for (int ph = 0; ph < NT / 2; ++ph) {
             __syncthreads();
-            for (int idx = tid; idx < kWavesPerSlice * 64 * cols; idx += 256) {
-                const int ww = idx / (64 * cols), rem = idx % (64 * cols);
-                const int fl = rem / cols, j = rem % cols;
-                const int T = (NT / 2) * ph + fl / 16, rho = fl % 16;
+            for (int idx = tid; idx < LY::io_rows * cols; idx += 256) {
+                const int fr = idx / cols, j = idx % cols;
+                const int ww = fr / 32, fl = fr % 32;
+                const int T = 2 * ph + fl / 16, rho = fl % 16;
                 const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
                                4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
-                ured[(ww * 64 + fl) * LY::UR + j] =
-                    F >= 0 ? rt.kscale[fi] * state[(int64_t)j * a.M_pad + F] : 0.0f;
+                io[fr * LY::IO + j] = F >= 0 ? rt.kscale[fi] * state[(int64_t)j * a.M_pad + F] : 0.0f;
             }
             __syncthreads();
 #pragma unroll
-            for (int Tl = 0; Tl < NT / 2; ++Tl)
+            for (int Tl = 0; Tl < 2; ++Tl)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * ct + li;
-                        S[(NT / 2) * ph + Tl][ct][r] =
-                            j < cols ? ured[(w * 64 + Tl * 16 + 4 * g + r) * LY::UR + j] : 0.0f;
+                        S[2 * ph + Tl][ct][r] = j < cols ? io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + j] : 0.0f;
                     }
         }
-        __syncthreads();
     }
+    // bf16 copy of the state in the readout's B-operand layout, refreshed at the end of
+    // every update (tile pair s covers the readout's K-step s)
+    bf16x8 Sb[KS][NCT];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) Sb[s2][ct] = pack_tiles(S[2 * s2][ct], S[2 * s2 + 1][ct]);
 
-    // constant columns of [v | 1] beyond d_V
+    // columns of [v | 1] past d_V are zero for good
+    __syncthreads();
     for (int idx = tid; idx < (NCT * 16 - cols) * kL; idx += 256) {
         const int j = cols + idx / kL, t = idx % kL;
-        vT[j * LY::VT + t] = (__bf16)0.0f;
+        vt16[j * LY::VT + t] = 0;
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // A slice's partial readout of chunk c (the sum of the 4 waves' regions, [col][token])
+    // is written at the start of chunk c + 1, so the stores complete during that chunk.
+    auto write_partial = [&](int c) {
+        float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)kL * cols +
+                    w * kL + lane;
+        const float* up = ured + w * LY::UT + lane;
+        constexpr int WS = NCT * 16 * LY::UT;                  // one wave's region
+        constexpr int NJ = (cols + 3) / 4;                     // columns per wave (last one partial)
+#pragma unroll
+        for (int i = 0; i < NJ; ++i) {
+            if (i < NJ - 1 || w + 4 * i < cols)
+                pp[4 * i * kL] = (up[4 * i * LY::UT] + up[4 * i * LY::UT + WS]) +
+                                 (up[4 * i * LY::UT + 2 * WS] + up[4 * i * LY::UT + 3 * WS]);
+        }
+    };
 
     for (int c = a.c_begin; c < a.c_end; ++c) {
-        const int64_t t0 = (int64_t)c * kL;
-        const int nvalid = (int)((a.n - t0) < kL ? (a.n - t0) : kL);
+        const int nvalid = nvalid_of(c);
+        if (c > a.c_begin) write_partial(c - 1);
+        const int64_t t1 = (int64_t)(c + 1) * kL;
+        const bool more = c + 1 < a.c_end;
+        const int nvalid1 = more ? nvalid_of(c + 1) : 0;
 
-        // ---- stage the chunk -------------------------------------------------
-        for (int idx = tid; idx < kL * (D / 4); idx += 256) {
-            const int t = idx / (D / 4), c4 = idx % (D / 4);
-            f32x4v x = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (t < nvalid) {
-                const uint2 raw = *reinterpret_cast<const uint2*>(q + (t0 + t) * D + 4 * c4);
-                x = f32x4v{bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
+        // ---- P1: [v | 1] transposed to bf16 columns, key parent products ---------------
+        static_assert(DV % 4 == 0 && (kL * DV / 4) % 256 == 0, "v staging shape");
+        {
+            constexpr int NV = kL * DV / 4 / 256;
+            uint2 r2[NV];
+#pragma unroll
+            for (int it = 0; it < NV; ++it) {            // all reads first: no LDS round trips
+                const int idx = tid + 256 * it;
+                r2[it] = *reinterpret_cast<const uint2*>(rv + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4)));
             }
-            *reinterpret_cast<f32x4v*>(qs + t * LY::QS + 4 * c4) = x;
-        }
-        for (int idx = tid; idx < kL * 8; idx += 256) {
-            const int t = idx >> 3, e = idx & 7;
-            qs[t * LY::QS + D + e] = e == 0 ? 1.0f : 0.0f;
-            kT[(D + e) * LY::KT + t] = e == 0 ? 1.0f : 0.0f;
-        }
-        for (int idx = tid; idx < kL * (D / 4); idx += 256) {
-            const int t = idx % kL, c4 = idx / kL;
-            float x0 = 0.0f, x1 = 0.0f, x2 = 0.0f, x3 = 0.0f;
-            if (t < nvalid) {
-                const uint2 raw = *reinterpret_cast<const uint2*>(k + (t0 + t) * D + 4 * c4);
-                x0 = bf16_lo(raw.x); x1 = bf16_hi(raw.x); x2 = bf16_lo(raw.y); x3 = bf16_hi(raw.y);
+#pragma unroll
+            for (int it = 0; it < NV; ++it) {
+                const int idx = tid + 256 * it;
+                const int t = idx / (DV / 4), c4 = idx % (DV / 4);
+                const uint2 x = t < nvalid ? r2[it] : uint2{0u, 0u};
+                uint16_t* dst = vt16 + 4 * c4 * LY::VT + t;
+                dst[0] = (uint16_t)(x.x & 0xffffu);
+                dst[LY::VT] = (uint16_t)(x.x >> 16);
+                dst[2 * LY::VT] = (uint16_t)(x.y & 0xffffu);
+                dst[3 * LY::VT] = (uint16_t)(x.y >> 16);
             }
-            kT[(4 * c4 + 0) * LY::KT + t] = x0;
-            kT[(4 * c4 + 1) * LY::KT + t] = x1;
-            kT[(4 * c4 + 2) * LY::KT + t] = x2;
-            kT[(4 * c4 + 3) * LY::KT + t] = x3;
         }
-        for (int idx = tid; idx < kL * (d_V / 4); idx += 256) {
-            const int t = idx % kL, c4 = idx / kL;
-            uint2 raw = {0u, 0u};
-            if (t < nvalid) raw = *reinterpret_cast<const uint2*>(v + (t0 + t) * d_V + 4 * c4);
-            uint16_t* vt16 = reinterpret_cast<uint16_t*>(vT);
-            vt16[(4 * c4 + 0) * LY::VT + t] = (uint16_t)(raw.x & 0xffffu);
-            vt16[(4 * c4 + 1) * LY::VT + t] = (uint16_t)(raw.x >> 16);
-            vt16[(4 * c4 + 2) * LY::VT + t] = (uint16_t)(raw.y & 0xffffu);
-            vt16[(4 * c4 + 3) * LY::VT + t] = (uint16_t)(raw.y >> 16);
+        if (tid < kL) vt16[DV * LY::VT + tid] = tid < nvalid ? (uint16_t)0x3f80u : (uint16_t)0u;
+        {
+            // each wave builds the parent products of its own 16 rows; lane = token.
+            // The parent words are wave-uniform (scalar loads).
+            const uint16_t* xrow = rk + lane * XR;
+            float* kdst = kpar + (w * kRowsPerWave) * LY::KP + lane;
+            const bool tv = lane < nvalid;
+            const int row_u = __builtin_amdgcn_readfirstlane(row_w);
+            float kp[kRowsPerWave];
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave; ++i) {      // all reads first: no LDS round trips
+                const uint32_t p3 = rt.parent[row_u + i];
+                kp[i] = 1.0f;
+#pragma unroll
+                for (int e = 0; e < NPC; ++e) kp[i] *= bf16_at(xrow, (p3 >> (10 * e)) & 1023u);
+            }
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave; ++i) kdst[i * LY::KP] = tv ? kp[i] : 0.0f;
         }
-        for (int t = tid; t < kL; t += 256) vT[d_V * LY::VT + t] = (__bf16)(t < nvalid ? 1.0f : 0.0f);
-        __syncthreads();
+        __syncthreads();                                               // B1
+        if (more) prefetch_v<D, NCT>(v, t1, nvalid1, d_V, lds_raw + LY::rawv, w, lane);
 
-        // ---- parent products of the key side, one per row of the slice --------
-        for (int idx = tid; idx < kRowsPerSlice * kL; idx += 256) {
-            const int r = idx / kL, t = idx % kL;
-            const uint32_t p3 = rt.parent[row_wg + r];
-            const float x = kT[(p3 & 1023u) * LY::KT + t] * kT[((p3 >> 10) & 1023u) * LY::KT + t] *
-                            kT[((p3 >> 20) & 1023u) * LY::KT + t];
-            kpar[r * LY::KT + t] = x;
-        }
-        __syncthreads();
-
-        // ---- readout: U = Q^ . bf16(S) ------------------------------------------
-        f32x4v U[4][NCT];
+        // ---- P2: readout U = Q^ . bf16(S) ------------------------------------------
+        {
+            f32x4v U[4][NCT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) U[mt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            bf16x8 Sb[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Sb[ct] = pack_tiles(S[2 * s][ct], S[2 * s + 1][ct]);
-            const uint32_t p3 = pc[s];
-            const int i0 = p3 & 1023u, i1 = (p3 >> 10) & 1023u, i2 = (p3 >> 20) & 1023u;
+                for (int ct = 0; ct < NCT; ++ct) U[mt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+            float qreg[4][8];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const float* qrow = qs + (16 * mt + li) * LY::QS;
-                const f32x4v q0 = *reinterpret_cast<const f32x4v*>(qrow + 8 * lb);
-                const f32x4v q1 = *reinterpret_cast<const f32x4v*>(qrow + 8 * lb + 4);
-                const float qp = Wq[s] * qrow[i0] * qrow[i1] * qrow[i2];
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = qp * q0[e];
-                    x[4 + e] = qp * q1[e];
-                }
-                const bf16x8 A = pack_bf16(x);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    U[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Sb[ct], U[mt][ct], 0, 0, 0);
+                const uint4 raw = *reinterpret_cast<const uint4*>(rq + (16 * mt + li) * XR + 8 * lb);
+                qreg[mt][0] = bf16_lo(raw.x); qreg[mt][1] = bf16_hi(raw.x);
+                qreg[mt][2] = bf16_lo(raw.y); qreg[mt][3] = bf16_hi(raw.y);
+                qreg[mt][4] = bf16_lo(raw.z); qreg[mt][5] = bf16_hi(raw.z);
+                qreg[mt][6] = bf16_lo(raw.w); qreg[mt][7] = bf16_hi(raw.w);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        {
-            float* ur = ured + w * kL * LY::UR;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    float qp = Wq[s];
+#pragma unroll
+                    for (int e = 0; e < NPC; ++e)
+                        qp *= bf16_at(reinterpret_cast<const uint16_t*>(lds_raw + qoff[s][e] + mt * 16 * XR * 2), 0);
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = qp * qreg[mt][e];
+                    const bf16x8 A = pack_bf16(x);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        U[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Sb[s][ct], U[mt][ct], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0x100);   // only LDS reads may move across
+            }
+            // this wave's readout, column-major: ured[w][col][token], 4 tokens per store
+            float* ur = ured + w * (NCT * 16 * LY::UT);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
+                    *reinterpret_cast<f32x4v*>(ur + (16 * ct + li) * LY::UT + 16 * mt + 4 * g) = U[mt][ct];
+        }
+        // the wave's key coordinates k_l (l = 8 lb + 4 h + li % 4) for its tokens
+        float kreg[2][2][8];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) ur[(16 * mt + 4 * g + r) * LY::UR + 16 * ct + li] = U[mt][ct][r];
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    kreg[h][kk][e] = bf16_at(rk, (32 * kk + 8 * g + e) * XR + 8 * lb + 4 * h + (li & 3));
+        __syncthreads();                                               // B2
+        // the raw buffers are free: the next chunk streams in during the update
+        if (more) {
+            prefetch_x<D, NCT>(q, rt.one_row, t1, nvalid1, lds_raw + LY::rawq, w, lane);
+            prefetch_x<D, NCT>(k, rt.one_row, t1, nvalid1, lds_raw + LY::rawk, w, lane);
         }
 
-        // ---- update: S += K^^T . [v | 1] ------------------------------------------
+        // ---- P3: update S += K^^T . [v | 1] ------------------------------------------
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 Vop[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Vop[ct] = *reinterpret_cast<const bf16x8*>(vT + (16 * ct + li) * LY::VT + 32 * kk + 8 * g);
+                Vop[ct] = *reinterpret_cast<const bf16x8*>(vt16 + (16 * ct + li) * LY::VT + 32 * kk + 8 * g);
 #pragma unroll
-            for (int T = 0; T < NT; ++T) {
-                const int s = T >> 1, h = T & 1;
-                const float* kp = kpar + (w * kRowsPerWave + 4 * s + (li >> 2)) * LY::KT + 32 * kk + 8 * g;
-                const float* kv = kT + (8 * lb + 4 * h + (li & 3)) * LY::KT + 32 * kk + 8 * g;
+            for (int s = 0; s < KS; ++s) {
+                const float* kp = kpar + (w * kRowsPerWave + 4 * s + (li >> 2)) * LY::KP + 32 * kk + 8 * g;
                 const f32x4v p0 = *reinterpret_cast<const f32x4v*>(kp);
                 const f32x4v p1 = *reinterpret_cast<const f32x4v*>(kp + 4);
-                const f32x4v v0 = *reinterpret_cast<const f32x4v*>(kv);
-                const f32x4v v1 = *reinterpret_cast<const f32x4v*>(kv + 4);
-                float x[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = p0[e] * v0[e];
-                    x[4 + e] = p1[e] * v1[e];
+                for (int h = 0; h < 2; ++h) {
+                    const int T = 2 * s + h;
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = p0[e] * kreg[h][kk][e];
+                        x[4 + e] = p1[e] * kreg[h][kk][4 + e];
+                    }
+                    if (!ones[T]) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] *= cK[T];
+                    }
+                    const bf16x8 A = pack_bf16(x);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Vop[ct], S[T][ct], 0, 0, 0);
                 }
-                if (!ones[T]) {
+                // on the last token step, tile pair s - 1 is final: pack it for the next
+                // readout while pair s is still in the matrix pipe
+                if (kk == 1 && s > 0) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] *= cK[T];
+                    for (int ct = 0; ct < NCT; ++ct) Sb[s - 1][ct] = pack_tiles(S[2 * s - 2][ct], S[2 * s - 1][ct]);
                 }
-                const bf16x8 A = pack_bf16(x);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Vop[ct], S[T][ct], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0x100);   // only LDS reads may move across
             }
         }
-        __syncthreads();
-
-        // ---- sum the 4 waves' readouts into this slice's partial ------------------
-        float* part = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)kL * cols;
-        for (int idx = tid; idx < kL * cols; idx += 256) {
-            const int t = idx / cols, j = idx % cols;
-            float s = 0.0f;
 #pragma unroll
-            for (int ww = 0; ww < kWavesPerSlice; ++ww) s += ured[(ww * kL + t) * LY::UR + j];
-            part[idx] = s;
-        }
+        for (int ct = 0; ct < NCT; ++ct) Sb[KS - 1][ct] = pack_tiles(S[2 * KS - 2][ct], S[2 * KS - 1][ct]);
+
+        __builtin_amdgcn_s_waitcnt(0);          // the next chunk has landed
+        __syncthreads();                                               // B3
     }
+    if (a.c_end > a.c_begin) write_partial(a.c_end - 1);
 
     if (a.store_state) {
-        // through LDS as for the load; internal S' = c S is scaled back by 1/c
+        // through LDS as for the load; the internal S' = c S is scaled back by 1/c
+        float* io = ured;
 #pragma unroll
-        for (int ph = 0; ph < 2; ++ph) {
+        for (int ph = 0; ph < NT / 2; ++ph) {
             __syncthreads();
 #pragma unroll
-            for (int Tl = 0; Tl < NT / 2; ++Tl)
+            for (int Tl = 0; Tl < 2; ++Tl)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        ured[(w * 64 + Tl * 16 + 4 * g + r) * LY::UR + 16 * ct + li] =
-                            S[(NT / 2) * ph + Tl][ct][r];
+                        io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + 16 * ct + li] = S[2 * ph + Tl][ct][r];
             __syncthreads();
-            for (int idx = tid; idx < kWavesPerSlice * 64 * cols; idx += 256) {
-                const int ww = idx / (64 * cols), rem = idx % (64 * cols);
-                const int fl = rem / cols, j = rem % cols;
-                const int T = (NT / 2) * ph + fl / 16, rho = fl % 16;
+            for (int idx = tid; idx < LY::io_rows * cols; idx += 256) {
+                const int fr = idx / cols, j = idx % cols;
+                const int ww = fr / 32, fl = fr % 32;
+                const int T = 2 * ph + fl / 16, rho = fl % 16;
                 const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
                                4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
-                if (F >= 0) state[(int64_t)j * a.M_pad + F] = ured[(ww * 64 + fl) * LY::UR + j] / rt.kscale[fi];
+                if (F >= 0) state[(int64_t)j * a.M_pad + F] = io[fr * LY::IO + j] / rt.kscale[fi];
             }
         }
         if (slice == 0) {
@@ -347,15 +451,15 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     }
 }
 
-template <int D, int NCT>
+template <int D, int DV, int NPC>
 hipError_t launch_t(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
-    using LY = Layout<D, NCT>;
+    using LY = Layout<D, (DV + 1 + 15) / 16>;
     static_assert(LY::bytes <= 160 * 1024, "LDS budget");
-    RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock};
-    hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, NCT>,
+    RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock, m.one_row};
+    hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, NPC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<D, NCT>), dim3(a.nslices, a.BH), dim3(256), LY::bytes, st,
+    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, NPC>), dim3(a.nslices, a.BH), dim3(256), LY::bytes, st,
                        a, rt);
     return hipGetLastError();
 }
@@ -367,7 +471,7 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
     MfmaHostRows r;
     if (!build_mfma_rows(h, r)) return 0;        // not an MFMA shape: the VALU scan is used
     const size_t nr = (size_t)r.nrows, nw = r.wave_lblock.size();
-    const size_t bytes = nr * 4 + nr * 4 + nr * 8 * 4 + nr * 8 * 4 + nw * 4;
+    const size_t bytes = 16 + nr * 4 + nr * 4 + nr * 8 * 4 + nr * 8 * 4 + nw * 4;
     char* base = nullptr;
     if (hipMalloc(&base, bytes) != hipSuccess) {
         (void)hipGetLastError();
@@ -379,13 +483,15 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
         off += n;
         return hipMemcpy(dst, src, n, hipMemcpyHostToDevice) == hipSuccess ? dst : nullptr;
     };
+    const uint16_t one_row[8] = {0x3f80u, 0, 0, 0, 0, 0, 0, 0};
+    m.one_row = (const uint16_t*)put(one_row, 16);
     m.parent = (const uint32_t*)put(r.parent.data(), nr * 4);
     m.weight = (const float*)put(r.weight.data(), nr * 4);
     m.kscale = (const float*)put(r.kscale.data(), nr * 8 * 4);
     m.canon = (const int32_t*)put(r.canon.data(), nr * 8 * 4);
     m.wave_lblock = (const int32_t*)put(r.wave_lblock.data(), nw * 4);
     m.d_rows = base;
-    if (!m.parent || !m.weight || !m.kscale || !m.canon || !m.wave_lblock) {
+    if (!m.one_row || !m.parent || !m.weight || !m.kscale || !m.canon || !m.wave_lblock) {
         free_mfma_tables(m);
         return -4;
     }
@@ -403,12 +509,17 @@ void free_mfma_tables(MfmaTables& m) {
 }
 
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L) {
-    return m.ok && bf16 && d_K == m.d_K && P == m.P && L == kL && d_K == 64 && d_V % 4 == 0 &&
-           d_V + 1 <= 80 && d_V + 1 > 64;
+    return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && L == kL && d_K == 64 &&
+           d_V == 64;
 }
 
 hipError_t launch_scan_mfma(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
-    return launch_t<64, 5>(a, m, st);
+    switch (a.P) {
+        case 2: return launch_t<64, 64, 0>(a, m, st);
+        case 3: return launch_t<64, 64, 1>(a, m, st);
+        case 4: return launch_t<64, 64, 2>(a, m, st);
+        default: return launch_t<64, 64, 3>(a, m, st);
+    }
 }
 
 }  // namespace sata

@@ -34,7 +34,7 @@ struct PrefillSegArgs {
     const void* v;
     float* y;
     float* state;            // [BH][d_V+1][M_pad]; read if load_state, written if store_state
-    float* partial;          // [BH][c_end-c_begin][nslices][L][d_V+1] workspace
+    float* partial;          // [BH][c_end-c_begin][nslices][d_V+1][L] workspace
     const uint32_t* fidx;    // packed feature indices [M_pad]
     const float* qw;         // alpha_p C_p [M_pad]
     const void* mfma_rows;   // slice tables of the MFMA scan (nullptr for the VALU scan)
