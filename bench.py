@@ -164,6 +164,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one part only (for profiler runs)")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB, 3 times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -179,7 +184,22 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_only:
+        n = args.copy_only * (1 << 20) // 4
+        src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4}))
+        return
     w = inputs.WORKLOADS[args.workload]
+    if args.only == "decode":
+        dwall, dtim, dbytes, dw = bench_decode(args.decode_steps, args.decode_warmup)
+        dk_ms, dk_n = dtim["decode"]
+        print(json.dumps({"decode_kernel_gbs": dbytes / (dk_ms / dk_n * 1e-3) / 1e9,
+                          "decode_step_ms": dwall / args.decode_steps * 1e3}))
+        return
 
     wall, tim = bench_prefill(w, args.steps, args.warmup)
     tokens = w.B * w.n
@@ -218,7 +238,7 @@ def main():
                          "kernels_ms_per_step": {k: v[0] / args.steps for k, v in tim.items()}},
     }
 
-    if not args.no_decode:
+    if not args.no_decode and args.only is None:
         dwall, dtim, dbytes, dw = bench_decode(args.decode_steps, args.decode_warmup)
         dk_ms, dk_n = dtim["decode"]
         kern_gbs = dbytes / (dk_ms / dk_n * 1e-3) / 1e9
@@ -239,7 +259,7 @@ def main():
             "reduce_ms_per_step": dtim["decode_reduce"][0] / max(dtim["decode_reduce"][1], 1),
         }
 
-    if not args.no_cpu:
+    if not args.no_cpu and args.only is None:
         log("cpu baseline: oracle on %d tokens" % args.cpu_tokens)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
 
