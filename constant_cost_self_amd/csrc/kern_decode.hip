@@ -24,8 +24,8 @@ namespace sata {
 
 namespace {
 
-constexpr int kDecGroups = 4;                         // feature groups per thread
-constexpr int kDecFeatPerBlock = kThreads * 4 * kDecGroups;   // 4096
+constexpr int kDecGroups = 1;                         // feature groups per thread (measured best)
+constexpr int kDecFeatPerBlock = kThreads * 4 * kDecGroups;   // 1024
 
 template <typename In, int CMAX>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(

@@ -8,26 +8,28 @@
 // axis, run as v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
 //     readout  (64 tokens x 32 features) x (32 features x 16 columns)
 //     update   (16 features x 32 tokens) x (32 tokens x 16 columns)
-// with d_V + 1 = 65 columns padded to 5 tiles of 16.
 //
-// Work split.  One workgroup (4 waves) owns one slice of 64 rows = 512 kernel
-// features of one head and walks all chunks of the segment in order; its fp32
-// state slice never leaves the registers (8 update tiles x 5 column tiles x 4
-// VGPRs = 160 per lane per wave).  A wave owns 16 rows of one l-block b: its
-// kernel features are (parent a, l = 8b + e), e = 0..7 (see mfma_rows.cpp).
-// Feature tiles are never written to HBM: per chunk the wave keeps the 8
-// coordinates x_{8b..8b+7} of its tokens in registers and builds
+// Work split.  The columns of [v | 1] are cut into groups of 64 value columns;
+// group 0 also carries the normaliser column (65 columns, 5 tiles of 16), the
+// others 4 tiles.  One workgroup (4 waves) owns one slice of 64 rows = 512 kernel
+// features of one head for one column group, and walks all chunks of the segment
+// in order; its fp32 state never leaves the registers (8 update tiles x 5 column
+// tiles x 4 = 160 accumulator registers per lane per wave).  A wave owns 16 rows
+// of one l-block b: its kernel features are (parent a, l = 8b + e), e = 0..7 (see
+// mfma_rows.cpp).  Feature tiles are never written to HBM: per chunk the wave keeps
+// the 8 coordinates x_{8b..8b+7} of its tokens in registers and builds
 //     query side  q^(a, l)[t] = (W_a q_a[t]) * q_l[t]        (W_a = alpha_p C(a) p)
 //     key side    k^(a, l)[t] = kpar_a[t] * k_l[t] * c_(a,l)  (c: 0 / 1/(1+m) / 1)
-// directly in the MFMA operand layout, where q_a, kpar_a are the parent products
-// (kpar_a from a per-chunk LDS table).  The readout uses the register state
-// converted to bf16 in place: the update's accumulator layout (lane = column,
-// 4 rows each) concatenated over two tiles is exactly a 32-deep B operand, as
-// long as the query operand uses the same feature order, which it does.
+// directly in the MFMA operand layout (q_a, kpar_a: parent products).  The readout
+// takes the state packed to bf16 after its last update of the previous chunk: the
+// update's accumulator layout (lane = column, 4 rows each) over two tiles is a
+// 32-deep B operand when the query operand uses the same feature order.
 //
-// Per chunk: stage q, k (fp32) and [v | 1] (bf16) in LDS; build the parent-product
-// table; readout MFMAs (per-wave accumulators) written to LDS; update MFMAs; sum
-// the 4 waves' readouts and write one 64 x (d_V + 1) partial per slice and chunk.
+// Per chunk: q, k, v arrive in LDS by direct-to-LDS loads issued during the
+// previous chunk; parent products of the key side go to an LDS table; readout
+// MFMAs (per-wave accumulators) go to four LDS regions; update MFMAs; the sum of
+// the four regions is this slice's partial readout, written at the start of the
+// next chunk.
 #include "scan_mfma.h"
 
 #include <hip/hip_runtime.h>
@@ -45,24 +47,24 @@ template <int D, int NCT>
 struct Layout {
     static constexpr int XR = D + 8;         // raw q/k row (bf16): D coords, 1, then 7 zeros
     static constexpr int XSLOTS = XR / 8;    // 16-byte slots per raw row
+    static constexpr int VG = 64;            // value columns per column group
     static constexpr int KP = 68;            // kpar row stride (floats): 64 tokens + pad
     static constexpr int VT = 72;            // vT row stride (bf16): 64 tokens + pad
     static constexpr int UT = 68;            // readout region row stride (floats, rows = columns)
-    static constexpr int DV_MAX = NCT * 16;  // raw v row capacity (bf16)
     static constexpr int rawq = 0;                                  // bytes
     static constexpr int rawk = rawq + kL * XR * 2;
     static constexpr int rawv = rawk + kL * XR * 2;
-    static constexpr int vt = rawv + kL * DV_MAX * 2;
+    static constexpr int vt = rawv + kL * VG * 2;
     static constexpr int kp = vt + NCT * 16 * VT * 2;
     static constexpr int ur = kp + kRowsPerSlice * KP * 4;
-    static constexpr int rp = ur + kWavesPerSlice * NCT * 16 * UT * 4;
-    static constexpr int bytes = rp + kRowsPerSlice * 4;
+    static constexpr int bytes = ur + kWavesPerSlice * NCT * 16 * UT * 4;
     // state load/store staging (outside the chunk loop) aliases the readout regions
     static constexpr int IO = NCT * 16 + 4;                         // floats per feature row
     static constexpr int io_rows = kWavesPerSlice * 32;             // 2 tiles per wave per phase
     static_assert(io_rows * IO * 4 <= kWavesPerSlice * NCT * 16 * UT * 4, "state staging size");
     static_assert(rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kp % 16 == 0 && ur % 16 == 0,
                   "16-byte alignment of LDS regions");
+    static_assert((kL * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
 };
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -97,7 +99,7 @@ struct RowPtrs {
 
 // Direct-to-LDS copies of one chunk.  A wave instruction moves 64 lanes x 16 bytes
 // into a contiguous 1 KiB block; lane i fills bytes [16 i, 16 i + 16).  q and k rows
-// get a ninth slot holding the constant coordinates (1, 0, ..., 0).  Rows past n
+// get one more slot holding the constant coordinates (1, 0, ..., 0).  Rows past n
 // read row 0 of the chunk instead (masked later).
 template <int D, int NCT>
 __device__ inline void prefetch_x(const uint16_t* x, const uint16_t* one_row, int64_t t0, int nvalid,
@@ -115,24 +117,27 @@ __device__ inline void prefetch_x(const uint16_t* x, const uint16_t* one_row, in
     }
 }
 
+// The 64 value columns [col0, col0 + 64) of the chunk's v rows (row length d_V).
 template <int D, int NCT>
-__device__ inline void prefetch_v(const uint16_t* v, int64_t t0, int nvalid, int d_V, unsigned char* dst,
-                                  int w, int lane) {
-    const int VB = kL * d_V * 2;
-    for (int blk = w; blk < (VB + 1023) / 1024; blk += kWavesPerSlice) {
-        int off = blk * 1024 + lane * 16;
-        if (off >= VB) off = 0;                        // lanes past the chunk reload its start
-        const int t = off / (d_V * 2);
-        const int src = t < nvalid ? off : off % (d_V * 2);
-        __builtin_amdgcn_global_load_lds((const void*)((const char*)(v + t0 * d_V) + src),
+__device__ inline void prefetch_v(const uint16_t* v, int64_t t0, int nvalid, int d_V, int col0,
+                                  unsigned char* dst, int w, int lane) {
+#pragma unroll
+    for (int blk = w; blk < kL * 8 / 64; blk += kWavesPerSlice) {
+        const int sl = blk * 64 + lane;
+        const int t = sl >> 3, cs = sl & 7;
+        const uint16_t* src = v + (t0 + (t < nvalid ? t : 0)) * d_V + col0 + 8 * cs;
+        __builtin_amdgcn_global_load_lds((const void*)src,
                                          (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
     }
 }
 
-template <int D, int DV, int NPC>
+template <int D, int DV, int G, int NPC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
-    constexpr int NCT = (DV + 1 + 15) / 16;  // column tiles of [v | 1]
+    constexpr bool ONES = G == 0;            // group 0 carries the normaliser column
+    constexpr int col0 = 64 * G;             // first value column of the group
+    constexpr int NCT = ONES ? 5 : 4;        // column tiles of this group
+    constexpr int NCL = ONES ? 65 : 64;      // live columns of this group
     using LY = Layout<D, NCT>;
     constexpr int KS = kRowsPerWave / 4;     // readout K-steps per wave (32 features each)
     constexpr int NT = 2 * KS;               // update tiles per wave (16 features each)
@@ -144,7 +149,6 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     uint16_t* vt16 = reinterpret_cast<uint16_t*>(lds_raw + LY::vt);
     float* kpar = reinterpret_cast<float*>(lds_raw + LY::kp);
     float* ured = reinterpret_cast<float*>(lds_raw + LY::ur);
-    uint32_t* rowpar = reinterpret_cast<uint32_t*>(lds_raw + LY::rp);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -152,9 +156,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const int64_t bh = blockIdx.y;
     constexpr int d_V = DV, cols = DV + 1;
     const int nch = a.c_end - a.c_begin;
-    const int row_wg = slice * kRowsPerSlice;               // first row of the workgroup
-    const int row_w = row_wg + w * kRowsPerWave;            // first row of this wave
+    const int row_w = slice * kRowsPerSlice + w * kRowsPerWave;   // first row of this wave
     const int lb = rt.wave_lblock[slice * kWavesPerSlice + w];
+    // global column of local column j of this group (local 64 is the normaliser)
+    auto gcol = [&](int j) { return (ONES && j == 64) ? d_V : col0 + j; };
 
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + bh * (int64_t)a.n * D;
     const uint16_t* k = static_cast<const uint16_t*>(a.k) + bh * (int64_t)a.n * D;
@@ -170,7 +175,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const int nv = nvalid_of(a.c_begin);
         prefetch_x<D, NCT>(q, rt.one_row, t0, nv, lds_raw + LY::rawq, w, lane);
         prefetch_x<D, NCT>(k, rt.one_row, t0, nv, lds_raw + LY::rawk, w, lane);
-        prefetch_v<D, NCT>(v, t0, nv, d_V, lds_raw + LY::rawv, w, lane);
+        prefetch_v<D, NCT>(v, t0, nv, d_V, col0, lds_raw + LY::rawv, w, lane);
     }
 
     // per-lane row constants: query weight and LDS addresses of the parent coordinates
@@ -193,7 +198,6 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         cK[T] = rt.kscale[(row_w + 4 * s + (li >> 2)) * 8 + 4 * h + (li & 3)];
         ones[T] = __all(cK[T] == 1.0f);
     }
-    if (tid < kRowsPerSlice) rowpar[tid] = rt.parent[row_wg + tid];
 
     // Resident state slice, update-accumulator layout: lane (column 16 ct + li, g)
     // register r of tile T = 2 s + h holds kernel feature (row 4 s + g, element 4 h + r).
@@ -206,17 +210,18 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         // through LDS, 2 tiles per wave at a time: plain gather loop, then a register
         // fill with compile-time indices (keeps the unrolled code free of table loads)
         float* io = ured;
+        const int row_wg = slice * kRowsPerSlice;
 #pragma unroll
         for (int ph = 0; ph < NT / 2; ++ph) {
             __syncthreads();
-            for (int idx = tid; idx < LY::io_rows * cols; idx += 256) {
-                const int fr = idx / cols, j = idx % cols;
+            for (int idx = tid; idx < LY::io_rows * NCL; idx += 256) {
+                const int fr = idx / NCL, j = idx % NCL;
                 const int ww = fr / 32, fl = fr % 32;
                 const int T = 2 * ph + fl / 16, rho = fl % 16;
                 const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
                                4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
-                io[fr * LY::IO + j] = F >= 0 ? rt.kscale[fi] * state[(int64_t)j * a.M_pad + F] : 0.0f;
+                io[fr * LY::IO + j] = F >= 0 ? rt.kscale[fi] * state[(int64_t)gcol(j) * a.M_pad + F] : 0.0f;
             }
             __syncthreads();
 #pragma unroll
@@ -226,7 +231,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * ct + li;
-                        S[2 * ph + Tl][ct][r] = j < cols ? io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + j] : 0.0f;
+                        S[2 * ph + Tl][ct][r] = j < NCL ? io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + j] : 0.0f;
                     }
         }
     }
@@ -238,10 +243,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) Sb[s2][ct] = pack_tiles(S[2 * s2][ct], S[2 * s2 + 1][ct]);
 
-    // columns of [v | 1] past d_V are zero for good
+    // columns of [v | 1] past the live ones are zero for good
     __syncthreads();
-    for (int idx = tid; idx < (NCT * 16 - cols) * kL; idx += 256) {
-        const int j = cols + idx / kL, t = idx % kL;
+    for (int idx = tid; idx < (NCT * 16 - NCL) * kL; idx += 256) {
+        const int j = NCL + idx / kL, t = idx % kL;
         vt16[j * LY::VT + t] = 0;
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -250,40 +255,39 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     // A slice's partial readout of chunk c (the sum of the 4 waves' regions, [col][token])
     // is written at the start of chunk c + 1, so the stores complete during that chunk.
     auto write_partial = [&](int c) {
-        float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)kL * cols +
-                    w * kL + lane;
+        float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)kL * cols + lane;
         const float* up = ured + w * LY::UT + lane;
         constexpr int WS = NCT * 16 * LY::UT;                  // one wave's region
-        constexpr int NJ = (cols + 3) / 4;                     // columns per wave (last one partial)
+        constexpr int NJ = (NCL + 3) / 4;                      // columns per wave (last one partial)
 #pragma unroll
         for (int i = 0; i < NJ; ++i) {
-            if (i < NJ - 1 || w + 4 * i < cols)
-                pp[4 * i * kL] = (up[4 * i * LY::UT] + up[4 * i * LY::UT + WS]) +
-                                 (up[4 * i * LY::UT + 2 * WS] + up[4 * i * LY::UT + 3 * WS]);
+            const int j = w + 4 * i;
+            if (i < NJ - 1 || j < NCL)
+                pp[gcol(j) * kL] = (up[4 * i * LY::UT] + up[4 * i * LY::UT + WS]) +
+                                   (up[4 * i * LY::UT + 2 * WS] + up[4 * i * LY::UT + 3 * WS]);
         }
     };
 
     for (int c = a.c_begin; c < a.c_end; ++c) {
         const int nvalid = nvalid_of(c);
-        if (c > a.c_begin) write_partial(c - 1);
         const int64_t t1 = (int64_t)(c + 1) * kL;
         const bool more = c + 1 < a.c_end;
         const int nvalid1 = more ? nvalid_of(c + 1) : 0;
+        if (c > a.c_begin) write_partial(c - 1);
 
-        // ---- P1: [v | 1] transposed to bf16 columns, key parent products ---------------
-        static_assert(DV % 4 == 0 && (kL * DV / 4) % 256 == 0, "v staging shape");
+        // ---- P1: value columns transposed to bf16, key parent products ---------------
         {
-            constexpr int NV = kL * DV / 4 / 256;
+            constexpr int NV = kL * LY::VG / 4 / 256;
             uint2 r2[NV];
 #pragma unroll
             for (int it = 0; it < NV; ++it) {            // all reads first: no LDS round trips
                 const int idx = tid + 256 * it;
-                r2[it] = *reinterpret_cast<const uint2*>(rv + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4)));
+                r2[it] = *reinterpret_cast<const uint2*>(rv + (idx / (LY::VG / 4)) * LY::VG + 4 * (idx % (LY::VG / 4)));
             }
 #pragma unroll
             for (int it = 0; it < NV; ++it) {
                 const int idx = tid + 256 * it;
-                const int t = idx / (DV / 4), c4 = idx % (DV / 4);
+                const int t = idx / (LY::VG / 4), c4 = idx % (LY::VG / 4);
                 const uint2 x = t < nvalid ? r2[it] : uint2{0u, 0u};
                 uint16_t* dst = vt16 + 4 * c4 * LY::VT + t;
                 dst[0] = (uint16_t)(x.x & 0xffffu);
@@ -292,7 +296,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 dst[3 * LY::VT] = (uint16_t)(x.y >> 16);
             }
         }
-        if (tid < kL) vt16[DV * LY::VT + tid] = tid < nvalid ? (uint16_t)0x3f80u : (uint16_t)0u;
+        if (ONES && tid < kL) vt16[64 * LY::VT + tid] = tid < nvalid ? (uint16_t)0x3f80u : (uint16_t)0u;
         {
             // each wave builds the parent products of its own 16 rows; lane = token.
             // The parent words are wave-uniform (scalar loads).
@@ -312,7 +316,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             for (int i = 0; i < kRowsPerWave; ++i) kdst[i * LY::KP] = tv ? kp[i] : 0.0f;
         }
         __syncthreads();                                               // B1
-        if (more) prefetch_v<D, NCT>(v, t1, nvalid1, d_V, lds_raw + LY::rawv, w, lane);
+        if (more) prefetch_v<D, NCT>(v, t1, nvalid1, d_V, col0, lds_raw + LY::rawv, w, lane);
 
         // ---- P2: readout U = Q^ . bf16(S) ------------------------------------------
         {
@@ -366,7 +370,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 for (int e = 0; e < 8; ++e)
                     kreg[h][kk][e] = bf16_at(rk, (32 * kk + 8 * g + e) * XR + 8 * lb + 4 * h + (li & 3));
         __syncthreads();                                               // B2
-        // the raw buffers are free: the next chunk streams in during the update
+        // the raw q/k buffers are free: the next chunk streams in during the update
         if (more) {
             prefetch_x<D, NCT>(q, rt.one_row, t1, nvalid1, lds_raw + LY::rawq, w, lane);
             prefetch_x<D, NCT>(k, rt.one_row, t1, nvalid1, lds_raw + LY::rawk, w, lane);
@@ -381,9 +385,9 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 Vop[ct] = *reinterpret_cast<const bf16x8*>(vt16 + (16 * ct + li) * LY::VT + 32 * kk + 8 * g);
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const float* kp = kpar + (w * kRowsPerWave + 4 * s + (li >> 2)) * LY::KP + 32 * kk + 8 * g;
-                const f32x4v p0 = *reinterpret_cast<const f32x4v*>(kp);
-                const f32x4v p1 = *reinterpret_cast<const f32x4v*>(kp + 4);
+                const float* kpr = kpar + (w * kRowsPerWave + 4 * s + (li >> 2)) * LY::KP + 32 * kk + 8 * g;
+                const f32x4v p0 = *reinterpret_cast<const f32x4v*>(kpr);
+                const f32x4v p1 = *reinterpret_cast<const f32x4v*>(kpr + 4);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int T = 2 * s + h;
@@ -413,7 +417,6 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) Sb[KS - 1][ct] = pack_tiles(S[2 * KS - 2][ct], S[2 * KS - 1][ct]);
-
         __builtin_amdgcn_s_waitcnt(0);          // the next chunk has landed
         __syncthreads();                                               // B3
     }
@@ -422,6 +425,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     if (a.store_state) {
         // through LDS as for the load; the internal S' = c S is scaled back by 1/c
         float* io = ured;
+        const int row_wg = slice * kRowsPerSlice;
 #pragma unroll
         for (int ph = 0; ph < NT / 2; ++ph) {
             __syncthreads();
@@ -433,35 +437,53 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                     for (int r = 0; r < 4; ++r)
                         io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + 16 * ct + li] = S[2 * ph + Tl][ct][r];
             __syncthreads();
-            for (int idx = tid; idx < LY::io_rows * cols; idx += 256) {
-                const int fr = idx / cols, j = idx % cols;
+            for (int idx = tid; idx < LY::io_rows * NCL; idx += 256) {
+                const int fr = idx / NCL, j = idx % NCL;
                 const int ww = fr / 32, fl = fr % 32;
                 const int T = 2 * ph + fl / 16, rho = fl % 16;
                 const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
                                4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
-                if (F >= 0) state[(int64_t)j * a.M_pad + F] = io[fr * LY::IO + j] / rt.kscale[fi];
+                if (F >= 0) state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / rt.kscale[fi];
             }
         }
         if (slice == 0) {
             const int64_t padn = a.M_pad - a.M;
-            for (int64_t idx = tid; idx < cols * padn; idx += 256)
-                state[(idx / padn) * a.M_pad + a.M + idx % padn] = 0.0f;
+            for (int64_t idx = tid; idx < NCL * padn; idx += 256)
+                state[(int64_t)gcol((int)(idx / padn)) * a.M_pad + a.M + idx % padn] = 0.0f;
         }
     }
 }
 
-template <int D, int DV, int NPC>
+template <int D, int DV, int G, int NPC>
 hipError_t launch_t(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
-    using LY = Layout<D, (DV + 1 + 15) / 16>;
+    using LY = Layout<D, G == 0 ? 5 : 4>;
     static_assert(LY::bytes <= 160 * 1024, "LDS budget");
     RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock, m.one_row};
-    hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, NPC>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, G, NPC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, NPC>), dim3(a.nslices, a.BH), dim3(256), LY::bytes, st,
+    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, G, NPC>), dim3(a.nslices, a.BH), dim3(256), LY::bytes, st,
                        a, rt);
     return hipGetLastError();
+}
+
+// one launch per column group of 64 value columns; group 0 carries the normaliser
+template <int D, int NPC>
+hipError_t launch_groups(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
+    if (a.d_V == 64) return launch_t<D, 64, 0, NPC>(a, m, st);
+    hipError_t e = launch_t<D, 128, 0, NPC>(a, m, st);
+    return e == hipSuccess ? launch_t<D, 128, 1, NPC>(a, m, st) : e;
+}
+
+template <int D>
+hipError_t launch_d(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
+    switch (a.P) {
+        case 2: return launch_groups<D, 0>(a, m, st);
+        case 3: return launch_groups<D, 1>(a, m, st);
+        case 4: return launch_groups<D, 2>(a, m, st);
+        default: return launch_groups<D, 3>(a, m, st);
+    }
 }
 
 }  // namespace
@@ -509,17 +531,12 @@ void free_mfma_tables(MfmaTables& m) {
 }
 
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L) {
-    return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && L == kL && d_K == 64 &&
-           d_V == 64;
+    return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && L == kL &&
+           (d_K == 64 || d_K == 128) && (d_V == 64 || d_V == 128);
 }
 
 hipError_t launch_scan_mfma(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
-    switch (a.P) {
-        case 2: return launch_t<64, 64, 0>(a, m, st);
-        case 3: return launch_t<64, 64, 1>(a, m, st);
-        case 4: return launch_t<64, 64, 2>(a, m, st);
-        default: return launch_t<64, 64, 3>(a, m, st);
-    }
+    return a.d_K == 64 ? launch_d<64>(a, m, st) : launch_d<128>(a, m, st);
 }
 
 }  // namespace sata

@@ -64,6 +64,9 @@ def _load():
     lib.oracle_direct.restype = None
     lib.oracle_direct.argtypes = [dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp]
+    lib.oracle_direct_rows.restype = None
+    lib.oracle_direct_rows.argtypes = [dp, dp, dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, i64p, i64p, ctypes.c_int64, dp]
     lib.oracle_feature_dim.restype = ctypes.c_int64
     lib.oracle_feature_dim.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.oracle_feature_form.restype = ctypes.c_int64
@@ -144,6 +147,30 @@ def direct(q, k, v, P: int, return_den: bool = False):
     den = np.zeros(lead + (n,), dtype=np.float64)
     _load().oracle_direct(_dp(q), _dp(k), _dp(v), heads, n, dK, dV, P, _dp(y), _dp(den))
     return (y, den) if return_den else y
+
+
+def direct_rows(q, k, v, P: int, heads, rows):
+    """Sampled rows of the direct form, fp64: out[r] = y[heads[r], rows[r]].
+    q, k: [heads, n, dK]; v: [heads, n, dV] (leading dims flattened)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, dK = q.shape[-2:]
+    dV = v.shape[-1]
+    q = q.reshape(-1, n, dK)
+    k = k.reshape(-1, n, dK)
+    v = v.reshape(-1, n, dV)
+    heads = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if heads.shape != rows.shape or heads.ndim != 1:
+        raise ValueError("heads and rows must be 1-D of one length")
+    if heads.size and (heads.min() < 0 or heads.max() >= q.shape[0] or rows.min() < 0
+                       or rows.max() >= n):
+        raise ValueError("sampled head or row out of range")
+    out = np.zeros((rows.shape[0], dV), dtype=np.float64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    _load().oracle_direct_rows(_dp(q), _dp(k), _dp(v), n, dK, dV, P,
+                               heads.ctypes.data_as(i64p), rows.ctypes.data_as(i64p),
+                               rows.shape[0], _dp(out))
+    return out
 
 
 def feature_form(q, k, v, P: int, want_y: bool = True):

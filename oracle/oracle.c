@@ -131,6 +131,28 @@ double oracle_alpha(int p, int dK) { return alpha(p, dK); }
  * The sum includes t = T (the recurrence of [TA Features] runs t = 1..T).
  * den_out (nullable) receives the denominator of every row.
  */
+/* One output row of the direct form: y_T = sum_{t<=T} w(q_T,k_t) v_t / sum_{t<=T} w(q_T,k_t)
+ * for one head (q, k, v point at that head's rows). */
+static double direct_row(const double *q, const double *k, const double *v, int64_t T,
+                         int dK, int dV, int P, const double *a, double *yT)
+{
+    const double *qT = q + T * dK;
+    double den = 0.0;
+    for (int j = 0; j < dV; ++j) yT[j] = 0.0;
+    for (int64_t t = 0; t <= T; ++t) {
+        const double *kt = k + t * dK;
+        const double *vt = v + t * dV;
+        double x = 0.0;
+        for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
+        double w = 0.0, xp = 1.0;
+        for (int p = 0; p < P; ++p) { w += a[p] * xp; xp *= x; }
+        den += w;
+        for (int j = 0; j < dV; ++j) yT[j] += w * vt[j];
+    }
+    for (int j = 0; j < dV; ++j) yT[j] /= den;
+    return den;
+}
+
 void oracle_direct(const double *q, const double *k, const double *v,
                    int64_t heads, int64_t n, int dK, int dV, int P,
                    double *y, double *den_out)
@@ -141,23 +163,27 @@ void oracle_direct(const double *q, const double *k, const double *v,
 #pragma omp parallel for collapse(2) schedule(dynamic, 16)
     for (int64_t h = 0; h < heads; ++h) {
         for (int64_t T = 0; T < n; ++T) {
-            const double *qT = q + (h * n + T) * dK;
-            double *yT = y + (h * n + T) * dV;
-            double den = 0.0;
-            for (int j = 0; j < dV; ++j) yT[j] = 0.0;
-            for (int64_t t = 0; t <= T; ++t) {
-                const double *kt = k + (h * n + t) * dK;
-                const double *vt = v + (h * n + t) * dV;
-                double x = 0.0;
-                for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
-                double w = 0.0, xp = 1.0;
-                for (int p = 0; p < P; ++p) { w += a[p] * xp; xp *= x; }
-                den += w;
-                for (int j = 0; j < dV; ++j) yT[j] += w * vt[j];
-            }
-            for (int j = 0; j < dV; ++j) yT[j] /= den;
+            const double den = direct_row(q + h * n * dK, k + h * n * dK, v + h * n * dV, T,
+                                          dK, dV, P, a, y + (h * n + T) * dV);
             if (den_out) den_out[h * n + T] = den;
         }
+    }
+}
+
+/* Sampled rows of the direct form: out[r] = y of token rows[r] of head heads_of[r]
+ * (q, k: [heads][n][dK], v: [heads][n][dV]); each row costs O(T (dK + dV)). */
+void oracle_direct_rows(const double *q, const double *k, const double *v,
+                        int64_t n, int dK, int dV, int P,
+                        const int64_t *heads_of, const int64_t *rows, int64_t nr, double *out)
+{
+    double a[32];
+    for (int p = 0; p < P && p < 32; ++p) a[p] = alpha(p, dK);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nr; ++r) {
+        const int64_t h = heads_of[r];
+        direct_row(q + h * n * dK, k + h * n * dK, v + h * n * dV, rows[r], dK, dV, P, a,
+                   out + r * dV);
     }
 }
 

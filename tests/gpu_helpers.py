@@ -55,11 +55,24 @@ def state_col_err(S_gpu, S_ref) -> float:
     return float(np.max(num / np.where(den > 0, den, 1.0)))
 
 
-def state_rows_err(S_gpu_rows, S_ref_rows, col_scale) -> float:
-    """Sampled rows: |dS[f,j]| / col_scale[j] (col_scale from an exact bound)."""
-    d = np.abs(np.asarray(S_gpu_rows, dtype=np.float64) - S_ref_rows) / col_scale[None, :]
-    return float(np.max(d))
+def sample_feature_rows(M: int, count: int, seed: int) -> np.ndarray:
+    """Rows of the state to check: the first few (p = 0 and degree-1 features), the
+    last two, and `count` drawn at random."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 3, M - 2, M - 1]
+    return np.unique(np.concatenate([fixed, rng.choice(M, size=count, replace=False)]))
+
+
+def sampled_state_err(S_gpu, S_ref_rows, rows) -> float:
+    """The state bound on sampled rows: S_gpu is one head's [cols, M_pad] state,
+    S_ref_rows[r, j] = S[rows[r], j] from the oracle.  max over columns j of
+    max_r |dS| / max_r |S_ref| (row 0, the largest row, is always sampled)."""
+    got = np.asarray(S_gpu, dtype=np.float64)[:, rows].T
+    num = np.max(np.abs(got - S_ref_rows), axis=0)
+    den = np.max(np.abs(S_ref_rows), axis=0)
+    return float(np.max(num / np.where(den > 0, den, 1.0)))
 
 
 __all__ = ["inputs", "oracle", "sata", "TOL_BF16", "TOL_F32", "say", "dev_tensor", "upload",
-           "prefill", "new_state", "max_row_err", "state_col_err", "state_rows_err"]
+           "prefill", "new_state", "max_row_err", "state_col_err", "sample_feature_rows",
+           "sampled_state_err"]

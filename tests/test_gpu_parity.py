@@ -316,3 +316,72 @@ def test_mfma_segmented_matches_single_segment(torch_cuda):
     say("  rel diffs y %.2e %.2e state %.2e" % (d12, d13, dS))
     assert d12 <= 1e-5 and d13 <= 1e-5 and dS <= 1e-5
     t.close()
+
+
+# --------------------------------------------------------------------------
+# bf16 MFMA scan with 128-wide heads: two column groups (d_V = 128) and the
+# 17-slot raw rows of d_K = 128; state checked on sampled rows
+# --------------------------------------------------------------------------
+
+def _state_check(S_head, x_k, x_v, P, n_rows, seed, tol):
+    from gpu_helpers import sample_feature_rows, sampled_state_err
+    M = oracle.feature_dim(x_k.shape[-1], P)
+    rows = sample_feature_rows(M, n_rows, seed)
+    ref = oracle.state_rows(x_k, x_v, P, rows)
+    Sg = S_head.cpu().numpy()
+    err = sampled_state_err(Sg, ref, rows)
+    say("  state err %.3e on %d sampled rows" % (err, rows.size))
+    assert err <= tol
+    assert np.all(Sg[:, M:] == 0.0), "padding of the state must stay zero"
+
+
+@pytest.mark.parametrize("dK,dV,n", [(128, 128, 200), (128, 64, 130), (64, 128, 129)])
+def test_mfma_wide_heads(torch_cuda, dK, dV, n):
+    say("mfma bf16 d_K=%d d_V=%d n=%d" % (dK, dV, n))
+    x = inputs.draw((1, 2, n, dK), (1, 2, n, dV), "bf16", 0.35, 1.0, 50 + dK + dV)
+    q, k, v = upload(x, "bf16")
+    t = _tables(dK, 4)
+    S = new_state(1, 2, dK, dV, 4)
+    y = prefill(t, q, k, v, 64, S)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    err = max_row_err(y.cpu().numpy(), ref)
+    say("  y err %.3e" % err)
+    assert err <= TOL_BF16
+    for h in (0, 1):
+        _state_check(S[0, h], x["k"][0, h], x["v"][0, h], 4, 150, h, TOL_BF16)
+    assert float(S[0, 1, dV, 0]) == n
+    t.close()
+
+
+def test_mfma_wide_continue_and_segmented(torch_cuda):
+    """d = 128: a continued prefill reaches the oracle, and a run cut into segments
+    by a small workspace equals one segment to fp32 rounding."""
+    say("mfma d=128 continue + segmented")
+    n1, n2 = 150, 190
+    x = inputs.draw((1, 2, n1 + n2, 128), (1, 2, n1 + n2, 128), "bf16", 0.35, 1.0, 61)
+    q, k, v = upload(x, "bf16")
+    t = _tables(128, 4)
+    S = new_state(1, 2, 128, 128, 4)
+    prefill(t, q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(),
+            64, S)
+    y2 = prefill(t, q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(),
+                 v[:, :, n1:].contiguous(), 64, S, continue_state=True)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    err = max_row_err(y2.cpu().numpy(), ref[:, :, n1:])
+    say("  continued y err %.3e" % err)
+    assert err <= TOL_BF16
+    _state_check(S[0, 0], x["k"][0, 0], x["v"][0, 0], 4, 100, 7, TOL_BF16)
+
+    S1 = new_state(1, 2, 128, 128, 4)
+    y1 = prefill(t, q, k, v, 64, S1)
+    t.set_workspace_limit(64 << 20)          # a few chunks per segment at d = 128
+    S2 = new_state(1, 2, 128, 128, 4)
+    y3 = prefill(t, q, k, v, 64, S2)
+    torch_cuda.cuda.synchronize()
+    d13 = float((y1 - y3).abs().max() / y1.abs().max())
+    dS = float((S1 - S2).abs().max() / S1.abs().max())
+    say("  segmented rel diffs y %.2e state %.2e" % (d13, dS))
+    assert d13 <= 1e-5 and dS <= 1e-5
+    t.close()

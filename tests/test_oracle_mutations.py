@@ -54,9 +54,9 @@ MUTANTS = {
     "power_index": ("for (int p = 0; p < P; ++p) { w += a[p] * xp; xp *= x; }",
                     "for (int p = 0; p < P; ++p) { xp *= x; w += a[p] * xp; }", _alpha_pins),
     # causal sum excludes the diagonal
-    "causal": ("den += w;\n                for (int j = 0; j < dV; ++j) yT[j] += w * vt[j];",
-               "if (t == T) continue;\n                den += w;\n"
-               "                for (int j = 0; j < dV; ++j) yT[j] += w * vt[j];",
+    "causal": ("den += w;\n        for (int j = 0; j < dV; ++j) yT[j] += w * vt[j];",
+               "if (t == T) continue;\n        den += w;\n"
+               "        for (int j = 0; j < dV; ++j) yT[j] += w * vt[j];",
                _causal_pins),
     # tables: a multiplicity of one for every monomial
     "multiplicity": ("count[key] += 1;", "count[key] = 1;", _table_pins),

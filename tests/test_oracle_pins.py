@@ -151,6 +151,24 @@ def test_P3_is_quadratic_kernel():
     np.testing.assert_allclose(y, expect, rtol=1e-12, atol=1e-12)
 
 
+def test_direct_rows_sampled():
+    """Sampled rows across heads equal the P = 3 quadratic kernel written with
+    numpy, and oracle.direct's rows at P = 4."""
+    c = math.sqrt(8)
+    heads = [_rand(60, 8, 4, 0.5, 40 + h) for h in range(3)]
+    q = np.stack([x[0] for x in heads]); k = np.stack([x[1] for x in heads])
+    v = np.stack([x[2] for x in heads])
+    hs = np.array([0, 2, 1, 1, 2, 0, 2])
+    ts = np.array([0, 59, 17, 1, 33, 58, 0])
+    got = oracle.direct_rows(q, k, v, 3, hs, ts)
+    for r, (h, t) in enumerate(zip(hs, ts)):
+        expect = _np_attention(q[h], k[h], v[h], lambda s: 1.0 + s / c + (s / c) ** 2 / 2.0)
+        np.testing.assert_allclose(got[r], expect[t], rtol=1e-12, atol=1e-12)
+    full = oracle.direct(q, k, v, 4)
+    np.testing.assert_allclose(oracle.direct_rows(q, k, v, 4, hs, ts), full[hs, ts],
+                               rtol=1e-14, atol=1e-14)
+
+
 def test_large_P_converges_to_softmax():
     """The Taylor series of exp(q.k/c) converges to exp: at large P the direct
     form is softmax attention (scipy.special.softmax over the causal row)."""
