@@ -1,35 +1,45 @@
-// kern_scan_mfma.hip -- bf16 MFMA chunked prefill scan for gfx950.
+// kern_scan_mfma.hip -- MFMA chunked prefill scan for gfx950 (fp16 operands, fp32 state).
 //
 // The inter-chunk half of the chunked prefill ([TA] "Feature maps and linear
 // attention": the state recurrence, evaluated chunk by chunk):
 //     readout   part[t][j] = sum_f qw_f phi_f(q_t) S[f][j]      (S before the chunk)
 //     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
 // Both are dense contractions over a 64-token chunk and a slice of the feature
-// axis, run as v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
+// axis, run as v_mfma_f32_16x16x32_f16 with fp32 accumulation:
 //     readout  (64 tokens x 32 features) x (32 features x 16 columns)
 //     update   (16 features x 32 tokens) x (32 tokens x 16 columns)
+//
+// Operands are fp16, not bf16: gfx950 multiplies fp16 pairs in one VALU
+// instruction (bf16 only one value at a time) and converts two fp32 values to fp16
+// in one, and the operand building is what bounds this kernel; the matrix rate of
+// the two types is the same, and fp16 keeps 3 more mantissa bits.  Exact powers of
+// two keep every operand inside fp16's range: the [v | 1] operand carries 2^-8
+// (the internal state is S' = 2^-8 c S, with c the key-side factor below), the
+// query operand 2^12, and the readout is scaled back by 2^-4 before it is stored.
+// The state stays fp32 in registers; its fp16 copy only feeds the readout.
 //
 // Work split.  The columns of [v | 1] are cut into groups of 64 value columns;
 // group 0 also carries the normaliser column (65 columns, 5 tiles of 16), the
 // others 4 tiles.  One workgroup (4 waves) owns one slice of 64 rows = 512 kernel
 // features of one head for one column group, and walks all chunks of the segment
 // in order; its fp32 state never leaves the registers (8 update tiles x 5 column
-// tiles x 4 = 160 accumulator registers per lane per wave).  A wave owns 16 rows
-// of one l-block b: its kernel features are (parent a, l = 8b + e), e = 0..7 (see
-// mfma_rows.cpp).  Feature tiles are never written to HBM: per chunk the wave keeps
-// the 8 coordinates x_{8b..8b+7} of its tokens in registers and builds
+// tiles x 4 = 160 registers per lane per wave).  A wave owns 16 rows of one
+// l-block b: its kernel features are (parent a, l = 8b + e), e = 0..7 (see
+// mfma_rows.cpp).  Feature tiles are never written to HBM: per chunk the wave
+// builds
 //     query side  q^(a, l)[t] = (W_a q_a[t]) * q_l[t]        (W_a = alpha_p C(a) p)
 //     key side    k^(a, l)[t] = kpar_a[t] * k_l[t] * c_(a,l)  (c: 0 / 1/(1+m) / 1)
 // directly in the MFMA operand layout (q_a, kpar_a: parent products).  The readout
-// takes the state packed to bf16 after its last update of the previous chunk: the
+// takes the state packed to fp16 after its last update of the previous chunk: the
 // update's accumulator layout (lane = column, 4 rows each) over two tiles is a
 // 32-deep B operand when the query operand uses the same feature order.
 //
-// Per chunk: q, k, v arrive in LDS by direct-to-LDS loads issued during the
-// previous chunk; parent products of the key side go to an LDS table; readout
-// MFMAs (per-wave accumulators) go to four LDS regions; update MFMAs; the sum of
-// the four regions is this slice's partial readout, written at the start of the
-// next chunk.
+// Per chunk: q, k, v arrive in LDS (bf16) by direct-to-LDS loads issued during the
+// previous chunk; the values are moved to fp16 token-major tables (v transposed,
+// each wave's 8 key coordinates, the key parent products); readout MFMAs
+// (per-wave accumulators) go to four LDS regions; update MFMAs; the sum of the
+// four regions is this slice's partial readout, written at the start of the next
+// chunk.
 #include "scan_mfma.h"
 
 #include <hip/hip_runtime.h>
@@ -38,32 +48,35 @@ namespace sata {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kL = 64;     // chunk length of the MFMA scan
+constexpr int kL = 64;                      // chunk length of the MFMA scan
+constexpr float kVScale = 1.0f / 256.0f;    // on the [v | 1] operand of the update
+constexpr float kQScale = 4096.0f;          // on the query operand of the readout
+constexpr float kUScale = 1.0f / 16.0f;     // 1 / (kQScale kVScale): readout back to S's units
 
 template <int D, int NCT>
 struct Layout {
     static constexpr int XR = D + 8;         // raw q/k row (bf16): D coords, 1, then 7 zeros
     static constexpr int XSLOTS = XR / 8;    // 16-byte slots per raw row
     static constexpr int VG = 64;            // value columns per column group
-    static constexpr int KP = 68;            // kpar row stride (floats): 64 tokens + pad
-    static constexpr int VT = 72;            // vT row stride (bf16): 64 tokens + pad
+    static constexpr int TS = 72;            // fp16 token-major row stride: 64 tokens + pad
     static constexpr int UT = 68;            // readout region row stride (floats, rows = columns)
     static constexpr int rawq = 0;                                  // bytes
     static constexpr int rawk = rawq + kL * XR * 2;
     static constexpr int rawv = rawk + kL * XR * 2;
-    static constexpr int vt = rawv + kL * VG * 2;
-    static constexpr int kp = vt + NCT * 16 * VT * 2;
-    static constexpr int ur = kp + kRowsPerSlice * KP * 4;
+    static constexpr int vt = rawv + kL * VG * 2;                   // [NCT*16 columns][TS]
+    static constexpr int kt = vt + NCT * 16 * TS * 2;               // [wave][8 coordinates][TS]
+    static constexpr int kp = kt + kWavesPerSlice * 8 * TS * 2;     // [64 rows][TS]
+    static constexpr int ur = kp + kRowsPerSlice * TS * 2;
     static constexpr int bytes = ur + kWavesPerSlice * NCT * 16 * UT * 4;
     // state load/store staging (outside the chunk loop) aliases the readout regions
     static constexpr int IO = NCT * 16 + 4;                         // floats per feature row
     static constexpr int io_rows = kWavesPerSlice * 32;             // 2 tiles per wave per phase
     static_assert(io_rows * IO * 4 <= kWavesPerSlice * NCT * 16 * UT * 4, "state staging size");
-    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kp % 16 == 0 && ur % 16 == 0,
-                  "16-byte alignment of LDS regions");
+    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kt % 16 == 0 && kp % 16 == 0 &&
+                  ur % 16 == 0, "16-byte alignment of LDS regions");
     static_assert((kL * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
 };
 
@@ -71,22 +84,28 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ inline float bf16_at(const uint16_t* p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
 
-__device__ inline bf16x8 pack_bf16(const float* x) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
-    return r;
+// 8 bf16 values (one 16-byte slot) to fp16; exact for |x| in fp16's normal range
+__device__ inline f16x8 bf16x8_to_f16(const uint4& r) {
+    f16x8 o;
+    o[0] = (_Float16)bf16_lo(r.x); o[1] = (_Float16)bf16_hi(r.x);
+    o[2] = (_Float16)bf16_lo(r.y); o[3] = (_Float16)bf16_hi(r.y);
+    o[4] = (_Float16)bf16_lo(r.z); o[5] = (_Float16)bf16_hi(r.z);
+    o[6] = (_Float16)bf16_lo(r.w); o[7] = (_Float16)bf16_hi(r.w);
+    return o;
 }
 
-__device__ inline bf16x8 pack_tiles(const f32x4v& lo, const f32x4v& hi) {
-    bf16x8 r;
+__device__ inline f16x8 pack_tiles(const f32x4v& lo, const f32x4v& hi) {
+    f16x8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        r[e] = (__bf16)lo[e];
-        r[4 + e] = (__bf16)hi[e];
+        r[e] = (_Float16)lo[e];
+        r[4 + e] = (_Float16)hi[e];
     }
     return r;
 }
+
+// the key-side factor as the update applies it (rounded to fp16)
+__device__ inline float kfactor(float c) { return (float)(_Float16)c; }
 
 struct RowPtrs {
     const uint32_t* parent;
@@ -141,13 +160,14 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     using LY = Layout<D, NCT>;
     constexpr int KS = kRowsPerWave / 4;     // readout K-steps per wave (32 features each)
     constexpr int NT = 2 * KS;               // update tiles per wave (16 features each)
-    constexpr int XR = LY::XR;
+    constexpr int XR = LY::XR, TS = LY::TS;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint16_t* rq = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawq);
     const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
     const uint16_t* rv = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawv);
-    uint16_t* vt16 = reinterpret_cast<uint16_t*>(lds_raw + LY::vt);
-    float* kpar = reinterpret_cast<float*>(lds_raw + LY::kp);
+    _Float16* vt = reinterpret_cast<_Float16*>(lds_raw + LY::vt);
+    _Float16* kt = reinterpret_cast<_Float16*>(lds_raw + LY::kt);
+    _Float16* kp = reinterpret_cast<_Float16*>(lds_raw + LY::kp);
     float* ured = reinterpret_cast<float*>(lds_raw + LY::ur);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -178,8 +198,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         prefetch_v<D, NCT>(v, t0, nv, d_V, col0, lds_raw + LY::rawv, w, lane);
     }
 
-    // per-lane row constants: query weight and LDS addresses of the parent coordinates
-    // of row 4 s + g in this lane's token row of the raw q buffer (m-tile 0)
+    // per-lane row constants: query weight (with the operand scale) and LDS addresses of
+    // the parent coordinates of row 4 s + g in this lane's token row of the raw q buffer
     uint32_t qoff[KS][NPC > 0 ? NPC : 1];
     float Wq[KS];
 #pragma unroll
@@ -188,18 +208,17 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
         for (int e = 0; e < NPC; ++e)
             qoff[s][e] = (uint32_t)(LY::rawq + (li * XR + ((p3 >> (10 * e)) & 1023u)) * 2);
-        Wq[s] = rt.weight[row_w + 4 * s + g];
+        Wq[s] = rt.weight[row_w + 4 * s + g] * kQScale;
     }
-    float cK[NT];
-    bool ones[NT];
+    // key-side factor of this lane's feature in update tile T
+    _Float16 cK[NT];
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
         const int s = T >> 1, h = T & 1;
-        cK[T] = rt.kscale[(row_w + 4 * s + (li >> 2)) * 8 + 4 * h + (li & 3)];
-        ones[T] = __all(cK[T] == 1.0f);
+        cK[T] = (_Float16)rt.kscale[(row_w + 4 * s + (li >> 2)) * 8 + 4 * h + (li & 3)];
     }
 
-    // Resident state slice, update-accumulator layout: lane (column 16 ct + li, g)
+    // Resident state slice S', update-accumulator layout: lane (column 16 ct + li, g)
     // register r of tile T = 2 s + h holds kernel feature (row 4 s + g, element 4 h + r).
     f32x4v S[NT][NCT];
 #pragma unroll
@@ -221,7 +240,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
                                4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
-                io[fr * LY::IO + j] = F >= 0 ? rt.kscale[fi] * state[(int64_t)gcol(j) * a.M_pad + F] : 0.0f;
+                io[fr * LY::IO + j] =
+                    F >= 0 ? kfactor(rt.kscale[fi]) * kVScale * state[(int64_t)gcol(j) * a.M_pad + F] : 0.0f;
             }
             __syncthreads();
 #pragma unroll
@@ -235,9 +255,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                     }
         }
     }
-    // bf16 copy of the state in the readout's B-operand layout, refreshed at the end of
+
+    // fp16 copy of the state in the readout's B-operand layout, refreshed at the end of
     // every update (tile pair s covers the readout's K-step s)
-    bf16x8 Sb[KS][NCT];
+    f16x8 Sb[KS][NCT];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
@@ -245,10 +266,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 
     // columns of [v | 1] past the live ones are zero for good
     __syncthreads();
-    for (int idx = tid; idx < (NCT * 16 - NCL) * kL; idx += 256) {
-        const int j = NCL + idx / kL, t = idx % kL;
-        vt16[j * LY::VT + t] = 0;
-    }
+    for (int idx = tid; idx < (NCT * 16 - NCL) * TS; idx += 256) vt[NCL * TS + idx] = (_Float16)0.0f;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -263,8 +281,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         for (int i = 0; i < NJ; ++i) {
             const int j = w + 4 * i;
             if (i < NJ - 1 || j < NCL)
-                pp[gcol(j) * kL] = (up[4 * i * LY::UT] + up[4 * i * LY::UT + WS]) +
-                                   (up[4 * i * LY::UT + 2 * WS] + up[4 * i * LY::UT + 3 * WS]);
+                pp[gcol(j) * kL] = ((up[4 * i * LY::UT] + up[4 * i * LY::UT + WS]) +
+                                    (up[4 * i * LY::UT + 2 * WS] + up[4 * i * LY::UT + 3 * WS])) * kUScale;
         }
     };
 
@@ -275,8 +293,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const int nvalid1 = more ? nvalid_of(c + 1) : 0;
         if (c > a.c_begin) write_partial(c - 1);
 
-        // ---- P1: value columns transposed to bf16, key parent products ---------------
-        {
+        // ---- P1: fp16 tables of the chunk -------------------------------------------
+        {   // value columns, transposed to [column][token] and scaled; zero past nvalid
             constexpr int NV = kL * LY::VG / 4 / 256;
             uint2 r2[NV];
 #pragma unroll
@@ -289,51 +307,55 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 const int idx = tid + 256 * it;
                 const int t = idx / (LY::VG / 4), c4 = idx % (LY::VG / 4);
                 const uint2 x = t < nvalid ? r2[it] : uint2{0u, 0u};
-                uint16_t* dst = vt16 + 4 * c4 * LY::VT + t;
-                dst[0] = (uint16_t)(x.x & 0xffffu);
-                dst[LY::VT] = (uint16_t)(x.x >> 16);
-                dst[2 * LY::VT] = (uint16_t)(x.y & 0xffffu);
-                dst[3 * LY::VT] = (uint16_t)(x.y >> 16);
+                _Float16* dst = vt + 4 * c4 * TS + t;
+                dst[0] = (_Float16)(bf16_lo(x.x) * kVScale);
+                dst[TS] = (_Float16)(bf16_hi(x.x) * kVScale);
+                dst[2 * TS] = (_Float16)(bf16_lo(x.y) * kVScale);
+                dst[3 * TS] = (_Float16)(bf16_hi(x.y) * kVScale);
             }
         }
-        if (ONES && tid < kL) vt16[64 * LY::VT + tid] = tid < nvalid ? (uint16_t)0x3f80u : (uint16_t)0u;
+        if (ONES && tid < kL) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
         {
-            // each wave builds the parent products of its own 16 rows; lane = token.
-            // The parent words are wave-uniform (scalar loads).
+            // each wave: its 8 key coordinates l = 8 lb + e, transposed (lane = token), and
+            // the parent products of its 16 rows, zero past nvalid.  The parent words are
+            // wave-uniform (scalar loads).
             const uint16_t* xrow = rk + lane * XR;
-            float* kdst = kpar + (w * kRowsPerWave) * LY::KP + lane;
+            const f16x8 kx = bf16x8_to_f16(*reinterpret_cast<const uint4*>(xrow + 8 * lb));
+            _Float16* ktw = kt + w * 8 * TS + lane;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ktw[e * TS] = kx[e];
+            _Float16* kdst = kp + (w * kRowsPerWave) * TS + lane;
             const bool tv = lane < nvalid;
             const int row_u = __builtin_amdgcn_readfirstlane(row_w);
-            float kp[kRowsPerWave];
+            float kpv[kRowsPerWave];
 #pragma unroll
             for (int i = 0; i < kRowsPerWave; ++i) {      // all reads first: no LDS round trips
                 const uint32_t p3 = rt.parent[row_u + i];
-                kp[i] = 1.0f;
+                kpv[i] = 1.0f;
 #pragma unroll
-                for (int e = 0; e < NPC; ++e) kp[i] *= bf16_at(xrow, (p3 >> (10 * e)) & 1023u);
+                for (int e = 0; e < NPC; ++e) kpv[i] *= bf16_at(xrow, (p3 >> (10 * e)) & 1023u);
             }
 #pragma unroll
-            for (int i = 0; i < kRowsPerWave; ++i) kdst[i * LY::KP] = tv ? kp[i] : 0.0f;
+            for (int i = 0; i < kRowsPerWave; ++i) kdst[i * TS] = (_Float16)(tv ? kpv[i] : 0.0f);
         }
         __syncthreads();                                               // B1
-        if (more) prefetch_v<D, NCT>(v, t1, nvalid1, d_V, col0, lds_raw + LY::rawv, w, lane);
+        // raw k and v are free: the next chunk streams in during the readout and update
+        if (more) {
+            prefetch_x<D, NCT>(k, rt.one_row, t1, nvalid1, lds_raw + LY::rawk, w, lane);
+            prefetch_v<D, NCT>(v, t1, nvalid1, d_V, col0, lds_raw + LY::rawv, w, lane);
+        }
 
-        // ---- P2: readout U = Q^ . bf16(S) ------------------------------------------
+        // ---- P2: readout U = Q^ . fp16(S') ------------------------------------------
         {
             f32x4v U[4][NCT];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) U[mt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-            float qreg[4][8];
+            f16x8 qreg[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(rq + (16 * mt + li) * XR + 8 * lb);
-                qreg[mt][0] = bf16_lo(raw.x); qreg[mt][1] = bf16_hi(raw.x);
-                qreg[mt][2] = bf16_lo(raw.y); qreg[mt][3] = bf16_hi(raw.y);
-                qreg[mt][4] = bf16_lo(raw.z); qreg[mt][5] = bf16_hi(raw.z);
-                qreg[mt][6] = bf16_lo(raw.w); qreg[mt][7] = bf16_hi(raw.w);
-            }
+            for (int mt = 0; mt < 4; ++mt)
+                qreg[mt] = bf16x8_to_f16(*reinterpret_cast<const uint4*>(rq + (16 * mt + li) * XR + 8 * lb));
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -342,13 +364,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
                     for (int e = 0; e < NPC; ++e)
                         qp *= bf16_at(reinterpret_cast<const uint16_t*>(lds_raw + qoff[s][e] + mt * 16 * XR * 2), 0);
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = qp * qreg[mt][e];
-                    const bf16x8 A = pack_bf16(x);
+                    const f16x8 A = qreg[mt] * (_Float16)qp;
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
-                        U[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Sb[s][ct], U[mt][ct], 0, 0, 0);
+                        U[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Sb[s][ct], U[mt][ct], 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0x100);   // only LDS reads may move across
             }
@@ -360,51 +379,35 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 for (int ct = 0; ct < NCT; ++ct)
                     *reinterpret_cast<f32x4v*>(ur + (16 * ct + li) * LY::UT + 16 * mt + 4 * g) = U[mt][ct];
         }
-        // the wave's key coordinates k_l (l = 8 lb + 4 h + li % 4) for its tokens
-        float kreg[2][2][8];
+        __syncthreads();                                               // B2
+        // raw q is free
+        if (more) prefetch_x<D, NCT>(q, rt.one_row, t1, nvalid1, lds_raw + LY::rawq, w, lane);
+
+        // ---- P3: update S' += K^^T . [v | 1] ----------------------------------------
+        // this lane's key coordinates l = 8 lb + 4 h + li % 4 over its 8 tokens of step kk
+        f16x8 kreg[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    kreg[h][kk][e] = bf16_at(rk, (32 * kk + 8 * g + e) * XR + 8 * lb + 4 * h + (li & 3));
-        __syncthreads();                                               // B2
-        // the raw q/k buffers are free: the next chunk streams in during the update
-        if (more) {
-            prefetch_x<D, NCT>(q, rt.one_row, t1, nvalid1, lds_raw + LY::rawq, w, lane);
-            prefetch_x<D, NCT>(k, rt.one_row, t1, nvalid1, lds_raw + LY::rawk, w, lane);
-        }
-
-        // ---- P3: update S += K^^T . [v | 1] ------------------------------------------
+                kreg[h][kk] = *reinterpret_cast<const f16x8*>(kt + (w * 8 + 4 * h + (li & 3)) * TS + 32 * kk + 8 * g);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 Vop[NCT];
+            f16x8 Vop[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Vop[ct] = *reinterpret_cast<const bf16x8*>(vt16 + (16 * ct + li) * LY::VT + 32 * kk + 8 * g);
+                Vop[ct] = *reinterpret_cast<const f16x8*>(vt + (16 * ct + li) * TS + 32 * kk + 8 * g);
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const float* kpr = kpar + (w * kRowsPerWave + 4 * s + (li >> 2)) * LY::KP + 32 * kk + 8 * g;
-                const f32x4v p0 = *reinterpret_cast<const f32x4v*>(kpr);
-                const f32x4v p1 = *reinterpret_cast<const f32x4v*>(kpr + 4);
+                const f16x8 kp8 = *reinterpret_cast<const f16x8*>(
+                    kp + (w * kRowsPerWave + 4 * s + (li >> 2)) * TS + 32 * kk + 8 * g);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int T = 2 * s + h;
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[e] = p0[e] * kreg[h][kk][e];
-                        x[4 + e] = p1[e] * kreg[h][kk][4 + e];
-                    }
-                    if (!ones[T]) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] *= cK[T];
-                    }
-                    const bf16x8 A = pack_bf16(x);
+                    const f16x8 A = kp8 * kreg[h][kk] * cK[T];
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
-                        S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Vop[ct], S[T][ct], 0, 0, 0);
+                        S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Vop[ct], S[T][ct], 0, 0, 0);
                 }
                 // on the last token step, tile pair s - 1 is final: pack it for the next
                 // readout while pair s is still in the matrix pipe
@@ -423,7 +426,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     if (a.c_end > a.c_begin) write_partial(a.c_end - 1);
 
     if (a.store_state) {
-        // through LDS as for the load; the internal S' = c S is scaled back by 1/c
+        // through LDS as for the load; S = S' / (2^-8 c)
         float* io = ured;
         const int row_wg = slice * kRowsPerSlice;
 #pragma unroll
@@ -444,7 +447,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
                                4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
-                if (F >= 0) state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / rt.kscale[fi];
+                if (F >= 0)
+                    state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / (kfactor(rt.kscale[fi]) * kVScale);
             }
         }
         if (slice == 0) {
