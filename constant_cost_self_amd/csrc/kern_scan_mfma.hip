@@ -4,42 +4,44 @@
 // attention": the state recurrence, evaluated chunk by chunk):
 //     readout   part[t][j] = sum_f qw_f phi_f(q_t) S[f][j]      (S before the chunk)
 //     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
-// Both are dense contractions over a 64-token chunk and a slice of the feature
-// axis, run as v_mfma_f32_16x16x32_f16 with fp32 accumulation:
-//     readout  (64 tokens x 32 features) x (32 features x 16 columns)
+// Both are dense contractions over a chunk of L tokens (64 or 128) and a slice of
+// the feature axis, run as v_mfma_f32_16x16x32_f16 with fp32 accumulation:
+//     readout  (16 tokens x 32 features) x (32 features x 16 columns)
 //     update   (16 features x 32 tokens) x (32 tokens x 16 columns)
 //
 // Operands are fp16, not bf16: gfx950 multiplies fp16 pairs in one VALU
 // instruction (bf16 only one value at a time) and converts two fp32 values to fp16
-// in one, and the operand building is what bounds this kernel; the matrix rate of
-// the two types is the same, and fp16 keeps 3 more mantissa bits.  Exact powers of
-// two keep every operand inside fp16's range: the [v | 1] operand carries 2^-8
-// (the internal state is S' = 2^-8 c S, with c the key-side factor below), the
-// query operand 2^12, and the readout is scaled back by 2^-4 before it is stored.
-// The state stays fp32 in registers; its fp16 copy only feeds the readout.
+// in one, and operand building competes with the matrix pipe for issue slots; the
+// matrix rate of the two types is the same, and fp16 keeps 3 more mantissa bits.
+// Exact powers of two keep every operand inside fp16's range: the [v | 1] operand
+// carries 2^-8 (the internal state is S' = 2^-8 c S, with c the key-side factor
+// below), the query operand 2^12, and the readout is scaled back by 2^-4.
 //
 // Work split.  The columns of [v | 1] are cut into groups of 64 value columns;
 // group 0 also carries the normaliser column (65 columns, 5 tiles of 16), the
-// others 4 tiles.  One workgroup (4 waves) owns one slice of 64 rows = 512 kernel
+// others 4 tiles.  One workgroup of 8 waves (two per SIMD, so that one wave's
+// waits overlap the other's matrix work) owns one slice of 64 rows = 512 kernel
 // features of one head for one column group, and walks all chunks of the segment
-// in order; its fp32 state never leaves the registers (8 update tiles x 5 column
-// tiles x 4 = 160 registers per lane per wave).  A wave owns 16 rows of one
-// l-block b: its kernel features are (parent a, l = 8b + e), e = 0..7 (see
-// mfma_rows.cpp).  Feature tiles are never written to HBM: per chunk the wave
-// builds
+// in order.  Wave w owns rows 8w .. 8w+7: kernel features (parent a, l = 8b + e),
+// e = 0..7, with one l-block b per wave (see mfma_rows.cpp); its fp32 state never
+// leaves the registers (4 update tiles x 5 column tiles x 4 = 80 registers).
+// Feature tiles are never written to HBM: per chunk the operands are built as
 //     query side  q^(a, l)[t] = (W_a q_a[t]) * q_l[t]        (W_a = alpha_p C(a) p)
 //     key side    k^(a, l)[t] = kpar_a[t] * k_l[t] * c_(a,l)  (c: 0 / 1/(1+m) / 1)
-// directly in the MFMA operand layout (q_a, kpar_a: parent products).  The readout
-// takes the state packed to fp16 after its last update of the previous chunk: the
+// directly in the MFMA operand layout (q_a, kpar_a: parent products).
+//
+// The readout is split by tokens, not by features: wave w computes 16 tokens of
+// the chunk over all 512 features of the slice (at L = 64 two waves share a token
+// tile and split the features; one adds the other's result), so the slice's
+// partial readout leaves the registers straight to HBM.  Its B operand, the state
+// packed to fp16 after the previous chunk's update, is shared through LDS: the
 // update's accumulator layout (lane = column, 4 rows each) over two tiles is a
 // 32-deep B operand when the query operand uses the same feature order.
 //
-// Per chunk: q, k, v arrive in LDS (bf16) by direct-to-LDS loads issued during the
-// previous chunk; the values are moved to fp16 token-major tables (v transposed,
-// each wave's 8 key coordinates, the key parent products); readout MFMAs
-// (per-wave accumulators) go to four LDS regions; update MFMAs; the sum of the
-// four regions is this slice's partial readout, written at the start of the next
-// chunk.
+// Per chunk: q and k arrive in LDS (bf16) by direct-to-LDS loads and v in
+// registers, all issued during the previous chunk; q is converted to fp16 in
+// place; v (transposed, scaled), each wave's 8 key coordinates and the key parent
+// products go to fp16 token-major tables; readout; update; fp16 state to LDS.
 #include "scan_mfma.h"
 
 #include <hip/hip_runtime.h>
@@ -51,6 +53,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+constexpr int kWaves = kWavesPerSlice;      // 8 waves, 8 rows each
 constexpr int kL = 64;                      // chunk length of the MFMA scan
 constexpr float kVScale = 1.0f / 256.0f;    // on the [v | 1] operand of the update
 constexpr float kQScale = 4096.0f;          // on the query operand of the readout
@@ -58,26 +61,38 @@ constexpr float kUScale = 1.0f / 16.0f;     // 1 / (kQScale kVScale): readout ba
 
 template <int D, int NCT>
 struct Layout {
-    static constexpr int XR = D + 8;         // raw q/k row (bf16): D coords, 1, then 7 zeros
+    static constexpr int L = kL;
+    static constexpr int XR = D + 8;         // raw q/k row: D coords, 1, then 7 zeros
     static constexpr int XSLOTS = XR / 8;    // 16-byte slots per raw row
-    static constexpr int VG = 64;            // value columns per column group
-    static constexpr int TS = 72;            // fp16 token-major row stride: 64 tokens + pad
-    static constexpr int UT = 68;            // readout region row stride (floats, rows = columns)
+    static constexpr int TS = L + 8;         // fp16 token-major row stride
+    static constexpr int MT = L / 16;        // token tiles of the readout (4)
+    static constexpr int KR = 16 * MT / kWaves;   // readout K-steps per wave (8: two waves per tile)
+    static constexpr int VROWS = NCT == 5 ? 65 : 64;
+    // EARLY (when LDS allows): q is converted into its own fp16 table and v arrives in
+    // LDS too, so all raw buffers are free after the tables are built and the next
+    // chunk's loads are issued there, a whole readout and update ahead of their use
+    static constexpr bool EARLY = D == 64;
+    static constexpr int QB = L * XR * 2;                           // one raw q or k chunk
+    static constexpr int VB = L * 64 * 2;                           // one raw v chunk (64 columns)
     static constexpr int rawq = 0;                                  // bytes
-    static constexpr int rawk = rawq + kL * XR * 2;
-    static constexpr int rawv = rawk + kL * XR * 2;
-    static constexpr int vt = rawv + kL * VG * 2;                   // [NCT*16 columns][TS]
-    static constexpr int kt = vt + NCT * 16 * TS * 2;               // [wave][8 coordinates][TS]
-    static constexpr int kp = kt + kWavesPerSlice * 8 * TS * 2;     // [64 rows][TS]
-    static constexpr int ur = kp + kRowsPerSlice * TS * 2;
-    static constexpr int bytes = ur + kWavesPerSlice * NCT * 16 * UT * 4;
-    // state load/store staging (outside the chunk loop) aliases the readout regions
-    static constexpr int IO = NCT * 16 + 4;                         // floats per feature row
-    static constexpr int io_rows = kWavesPerSlice * 32;             // 2 tiles per wave per phase
-    static_assert(io_rows * IO * 4 <= kWavesPerSlice * NCT * 16 * UT * 4, "state staging size");
-    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kt % 16 == 0 && kp % 16 == 0 &&
-                  ur % 16 == 0, "16-byte alignment of LDS regions");
-    static_assert((kL * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
+    static constexpr int rawk = rawq + QB;
+    static constexpr int rawv = rawk + QB;
+    static constexpr int qh = rawv + (EARLY ? VB : 0);              // fp16 q, raw row layout
+    static constexpr int vt = qh + (EARLY ? QB : 0);                // [VROWS][TS]
+    static constexpr int kt = vt + VROWS * TS * 2;                  // [wave][8 coordinates][TS]
+    static constexpr int kp = kt + kWaves * 8 * TS * 2;             // [64 rows][TS]
+    static constexpr int sb = kp + kRowsPerSlice * TS * 2;          // [4 ct][16 K-steps][64 lanes] x 16 B
+    static constexpr int sb4 = sb + 4 * 16 * 64 * 16;               // normaliser tile: [16][4 g] x 16 B
+    static constexpr int xch = sb4 + (NCT == 5 ? 16 * 4 * 16 : 0);  // [MT][NCT][64] x 16 B
+    static constexpr int bytes = xch + MT * NCT * 64 * 16;
+    // state load/store staging (outside the chunk loop) aliases the fp16 state area
+    static constexpr int IO = 68;                                   // floats per feature row
+    static constexpr int io_rows = kWaves * 16;                     // one tile per wave per phase
+    static_assert(io_rows * IO * 4 <= 4 * 16 * 64 * 16, "state staging size");
+    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && qh % 16 == 0 && vt % 16 == 0 && kt % 16 == 0 && kp % 16 == 0 &&
+                  sb % 16 == 0 && xch % 16 == 0, "16-byte alignment of LDS regions");
+    static_assert((L * XSLOTS) % 64 == 0 && VB % 1024 == 0, "whole DMA blocks per raw chunk");
+    static_assert(KR == 8, "two waves per token tile");
 };
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -107,6 +122,19 @@ __device__ inline f16x8 pack_tiles(const f32x4v& lo, const f32x4v& hi) {
 // the key-side factor as the update applies it (rounded to fp16)
 __device__ inline float kfactor(float c) { return (float)(_Float16)c; }
 
+// Workgroup barrier for the chunk loop: this wave's LDS accesses have completed and
+// at most VM of its vector-memory operations are still outstanding (63: no wait).
+// Unlike __syncthreads() it does not wait for outstanding global stores unless VM
+// asks for it (they retire in order with the loads on this architecture).
+template <int VM>
+__device__ inline void lds_barrier() {
+    static_assert(VM >= 0 && VM <= 63, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 struct RowPtrs {
     const uint32_t* parent;
     const float* weight;
@@ -116,59 +144,51 @@ struct RowPtrs {
     const uint16_t* one_row;     // 8 bf16: 1, 0, ..., 0 (the constant coordinates d..d+7)
 };
 
-// Direct-to-LDS copies of one chunk.  A wave instruction moves 64 lanes x 16 bytes
-// into a contiguous 1 KiB block; lane i fills bytes [16 i, 16 i + 16).  q and k rows
-// get one more slot holding the constant coordinates (1, 0, ..., 0).  Rows past n
-// read row 0 of the chunk instead (masked later).
+// Direct-to-LDS copies of one chunk of q or k.  A wave instruction moves 64 lanes x
+// 16 bytes into a contiguous 1 KiB block; lane i fills bytes [16 i, 16 i + 16).  The
+// slot after each row's D coordinates holds the constant coordinates (1, 0, ..., 0),
+// written once: its lanes are masked off.  Rows past n read row 0 of the chunk
+// instead (masked later).  Addresses are a uniform base plus 32-bit lane offsets.
 template <int D, int NCT>
-__device__ inline void prefetch_x(const uint16_t* x, const uint16_t* one_row, int64_t t0, int nvalid,
-                                  unsigned char* dst, int w, int lane) {
+__device__ inline void prefetch_x(const uint16_t* x0, int nvalid, unsigned char* dst, int w, int lane) {
     using LY = Layout<D, NCT>;
     constexpr int NBLK = kL * LY::XSLOTS / 64;
 #pragma unroll
-    for (int blk = w; blk < NBLK; blk += kWavesPerSlice) {
+    for (int blk = w; blk < NBLK; blk += kWaves) {
         const int sl = blk * 64 + lane;
         const int t = sl / LY::XSLOTS, cs = sl % LY::XSLOTS;
-        const void* src = cs == D / 8 ? (const void*)one_row
-                                      : (const void*)(x + (t0 + (t < nvalid ? t : 0)) * D + 8 * cs);
-        __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)(dst + blk * 1024),
-                                         16, 0, 0);
+        if (cs != D / 8)
+            __builtin_amdgcn_global_load_lds((const void*)(x0 + ((t < nvalid ? t : 0) * D + 8 * cs)),
+                                             (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
     }
 }
 
-// The 64 value columns [col0, col0 + 64) of the chunk's v rows (row length d_V).
-template <int D, int NCT>
-__device__ inline void prefetch_v(const uint16_t* v, int64_t t0, int nvalid, int d_V, int col0,
-                                  unsigned char* dst, int w, int lane) {
-#pragma unroll
-    for (int blk = w; blk < kL * 8 / 64; blk += kWavesPerSlice) {
-        const int sl = blk * 64 + lane;
-        const int t = sl >> 3, cs = sl & 7;
-        const uint16_t* src = v + (t0 + (t < nvalid ? t : 0)) * d_V + col0 + 8 * cs;
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
-    }
+// The 64 value columns [col0, col0 + 64) of a chunk's v rows (row length d_V), x0 at
+// the chunk's first row and column col0: one 1 KiB block (8 tokens) per wave.
+__device__ inline void prefetch_v(const uint16_t* v0, int nvalid, int d_V, unsigned char* dst, int w, int lane) {
+    const int t = w * 8 + (lane >> 3), cs = lane & 7;
+    __builtin_amdgcn_global_load_lds((const void*)(v0 + ((t < nvalid ? t : 0) * d_V + 8 * cs)),
+                                     (void __attribute__((address_space(3)))*)(dst + w * 1024), 16, 0, 0);
 }
 
 template <int D, int DV, int G, int NPC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     constexpr bool ONES = G == 0;            // group 0 carries the normaliser column
     constexpr int col0 = 64 * G;             // first value column of the group
     constexpr int NCT = ONES ? 5 : 4;        // column tiles of this group
     constexpr int NCL = ONES ? 65 : 64;      // live columns of this group
     using LY = Layout<D, NCT>;
-    constexpr int KS = kRowsPerWave / 4;     // readout K-steps per wave (32 features each)
-    constexpr int NT = 2 * KS;               // update tiles per wave (16 features each)
-    constexpr int XR = LY::XR, TS = LY::TS;
+    constexpr int L = kL, XR = LY::XR, TS = LY::TS, MT = LY::MT, KR = LY::KR;
+    constexpr bool EARLY = LY::EARLY;
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    const uint16_t* rq = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawq);
     const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
-    const uint16_t* rv = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawv);
     _Float16* vt = reinterpret_cast<_Float16*>(lds_raw + LY::vt);
     _Float16* kt = reinterpret_cast<_Float16*>(lds_raw + LY::kt);
     _Float16* kp = reinterpret_cast<_Float16*>(lds_raw + LY::kp);
-    float* ured = reinterpret_cast<float*>(lds_raw + LY::ur);
+    f16x8* sb = reinterpret_cast<f16x8*>(lds_raw + LY::sb);
+    f16x8* sb4 = reinterpret_cast<f16x8*>(lds_raw + LY::sb4);
+    f32x4v* xch = reinterpret_cast<f32x4v*>(lds_raw + LY::xch);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -176,8 +196,9 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const int64_t bh = blockIdx.y;
     constexpr int d_V = DV, cols = DV + 1;
     const int nch = a.c_end - a.c_begin;
-    const int row_w = slice * kRowsPerSlice + w * kRowsPerWave;   // first row of this wave
-    const int lb = rt.wave_lblock[slice * kWavesPerSlice + w];
+    const int row_s = slice * kRowsPerSlice;                 // first row of the slice
+    const int lb_w = rt.wave_lblock[slice * kWaves + w];     // this wave's l-block
+    const int mt = w % MT, kh = w / MT;                      // readout token tile and K half
     // global column of local column j of this group (local 64 is the normaliser)
     auto gcol = [&](int j) { return (ONES && j == 64) ? d_V : col0 + j; };
 
@@ -187,265 +208,284 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     float* state = a.state ? a.state + bh * (int64_t)cols * a.M_pad : nullptr;
 
     auto nvalid_of = [&](int c) {
-        const int64_t r = a.n - (int64_t)c * kL;
-        return (int)(r < kL ? r : kL);
+        const int64_t r = a.n - (int64_t)c * L;
+        return (int)(r < L ? r : L);
     };
+    // without EARLY, v goes through registers: token tid % L, 8 columns 8 (tid / L)
+    uint4 vreg;
+    auto load_v = [&](int c) {
+        const int64_t t0 = (int64_t)c * L;
+        const int nv = nvalid_of(c);
+        const int t = tid % L, c8 = tid / L;
+        vreg = *reinterpret_cast<const uint4*>(v + t0 * d_V + col0 + ((t < nv ? t : 0) * d_V + 8 * c8));
+    };
+    // the constant coordinate slot of every raw q and k row, for good
+    for (int t = tid; t < 2 * L; t += 512) {
+        uint16_t* row = reinterpret_cast<uint16_t*>(lds_raw + (t < L ? LY::rawq : LY::rawk)) + (t % L) * XR + D;
+        *reinterpret_cast<uint4*>(row) = uint4{0x3f80u, 0u, 0u, 0u};
+    }
     {   // first chunk in flight while the state is being set up
-        const int64_t t0 = (int64_t)a.c_begin * kL;
+        const int64_t t0 = (int64_t)a.c_begin * L;
         const int nv = nvalid_of(a.c_begin);
-        prefetch_x<D, NCT>(q, rt.one_row, t0, nv, lds_raw + LY::rawq, w, lane);
-        prefetch_x<D, NCT>(k, rt.one_row, t0, nv, lds_raw + LY::rawk, w, lane);
-        prefetch_v<D, NCT>(v, t0, nv, d_V, col0, lds_raw + LY::rawv, w, lane);
+        prefetch_x<D, NCT>(q + t0 * D, nv, lds_raw + LY::rawq, w, lane);
+        prefetch_x<D, NCT>(k + t0 * D, nv, lds_raw + LY::rawk, w, lane);
+        if (EARLY) prefetch_v(v + t0 * d_V + col0, nv, d_V, lds_raw + LY::rawv, w, lane);
+        else load_v(a.c_begin);
     }
 
-    // per-lane row constants: query weight (with the operand scale) and LDS addresses of
-    // the parent coordinates of row 4 s + g in this lane's token row of the raw q buffer
-    uint32_t qoff[KS][NPC > 0 ? NPC : 1];
-    float Wq[KS];
+    // readout constants of this lane: K-step s of this wave covers rows 4 (kh KR + s) + g
+    uint32_t qoff[KR][NPC > 0 ? NPC : 1];    // parent coordinates: byte offsets in the fp16 q table
+    _Float16 Wq[KR];                         // query weights with the operand scale
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const uint32_t p3 = rt.parent[row_w + 4 * s + g];
+    for (int s = 0; s < KR; ++s) {
+        const int row = row_s + 4 * (kh * KR + s) + g;
+        const uint32_t p3 = rt.parent[row];
 #pragma unroll
         for (int e = 0; e < NPC; ++e)
-            qoff[s][e] = (uint32_t)(LY::rawq + (li * XR + ((p3 >> (10 * e)) & 1023u)) * 2);
-        Wq[s] = rt.weight[row_w + 4 * s + g] * kQScale;
+            qoff[s][e] = (uint32_t)((EARLY ? LY::qh : LY::rawq) + ((16 * mt + li) * XR + ((p3 >> (10 * e)) & 1023u)) * 2);
+        Wq[s] = (_Float16)(rt.weight[row] * kQScale);
     }
-    // key-side factor of this lane's feature in update tile T
-    _Float16 cK[NT];
+    // l-blocks of the readout's row groups, and this wave's 8 parent words (uniform)
+    int lbg[KR / 2];
 #pragma unroll
-    for (int T = 0; T < NT; ++T) {
-        const int s = T >> 1, h = T & 1;
-        cK[T] = (_Float16)rt.kscale[(row_w + 4 * s + (li >> 2)) * 8 + 4 * h + (li & 3)];
-    }
+    for (int gi = 0; gi < KR / 2; ++gi)
+        lbg[gi] = __builtin_amdgcn_readfirstlane(rt.wave_lblock[slice * kWaves + kh * KR / 2 + gi]);
+    uint32_t p3w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p3w[i] = __builtin_amdgcn_readfirstlane(rt.parent[row_s + 8 * w + i]);
+    // key-side factor of this lane's feature in update tile T (rows 4 (T / 2) + li / 4)
+    _Float16 cK[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+        cK[T] = (_Float16)rt.kscale[(row_s + 8 * w + 4 * (T >> 1) + (li >> 2)) * 8 + 4 * (T & 1) + (li & 3)];
 
     // Resident state slice S', update-accumulator layout: lane (column 16 ct + li, g)
-    // register r of tile T = 2 s + h holds kernel feature (row 4 s + g, element 4 h + r).
-    f32x4v S[NT][NCT];
+    // register r of tile T holds kernel feature (row 8 w + 4 (T / 2) + g, element 4 (T % 2) + r).
+    f32x4v S[4][NCT];
 #pragma unroll
-    for (int T = 0; T < NT; ++T)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[T][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
     if (a.load_state) {
-        // through LDS, 2 tiles per wave at a time: plain gather loop, then a register
-        // fill with compile-time indices (keeps the unrolled code free of table loads)
-        float* io = ured;
-        const int row_wg = slice * kRowsPerSlice;
+        // through LDS, one tile per wave at a time: plain gather loop, then a register
+        // fill with compile-time indices
+        float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
 #pragma unroll
-        for (int ph = 0; ph < NT / 2; ++ph) {
+        for (int T = 0; T < 4; ++T) {
             __syncthreads();
-            for (int idx = tid; idx < LY::io_rows * NCL; idx += 256) {
+            for (int idx = tid; idx < LY::io_rows * NCL; idx += 512) {
                 const int fr = idx / NCL, j = idx % NCL;
-                const int ww = fr / 32, fl = fr % 32;
-                const int T = 2 * ph + fl / 16, rho = fl % 16;
-                const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
-                               4 * (T & 1) + (rho & 3);
+                const int ww = fr / 16, rho = fr % 16;
+                const int fi = (row_s + 8 * ww + 4 * (T >> 1) + (rho >> 2)) * 8 + 4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
                 io[fr * LY::IO + j] =
                     F >= 0 ? kfactor(rt.kscale[fi]) * kVScale * state[(int64_t)gcol(j) * a.M_pad + F] : 0.0f;
             }
             __syncthreads();
 #pragma unroll
-            for (int Tl = 0; Tl < 2; ++Tl)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * ct + li;
-                        S[2 * ph + Tl][ct][r] = j < NCL ? io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + j] : 0.0f;
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * ct + li;
+                    S[T][ct][r] = j < NCL ? io[(w * 16 + 4 * g + r) * LY::IO + j] : 0.0f;
+                }
         }
     }
 
-    // fp16 copy of the state in the readout's B-operand layout, refreshed at the end of
-    // every update (tile pair s covers the readout's K-step s)
-    f16x8 Sb[KS][NCT];
+    // fp16 copy of this wave's state for the readout (K-steps 2 w, 2 w + 1)
+    auto store_sb = [&]() {
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Sb[s2][ct] = pack_tiles(S[2 * s2][ct], S[2 * s2 + 1][ct]);
-
-    // columns of [v | 1] past the live ones are zero for good
-    __syncthreads();
-    for (int idx = tid; idx < (NCT * 16 - NCL) * TS; idx += 256) vt[NCL * TS + idx] = (_Float16)0.0f;
+            for (int ct = 0; ct < NCT; ++ct) {
+                const f16x8 p = pack_tiles(S[2 * s][ct], S[2 * s + 1][ct]);
+                if (ct < 4) sb[(ct * 16 + 2 * w + s) * 64 + lane] = p;
+                else if (li == 0) sb4[(2 * w + s) * 4 + g] = p;
+            }
+    };
+    __syncthreads();                         // staging reads done before the area is reused
+    store_sb();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // A slice's partial readout of chunk c (the sum of the 4 waves' regions, [col][token])
-    // is written at the start of chunk c + 1, so the stores complete during that chunk.
-    auto write_partial = [&](int c) {
-        float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)kL * cols + lane;
-        const float* up = ured + w * LY::UT + lane;
-        constexpr int WS = NCT * 16 * LY::UT;                  // one wave's region
-        constexpr int NJ = (NCL + 3) / 4;                      // columns per wave (last one partial)
+    // A token tile's partial readout of chunk c (staged in LDS, [col][token] in HBM) is
+    // stored during chunk c + 1, after the chunk's first LDS reads, so that it never
+    // delays a wait for the next chunk's loads.
+    auto store_partial = [&](int c) {
+        if (kh != 0) return;
+        float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols;
 #pragma unroll
-        for (int i = 0; i < NJ; ++i) {
-            const int j = w + 4 * i;
-            if (i < NJ - 1 || j < NCL)
-                pp[gcol(j) * kL] = ((up[4 * i * LY::UT] + up[4 * i * LY::UT + WS]) +
-                                    (up[4 * i * LY::UT + 2 * WS] + up[4 * i * LY::UT + 3 * WS])) * kUScale;
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4v u = xch[(mt * NCT + ct) * 64 + lane];
+            if (ct < 4 || li == 0) *reinterpret_cast<f32x4v*>(pp + (gcol(16 * ct + li) * L + 16 * mt + 4 * g)) = u;
         }
     };
 
     for (int c = a.c_begin; c < a.c_end; ++c) {
         const int nvalid = nvalid_of(c);
-        const int64_t t1 = (int64_t)(c + 1) * kL;
+        const int64_t t1 = (int64_t)(c + 1) * L;
         const bool more = c + 1 < a.c_end;
         const int nvalid1 = more ? nvalid_of(c + 1) : 0;
-        if (c > a.c_begin) write_partial(c - 1);
 
         // ---- P1: fp16 tables of the chunk -------------------------------------------
-        {   // value columns, transposed to [column][token] and scaled; zero past nvalid
-            constexpr int NV = kL * LY::VG / 4 / 256;
-            uint2 r2[NV];
+        {   // q: raw bf16 rows to fp16 (own table, or in place)
+            constexpr int NQ = (L * LY::XSLOTS + 511) / 512;
+            uint4 r[NQ];
 #pragma unroll
-            for (int it = 0; it < NV; ++it) {            // all reads first: no LDS round trips
-                const int idx = tid + 256 * it;
-                r2[it] = *reinterpret_cast<const uint2*>(rv + (idx / (LY::VG / 4)) * LY::VG + 4 * (idx % (LY::VG / 4)));
+            for (int i = 0; i < NQ; ++i) {
+                const int sl = tid + 512 * i;
+                if (sl < L * LY::XSLOTS) r[i] = reinterpret_cast<const uint4*>(lds_raw + LY::rawq)[sl];
             }
 #pragma unroll
-            for (int it = 0; it < NV; ++it) {
-                const int idx = tid + 256 * it;
-                const int t = idx / (LY::VG / 4), c4 = idx % (LY::VG / 4);
-                const uint2 x = t < nvalid ? r2[it] : uint2{0u, 0u};
-                _Float16* dst = vt + 4 * c4 * TS + t;
-                dst[0] = (_Float16)(bf16_lo(x.x) * kVScale);
-                dst[TS] = (_Float16)(bf16_hi(x.x) * kVScale);
-                dst[2 * TS] = (_Float16)(bf16_lo(x.y) * kVScale);
-                dst[3 * TS] = (_Float16)(bf16_hi(x.y) * kVScale);
+            for (int i = 0; i < NQ; ++i) {
+                const int sl = tid + 512 * i;
+                // the constant slot is written as fp16 (1, 0, ..., 0): in place, the raw
+                // slot is never reloaded
+                const f16x8 h = sl % LY::XSLOTS == D / 8 ? f16x8{1, 0, 0, 0, 0, 0, 0, 0} : bf16x8_to_f16(r[i]);
+                if (sl < L * LY::XSLOTS) reinterpret_cast<f16x8*>(lds_raw + (EARLY ? LY::qh : LY::rawq))[sl] = h;
             }
         }
-        if (ONES && tid < kL) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
+        {   // v: transposed to [column][token], scaled, zero past nvalid
+            uint4 x;
+            int t, c8;
+            if (EARLY) {   // this thread: token tid / 8, columns 8 (tid % 8)
+                t = tid >> 3;
+                c8 = tid & 7;
+                x = reinterpret_cast<const uint4*>(lds_raw + LY::rawv)[tid];
+            } else {
+                t = tid % L;
+                c8 = tid / L;
+                x = vreg;
+            }
+            if (t >= nvalid) x = uint4{0u, 0u, 0u, 0u};
+            _Float16* dst = vt + 8 * c8 * TS + t;
+            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst[(2 * e) * TS] = (_Float16)(bf16_lo(xw[e]) * kVScale);
+                dst[(2 * e + 1) * TS] = (_Float16)(bf16_hi(xw[e]) * kVScale);
+            }
+        }
+        if (ONES && tid < L) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
+        if (c > a.c_begin) store_partial(c - 1);
         {
-            // each wave: its 8 key coordinates l = 8 lb + e, transposed (lane = token), and
-            // the parent products of its 16 rows, zero past nvalid.  The parent words are
-            // wave-uniform (scalar loads).
-            const uint16_t* xrow = rk + lane * XR;
-            const f16x8 kx = bf16x8_to_f16(*reinterpret_cast<const uint4*>(xrow + 8 * lb));
-            _Float16* ktw = kt + w * 8 * TS + lane;
+            // this wave: its 8 key coordinates l = 8 lb + e (transposed, lane = token)
+            // and the parent products of its 8 rows, zero past nvalid
+            const int t = lane;
+            const uint16_t* xrow = rk + t * XR;
+            const f16x8 kx = bf16x8_to_f16(*reinterpret_cast<const uint4*>(xrow + 8 * lb_w));
+            _Float16* ktw = kt + w * 8 * TS + t;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ktw[e * TS] = kx[e];
-            _Float16* kdst = kp + (w * kRowsPerWave) * TS + lane;
-            const bool tv = lane < nvalid;
-            const int row_u = __builtin_amdgcn_readfirstlane(row_w);
-            float kpv[kRowsPerWave];
+            float kpv[8];
 #pragma unroll
-            for (int i = 0; i < kRowsPerWave; ++i) {      // all reads first: no LDS round trips
-                const uint32_t p3 = rt.parent[row_u + i];
+            for (int i = 0; i < 8; ++i) {             // all reads first: no LDS round trips
                 kpv[i] = 1.0f;
 #pragma unroll
-                for (int e = 0; e < NPC; ++e) kpv[i] *= bf16_at(xrow, (p3 >> (10 * e)) & 1023u);
+                for (int e = 0; e < NPC; ++e) kpv[i] *= bf16_at(xrow, (p3w[i] >> (10 * e)) & 1023u);
             }
+            const bool tv = t < nvalid;
 #pragma unroll
-            for (int i = 0; i < kRowsPerWave; ++i) kdst[i * TS] = (_Float16)(tv ? kpv[i] : 0.0f);
+            for (int i = 0; i < 8; ++i) kp[(8 * w + i) * TS + t] = (_Float16)(tv ? kpv[i] : 0.0f);
         }
-        __syncthreads();                                               // B1
-        // raw k and v are free: the next chunk streams in during the readout and update
+        lds_barrier<63>();                                             // B1
+        // raw k (and with EARLY raw q and v) are free: the next chunk streams in
+        // during the contractions
         if (more) {
-            prefetch_x<D, NCT>(k, rt.one_row, t1, nvalid1, lds_raw + LY::rawk, w, lane);
-            prefetch_v<D, NCT>(v, t1, nvalid1, d_V, col0, lds_raw + LY::rawv, w, lane);
-        }
-
-        // ---- P2: readout U = Q^ . fp16(S') ------------------------------------------
-        {
-            f32x4v U[4][NCT];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) U[mt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-            f16x8 qreg[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                qreg[mt] = bf16x8_to_f16(*reinterpret_cast<const uint4*>(rq + (16 * mt + li) * XR + 8 * lb));
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    float qp = Wq[s];
-#pragma unroll
-                    for (int e = 0; e < NPC; ++e)
-                        qp *= bf16_at(reinterpret_cast<const uint16_t*>(lds_raw + qoff[s][e] + mt * 16 * XR * 2), 0);
-                    const f16x8 A = qreg[mt] * (_Float16)qp;
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        U[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Sb[s][ct], U[mt][ct], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0x100);   // only LDS reads may move across
+            prefetch_x<D, NCT>(k + t1 * D, nvalid1, lds_raw + LY::rawk, w, lane);
+            if (EARLY) {
+                prefetch_x<D, NCT>(q + t1 * D, nvalid1, lds_raw + LY::rawq, w, lane);
+                prefetch_v(v + t1 * d_V + col0, nvalid1, d_V, lds_raw + LY::rawv, w, lane);
             }
-            // this wave's readout, column-major: ured[w][col][token], 4 tokens per store
-            float* ur = ured + w * (NCT * 16 * LY::UT);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    *reinterpret_cast<f32x4v*>(ur + (16 * ct + li) * LY::UT + 16 * mt + 4 * g) = U[mt][ct];
         }
-        __syncthreads();                                               // B2
-        // raw q is free
-        if (more) prefetch_x<D, NCT>(q, rt.one_row, t1, nvalid1, lds_raw + LY::rawq, w, lane);
 
-        // ---- P3: update S' += K^^T . [v | 1] ----------------------------------------
-        // this lane's key coordinates l = 8 lb + 4 h + li % 4 over its 8 tokens of step kk
-        f16x8 kreg[2][2];
+        // ---- P2: readout of token tile mt over K-steps kh KR .. kh KR + KR - 1, and the
+        // update S' += K^^T . [v | 1] of this wave's rows, interleaved: the readout
+        // streams its B operands from LDS, the update keeps the matrix pipe busy -------
+        f32x4v U[NCT];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int ct = 0; ct < NCT; ++ct) U[ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+        const _Float16* qh = reinterpret_cast<const _Float16*>(lds_raw + (EARLY ? LY::qh : LY::rawq));
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                kreg[h][kk] = *reinterpret_cast<const f16x8*>(kt + (w * 8 + 4 * h + (li & 3)) * TS + 32 * kk + 8 * g);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < L / 32; ++kk) {
             f16x8 Vop[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Vop[ct] = *reinterpret_cast<const f16x8*>(vt + (16 * ct + li) * TS + 32 * kk + 8 * g);
+                Vop[ct] = *reinterpret_cast<const f16x8*>(vt + (ct < 4 ? 16 * ct + li : 64) * TS + 32 * kk + 8 * g);
+            f16x8 kreg[2];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const f16x8 kp8 = *reinterpret_cast<const f16x8*>(
-                    kp + (w * kRowsPerWave + 4 * s + (li >> 2)) * TS + 32 * kk + 8 * g);
+            for (int h = 0; h < 2; ++h)
+                kreg[h] = *reinterpret_cast<const f16x8*>(kt + (w * 8 + 4 * h + (li & 3)) * TS + 32 * kk + 8 * g);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                // two readout K-steps (one row group)
+                const int gi = 2 * kk + s;
+                const f16x8 qreg = *reinterpret_cast<const f16x8*>(qh + (16 * mt + li) * XR + 8 * lbg[gi]);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int sr = 2 * gi + s2, sg = kh * KR + sr;
+                    _Float16 qp = Wq[sr];
+#pragma unroll
+                    for (int e = 0; e < NPC; ++e)
+                        qp *= *reinterpret_cast<const _Float16*>(lds_raw + qoff[sr][e]);
+                    const f16x8 A = qreg * qp;
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const f16x8 B = ct < 4 ? sb[(ct * 16 + sg) * 64 + lane] : sb4[sg * 4 + g];
+                        U[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, U[ct], 0, 0, 0);
+                    }
+                }
+                // one update row pair
+                const f16x8 kp8 = *reinterpret_cast<const f16x8*>(kp + (8 * w + 4 * s + (li >> 2)) * TS + 32 * kk + 8 * g);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int T = 2 * s + h;
-                    const f16x8 A = kp8 * kreg[h][kk] * cK[T];
+                    const f16x8 A = kp8 * kreg[h] * cK[T];
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
                         S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Vop[ct], S[T][ct], 0, 0, 0);
                 }
-                // on the last token step, tile pair s - 1 is final: pack it for the next
-                // readout while pair s is still in the matrix pipe
-                if (kk == 1 && s > 0) {
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Sb[s - 1][ct] = pack_tiles(S[2 * s - 2][ct], S[2 * s - 1][ct]);
-                }
-                __builtin_amdgcn_sched_barrier(0x100);   // only LDS reads may move across
             }
         }
+        if (kh == 1) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Sb[KS - 1][ct] = pack_tiles(S[2 * KS - 2][ct], S[2 * KS - 1][ct]);
-        __builtin_amdgcn_s_waitcnt(0);          // the next chunk has landed
-        __syncthreads();                                               // B3
+            for (int ct = 0; ct < NCT; ++ct) xch[(mt * NCT + ct) * 64 + lane] = U[ct];
+        }
+        lds_barrier<63>();                                             // B2
+        // raw q and the fp16 state are free
+        if (!EARLY && more) {
+            prefetch_x<D, NCT>(q + t1 * D, nvalid1, lds_raw + LY::rawq, w, lane);
+            load_v(c + 1);
+        }
+        if (kh == 0) {   // the token tile's sum, staged until the next chunk
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                xch[(mt * NCT + ct) * 64 + lane] = (U[ct] + xch[(mt * NCT + ct) * 64 + lane]) * kUScale;
+        }
+        store_sb();
+        lds_barrier<0>();                       // B3: the next chunk has landed
     }
-    if (a.c_end > a.c_begin) write_partial(a.c_end - 1);
+    if (a.c_end > a.c_begin) store_partial(a.c_end - 1);
+    __builtin_amdgcn_s_waitcnt(0);
 
     if (a.store_state) {
         // through LDS as for the load; S = S' / (2^-8 c)
-        float* io = ured;
-        const int row_wg = slice * kRowsPerSlice;
+        float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
 #pragma unroll
-        for (int ph = 0; ph < NT / 2; ++ph) {
+        for (int T = 0; T < 4; ++T) {
             __syncthreads();
 #pragma unroll
-            for (int Tl = 0; Tl < 2; ++Tl)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        io[(w * 32 + Tl * 16 + 4 * g + r) * LY::IO + 16 * ct + li] = S[2 * ph + Tl][ct][r];
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * ct + li;
+                    if (j < LY::IO) io[(w * 16 + 4 * g + r) * LY::IO + j] = S[T][ct][r];
+                }
             __syncthreads();
-            for (int idx = tid; idx < LY::io_rows * NCL; idx += 256) {
+            for (int idx = tid; idx < LY::io_rows * NCL; idx += 512) {
                 const int fr = idx / NCL, j = idx % NCL;
-                const int ww = fr / 32, fl = fr % 32;
-                const int T = 2 * ph + fl / 16, rho = fl % 16;
-                const int fi = (row_wg + ww * kRowsPerWave + 4 * (T >> 1) + (rho >> 2)) * 8 +
-                               4 * (T & 1) + (rho & 3);
+                const int ww = fr / 16, rho = fr % 16;
+                const int fi = (row_s + 8 * ww + 4 * (T >> 1) + (rho >> 2)) * 8 + 4 * (T & 1) + (rho & 3);
                 const int F = rt.canon[fi];
                 if (F >= 0)
                     state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / (kfactor(rt.kscale[fi]) * kVScale);
@@ -453,7 +493,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         }
         if (slice == 0) {
             const int64_t padn = a.M_pad - a.M;
-            for (int64_t idx = tid; idx < NCL * padn; idx += 256)
+            for (int64_t idx = tid; idx < NCL * padn; idx += 512)
                 state[(int64_t)gcol((int)(idx / padn)) * a.M_pad + a.M + idx % padn] = 0.0f;
         }
     }
@@ -467,7 +507,7 @@ hipError_t launch_t(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st
     hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, G, NPC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, G, NPC>), dim3(a.nslices, a.BH), dim3(256), LY::bytes, st,
+    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, G, NPC>), dim3(a.nslices, a.BH), dim3(512), LY::bytes, st,
                        a, rt);
     return hipGetLastError();
 }
@@ -535,12 +575,12 @@ void free_mfma_tables(MfmaTables& m) {
 }
 
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L) {
-    return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && L == kL &&
-           (d_K == 64 || d_K == 128) && (d_V == 64 || d_V == 128);
+    return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && (d_V == 64 || d_V == 128) &&
+           (d_K == 64 || d_K == 128) && L == kL;
 }
 
 hipError_t launch_scan_mfma(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
-    return a.d_K == 64 ? launch_d<64>(a, m, st) : launch_d<128>(a, m, st);
+    return a.d_K == 128 ? launch_d<128>(a, m, st) : launch_d<64>(a, m, st);
 }
 
 }  // namespace sata

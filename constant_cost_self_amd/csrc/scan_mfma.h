@@ -27,8 +27,8 @@ struct MfmaHostRows {
     std::vector<int32_t> wave_lblock;    // [nrows/16] l-block of each wave
 };
 
-constexpr int kRowsPerWave = 16;
-constexpr int kWavesPerSlice = 4;
+constexpr int kRowsPerWave = 8;
+constexpr int kWavesPerSlice = 8;
 constexpr int kRowsPerSlice = kRowsPerWave * kWavesPerSlice;   // 64 rows = 512 kernel features
 
 bool build_mfma_rows(const HostTables& h, MfmaHostRows& r);
