@@ -98,11 +98,175 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA variant for bf16 inputs, L = 64, d_K in {64, 128}, d_V in {64, 128}.
+// Same quantities, computed transposed so that no layout change is needed:
+//     S^T[j][i] = k_j . q_i            v_mfma_f32_16x16x32_bf16 (exact products)
+//     W^T[j][i] = w(S^T[j][i]) for j <= i < nvalid, else 0     (fp32, Horner)
+//     O^T[c][i] = sum_j U^T[c][j] W^T[j][i]     v_mfma_f32_16x16x32_f16, W^T in fp16
+// The accumulator layout of two 16-key tiles of W^T is the B operand of the second
+// contraction when the A operand (U^T, [column][token] in LDS) lists its keys in
+// the same order: keys {4 g + r, 16 + 4 g + r} for lane group g.  Wave w owns
+// query tile w (16 tokens).  The slice partials, [column][token] per slice, are
+// summed first by all threads with 16-byte loads (the memory-bound part).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DK, int DV>
+struct FinLayout {
+    static constexpr int L = 64;
+    static constexpr int XR = DK + 8;                  // q/k row (bf16)
+    static constexpr int TS = L + 8;                   // U^T row (fp16)
+    static constexpr int COLS = DV + 1;
+    static constexpr int NS = COLS + 3;                // num row (floats)
+    static constexpr int qs = 0;
+    static constexpr int ks = qs + L * XR * 2;
+    static constexpr int vt = ks + L * XR * 2;
+    static constexpr int num = vt + ((COLS * TS * 2 + 15) / 16) * 16;
+    static constexpr int bytes = num + L * NS * 4;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
+    using LY = FinLayout<DK, DV>;
+    constexpr int L = LY::L, XR = LY::XR, TS = LY::TS, COLS = LY::COLS, NS = LY::NS;
+    constexpr int NCT = (COLS + 15) / 16;              // column tiles of U (last one: the normaliser)
+    extern __shared__ __align__(16) unsigned char fl[];
+    uint16_t* qs = reinterpret_cast<uint16_t*>(fl + LY::qs);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(fl + LY::ks);
+    _Float16* vt = reinterpret_cast<_Float16*>(fl + LY::vt);
+    float* num = reinterpret_cast<float*>(fl + LY::num);
+
+    const int cl = blockIdx.x;                  // chunk within the segment
+    const int64_t bh = blockIdx.y;
+    const int c = a.c_begin + cl;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int nch = a.c_end - a.c_begin;
+    const int64_t t0 = (int64_t)c * L;
+    const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
+
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (bh * a.n + t0) * DK;
+    const uint16_t* k = static_cast<const uint16_t*>(a.k) + (bh * a.n + t0) * DK;
+    const uint16_t* v = static_cast<const uint16_t*>(a.v) + (bh * a.n + t0) * DV;
+
+    for (int idx = tid; idx < L * DK / 8; idx += 256) {
+        const int t = idx / (DK / 8), s8 = idx % (DK / 8);
+        uint4 xq = uint4{0u, 0u, 0u, 0u}, xk = xq;
+        if (t < nvalid) {
+            xq = *reinterpret_cast<const uint4*>(q + t * DK + 8 * s8);
+            xk = *reinterpret_cast<const uint4*>(k + t * DK + 8 * s8);
+        }
+        *reinterpret_cast<uint4*>(qs + t * XR + 8 * s8) = xq;
+        *reinterpret_cast<uint4*>(ks + t * XR + 8 * s8) = xk;
+    }
+    for (int idx = tid; idx < L * DV / 8; idx += 256) {
+        const int t = idx % L, c8 = idx / L;
+        uint4 x = uint4{0u, 0u, 0u, 0u};
+        if (t < nvalid) x = *reinterpret_cast<const uint4*>(v + t * DV + 8 * c8);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vt[(8 * c8 + 2 * e) * TS + t] = (_Float16)__uint_as_float(xw[e] << 16);
+            vt[(8 * c8 + 2 * e + 1) * TS + t] = (_Float16)__uint_as_float(xw[e] & 0xffff0000u);
+        }
+    }
+    if (tid < L) vt[DV * TS + tid] = (_Float16)(tid < nvalid ? 1.0f : 0.0f);
+
+    // slice partials: num[t][col] = sum over slices, 4 tokens per item, 8 loads in flight
+    {
+        const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * L * COLS;
+        const int64_t stride = (int64_t)L * COLS;
+        for (int item = tid; item < COLS * (L / 4); item += 256) {
+            const int col = item / (L / 4), tg = item % (L / 4);
+            const float* p = part + col * L + 4 * tg;
+            f32x4_t acc[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            int sl = 0;
+            for (; sl + 8 <= a.nslices; sl += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    acc[u] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + (sl + u) * stride));
+            }
+            for (; sl < a.nslices; ++sl)
+                acc[0] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + sl * stride));
+            const f32x4_t s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[(4 * tg + e) * NS + col] = s[e];
+        }
+    }
+    __syncthreads();
+
+    // wave w: query tile w.  S^T tiles over the 4 key tiles, then the causal weights
+    const int iq = 16 * w + li;                 // this lane's query token
+    f16x8_t Wb[2];                              // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kd = 0; kd < DK / 32; ++kd) {
+            const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kt + li) * XR + 32 * kd + 8 * g);
+            const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(qs + iq * XR + 32 * kd + 8 * g);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, st, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * kt + 4 * g + r;          // key token
+            const float wgt = taylor_weight(st[r], a.alpha, a.P);
+            Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)((j <= iq && iq < nvalid) ? wgt : 0.0f);
+        }
+    }
+    f32x4_t O[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        O[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int row = 16 * ct + li < COLS ? 16 * ct + li : DV;   // dead columns read the ones row
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+            const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 4 * g);
+            const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 16 + 4 * g);
+            const f16x8_t A = f16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Wb[kq], O[ct], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int col = 16 * ct + 4 * g + r;
+            if (col < COLS) num[iq * NS + col] += O[ct][r];
+        }
+    __syncthreads();
+    float* y = a.y + (bh * a.n + t0) * DV;
+    for (int idx = tid; idx < nvalid * DV; idx += 256) {
+        const int t = idx / DV, j = idx % DV;
+        y[idx] = num[t * NS + j] / num[t * NS + DV];
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_fin_mfma(const PrefillSegArgs& a, hipStream_t st) {
+    constexpr int bytes = FinLayout<DK, DV>::bytes;
+    hipError_t e = hipFuncSetAttribute((const void*)finalize_mfma_kernel<DK, DV>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((finalize_mfma_kernel<DK, DV>), dim3(a.c_end - a.c_begin, a.BH), dim3(256), bytes, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t finalize_lds_bytes(int d_K, int d_V, int L) { return finalize_lds_floats(d_K, d_V, L) * 4; }
 
 hipError_t launch_finalize(const PrefillSegArgs& a, hipStream_t st) {
+    if (a.bf16 && a.L == 64 && (a.d_K == 64 || a.d_K == 128) && (a.d_V == 64 || a.d_V == 128)) {
+        if (a.d_K == 64) return a.d_V == 64 ? launch_fin_mfma<64, 64>(a, st) : launch_fin_mfma<64, 128>(a, st);
+        return a.d_V == 64 ? launch_fin_mfma<128, 64>(a, st) : launch_fin_mfma<128, 128>(a, st);
+    }
     const size_t lds = (size_t)finalize_lds_bytes(a.d_K, a.d_V, a.L);
     dim3 grid(a.c_end - a.c_begin, a.BH);
     if (a.bf16) {
