@@ -122,6 +122,18 @@ __device__ inline f16x8 pack_tiles(const f32x4v& lo, const f32x4v& hi) {
 // the key-side factor as the update applies it (rounded to fp16)
 __device__ inline float kfactor(float c) { return (float)(_Float16)c; }
 
+// An LDS byte address the compiler may not re-derive: the constant parts of the
+// accesses made from it then fit the 16-bit offset field of ds_read/ds_write, and one
+// register serves a whole table.
+__device__ inline uint32_t lds_base(uint32_t a) {
+    asm volatile("" : "+v"(a));
+    return a;
+}
+template <typename T>
+__device__ inline const T& lds_at(const unsigned char* lds, uint32_t base, uint32_t off) {
+    return *reinterpret_cast<const T*>(lds + base + off);
+}
+
 // Workgroup barrier for the chunk loop: this wave's LDS accesses have completed and
 // at most VM of its vector-memory operations are still outstanding (63: no wait).
 // Unlike __syncthreads() it does not wait for outstanding global stores unless VM
@@ -163,11 +175,11 @@ __device__ inline void prefetch_x(const uint16_t* x0, int nvalid, unsigned char*
     }
 }
 
-// The 64 value columns [col0, col0 + 64) of a chunk's v rows (row length d_V), x0 at
-// the chunk's first row and column col0: one 1 KiB block (8 tokens) per wave.
+// The 64 value columns [col0, col0 + 64) of a chunk's v rows (row length d_V), v0 at
+// the chunk's first row and column col0, stored column-group major: wave w moves
+// columns 8w .. 8w+7 of all 64 tokens (lane = token) into one 1 KiB block.
 __device__ inline void prefetch_v(const uint16_t* v0, int nvalid, int d_V, unsigned char* dst, int w, int lane) {
-    const int t = w * 8 + (lane >> 3), cs = lane & 7;
-    __builtin_amdgcn_global_load_lds((const void*)(v0 + ((t < nvalid ? t : 0) * d_V + 8 * cs)),
+    __builtin_amdgcn_global_load_lds((const void*)(v0 + ((lane < nvalid ? lane : 0) * d_V + 8 * w)),
                                      (void __attribute__((address_space(3)))*)(dst + w * 1024), 16, 0, 0);
 }
 
@@ -211,7 +223,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const int64_t r = a.n - (int64_t)c * L;
         return (int)(r < L ? r : L);
     };
-    // without EARLY, v goes through registers: token tid % L, 8 columns 8 (tid / L)
+    // without EARLY, v goes through registers: token tid % L, 8 columns 8 (tid / L), as in LDS
     uint4 vreg;
     auto load_v = [&](int c) {
         const int64_t t0 = (int64_t)c * L;
@@ -308,15 +320,25 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // A token tile's partial readout of chunk c (staged in LDS, [col][token] in HBM) is
-    // stored during chunk c + 1, after the chunk's first LDS reads, so that it never
-    // delays a wait for the next chunk's loads.
+    // per-lane LDS bases of the contraction's operand tables (byte addresses)
+    const uint32_t a_sb = lds_base(LY::sb + (kh * KR * 64 + lane) * 16);          // [ct][K-step][lane]
+    const uint32_t a_sb4 = lds_base(LY::sb4 + (kh * KR * 4 + g) * 16);            // [K-step][g]
+    const uint32_t a_vt = lds_base(LY::vt + (li * TS + 8 * g) * 2);               // row 16 ct + li
+    const uint32_t a_vt4 = lds_base(LY::vt + (64 * TS + 8 * g) * 2);              // the ones row
+    const uint32_t a_kt = lds_base(LY::kt + ((w * 8 + (li & 3)) * TS + 8 * g) * 2);
+    const uint32_t a_kp = lds_base(LY::kp + ((8 * w + (li >> 2)) * TS + 8 * g) * 2);
+    const uint32_t a_qh = lds_base((EARLY ? LY::qh : LY::rawq) + (16 * mt + li) * XR * 2);
+
+    // A token tile's partial readout of chunk c ([col][token] in HBM): the wave with
+    // kh = 0 keeps its half in registers, adds its partner's half (left in LDS before the
+    // chunk's last barrier) at the start of chunk c + 1 and stores the sum.
+    f32x4v Uprev[NCT];
     auto store_partial = [&](int c) {
         if (kh != 0) return;
         float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4v u = xch[(mt * NCT + ct) * 64 + lane];
+            const f32x4v u = (Uprev[ct] + xch[(mt * NCT + ct) * 64 + lane]) * kUScale;
             if (ct < 4 || li == 0) *reinterpret_cast<f32x4v*>(pp + (gcol(16 * ct + li) * L + 16 * mt + 4 * g)) = u;
         }
     };
@@ -327,7 +349,11 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const bool more = c + 1 < a.c_end;
         const int nvalid1 = more ? nvalid_of(c + 1) : 0;
 
-        // ---- P1: fp16 tables of the chunk -------------------------------------------
+        // ---- P1: the previous chunk's partial and fp16 state; fp16 tables of the chunk ---
+        if (c > a.c_begin) {
+            store_partial(c - 1);
+            store_sb();
+        }
         {   // q: raw bf16 rows to fp16 (own table, or in place)
             constexpr int NQ = (L * LY::XSLOTS + 511) / 512;
             uint4 r[NQ];
@@ -348,15 +374,9 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         {   // v: transposed to [column][token], scaled, zero past nvalid
             uint4 x;
             int t, c8;
-            if (EARLY) {   // this thread: token tid / 8, columns 8 (tid % 8)
-                t = tid >> 3;
-                c8 = tid & 7;
-                x = reinterpret_cast<const uint4*>(lds_raw + LY::rawv)[tid];
-            } else {
-                t = tid % L;
-                c8 = tid / L;
-                x = vreg;
-            }
+            t = lane;                                // this thread: token lane, columns 8 w
+            c8 = w;
+            x = EARLY ? reinterpret_cast<const uint4*>(lds_raw + LY::rawv)[tid] : vreg;
             if (t >= nvalid) x = uint4{0u, 0u, 0u, 0u};
             _Float16* dst = vt + 8 * c8 * TS + t;
             const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
@@ -367,7 +387,6 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             }
         }
         if (ONES && tid < L) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
-        if (c > a.c_begin) store_partial(c - 1);
         {
             // this wave: its 8 key coordinates l = 8 lb + e (transposed, lane = token)
             // and the parent products of its 8 rows, zero past nvalid
@@ -399,70 +418,74 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             }
         }
 
-        // ---- P2: readout of token tile mt over K-steps kh KR .. kh KR + KR - 1, and the
-        // update S' += K^^T . [v | 1] of this wave's rows, interleaved: the readout
-        // streams its B operands from LDS, the update keeps the matrix pipe busy -------
+        // ---- P2: readout of token tile mt over K-steps kh KR .. kh KR + KR - 1, then the
+        // update S' += K^^T . [v | 1] of this wave's rows ----------------------------------
         f32x4v U[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) U[ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-        const _Float16* qh = reinterpret_cast<const _Float16*>(lds_raw + (EARLY ? LY::qh : LY::rawq));
-#pragma unroll
-        for (int kk = 0; kk < L / 32; ++kk) {
-            f16x8 Vop[NCT];
+        // Readout, software-pipelined: the B operands (LDS) of K-step sr + 1 are requested
+        // before the MFMAs of step sr.
+        {
+            f16x8 B[2][NCT], qreg;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Vop[ct] = *reinterpret_cast<const f16x8*>(vt + (ct < 4 ? 16 * ct + li : 64) * TS + 32 * kk + 8 * g);
-            f16x8 kreg[2];
+                B[0][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, ct * 16 * 64 * 16) : lds_at<f16x8>(lds_raw, a_sb4, 0);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                kreg[h] = *reinterpret_cast<const f16x8*>(kt + (w * 8 + 4 * h + (li & 3)) * TS + 32 * kk + 8 * g);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // two readout K-steps (one row group)
-                const int gi = 2 * kk + s;
-                const f16x8 qreg = *reinterpret_cast<const f16x8*>(qh + (16 * mt + li) * XR + 8 * lbg[gi]);
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int sr = 2 * gi + s2, sg = kh * KR + sr;
-                    _Float16 qp = Wq[sr];
-#pragma unroll
-                    for (int e = 0; e < NPC; ++e)
-                        qp *= *reinterpret_cast<const _Float16*>(lds_raw + qoff[sr][e]);
-                    const f16x8 A = qreg * qp;
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        const f16x8 B = ct < 4 ? sb[(ct * 16 + sg) * 64 + lane] : sb4[sg * 4 + g];
-                        U[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, U[ct], 0, 0, 0);
-                    }
-                }
-                // one update row pair
-                const f16x8 kp8 = *reinterpret_cast<const f16x8*>(kp + (8 * w + 4 * s + (li >> 2)) * TS + 32 * kk + 8 * g);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int T = 2 * s + h;
-                    const f16x8 A = kp8 * kreg[h] * cK[T];
+            for (int sr = 0; sr < KR; ++sr) {
+                if (sr + 1 < KR) {
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
-                        S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Vop[ct], S[T][ct], 0, 0, 0);
+                        B[(sr + 1) & 1][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, (ct * 16 * 64 + (sr + 1) * 64) * 16)
+                                                     : lds_at<f16x8>(lds_raw, a_sb4, (sr + 1) * 64);
                 }
+                if (sr % 2 == 0) qreg = lds_at<f16x8>(lds_raw, a_qh, 8 * lbg[sr / 2] * 2);
+                _Float16 qp = Wq[sr];
+#pragma unroll
+                for (int e = 0; e < NPC; ++e) qp *= *reinterpret_cast<const _Float16*>(lds_raw + qoff[sr][e]);
+                const f16x8 A = qreg * qp;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    U[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[sr & 1][ct], U[ct], 0, 0, 0);
             }
         }
         if (kh == 1) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) xch[(mt * NCT + ct) * 64 + lane] = U[ct];
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) Uprev[ct] = U[ct];
         }
-        lds_barrier<63>();                                             // B2
-        // raw q and the fp16 state are free
-        if (!EARLY && more) {
-            prefetch_x<D, NCT>(q + t1 * D, nvalid1, lds_raw + LY::rawq, w, lane);
-            load_v(c + 1);
+        if (!EARLY) {
+            // the raw q buffer holds this chunk's fp16 q until every readout is done
+            lds_barrier<63>();                                         // B2
+            if (more) {
+                prefetch_x<D, NCT>(q + t1 * D, nvalid1, lds_raw + LY::rawq, w, lane);
+                load_v(c + 1);
+            }
         }
-        if (kh == 0) {   // the token tile's sum, staged until the next chunk
+        // update S' += K^^T . [v | 1] of this wave's rows
+#pragma unroll
+        for (int kk = 0; kk < L / 32; ++kk) {
+            f16x8 Vop[NCT], kreg[2];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                xch[(mt * NCT + ct) * 64 + lane] = (U[ct] + xch[(mt * NCT + ct) * 64 + lane]) * kUScale;
+                Vop[ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_vt, (16 * ct * TS + 32 * kk) * 2)
+                                 : lds_at<f16x8>(lds_raw, a_vt4, 32 * kk * 2);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) kreg[hh] = lds_at<f16x8>(lds_raw, a_kt, (4 * hh * TS + 32 * kk) * 2);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const f16x8 kp8 = lds_at<f16x8>(lds_raw, a_kp, (4 * s * TS + 32 * kk) * 2);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int T = 2 * s + h;
+                    const f16x8 Au = kp8 * kreg[h] * cK[T];
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Au, Vop[ct], S[T][ct], 0, 0, 0);
+                }
+            }
         }
-        store_sb();
         lds_barrier<0>();                       // B3: the next chunk has landed
     }
     if (a.c_end > a.c_begin) store_partial(a.c_end - 1);
