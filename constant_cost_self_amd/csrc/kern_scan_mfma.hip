@@ -79,9 +79,8 @@ struct Layout {
     static constexpr int rawv = rawk + QB;
     static constexpr int qh = rawv + (EARLY ? VB : 0);              // fp16 q, raw row layout
     static constexpr int vt = qh + (EARLY ? QB : 0);                // [VROWS][TS]
-    static constexpr int kt = vt + VROWS * TS * 2;                  // [wave][8 coordinates][TS]
-    static constexpr int kp = kt + kWaves * 8 * TS * 2;             // [64 rows][TS]
-    static constexpr int sb = kp + kRowsPerSlice * TS * 2;          // [4 ct][16 K-steps][64 lanes] x 16 B
+    static constexpr int kT = vt + VROWS * TS * 2;                  // [XR coordinates][TS] fp16 keys
+    static constexpr int sb = kT + XR * TS * 2;                     // [4 ct][16 K-steps][64 lanes] x 16 B
     static constexpr int sb4 = sb + 4 * 16 * 64 * 16;               // normaliser tile: [16][4 g] x 16 B
     static constexpr int xch = sb4 + (NCT == 5 ? 16 * 4 * 16 : 0);  // [MT][NCT][64] x 16 B
     static constexpr int bytes = xch + MT * NCT * 64 * 16;
@@ -89,7 +88,7 @@ struct Layout {
     static constexpr int IO = 68;                                   // floats per feature row
     static constexpr int io_rows = kWaves * 16;                     // one tile per wave per phase
     static_assert(io_rows * IO * 4 <= 4 * 16 * 64 * 16, "state staging size");
-    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && qh % 16 == 0 && vt % 16 == 0 && kt % 16 == 0 && kp % 16 == 0 &&
+    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && qh % 16 == 0 && vt % 16 == 0 && kT % 16 == 0 &&
                   sb % 16 == 0 && xch % 16 == 0, "16-byte alignment of LDS regions");
     static_assert((L * XSLOTS) % 64 == 0 && VB % 1024 == 0, "whole DMA blocks per raw chunk");
     static_assert(KR == 8, "two waves per token tile");
@@ -196,8 +195,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
     _Float16* vt = reinterpret_cast<_Float16*>(lds_raw + LY::vt);
-    _Float16* kt = reinterpret_cast<_Float16*>(lds_raw + LY::kt);
-    _Float16* kp = reinterpret_cast<_Float16*>(lds_raw + LY::kp);
+    _Float16* kT = reinterpret_cast<_Float16*>(lds_raw + LY::kT);
     f16x8* sb = reinterpret_cast<f16x8*>(lds_raw + LY::sb);
     f16x8* sb4 = reinterpret_cast<f16x8*>(lds_raw + LY::sb4);
     f32x4v* xch = reinterpret_cast<f32x4v*>(lds_raw + LY::xch);
@@ -236,6 +234,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         uint16_t* row = reinterpret_cast<uint16_t*>(lds_raw + (t < L ? LY::rawq : LY::rawk)) + (t % L) * XR + D;
         *reinterpret_cast<uint4*>(row) = uint4{0x3f80u, 0u, 0u, 0u};
     }
+    // key coordinates d + 1 .. d + 7 (the zeros after the constant one), for good
+    for (int idx = tid; idx < 7 * TS; idx += 512) kT[(D + 1) * TS + idx] = (_Float16)0.0f;
     {   // first chunk in flight while the state is being set up
         const int64_t t0 = (int64_t)a.c_begin * L;
         const int nv = nvalid_of(a.c_begin);
@@ -262,9 +262,18 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
     for (int gi = 0; gi < KR / 2; ++gi)
         lbg[gi] = __builtin_amdgcn_readfirstlane(rt.wave_lblock[slice * kWaves + kh * KR / 2 + gi]);
-    uint32_t p3w[8];
+    // key parents of this lane's update rows 8 w + 4 s + li / 4: byte offsets of their
+    // coordinate rows in the key table (a missing parent is the constant coordinate d,
+    // which is 1 for the chunk's tokens and 0 past them)
+    constexpr int NPR = NPC > 0 ? NPC : 1;
+    uint32_t kpa[2][NPR];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p3w[i] = __builtin_amdgcn_readfirstlane(rt.parent[row_s + 8 * w + i]);
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t p3 = rt.parent[row_s + 8 * w + 4 * s + (li >> 2)];
+#pragma unroll
+        for (int e = 0; e < NPR; ++e)
+            kpa[s][e] = lds_base(LY::kT + (((p3 >> (10 * e)) & 1023u) * TS + 8 * g) * 2);
+    }
     // key-side factor of this lane's feature in update tile T (rows 4 (T / 2) + li / 4)
     _Float16 cK[4];
 #pragma unroll
@@ -325,8 +334,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint32_t a_sb4 = lds_base(LY::sb4 + (kh * KR * 4 + g) * 16);            // [K-step][g]
     const uint32_t a_vt = lds_base(LY::vt + (li * TS + 8 * g) * 2);               // row 16 ct + li
     const uint32_t a_vt4 = lds_base(LY::vt + (64 * TS + 8 * g) * 2);              // the ones row
-    const uint32_t a_kt = lds_base(LY::kt + ((w * 8 + (li & 3)) * TS + 8 * g) * 2);
-    const uint32_t a_kp = lds_base(LY::kp + ((8 * w + (li >> 2)) * TS + 8 * g) * 2);
+    const uint32_t a_kt = lds_base(LY::kT + ((8 * lb_w + (li & 3)) * TS + 8 * g) * 2);
     const uint32_t a_qh = lds_base((EARLY ? LY::qh : LY::rawq) + (16 * mt + li) * XR * 2);
 
     // A token tile's partial readout of chunk c ([col][token] in HBM): the wave with
@@ -387,25 +395,18 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             }
         }
         if (ONES && tid < L) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
-        {
-            // this wave: its 8 key coordinates l = 8 lb + e (transposed, lane = token)
-            // and the parent products of its 8 rows, zero past nvalid
+        {   // keys: every coordinate transposed to [coordinate][token], fp16, zero past
+            // nvalid; wave w converts 16-byte slots w, w + 8, ... (lane = token)
             const int t = lane;
-            const uint16_t* xrow = rk + t * XR;
-            const f16x8 kx = bf16x8_to_f16(*reinterpret_cast<const uint4*>(xrow + 8 * lb_w));
-            _Float16* ktw = kt + w * 8 * TS + t;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ktw[e * TS] = kx[e];
-            float kpv[8];
+            for (int cs = w; cs < D / 8; cs += kWaves) {
+                uint4 x = *reinterpret_cast<const uint4*>(rk + t * XR + 8 * cs);
+                if (t >= nvalid) x = uint4{0u, 0u, 0u, 0u};
+                const f16x8 kx = bf16x8_to_f16(x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {             // all reads first: no LDS round trips
-                kpv[i] = 1.0f;
-#pragma unroll
-                for (int e = 0; e < NPC; ++e) kpv[i] *= bf16_at(xrow, (p3w[i] >> (10 * e)) & 1023u);
+                for (int e = 0; e < 8; ++e) kT[(8 * cs + e) * TS + t] = kx[e];
             }
-            const bool tv = t < nvalid;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) kp[(8 * w + i) * TS + t] = (_Float16)(tv ? kpv[i] : 0.0f);
+            if (tid < L) kT[D * TS + tid] = (_Float16)(tid < nvalid ? 1.0f : 0.0f);
         }
         lds_barrier<63>();                                             // B1
         // raw k (and with EARLY raw q and v) are free: the next chunk streams in
@@ -475,7 +476,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             for (int hh = 0; hh < 2; ++hh) kreg[hh] = lds_at<f16x8>(lds_raw, a_kt, (4 * hh * TS + 32 * kk) * 2);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const f16x8 kp8 = lds_at<f16x8>(lds_raw, a_kp, (4 * s * TS + 32 * kk) * 2);
+                // parent product of this lane's row for its 8 tokens
+                f16x8 kp8 = lds_at<f16x8>(lds_raw, kpa[s][0], 32 * kk * 2);
+#pragma unroll
+                for (int e = 1; e < NPR; ++e) kp8 = kp8 * lds_at<f16x8>(lds_raw, kpa[s][e], 32 * kk * 2);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int T = 2 * s + h;
