@@ -78,6 +78,10 @@ struct KernelTimer {
     }
 };
 
+// Default cap on the slice-partial workspace of one prefill call (about 11% of the
+// 288 GB of an MI355X); a call that needs more runs in segments of whole chunks.
+constexpr int64_t kDefaultWorkspace = 32LL << 30;
+
 struct sata_tables {
     sata::HostTables h;
     KernelTimer timer;
@@ -88,7 +92,7 @@ struct sata_tables {
     std::mutex mu;
     void* ws = nullptr;
     size_t ws_bytes = 0;
-    int64_t ws_limit = 16LL << 30;
+    int64_t ws_limit = kDefaultWorkspace;
 };
 
 namespace {
@@ -280,7 +284,7 @@ int sata_set_workspace_limit(sata_tables* t, int64_t bytes) {
     if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
     if (bytes < 0) return fail(SATA_ERR_ARG, "negative limit");
     std::lock_guard<std::mutex> lock(t->mu);
-    t->ws_limit = bytes == 0 ? (16LL << 30) : bytes;
+    t->ws_limit = bytes == 0 ? kDefaultWorkspace : bytes;
     return SATA_OK;
 }
 
@@ -348,6 +352,10 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     if (per_chunk * seg > t->ws_limit) {
         seg = (t->ws_limit - (state ? 0 : state_b)) / per_chunk;
         if (seg < 1) seg = 1;
+        // equal segments: every segment boundary stores and reloads the state, so no
+        // segment should be much shorter than the others
+        const int64_t ns = (nchunks + seg - 1) / seg;
+        seg = (nchunks + ns - 1) / ns;
     }
     const int nseg = (int)((nchunks + seg - 1) / seg);
     float* carrier = state;

@@ -154,7 +154,7 @@ const char *sata_last_error(void);
 /*
  * Optional: cap (bytes) on the workspace a handle may hold; prefill splits the
  * sequence into segments of whole chunks to stay under it.  0 restores the
- * default (16 GiB).
+ * default (32 GiB).
  */
 int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
 
