@@ -176,28 +176,55 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     }
     if (tid < L) vt[DV * TS + tid] = (_Float16)(tid < nvalid ? 1.0f : 0.0f);
 
-    // slice partials: num[t][col] = sum over slices, 4 tokens per item, 8 loads in flight
+    // slice partials: num[t][col] = sum over slices.  Value columns: DV / 16 items of 4
+    // tokens per thread, all of them loaded together, 4 slices at a time.  The
+    // normaliser column (16 items) is split over 16 slice groups, one per thread, and
+    // summed with LDS atomics, so that no thread walks the slices alone at the end.
     {
         const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * L * COLS;
         const int64_t stride = (int64_t)L * COLS;
-        for (int item = tid; item < COLS * (L / 4); item += 256) {
-            const int col = item / (L / 4), tg = item % (L / 4);
-            const float* p = part + col * L + 4 * tg;
-            f32x4_t acc[8];
+        constexpr int NI = DV * (L / 4) / 256;          // value-column items per thread
+        static_assert(NI * 256 == DV * (L / 4), "whole items per thread");
+        if (tid < L) num[tid * NS + DV] = 0.0f;
+        const float* p[NI];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            int sl = 0;
-            for (; sl + 8 <= a.nslices; sl += 8) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    acc[u] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + (sl + u) * stride));
-            }
-            for (; sl < a.nslices; ++sl)
-                acc[0] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + sl * stride));
-            const f32x4_t s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) num[(4 * tg + e) * NS + col] = s[e];
+        for (int i = 0; i < NI; ++i) {
+            const int item = tid + 256 * i;
+            p[i] = part + (item / (L / 4)) * L + 4 * (item % (L / 4));
         }
+        f32x4_t acc[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        int sl = 0;
+        for (; sl + 4 <= a.nslices; sl += 4) {
+            f32x4_t x[4][NI];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    x[u][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + (sl + u) * stride));
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[i] += (x[0][i] + x[1][i]) + (x[2][i] + x[3][i]);
+        }
+        for (; sl < a.nslices; ++sl)
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int item = tid + 256 * i, col = item / (L / 4), tg = item % (L / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[(4 * tg + e) * NS + col] = acc[i][e];
+        }
+        // normaliser column: token quad tid % 16, slices tid / 16, tid / 16 + 16, ...
+        const int tg = tid % (L / 4);
+        const float* pz = part + DV * L + 4 * tg;
+        f32x4_t z = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s2 = tid / (L / 4); s2 < a.nslices; s2 += 256 / (L / 4))
+            z += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pz + s2 * stride));
+        __syncthreads();                              // the normaliser column is zeroed
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&num[(4 * tg + e) * NS + DV], z[e]);
     }
     __syncthreads();
 
