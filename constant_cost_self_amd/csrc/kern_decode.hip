@@ -17,6 +17,9 @@
 // row of `cols` partial sums per (head, block).
 // Kernel 2 (decode_finalize_kernel): one block per head sums the partial rows and
 // divides by the normaliser column.
+// Pool form ([HW] "The fixed-size hidden state of SATA attention": the state's memory
+// is allocated up front and requests share the device in turns): batch entry b uses
+// the state in slot slots[b] of a preallocated pool instead of state b.
 #include "launch.h"
 #include "sata_common.h"
 
@@ -33,11 +36,22 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const typename In::T* __restrict__ k, const typename In::T* __restrict__ v,
     const uint32_t* __restrict__ fidx, const float* __restrict__ qw,
     float* __restrict__ partial, int64_t M, int64_t M_pad, int d_K, int d_V, int P,
-    int nblk) {
+    int nblk, const int32_t* __restrict__ slots, int64_t pool, int H) {
     const int blk = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int cols = d_V + 1;
+    // state of this head: its own (dense form) or the one in its entry's pool slot; an
+    // entry whose slot is outside the pool leaves the pool alone and reads out NaN
+    int64_t sh = bh;
+    if (slots) {
+        const int64_t s = slots[bh / H];
+        if (s < 0 || s >= pool) {
+            for (int j = tid; j < cols; j += kThreads) partial[(bh * nblk + blk) * cols + j] = __builtin_nanf("");
+            return;
+        }
+        sh = s * H + bh % H;
+    }
 
     __shared__ float xq[kMaxD + 1];
     __shared__ float xk[kMaxD + 1];
@@ -56,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 #pragma unroll
     for (int j = 0; j < CMAX; ++j) acc[j] = 0.0f;
 
-    float* __restrict__ S = state + bh * (int64_t)cols * M_pad;
+    float* __restrict__ S = state + sh * (int64_t)cols * M_pad;
     const int nidx = P - 1;
 
     for (int g = 0; g < kDecGroups; ++g) {
@@ -133,7 +147,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
                        a.state, static_cast<const typename In::T*>(a.q),
                        static_cast<const typename In::T*>(a.k),
                        static_cast<const typename In::T*>(a.v), a.fidx, a.qw, a.partial, a.M,
-                       a.M_pad, a.d_K, a.d_V, a.P, a.nblk);
+                       a.M_pad, a.d_K, a.d_V, a.P, a.nblk, a.slots, a.pool, a.H);
     return hipGetLastError();
 }
 

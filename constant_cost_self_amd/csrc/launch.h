@@ -20,6 +20,11 @@ struct DecodeArgs {
     int64_t M, M_pad;
     int BH, d_K, d_V, P, nblk;
     bool bf16;
+    // pool form: batch entry b = bh / H uses state slot slots[b] of `pool` slots (device
+    // array); NULL: entry bh uses state bh
+    const int32_t* slots;
+    int64_t pool;
+    int H;
 };
 
 // Number of feature blocks per head of the decode kernel.

@@ -387,15 +387,15 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     return SATA_OK;
 }
 
-int sata_decode_step(const sata_tables* tc, float* state, const void* q, const void* k,
-                     const void* v, float* y, int B, int H, int d_K, int d_V, int P,
-                     sata_dtype in_dtype, void* stream) {
-    clear_err();
-    sata_tables* t = const_cast<sata_tables*>(tc);
-    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
-    if (!state || !q || !k || !v || !y)
-        return fail(SATA_ERR_ARG, "state, q, k, v and y must be non-NULL");
-    if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
+}  // extern "C"
+
+namespace {
+
+// Decode step shared by the dense and the pool forms: BH = batch entries x H heads;
+// slots == NULL for the dense form.
+int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool, const void* q,
+                const void* k, const void* v, float* y, int B, int H, int d_K, int d_V, int P,
+                sata_dtype in_dtype, void* stream) {
     int rc = check_sizes(d_K, d_V, P);
     if (rc) return rc;
     if (d_K != t->h.d_K || P != t->h.P)
@@ -418,6 +418,9 @@ int sata_decode_step(const sata_tables* tc, float* state, const void* q, const v
     a.BH = B * H; a.d_K = d_K; a.d_V = d_V; a.P = P;
     a.nblk = sata::decode_blocks(t->h.M_pad);
     a.bf16 = in_dtype == SATA_BF16;
+    a.slots = slots;
+    a.pool = pool;
+    a.H = H;
 
     std::lock_guard<std::mutex> lock(t->mu);
     hipStream_t st = (hipStream_t)stream;
@@ -434,6 +437,39 @@ int sata_decode_step(const sata_tables* tc, float* state, const void* q, const v
     if (e != hipSuccess)
         return fail(SATA_ERR_HIP, "decode reduction launch failed: %s", hipGetErrorString(e));
     return SATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sata_decode_step(const sata_tables* tc, float* state, const void* q, const void* k,
+                     const void* v, float* y, int B, int H, int d_K, int d_V, int P,
+                     sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!state || !q || !k || !v || !y)
+        return fail(SATA_ERR_ARG, "state, q, k, v and y must be non-NULL");
+    if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
+    return decode_impl(t, state, nullptr, 0, q, k, v, y, B, H, d_K, d_V, P, in_dtype, stream);
+}
+
+int sata_decode_step_pool(const sata_tables* tc, float* state_pool, int64_t pool_size,
+                          const int32_t* slots, int count, const void* q, const void* k,
+                          const void* v, float* y, int H, int d_K, int d_V, int P,
+                          sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!state_pool || !slots || !q || !k || !v || !y)
+        return fail(SATA_ERR_ARG, "state_pool, slots, q, k, v and y must be non-NULL");
+    if (count < 1 || H < 1 || pool_size < 1)
+        return fail(SATA_ERR_ARG, "need count, H, pool_size >= 1 (got %d %d %lld)", count, H,
+                    (long long)pool_size);
+    if (((uintptr_t)slots & 3) != 0) return fail(SATA_ERR_ALIGN, "slots must be 4-byte aligned");
+    return decode_impl(t, state_pool, slots, pool_size, q, k, v, y, count, H, d_K, d_V, P,
+                       in_dtype, stream);
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@ SATA_ERR_OOM = -5
 
 EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "sata_tables_free", "sata_feature_dim",
             "sata_state_stride", "sata_state_bytes", "sata_prefill", "sata_decode_step",
+            "sata_decode_step_pool",
             "sata_last_error", "sata_set_workspace_limit", "sata_set_timing",
             "sata_read_timing")
 KERNELS = ("scan", "finalize", "decode", "decode_reduce")
@@ -70,6 +71,8 @@ def load():
                                  i32, i32, vp]
     lib.sata_decode_step.restype = i32
     lib.sata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.sata_decode_step_pool.restype = i32
+    lib.sata_decode_step_pool.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.sata_last_error.restype = ctypes.c_char_p
     lib.sata_last_error.argtypes = []
     lib.sata_set_workspace_limit.restype = i32
@@ -231,6 +234,18 @@ def sata_decode_step(t: Tables, state, q, k, v, y, *, stream=None):
     d_V = v.shape[-1]
     _check(load().sata_decode_step(t.handle, _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(y),
                                    B, H, d_K, d_V, t.P, _dtype_code(q), _stream(stream)))
+
+
+def sata_decode_step_pool(t: Tables, pool, slots, q, k, v, y, *, stream=None):
+    """Decode step over a state pool.  pool: fp32 [pool_size, H, d_V + 1, M_pad];
+    slots: int32 [count] on the device; q, k: [count, H, d_K]; v: [count, H, d_V];
+    y: fp32 [count, H, d_V]."""
+    _need(pool, slots, q, k, v, y)
+    count, H, d_K = q.shape
+    d_V = v.shape[-1]
+    _check(load().sata_decode_step_pool(t.handle, _ptr(pool), pool.shape[0], _ptr(slots), count,
+                                        _ptr(q), _ptr(k), _ptr(v), _ptr(y), H, d_K, d_V, t.P,
+                                        _dtype_code(q), _stream(stream)))
 
 
 def sata_last_error() -> str:

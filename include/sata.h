@@ -148,6 +148,30 @@ int sata_decode_step(const sata_tables *t, float *state, const void *q,
                      const void *k, const void *v, float *y, int B, int H,
                      int d_K, int d_V, int P, sata_dtype in_dtype, void *stream);
 
+/*
+ * The decode step for a batch whose states live in a pool ([HW] "The fixed-size
+ * hidden state of SATA attention": the state's memory is allocated up front and
+ * requests take turns on the device).  A sequence's whole history is its state, so
+ * sequences at different positions share a step, and sequences join and leave the
+ * batch by the slot list alone.  Batch entry i uses pool slot slots[i]; otherwise as
+ * sata_decode_step.
+ *
+ * state_pool  fp32 [pool_size][H][d_V + 1][M_pad], updated in place.  A slot is one
+ *             contiguous block of sata_state_bytes(1, H, ...) bytes: a sequence is
+ *             started by sata_prefill with B = 1 and `state` pointing at its slot, and
+ *             saved or restored by copying that block.
+ * slots       int32 [count], device memory, 4-byte aligned.  Slots of one call must be
+ *             distinct (entries that share a slot race).  An entry whose slot is
+ *             outside [0, pool_size) leaves the pool untouched and gets NaN in its y row.
+ * q, k        [count][H][d_K]; v: [count][H][d_V]; y: fp32 [count][H][d_V]
+ * Errors: SATA_ERR_ARG for NULL pointers, count, H or pool_size < 1; the checks of
+ * sata_decode_step otherwise.
+ */
+int sata_decode_step_pool(const sata_tables *t, float *state_pool, int64_t pool_size,
+                          const int32_t *slots, int count, const void *q, const void *k,
+                          const void *v, float *y, int H, int d_K, int d_V, int P,
+                          sata_dtype in_dtype, void *stream);
+
 /* The calling thread's last error message ("" if none). */
 const char *sata_last_error(void);
 

@@ -168,3 +168,36 @@ def test_workspace_limit_argument(host_tables):
     host_tables.set_workspace_limit(0)
     with pytest.raises(sata.SataError):
         host_tables.set_workspace_limit(-1)
+
+
+def _decode_pool(t, **kw):
+    args = dict(pool=A, pool_size=3, slots=A, count=2, q=A, k=A, v=A, y=A, H=2, d_K=8, d_V=8, P=4,
+                dtype=sata.SATA_F32)
+    args.update(kw)
+    lib = sata.load()
+    return lib.sata_decode_step_pool(t.handle if t else None, args["pool"] or None, args["pool_size"],
+                                     args["slots"] or None, args["count"], args["q"], args["k"],
+                                     args["v"], args["y"], args["H"], args["d_K"], args["d_V"],
+                                     args["P"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), sata.SATA_ERR_ARG),                       # valid args, but host-only handle
+    (dict(pool=0), sata.SATA_ERR_ARG),
+    (dict(slots=0), sata.SATA_ERR_ARG),
+    (dict(count=0), sata.SATA_ERR_ARG),
+    (dict(pool_size=0), sata.SATA_ERR_ARG),
+    (dict(H=0), sata.SATA_ERR_ARG),
+    (dict(d_K=16), sata.SATA_ERR_ARG),                 # handle mismatch
+    (dict(d_V=0), sata.SATA_ERR_UNSUPPORTED),
+    (dict(slots=A + 2), sata.SATA_ERR_ALIGN),
+    (dict(y=A + 4), sata.SATA_ERR_ALIGN),
+    (dict(count=40000, H=2), sata.SATA_ERR_UNSUPPORTED),
+])
+def test_decode_pool_argument_errors(host_tables, kw, code):
+    assert _decode_pool(host_tables, **kw) == code
+    assert sata.last_error() != ""
+
+
+def test_decode_pool_null_handle():
+    assert _decode_pool(None) == sata.SATA_ERR_ARG
