@@ -96,7 +96,6 @@ struct Layout {
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline float bf16_at(const uint16_t* p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
 
 // 8 bf16 values (one 16-byte slot) to fp16; exact for |x| in fp16's normal range
 __device__ inline f16x8 bf16x8_to_f16(const uint4& r) {
@@ -152,7 +151,6 @@ struct RowPtrs {
     const float* kscale;
     const int32_t* canon;
     const int32_t* wave_lblock;
-    const uint16_t* one_row;     // 8 bf16: 1, 0, ..., 0 (the constant coordinates d..d+7)
 };
 
 // Direct-to-LDS copies of one chunk of q or k.  A wave instruction moves 64 lanes x
@@ -164,7 +162,6 @@ template <int D, int NCT>
 __device__ inline void prefetch_x(const uint16_t* x0, int nvalid, unsigned char* dst, int w, int lane) {
     using LY = Layout<D, NCT>;
     constexpr int NBLK = kL * LY::XSLOTS / 64;
-#pragma unroll
     for (int blk = w; blk < NBLK; blk += kWaves) {
         const int sl = blk * 64 + lane;
         const int t = sl / LY::XSLOTS, cs = sl % LY::XSLOTS;
@@ -398,7 +395,6 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         {   // keys: every coordinate transposed to [coordinate][token], fp16, zero past
             // nvalid; wave w converts 16-byte slots w, w + 8, ... (lane = token)
             const int t = lane;
-#pragma unroll
             for (int cs = w; cs < D / 8; cs += kWaves) {
                 uint4 x = *reinterpret_cast<const uint4*>(rk + t * XR + 8 * cs);
                 if (t >= nvalid) x = uint4{0u, 0u, 0u, 0u};
@@ -530,7 +526,7 @@ template <int D, int DV, int G, int NPC>
 hipError_t launch_t(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
     using LY = Layout<D, G == 0 ? 5 : 4>;
     static_assert(LY::bytes <= 160 * 1024, "LDS budget");
-    RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock, m.one_row};
+    RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock};
     hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, G, NPC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (e != hipSuccess) return e;
@@ -564,7 +560,7 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
     MfmaHostRows r;
     if (!build_mfma_rows(h, r)) return 0;        // not an MFMA shape: the VALU scan is used
     const size_t nr = (size_t)r.nrows, nw = r.wave_lblock.size();
-    const size_t bytes = 16 + nr * 4 + nr * 4 + nr * 8 * 4 + nr * 8 * 4 + nw * 4;
+    const size_t bytes = nr * 4 + nr * 4 + nr * 8 * 4 + nr * 8 * 4 + nw * 4;
     char* base = nullptr;
     if (hipMalloc(&base, bytes) != hipSuccess) {
         (void)hipGetLastError();
@@ -576,15 +572,13 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
         off += n;
         return hipMemcpy(dst, src, n, hipMemcpyHostToDevice) == hipSuccess ? dst : nullptr;
     };
-    const uint16_t one_row[8] = {0x3f80u, 0, 0, 0, 0, 0, 0, 0};
-    m.one_row = (const uint16_t*)put(one_row, 16);
     m.parent = (const uint32_t*)put(r.parent.data(), nr * 4);
     m.weight = (const float*)put(r.weight.data(), nr * 4);
     m.kscale = (const float*)put(r.kscale.data(), nr * 8 * 4);
     m.canon = (const int32_t*)put(r.canon.data(), nr * 8 * 4);
     m.wave_lblock = (const int32_t*)put(r.wave_lblock.data(), nw * 4);
     m.d_rows = base;
-    if (!m.one_row || !m.parent || !m.weight || !m.kscale || !m.canon || !m.wave_lblock) {
+    if (!m.parent || !m.weight || !m.kscale || !m.canon || !m.wave_lblock) {
         free_mfma_tables(m);
         return -4;
     }

@@ -43,7 +43,6 @@ struct MfmaTables {
     const float* kscale = nullptr;
     const int32_t* canon = nullptr;
     const int32_t* wave_lblock = nullptr;
-    const uint16_t* one_row = nullptr;   // 8 bf16: 1, 0, ..., 0
     bool ok = false;
 };
 
