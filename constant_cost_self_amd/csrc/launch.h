@@ -16,7 +16,7 @@ struct DecodeArgs {
     float* y;
     const uint32_t* fidx;
     const float* qw;
-    float* partial;     // [BH][nblk][d_V+1] workspace
+    float* partial;     // workspace: decode_partial_floats(BH, d_V, M_pad) floats
     int64_t M, M_pad;
     int BH, d_K, d_V, P, nblk;
     bool bf16;
@@ -29,6 +29,8 @@ struct DecodeArgs {
 
 // Number of feature blocks per head of the decode kernel.
 int decode_blocks(int64_t M_pad);
+// Floats of decode workspace (per-wave partial readouts) for BH heads.
+int64_t decode_partial_floats(int BH, int d_V, int64_t M_pad);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);         // state RMW + partials
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);  // partials -> y
 

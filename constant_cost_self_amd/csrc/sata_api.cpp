@@ -424,7 +424,7 @@ int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool
 
     std::lock_guard<std::mutex> lock(t->mu);
     hipStream_t st = (hipStream_t)stream;
-    rc = ensure_ws(t, (size_t)a.BH * a.nblk * (d_V + 1) * 4, st);
+    rc = ensure_ws(t, (size_t)sata::decode_partial_floats(a.BH, d_V, a.M_pad) * 4, st);
     if (rc) return rc;
     a.partial = (float*)t->ws;
     hipEvent_t ev = t->timer.begin(st);
