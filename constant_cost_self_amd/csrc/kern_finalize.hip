@@ -1,13 +1,14 @@
 // kern_finalize.hip -- intra-chunk part, slice reduction and normalisation (gfx950).
 //
-// For every chunk of L tokens of a head, the rows T of the chunk attend to the
-// earlier tokens of the same chunk directly, with the truncated kernel on the
-// plain dot product ([TA] "Feature maps and linear attention": w(q,k) =
-// sum_{p<P} alpha_p (q.k)^p), and to everything before the chunk through the
-// state (the slice partials written by the scan):
-//     U[T][j] = sum_{t0<=t<=T} w(q_T, k_t) u_t[j]  +  sum_slices part[slice][T][j]
+// The scan reads the state out once per window of `win` chunks (the state before
+// the window's first chunk).  The rows T of a chunk attend to the earlier tokens of
+// their window directly, with the truncated kernel on the plain dot product ([TA]
+// "Feature maps and linear attention": w(q,k) = sum_{p<P} alpha_p (q.k)^p), and to
+// everything before the window through the state (the slice partials):
+//     U[T][j] = sum_{t_w<=t<=T} w(q_T, k_t) u_t[j]  +  sum_slices part[slice][T][j]
 //     y[T][j] = U[T][j] / U[T][d_V]               (u_t = [v_t | 1])
-// One block per (chunk, head); fp32 arithmetic; w by Horner's rule.
+// with t_w the window's first token.  One block per (chunk, head).  The fp32 kernel
+// below serves win = 1 (fp32 arithmetic, w by Horner's rule).
 #include "launch.h"
 #include "sata_common.h"
 
@@ -102,8 +103,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
 // MFMA variant for bf16 inputs, L = 64, d_K in {64, 128}, d_V in {64, 128}.
 // Same quantities, computed transposed so that no layout change is needed:
 //     S^T[j][i] = k_j . q_i            v_mfma_f32_16x16x32_bf16 (exact products)
-//     W^T[j][i] = w(S^T[j][i]) for j <= i < nvalid, else 0     (fp32, Horner)
+//     W^T[j][i] = w(S^T[j][i]) for live pairs, else 0           (fp32, Horner)
 //     O^T[c][i] = sum_j U^T[c][j] W^T[j][i]     v_mfma_f32_16x16x32_f16, W^T in fp16
+// summed over the key chunks of the window: a pair is live when i < nvalid and the key
+// chunk precedes the query chunk, or is the query chunk and j <= i.
 // The accumulator layout of two 16-key tiles of W^T is the B operand of the second
 // contraction when the A operand (U^T, [column][token] in LDS) lists its keys in
 // the same order: keys {4 g + r, 16 + 4 g + r} for lane group g.  Wave w owns
@@ -155,26 +158,35 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
 
     for (int idx = tid; idx < L * DK / 8; idx += 256) {
         const int t = idx / (DK / 8), s8 = idx % (DK / 8);
-        uint4 xq = uint4{0u, 0u, 0u, 0u}, xk = xq;
-        if (t < nvalid) {
-            xq = *reinterpret_cast<const uint4*>(q + t * DK + 8 * s8);
-            xk = *reinterpret_cast<const uint4*>(k + t * DK + 8 * s8);
-        }
+        uint4 xq = uint4{0u, 0u, 0u, 0u};
+        if (t < nvalid) xq = *reinterpret_cast<const uint4*>(q + t * DK + 8 * s8);
         *reinterpret_cast<uint4*>(qs + t * XR + 8 * s8) = xq;
-        *reinterpret_cast<uint4*>(ks + t * XR + 8 * s8) = xk;
     }
-    for (int idx = tid; idx < L * DV / 8; idx += 256) {
-        const int t = idx % L, c8 = idx / L;
-        uint4 x = uint4{0u, 0u, 0u, 0u};
-        if (t < nvalid) x = *reinterpret_cast<const uint4*>(v + t * DV + 8 * c8);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vt[(8 * c8 + 2 * e) * TS + t] = (_Float16)__uint_as_float(xw[e] << 16);
-            vt[(8 * c8 + 2 * e + 1) * TS + t] = (_Float16)__uint_as_float(xw[e] & 0xffff0000u);
+    // keys and [v | 1] of key chunk kc (zero past the sequence's end)
+    auto load_kv = [&](int kc) {
+        const int64_t dt = (int64_t)(kc - c) * L;
+        const int nvk = (int)((a.n - (int64_t)kc * L) < L ? (a.n - (int64_t)kc * L) : L);
+        for (int idx = tid; idx < L * DK / 8; idx += 256) {
+            const int t = idx / (DK / 8), s8 = idx % (DK / 8);
+            uint4 xk = uint4{0u, 0u, 0u, 0u};
+            if (t < nvk) xk = *reinterpret_cast<const uint4*>(k + (dt + t) * DK + 8 * s8);
+            *reinterpret_cast<uint4*>(ks + t * XR + 8 * s8) = xk;
         }
-    }
-    if (tid < L) vt[DV * TS + tid] = (_Float16)(tid < nvalid ? 1.0f : 0.0f);
+        for (int idx = tid; idx < L * DV / 8; idx += 256) {
+            const int t = idx % L, c8 = idx / L;
+            uint4 x = uint4{0u, 0u, 0u, 0u};
+            if (t < nvk) x = *reinterpret_cast<const uint4*>(v + (dt + t) * DV + 8 * c8);
+            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vt[(8 * c8 + 2 * e) * TS + t] = (_Float16)__uint_as_float(xw[e] << 16);
+                vt[(8 * c8 + 2 * e + 1) * TS + t] = (_Float16)__uint_as_float(xw[e] & 0xffff0000u);
+            }
+        }
+        if (tid < L) vt[DV * TS + tid] = (_Float16)(tid < nvk ? 1.0f : 0.0f);
+    };
+    const int cw = a.c_begin + (cl / a.win) * a.win;     // first chunk of this chunk's window
+    load_kv(cw);
 
     // slice partials: num[t][col] = sum over slices.  Value columns: DV / 16 items of 4
     // tokens per thread, all of them loaded together, 4 slices at a time.  The
@@ -228,36 +240,47 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     }
     __syncthreads();
 
-    // wave w: query tile w.  S^T tiles over the 4 key tiles, then the causal weights
+    // wave w: query tile w, over the key chunks of the window (the last one causal)
     const int iq = 16 * w + li;                 // this lane's query token
-    f16x8_t Wb[2];                              // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kd = 0; kd < DK / 32; ++kd) {
-            const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kt + li) * XR + 32 * kd + 8 * g);
-            const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(qs + iq * XR + 32 * kd + 8 * g);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, st, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = 16 * kt + 4 * g + r;          // key token
-            const float wgt = taylor_weight(st[r], a.alpha, a.P);
-            Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)((j <= iq && iq < nvalid) ? wgt : 0.0f);
-        }
-    }
     f32x4_t O[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        O[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const int row = 16 * ct + li < COLS ? 16 * ct + li : DV;   // dead columns read the ones row
+    for (int ct = 0; ct < NCT; ++ct) O[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kc = cw; kc <= c; ++kc) {
+        if (kc > cw) {
+            __syncthreads();                    // the previous key chunk is consumed
+            load_kv(kc);
+            __syncthreads();
+        }
+        // S^T tiles over the 4 key tiles, then the weights
+        f16x8_t Wb[2];                          // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
 #pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-            const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 4 * g);
-            const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 16 + 4 * g);
-            const f16x8_t A = f16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Wb[kq], O[ct], 0, 0, 0);
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kd = 0; kd < DK / 32; ++kd) {
+                const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kt + li) * XR + 32 * kd + 8 * g);
+                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(qs + iq * XR + 32 * kd + 8 * g);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, st, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * kt + 4 * g + r;      // key token within chunk kc
+                const float wgt = taylor_weight(st[r], a.alpha, a.P);
+                // earlier chunks of the window are whole; chunk c is causal
+                const bool live = iq < nvalid && (kc < c || j <= iq);
+                Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)(live ? wgt : 0.0f);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = 16 * ct + li < COLS ? 16 * ct + li : DV;   // dead columns read the ones row
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 4 * g);
+                const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 16 + 4 * g);
+                const f16x8_t A = f16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Wb[kq], O[ct], 0, 0, 0);
+            }
         }
     }
 #pragma unroll
@@ -294,6 +317,7 @@ hipError_t launch_finalize(const PrefillSegArgs& a, hipStream_t st) {
         if (a.d_K == 64) return a.d_V == 64 ? launch_fin_mfma<64, 64>(a, st) : launch_fin_mfma<64, 128>(a, st);
         return a.d_V == 64 ? launch_fin_mfma<128, 64>(a, st) : launch_fin_mfma<128, 128>(a, st);
     }
+    if (a.win != 1) return hipErrorInvalidValue;   // windows come only with the MFMA scan
     const size_t lds = (size_t)finalize_lds_bytes(a.d_K, a.d_V, a.L);
     dim3 grid(a.c_end - a.c_begin, a.BH);
     if (a.bf16) {

@@ -2,10 +2,13 @@
 //
 // The inter-chunk half of the chunked prefill ([TA] "Feature maps and linear
 // attention": the state recurrence, evaluated chunk by chunk):
-//     readout   part[t][j] = sum_f qw_f phi_f(q_t) S[f][j]      (S before the chunk)
+//     readout   part[t][j] = sum_f qw_f phi_f(q_t) S[f][j]      (S before the window)
 //     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
-// Both are dense contractions over a chunk of L tokens (64 or 128) and a slice of
-// the feature axis, run as v_mfma_f32_16x16x32_f16 with fp32 accumulation:
+// The readout is taken once per window of NSUB chunks of L = 64 tokens (R = 256
+// tokens at d_K = 64, 128 at d_K = 128) against the state before the window; the
+// finalize adds the direct part of the window's earlier chunks.  The update runs
+// chunk by chunk.  Both are dense contractions over tokens and a slice of the
+// feature axis, run as v_mfma_f32_16x16x32_f16 with fp32 accumulation:
 //     readout  (16 tokens x 32 features) x (32 features x 16 columns)
 //     update   (16 features x 32 tokens) x (32 tokens x 16 columns)
 //
@@ -30,18 +33,20 @@
 //     key side    k^(a, l)[t] = kpar_a[t] * k_l[t] * c_(a,l)  (c: 0 / 1/(1+m) / 1)
 // directly in the MFMA operand layout (q_a, kpar_a: parent products).
 //
-// The readout is split by tokens, not by features: wave w computes 16 tokens of
-// the chunk over all 512 features of the slice (at L = 64 two waves share a token
-// tile and split the features; one adds the other's result), so the slice's
-// partial readout leaves the registers straight to HBM.  Its B operand, the state
-// packed to fp16 after the previous chunk's update, is shared through LDS: the
+// The readout is split by tokens, not by features: wave w computes R / 8 tokens of
+// the window (two or one 16-token tiles) over all 512 features of the slice, so the
+// slice's partial readout leaves the registers straight to HBM with no exchange
+// between waves.  Its B operand, the state packed to fp16 after the previous
+// window's last update, is shared through LDS and read once per window: the
 // update's accumulator layout (lane = column, 4 rows each) over two tiles is a
-// 32-deep B operand when the query operand uses the same feature order.
+// 32-deep B operand when the query operand uses the same feature order.  A larger
+// window gives each B byte more tokens (R / 8 per wave) without more registers.
 //
-// Per chunk: q and k arrive in LDS (bf16) by direct-to-LDS loads and v in
-// registers, all issued during the previous chunk; q is converted to fp16 in
-// place; v (transposed, scaled), each wave's 8 key coordinates and the key parent
-// products go to fp16 token-major tables; readout; update; fp16 state to LDS.
+// Per window: the window's q arrives in LDS (bf16) by direct-to-LDS loads issued
+// during the previous window and is converted to fp16 in place; readout.  Per chunk:
+// k and v arrive by direct-to-LDS loads a chunk ahead; v (transposed, scaled) and
+// all key coordinates go to fp16 token-major tables; update.  After the window's last
+// update the fp16 state goes to LDS.
 #include "scan_mfma.h"
 
 #include <hip/hip_runtime.h>
@@ -61,37 +66,33 @@ constexpr float kUScale = 1.0f / 16.0f;     // 1 / (kQScale kVScale): readout ba
 
 template <int D, int NCT>
 struct Layout {
-    static constexpr int L = kL;
-    static constexpr int XR = D + 8;         // raw q/k row: D coords, 1, then 7 zeros
-    static constexpr int XSLOTS = XR / 8;    // 16-byte slots per raw row
-    static constexpr int TS = L + 8;         // fp16 token-major row stride
-    static constexpr int MT = L / 16;        // token tiles of the readout (4)
-    static constexpr int KR = 16 * MT / kWaves;   // readout K-steps per wave (8: two waves per tile)
+    static constexpr int L = kL;                     // update sub-chunk
+    static constexpr int NSUB = D == 64 ? 4 : 2;     // sub-chunks per readout window
+    static constexpr int R = L * NSUB;               // readout window (tokens)
+    static constexpr int TW = R / kWaves;            // readout tokens per wave (32 or 16)
+    static constexpr int MTW = TW / 16;              // readout token tiles per wave
+    static constexpr int KS = kRowsPerSlice / 4;     // readout K-steps (32 features each)
+    static constexpr int XR = D + 8;                 // raw q/k row: D coords, 1, then 7 zeros
+    static constexpr int XSLOTS = XR / 8;            // 16-byte slots per raw row
+    static constexpr int TS = L + 8;                 // fp16 token-major row stride
     static constexpr int VROWS = NCT == 5 ? 65 : 64;
-    // EARLY (when LDS allows): q is converted into its own fp16 table and v arrives in
-    // LDS too, so all raw buffers are free after the tables are built and the next
-    // chunk's loads are issued there, a whole readout and update ahead of their use
-    static constexpr bool EARLY = D == 64;
-    static constexpr int QB = L * XR * 2;                           // one raw q or k chunk
-    static constexpr int VB = L * 64 * 2;                           // one raw v chunk (64 columns)
-    static constexpr int rawq = 0;                                  // bytes
-    static constexpr int rawk = rawq + QB;
-    static constexpr int rawv = rawk + QB;
-    static constexpr int qh = rawv + (EARLY ? VB : 0);              // fp16 q, raw row layout
-    static constexpr int vt = qh + (EARLY ? QB : 0);                // [VROWS][TS]
+    static constexpr int sb = 0;                                    // [4 ct][KS][64 lanes] x 16 B
+    static constexpr int sb4 = sb + 4 * KS * 64 * 16;               // normaliser tile: [KS][4 g] x 16 B
+    static constexpr int qt = sb4 + (NCT == 5 ? KS * 4 * 16 : 0);   // window's q rows: bf16, then fp16 in place
+    static constexpr int rawk = qt + R * XR * 2;                    // one sub-chunk of raw k
+    static constexpr int rawv = rawk + L * XR * 2;                  // one sub-chunk of raw v (64 columns)
+    static constexpr int vt = rawv + L * 64 * 2;                    // [VROWS][TS]
     static constexpr int kT = vt + VROWS * TS * 2;                  // [XR coordinates][TS] fp16 keys
-    static constexpr int sb = kT + XR * TS * 2;                     // [4 ct][16 K-steps][64 lanes] x 16 B
-    static constexpr int sb4 = sb + 4 * 16 * 64 * 16;               // normaliser tile: [16][4 g] x 16 B
-    static constexpr int xch = sb4 + (NCT == 5 ? 16 * 4 * 16 : 0);  // [MT][NCT][64] x 16 B
-    static constexpr int bytes = xch + MT * NCT * 64 * 16;
+    static constexpr int ri = kT + XR * TS * 2;                      // [64 rows] readout row constants
+    static constexpr int bytes = ri + kRowsPerSlice * 8;
     // state load/store staging (outside the chunk loop) aliases the fp16 state area
     static constexpr int IO = 68;                                   // floats per feature row
     static constexpr int io_rows = kWaves * 16;                     // one tile per wave per phase
-    static_assert(io_rows * IO * 4 <= 4 * 16 * 64 * 16, "state staging size");
-    static_assert(rawk % 16 == 0 && rawv % 16 == 0 && qh % 16 == 0 && vt % 16 == 0 && kT % 16 == 0 &&
-                  sb % 16 == 0 && xch % 16 == 0, "16-byte alignment of LDS regions");
-    static_assert((L * XSLOTS) % 64 == 0 && VB % 1024 == 0, "whole DMA blocks per raw chunk");
-    static_assert(KR == 8, "two waves per token tile");
+    static_assert(io_rows * IO * 4 <= 4 * KS * 64 * 16, "state staging size");
+    static_assert(qt % 16 == 0 && rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kT % 16 == 0,
+                  "16-byte alignment of LDS regions");
+    static_assert((R * XSLOTS) % 64 == 0 && (L * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
+    static_assert(TW % 16 == 0 && L % TW == 0 && KS == 16, "readout tiling");
 };
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -153,18 +154,18 @@ struct RowPtrs {
     const int32_t* wave_lblock;
 };
 
-// Direct-to-LDS copies of one chunk of q or k.  A wave instruction moves 64 lanes x
+// Direct-to-LDS copies of ROWS rows of q or k.  A wave instruction moves 64 lanes x
 // 16 bytes into a contiguous 1 KiB block; lane i fills bytes [16 i, 16 i + 16).  The
 // slot after each row's D coordinates holds the constant coordinates (1, 0, ..., 0),
 // written once: its lanes are masked off.  Rows past n read row 0 of the chunk
 // instead (masked later).  Addresses are a uniform base plus 32-bit lane offsets.
-template <int D, int NCT>
+template <int D, int ROWS>
 __device__ inline void prefetch_x(const uint16_t* x0, int nvalid, unsigned char* dst, int w, int lane) {
-    using LY = Layout<D, NCT>;
-    constexpr int NBLK = kL * LY::XSLOTS / 64;
+    constexpr int XSLOTS = (D + 8) / 8;
+    constexpr int NBLK = ROWS * XSLOTS / 64;
     for (int blk = w; blk < NBLK; blk += kWaves) {
         const int sl = blk * 64 + lane;
-        const int t = sl / LY::XSLOTS, cs = sl % LY::XSLOTS;
+        const int t = sl / XSLOTS, cs = sl % XSLOTS;
         if (cs != D / 8)
             __builtin_amdgcn_global_load_lds((const void*)(x0 + ((t < nvalid ? t : 0) * D + 8 * cs)),
                                              (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
@@ -187,15 +188,14 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     constexpr int NCT = ONES ? 5 : 4;        // column tiles of this group
     constexpr int NCL = ONES ? 65 : 64;      // live columns of this group
     using LY = Layout<D, NCT>;
-    constexpr int L = kL, XR = LY::XR, TS = LY::TS, MT = LY::MT, KR = LY::KR;
-    constexpr bool EARLY = LY::EARLY;
+    constexpr int L = kL, XR = LY::XR, TS = LY::TS, NSUB = LY::NSUB, R = LY::R, TW = LY::TW;
+    constexpr int MTW = LY::MTW, KS = LY::KS;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
     _Float16* vt = reinterpret_cast<_Float16*>(lds_raw + LY::vt);
     _Float16* kT = reinterpret_cast<_Float16*>(lds_raw + LY::kT);
     f16x8* sb = reinterpret_cast<f16x8*>(lds_raw + LY::sb);
     f16x8* sb4 = reinterpret_cast<f16x8*>(lds_raw + LY::sb4);
-    f32x4v* xch = reinterpret_cast<f32x4v*>(lds_raw + LY::xch);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -204,8 +204,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     constexpr int d_V = DV, cols = DV + 1;
     const int nch = a.c_end - a.c_begin;
     const int row_s = slice * kRowsPerSlice;                 // first row of the slice
-    const int lb_w = rt.wave_lblock[slice * kWaves + w];     // this wave's l-block
-    const int mt = w % MT, kh = w / MT;                      // readout token tile and K half
+    const int lb_w = rt.wave_lblock[slice * kWaves + w];     // l-block of this wave's update rows
     // global column of local column j of this group (local 64 is the normaliser)
     auto gcol = [&](int j) { return (ONES && j == 64) ? d_V : col0 + j; };
 
@@ -214,51 +213,47 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint16_t* v = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.n * d_V;
     float* state = a.state ? a.state + bh * (int64_t)cols * a.M_pad : nullptr;
 
-    auto nvalid_of = [&](int c) {
+    // tokens of [c L, c L + len) that exist
+    auto nvalid_of = [&](int c, int len) {
         const int64_t r = a.n - (int64_t)c * L;
-        return (int)(r < L ? r : L);
+        return (int)(r < len ? r : len);
     };
-    // without EARLY, v goes through registers: token tid % L, 8 columns 8 (tid / L), as in LDS
-    uint4 vreg;
-    auto load_v = [&](int c) {
+    auto prefetch_q = [&](int cw) {
+        prefetch_x<D, R>(q + (int64_t)cw * L * D, nvalid_of(cw, R), lds_raw + LY::qt, w, lane);
+    };
+    auto prefetch_kv = [&](int c) {
         const int64_t t0 = (int64_t)c * L;
-        const int nv = nvalid_of(c);
-        const int t = tid % L, c8 = tid / L;
-        vreg = *reinterpret_cast<const uint4*>(v + t0 * d_V + col0 + ((t < nv ? t : 0) * d_V + 8 * c8));
+        const int nv = nvalid_of(c, L);
+        prefetch_x<D, L>(k + t0 * D, nv, lds_raw + LY::rawk, w, lane);
+        prefetch_v(v + t0 * d_V + col0, nv, d_V, lds_raw + LY::rawv, w, lane);
     };
     // the constant coordinate slot of every raw q and k row, for good
-    for (int t = tid; t < 2 * L; t += 512) {
-        uint16_t* row = reinterpret_cast<uint16_t*>(lds_raw + (t < L ? LY::rawq : LY::rawk)) + (t % L) * XR + D;
+    for (int t = tid; t < R + L; t += 512) {
+        uint16_t* row = reinterpret_cast<uint16_t*>(lds_raw + (t < R ? LY::qt : LY::rawk)) + (t < R ? t : t - R) * XR + D;
         *reinterpret_cast<uint4*>(row) = uint4{0x3f80u, 0u, 0u, 0u};
     }
     // key coordinates d + 1 .. d + 7 (the zeros after the constant one), for good
     for (int idx = tid; idx < 7 * TS; idx += 512) kT[(D + 1) * TS + idx] = (_Float16)0.0f;
-    {   // first chunk in flight while the state is being set up
-        const int64_t t0 = (int64_t)a.c_begin * L;
-        const int nv = nvalid_of(a.c_begin);
-        prefetch_x<D, NCT>(q + t0 * D, nv, lds_raw + LY::rawq, w, lane);
-        prefetch_x<D, NCT>(k + t0 * D, nv, lds_raw + LY::rawk, w, lane);
-        if (EARLY) prefetch_v(v + t0 * d_V + col0, nv, d_V, lds_raw + LY::rawv, w, lane);
-        else load_v(a.c_begin);
-    }
+    // the first window's q and first sub-chunk's k, v in flight while the state is set up
+    prefetch_q(a.c_begin);
+    prefetch_kv(a.c_begin);
 
-    // readout constants of this lane: K-step s of this wave covers rows 4 (kh KR + s) + g
-    uint32_t qoff[KR][NPC > 0 ? NPC : 1];    // parent coordinates: byte offsets in the fp16 q table
-    _Float16 Wq[KR];                         // query weights with the operand scale
-#pragma unroll
-    for (int s = 0; s < KR; ++s) {
-        const int row = row_s + 4 * (kh * KR + s) + g;
+    // readout constants of the slice's rows (K-step s covers rows 4 s .. 4 s + 3, lane group
+    // g row 4 s + g), in LDS: the parent coordinates as byte offsets in a q row (10 bits
+    // each) and the query weight with the operand scale (fp16 bits)
+    if (tid < kRowsPerSlice) {
+        const int row = row_s + tid;
         const uint32_t p3 = rt.parent[row];
+        uint32_t o = 0;
 #pragma unroll
-        for (int e = 0; e < NPC; ++e)
-            qoff[s][e] = (uint32_t)((EARLY ? LY::qh : LY::rawq) + ((16 * mt + li) * XR + ((p3 >> (10 * e)) & 1023u)) * 2);
-        Wq[s] = (_Float16)(rt.weight[row] * kQScale);
+        for (int e = 0; e < NPC; ++e) o |= (((p3 >> (10 * e)) & 1023u) * 2u) << (10 * e);
+        const _Float16 wq = (_Float16)(rt.weight[row] * kQScale);
+        reinterpret_cast<uint2*>(lds_raw + LY::ri)[tid] = uint2{o, (uint32_t)__builtin_bit_cast(uint16_t, wq)};
     }
-    // l-blocks of the readout's row groups, and this wave's 8 parent words (uniform)
-    int lbg[KR / 2];
+    // l-blocks of the slice's row octets (uniform)
+    int lbg[KS / 2];
 #pragma unroll
-    for (int gi = 0; gi < KR / 2; ++gi)
-        lbg[gi] = __builtin_amdgcn_readfirstlane(rt.wave_lblock[slice * kWaves + kh * KR / 2 + gi]);
+    for (int gi = 0; gi < KS / 2; ++gi) lbg[gi] = __builtin_amdgcn_readfirstlane(rt.wave_lblock[slice * kWaves + gi]);
     // key parents of this lane's update rows 8 w + 4 s + li / 4: byte offsets of their
     // coordinate rows in the key table (a missing parent is the constant coordinate d,
     // which is 1 for the chunk's tokens and 0 past them)
@@ -317,73 +312,30 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const f16x8 p = pack_tiles(S[2 * s][ct], S[2 * s + 1][ct]);
-                if (ct < 4) sb[(ct * 16 + 2 * w + s) * 64 + lane] = p;
+                if (ct < 4) sb[(ct * KS + 2 * w + s) * 64 + lane] = p;
                 else if (li == 0) sb4[(2 * w + s) * 4 + g] = p;
             }
     };
     __syncthreads();                         // staging reads done before the area is reused
     store_sb();
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     // per-lane LDS bases of the contraction's operand tables (byte addresses)
-    const uint32_t a_sb = lds_base(LY::sb + (kh * KR * 64 + lane) * 16);          // [ct][K-step][lane]
-    const uint32_t a_sb4 = lds_base(LY::sb4 + (kh * KR * 4 + g) * 16);            // [K-step][g]
+    const uint32_t a_sb = lds_base(LY::sb + lane * 16);                           // [ct][K-step][lane]
+    const uint32_t a_sb4 = lds_base(LY::sb4 + g * 16);                            // [K-step][g]
     const uint32_t a_vt = lds_base(LY::vt + (li * TS + 8 * g) * 2);               // row 16 ct + li
     const uint32_t a_vt4 = lds_base(LY::vt + (64 * TS + 8 * g) * 2);              // the ones row
     const uint32_t a_kt = lds_base(LY::kT + ((8 * lb_w + (li & 3)) * TS + 8 * g) * 2);
-    const uint32_t a_qh = lds_base((EARLY ? LY::qh : LY::rawq) + (16 * mt + li) * XR * 2);
+    const uint32_t a_q = lds_base(LY::qt + (TW * w + li) * XR * 2);               // token row, tile 0
+    const uint32_t a_ri = lds_base(LY::ri + g * 8);                               // row 4 s + g
 
-    // A token tile's partial readout of chunk c ([col][token] in HBM): the wave with
-    // kh = 0 keeps its half in registers, adds its partner's half (left in LDS before the
-    // chunk's last barrier) at the start of chunk c + 1 and stores the sum.
-    f32x4v Uprev[NCT];
-    auto store_partial = [&](int c) {
-        if (kh != 0) return;
-        float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4v u = (Uprev[ct] + xch[(mt * NCT + ct) * 64 + lane]) * kUScale;
-            if (ct < 4 || li == 0) *reinterpret_cast<f32x4v*>(pp + (gcol(16 * ct + li) * L + 16 * mt + 4 * g)) = u;
-        }
-    };
-
-    for (int c = a.c_begin; c < a.c_end; ++c) {
-        const int nvalid = nvalid_of(c);
-        const int64_t t1 = (int64_t)(c + 1) * L;
-        const bool more = c + 1 < a.c_end;
-        const int nvalid1 = more ? nvalid_of(c + 1) : 0;
-
-        // ---- P1: the previous chunk's partial and fp16 state; fp16 tables of the chunk ---
-        if (c > a.c_begin) {
-            store_partial(c - 1);
-            store_sb();
-        }
-        {   // q: raw bf16 rows to fp16 (own table, or in place)
-            constexpr int NQ = (L * LY::XSLOTS + 511) / 512;
-            uint4 r[NQ];
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int sl = tid + 512 * i;
-                if (sl < L * LY::XSLOTS) r[i] = reinterpret_cast<const uint4*>(lds_raw + LY::rawq)[sl];
-            }
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int sl = tid + 512 * i;
-                // the constant slot is written as fp16 (1, 0, ..., 0): in place, the raw
-                // slot is never reloaded
-                const f16x8 h = sl % LY::XSLOTS == D / 8 ? f16x8{1, 0, 0, 0, 0, 0, 0, 0} : bf16x8_to_f16(r[i]);
-                if (sl < L * LY::XSLOTS) reinterpret_cast<f16x8*>(lds_raw + (EARLY ? LY::qh : LY::rawq))[sl] = h;
-            }
-        }
-        {   // v: transposed to [column][token], scaled, zero past nvalid
-            uint4 x;
-            int t, c8;
-            t = lane;                                // this thread: token lane, columns 8 w
-            c8 = w;
-            x = EARLY ? reinterpret_cast<const uint4*>(lds_raw + LY::rawv)[tid] : vreg;
-            if (t >= nvalid) x = uint4{0u, 0u, 0u, 0u};
-            _Float16* dst = vt + 8 * c8 * TS + t;
+    // fp16 tables of sub-chunk c from its raw k and v
+    auto build_tables = [&](int c) {
+        const int nvalid = nvalid_of(c, L);
+        {   // v: transposed to [column][token], scaled, zero past nvalid; this thread:
+            // token lane, columns 8 w .. 8 w + 7
+            uint4 x = reinterpret_cast<const uint4*>(lds_raw + LY::rawv)[tid];
+            if (lane >= nvalid) x = uint4{0u, 0u, 0u, 0u};
+            _Float16* dst = vt + 8 * w * TS + lane;
             const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -394,73 +346,19 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         if (ONES && tid < L) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
         {   // keys: every coordinate transposed to [coordinate][token], fp16, zero past
             // nvalid; wave w converts 16-byte slots w, w + 8, ... (lane = token)
-            const int t = lane;
             for (int cs = w; cs < D / 8; cs += kWaves) {
-                uint4 x = *reinterpret_cast<const uint4*>(rk + t * XR + 8 * cs);
-                if (t >= nvalid) x = uint4{0u, 0u, 0u, 0u};
+                uint4 x = *reinterpret_cast<const uint4*>(rk + lane * XR + 8 * cs);
+                if (lane >= nvalid) x = uint4{0u, 0u, 0u, 0u};
                 const f16x8 kx = bf16x8_to_f16(x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kT[(8 * cs + e) * TS + t] = kx[e];
+                for (int e = 0; e < 8; ++e) kT[(8 * cs + e) * TS + lane] = kx[e];
             }
             if (tid < L) kT[D * TS + tid] = (_Float16)(tid < nvalid ? 1.0f : 0.0f);
         }
-        lds_barrier<63>();                                             // B1
-        // raw k (and with EARLY raw q and v) are free: the next chunk streams in
-        // during the contractions
-        if (more) {
-            prefetch_x<D, NCT>(k + t1 * D, nvalid1, lds_raw + LY::rawk, w, lane);
-            if (EARLY) {
-                prefetch_x<D, NCT>(q + t1 * D, nvalid1, lds_raw + LY::rawq, w, lane);
-                prefetch_v(v + t1 * d_V + col0, nvalid1, d_V, lds_raw + LY::rawv, w, lane);
-            }
-        }
+    };
 
-        // ---- P2: readout of token tile mt over K-steps kh KR .. kh KR + KR - 1, then the
-        // update S' += K^^T . [v | 1] of this wave's rows ----------------------------------
-        f32x4v U[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) U[ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-        // Readout, software-pipelined: the B operands (LDS) of K-step sr + 1 are requested
-        // before the MFMAs of step sr.
-        {
-            f16x8 B[2][NCT], qreg;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                B[0][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, ct * 16 * 64 * 16) : lds_at<f16x8>(lds_raw, a_sb4, 0);
-#pragma unroll
-            for (int sr = 0; sr < KR; ++sr) {
-                if (sr + 1 < KR) {
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        B[(sr + 1) & 1][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, (ct * 16 * 64 + (sr + 1) * 64) * 16)
-                                                     : lds_at<f16x8>(lds_raw, a_sb4, (sr + 1) * 64);
-                }
-                if (sr % 2 == 0) qreg = lds_at<f16x8>(lds_raw, a_qh, 8 * lbg[sr / 2] * 2);
-                _Float16 qp = Wq[sr];
-#pragma unroll
-                for (int e = 0; e < NPC; ++e) qp *= *reinterpret_cast<const _Float16*>(lds_raw + qoff[sr][e]);
-                const f16x8 A = qreg * qp;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    U[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[sr & 1][ct], U[ct], 0, 0, 0);
-            }
-        }
-        if (kh == 1) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) xch[(mt * NCT + ct) * 64 + lane] = U[ct];
-        } else {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Uprev[ct] = U[ct];
-        }
-        if (!EARLY) {
-            // the raw q buffer holds this chunk's fp16 q until every readout is done
-            lds_barrier<63>();                                         // B2
-            if (more) {
-                prefetch_x<D, NCT>(q + t1 * D, nvalid1, lds_raw + LY::rawq, w, lane);
-                load_v(c + 1);
-            }
-        }
-        // update S' += K^^T . [v | 1] of this wave's rows
+    // update S' += K^^T . [v | 1] of this wave's rows over the sub-chunk in the tables
+    auto update = [&]() {
 #pragma unroll
         for (int kk = 0; kk < L / 32; ++kk) {
             f16x8 Vop[NCT], kreg[2];
@@ -486,9 +384,105 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 }
             }
         }
-        lds_barrier<0>();                       // B3: the next chunk has landed
+    };
+
+    // Windows of NSUB sub-chunks: one readout of the window's R tokens against the state
+    // before the window, then the NSUB updates.  The finalize adds the direct part of the
+    // window's earlier sub-chunks.
+    for (int cw = a.c_begin; cw < a.c_end; cw += NSUB) {
+        const int nsub = a.c_end - cw < NSUB ? a.c_end - cw : NSUB;
+        const bool next_w = cw + NSUB < a.c_end;       // then nsub == NSUB
+        lds_barrier<0>();                  // the window's q and sub-chunk 0's k, v landed; sb written
+
+        // ---- q of the window to fp16 in place; tables of sub-chunk 0 ------------------------
+        {
+            constexpr int NQ = (R * LY::XSLOTS + 511) / 512;
+            uint4 r[NQ];
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int sl = tid + 512 * i;
+                if (sl < R * LY::XSLOTS) r[i] = reinterpret_cast<const uint4*>(lds_raw + LY::qt)[sl];
+            }
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int sl = tid + 512 * i;
+                // the constant slot is written as fp16 (1, 0, ..., 0); loads never refill it
+                const f16x8 h = sl % LY::XSLOTS == D / 8 ? f16x8{1, 0, 0, 0, 0, 0, 0, 0} : bf16x8_to_f16(r[i]);
+                if (sl < R * LY::XSLOTS) reinterpret_cast<f16x8*>(lds_raw + LY::qt)[sl] = h;
+            }
+        }
+        build_tables(cw);
+        lds_barrier<63>();
+        if (nsub > 1) prefetch_kv(cw + 1);             // raw k, v are free
+
+        // ---- readout: window tokens TW w .. TW w + TW - 1 over the slice's K-steps --------
+        f32x4v U[MTW][NCT];
+#pragma unroll
+        for (int m = 0; m < MTW; ++m)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) U[m][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            // software-pipelined: the B operands of K-step s + 1 are requested before the
+            // MFMAs of step s
+            f16x8 B[2][NCT], qreg[MTW];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                B[0][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, ct * KS * 64 * 16) : lds_at<f16x8>(lds_raw, a_sb4, 0);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                if (s + 1 < KS) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        B[(s + 1) & 1][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, (ct * KS * 64 + (s + 1) * 64) * 16)
+                                                    : lds_at<f16x8>(lds_raw, a_sb4, (s + 1) * 64);
+                }
+                if (s % 2 == 0) {
+#pragma unroll
+                    for (int m = 0; m < MTW; ++m)
+                        qreg[m] = lds_at<f16x8>(lds_raw, a_q + 16u * (uint32_t)lbg[s / 2], m * 16 * XR * 2);
+                }
+                const uint2 rc = lds_at<uint2>(lds_raw, a_ri, s * 4 * 8);
+#pragma unroll
+                for (int m = 0; m < MTW; ++m) {
+                    _Float16 qp = __builtin_bit_cast(_Float16, (uint16_t)rc.y);
+#pragma unroll
+                    for (int e = 0; e < NPC; ++e)
+                        qp *= lds_at<_Float16>(lds_raw, a_q + ((rc.x >> (10 * e)) & 1023u), m * 16 * XR * 2);
+                    const f16x8 A = qreg[m] * qp;
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        U[m][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[s & 1][ct], U[m][ct], 0, 0, 0);
+                }
+            }
+        }
+        {   // this wave's tokens lie in one sub-chunk: partials [column][token] in HBM
+            const int cs = (TW * w) / L;
+            if (cs < nsub) {
+                const int c = cw + cs;
+                float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols +
+                            (TW * w) % L + 4 * g;
+#pragma unroll
+                for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        if (ct < 4 || li == 0)
+                            *reinterpret_cast<f32x4v*>(pp + gcol(16 * ct + li) * L + 16 * m) = U[m][ct] * kUScale;
+            }
+        }
+
+        // ---- the window's updates -----------------------------------------------------------
+        update();
+        for (int i = 1; i < nsub; ++i) {
+            const int c = cw + i;
+            lds_barrier<0>();              // k, v of sub-chunk c landed; the update of c - 1 is done
+            if (i == 1 && next_w) prefetch_q(cw + NSUB);    // every readout of the window is done
+            build_tables(c);
+            lds_barrier<63>();
+            if (c + 1 < a.c_end) prefetch_kv(c + 1);        // this window's next, or the next window's first
+            update();
+        }
+        if (next_w) store_sb();            // nsub == NSUB > 1: no wave still reads sb
     }
-    if (a.c_end > a.c_begin) store_partial(a.c_end - 1);
     __builtin_amdgcn_s_waitcnt(0);
 
     if (a.store_state) {
@@ -594,6 +588,8 @@ void free_mfma_tables(MfmaTables& m) {
     if (m.d_rows) (void)hipFree(m.d_rows);
     m = MfmaTables();
 }
+
+int mfma_window(int d_K) { return d_K == 64 ? Layout<64, 5>::NSUB : Layout<128, 5>::NSUB; }
 
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L) {
     return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && (d_V == 64 || d_V == 128) &&

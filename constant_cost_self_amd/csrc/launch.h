@@ -50,6 +50,8 @@ struct PrefillSegArgs {
     int BH, n, d_K, d_V, P, L;
     int nslices, slice_feats; // slice decomposition of the feature axis
     int c_begin, c_end;
+    int win;                 // chunks per readout window: chunk c's state readout is taken at the
+                             // window's first chunk c_begin + win * floor((c - c_begin) / win)
     int load_state, store_state;
     bool bf16;
 };

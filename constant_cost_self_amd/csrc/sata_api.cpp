@@ -337,7 +337,9 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         a.nslices = t->mfma.nslices;
         a.slice_feats = t->mfma.slice_feats;
         a.mfma_rows = t->mfma.d_rows;
+        a.win = sata::mfma_window(d_K);
     } else {
+        a.win = 1;
         a.slice_feats = sata::valu_slice_feats(d_K, d_V, L);
         if (a.slice_feats == 0) return fail(SATA_ERR_UNSUPPORTED, "no VALU slice fits LDS");
         a.nslices = (int)((t->h.M + a.slice_feats - 1) / a.slice_feats);
@@ -351,11 +353,14 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     int64_t seg = nchunks;
     if (per_chunk * seg > t->ws_limit) {
         seg = (t->ws_limit - (state ? 0 : state_b)) / per_chunk;
-        if (seg < 1) seg = 1;
+        if (seg < a.win) seg = a.win;            // at least one readout window
         // equal segments: every segment boundary stores and reloads the state, so no
         // segment should be much shorter than the others
         const int64_t ns = (nchunks + seg - 1) / seg;
         seg = (nchunks + ns - 1) / ns;
+        // whole readout windows per segment: a segment starts a new window, so the
+        // windows (and the results) do not depend on the segmentation
+        seg -= seg % a.win;
     }
     const int nseg = (int)((nchunks + seg - 1) / seg);
     float* carrier = state;

@@ -49,6 +49,8 @@ struct MfmaTables {
 int build_mfma_tables(const HostTables& h, MfmaTables& m);
 void free_mfma_tables(MfmaTables& m);
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L);
+// Chunks per readout window of the MFMA scan (the finalize's direct part spans the window).
+int mfma_window(int d_K);
 hipError_t launch_scan_mfma(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st);
 
 }  // namespace sata

@@ -177,8 +177,9 @@ const char *sata_last_error(void);
 
 /*
  * Optional: cap (bytes) on the workspace a handle may hold; prefill splits the
- * sequence into segments of whole chunks to stay under it.  0 restores the
- * default (32 GiB).
+ * sequence into segments of whole chunks to stay under it (a segment holds at
+ * least one readout window: 4 chunks at d_K = 64, 2 at d_K = 128 on the bf16
+ * matrix-core path, 1 otherwise).  0 restores the default (32 GiB).
  */
 int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
 
