@@ -56,43 +56,51 @@ namespace sata {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kWavesPerSlice;      // 8 waves, 8 rows each
-constexpr int kL = 64;                      // chunk length of the MFMA scan
+constexpr int kL = 64;                      // chunk length (partials, finalize)
+constexpr int kLU = 128;                    // tokens per state update
 constexpr float kVScale = 1.0f / 256.0f;    // on the [v | 1] operand of the update
 constexpr float kQScale = 4096.0f;          // on the query operand of the readout
 constexpr float kUScale = 1.0f / 16.0f;     // 1 / (kQScale kVScale): readout back to S's units
 
 template <int D, int NCT>
 struct Layout {
-    static constexpr int L = kL;                     // update sub-chunk
-    static constexpr int NSUB = D == 64 ? 4 : 2;     // sub-chunks per readout window
-    static constexpr int R = L * NSUB;               // readout window (tokens)
+    static constexpr int L = kL;                     // chunk (partials)
+    static constexpr int LU = kLU;                   // update sub-chunk
+    static constexpr int R = D == 64 ? 256 : 128;    // readout window (tokens)
+    static constexpr int NSUB = R / L;               // chunks per window
     static constexpr int TW = R / kWaves;            // readout tokens per wave (32 or 16)
     static constexpr int MTW = TW / 16;              // readout token tiles per wave
     static constexpr int KS = kRowsPerSlice / 4;     // readout K-steps (32 features each)
     static constexpr int XR = D + 8;                 // raw q/k row: D coords, 1, then 7 zeros
     static constexpr int XSLOTS = XR / 8;            // 16-byte slots per raw row
-    static constexpr int TS = L + 8;                 // fp16 token-major row stride
+    static constexpr int TS = LU + 8;                // fp16 token-major row stride of the tables
     static constexpr int VROWS = NCT == 5 ? 65 : 64;
     static constexpr int sb = 0;                                    // [4 ct][KS][64 lanes] x 16 B
     static constexpr int sb4 = sb + 4 * KS * 64 * 16;               // normaliser tile: [KS][4 g] x 16 B
-    static constexpr int qt = sb4 + (NCT == 5 ? KS * 4 * 16 : 0);   // window's q rows: bf16, then fp16 in place
-    static constexpr int rawk = qt + R * XR * 2;                    // one sub-chunk of raw k
-    static constexpr int rawv = rawk + L * XR * 2;                  // one sub-chunk of raw v (64 columns)
-    static constexpr int vt = rawv + L * 64 * 2;                    // [VROWS][TS]
+    // the update's tables alias the fp16 state: they live between the window's readout
+    // and the next window's state copy
+    static constexpr int vt = 0;                                    // [VROWS][TS]
     static constexpr int kT = vt + VROWS * TS * 2;                  // [XR coordinates][TS] fp16 keys
-    static constexpr int ri = kT + XR * TS * 2;                      // [64 rows] readout row constants
+    static constexpr int tables_end = kT + XR * TS * 2;
+    static constexpr int sb_end = sb4 + (NCT == 5 ? KS * 4 * 16 : 0);
+    static constexpr int qt = ((tables_end > sb_end ? tables_end : sb_end) + 15) / 16 * 16;  // window's q rows
+    static constexpr int rawk = qt + R * XR * 2;                    // one sub-chunk of raw k
+    static constexpr int rawv = rawk + LU * XR * 2;                 // one sub-chunk of raw v (64 columns)
+    static constexpr int ri = rawv + LU * 64 * 2;                   // [64 rows] readout row constants
     static constexpr int bytes = ri + kRowsPerSlice * 8;
     // state load/store staging (outside the chunk loop) aliases the fp16 state area
     static constexpr int IO = 68;                                   // floats per feature row
     static constexpr int io_rows = kWaves * 16;                     // one tile per wave per phase
     static_assert(io_rows * IO * 4 <= 4 * KS * 64 * 16, "state staging size");
-    static_assert(qt % 16 == 0 && rawk % 16 == 0 && rawv % 16 == 0 && vt % 16 == 0 && kT % 16 == 0,
+    static_assert(qt % 16 == 0 && rawk % 16 == 0 && rawv % 16 == 0 && kT % 16 == 0 && ri % 16 == 0,
                   "16-byte alignment of LDS regions");
-    static_assert((R * XSLOTS) % 64 == 0 && (L * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
-    static_assert(TW % 16 == 0 && L % TW == 0 && KS == 16, "readout tiling");
+    static_assert((R * XSLOTS) % 64 == 0 && (LU * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
+    static_assert(TW % 16 == 0 && L % TW == 0 && KS == 16 && R % LU == 0, "readout tiling");
 };
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -172,12 +180,18 @@ __device__ inline void prefetch_x(const uint16_t* x0, int nvalid, unsigned char*
     }
 }
 
-// The 64 value columns [col0, col0 + 64) of a chunk's v rows (row length d_V), v0 at
-// the chunk's first row and column col0, stored column-group major: wave w moves
-// columns 8w .. 8w+7 of all 64 tokens (lane = token) into one 1 KiB block.
+// The 64 value columns [col0, col0 + 64) of a sub-chunk's v rows (row length d_V), v0
+// at its first row and column col0, stored column-group major per 64 tokens: wave w
+// moves columns 8w .. 8w+7 of tokens 64 h + lane into 1 KiB block 8 h + w.  Rows past
+// nvalid read row 0 instead (masked later).
+template <int ROWS>
 __device__ inline void prefetch_v(const uint16_t* v0, int nvalid, int d_V, unsigned char* dst, int w, int lane) {
-    __builtin_amdgcn_global_load_lds((const void*)(v0 + ((lane < nvalid ? lane : 0) * d_V + 8 * w)),
-                                     (void __attribute__((address_space(3)))*)(dst + w * 1024), 16, 0, 0);
+#pragma unroll
+    for (int h = 0; h < ROWS / 64; ++h) {
+        const int t = 64 * h + lane;
+        __builtin_amdgcn_global_load_lds((const void*)(v0 + ((t < nvalid ? t : 0) * d_V + 8 * w)),
+                                         (void __attribute__((address_space(3)))*)(dst + (8 * h + w) * 1024), 16, 0, 0);
+    }
 }
 
 template <int D, int DV, int G, int NPC>
@@ -188,7 +202,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     constexpr int NCT = ONES ? 5 : 4;        // column tiles of this group
     constexpr int NCL = ONES ? 65 : 64;      // live columns of this group
     using LY = Layout<D, NCT>;
-    constexpr int L = kL, XR = LY::XR, TS = LY::TS, NSUB = LY::NSUB, R = LY::R, TW = LY::TW;
+    constexpr int L = kL, LU = LY::LU, XR = LY::XR, TS = LY::TS, NSUB = LY::NSUB, R = LY::R, TW = LY::TW;
     constexpr int MTW = LY::MTW, KS = LY::KS;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
@@ -218,22 +232,26 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const int64_t r = a.n - (int64_t)c * L;
         return (int)(r < len ? r : len);
     };
+    // tokens of [c L, c L + LU) that belong to the segment (the update stops at its end)
+    const int64_t seg_end = (int64_t)a.c_end * L < a.n ? (int64_t)a.c_end * L : a.n;
+    auto nupd_of = [&](int c) {
+        const int64_t r = seg_end - (int64_t)c * L;
+        return (int)(r < LU ? r : LU);
+    };
     auto prefetch_q = [&](int cw) {
         prefetch_x<D, R>(q + (int64_t)cw * L * D, nvalid_of(cw, R), lds_raw + LY::qt, w, lane);
     };
-    auto prefetch_kv = [&](int c) {
+    auto prefetch_kv = [&](int c) {        // the update sub-chunk starting at chunk c
         const int64_t t0 = (int64_t)c * L;
-        const int nv = nvalid_of(c, L);
-        prefetch_x<D, L>(k + t0 * D, nv, lds_raw + LY::rawk, w, lane);
-        prefetch_v(v + t0 * d_V + col0, nv, d_V, lds_raw + LY::rawv, w, lane);
+        const int nv = nupd_of(c);
+        prefetch_x<D, LU>(k + t0 * D, nv, lds_raw + LY::rawk, w, lane);
+        prefetch_v<LU>(v + t0 * d_V + col0, nv, d_V, lds_raw + LY::rawv, w, lane);
     };
     // the constant coordinate slot of every raw q and k row, for good
-    for (int t = tid; t < R + L; t += 512) {
+    for (int t = tid; t < R + LU; t += 512) {
         uint16_t* row = reinterpret_cast<uint16_t*>(lds_raw + (t < R ? LY::qt : LY::rawk)) + (t < R ? t : t - R) * XR + D;
         *reinterpret_cast<uint4*>(row) = uint4{0x3f80u, 0u, 0u, 0u};
     }
-    // key coordinates d + 1 .. d + 7 (the zeros after the constant one), for good
-    for (int idx = tid; idx < 7 * TS; idx += 512) kT[(D + 1) * TS + idx] = (_Float16)0.0f;
     // the first window's q and first sub-chunk's k, v in flight while the state is set up
     prefetch_q(a.c_begin);
     prefetch_kv(a.c_begin);
@@ -317,7 +335,6 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             }
     };
     __syncthreads();                         // staging reads done before the area is reused
-    store_sb();
 
     // per-lane LDS bases of the contraction's operand tables (byte addresses)
     const uint32_t a_sb = lds_base(LY::sb + lane * 16);                           // [ct][K-step][lane]
@@ -328,39 +345,71 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint32_t a_q = lds_base(LY::qt + (TW * w + li) * XR * 2);               // token row, tile 0
     const uint32_t a_ri = lds_base(LY::ri + g * 8);                               // row 4 s + g
 
-    // fp16 tables of sub-chunk c from its raw k and v
+    // fp16 tables of the update sub-chunk starting at chunk c from its raw k and v.  A
+    // thread takes two consecutive tokens of one 16-byte slot: both raw rows are read
+    // before any conversion, and each transposed table row gets 4-byte token pairs.
     auto build_tables = [&](int c) {
-        const int nvalid = nvalid_of(c, L);
-        {   // v: transposed to [column][token], scaled, zero past nvalid; this thread:
-            // token lane, columns 8 w .. 8 w + 7
-            uint4 x = reinterpret_cast<const uint4*>(lds_raw + LY::rawv)[tid];
-            if (lane >= nvalid) x = uint4{0u, 0u, 0u, 0u};
-            _Float16* dst = vt + 8 * w * TS + lane;
-            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+        const int nvalid = nupd_of(c);
+        static_assert(LU == 128, "one token pair per lane");
+        const int t0 = 2 * lane;                                    // this lane's tokens t0, t0 + 1
+        const uint32_t m0 = t0 < nvalid ? 0xffffffffu : 0u, m1 = t0 + 1 < nvalid ? 0xffffffffu : 0u;
+        constexpr int NKS = D / 8 / kWaves;                         // key slots per thread (1 or 2)
+        uint4 kx[NKS][2], vx[2];
+        // raw v: block 8 h + w holds columns 8 w .. 8 w + 7 of tokens 64 h + (0 .. 63)
+        const uint4* rv = reinterpret_cast<const uint4*>(lds_raw + LY::rawv) + (8 * (t0 >> 6) + w) * 64 + (t0 & 63);
+        vx[0] = rv[0];
+        vx[1] = rv[1];
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+            const int cs = w + kWaves * j;
+            kx[j][0] = *reinterpret_cast<const uint4*>(rk + t0 * XR + 8 * cs);
+            kx[j][1] = *reinterpret_cast<const uint4*>(rk + (t0 + 1) * XR + 8 * cs);
+        }
+        auto mask = [&](uint4& x, uint32_t m) { x.x &= m; x.y &= m; x.z &= m; x.w &= m; };
+        mask(vx[0], m0);
+        mask(vx[1], m1);
+        {   // v: [column][token], scaled
+            const uint32_t a0[4] = {vx[0].x, vx[0].y, vx[0].z, vx[0].w};
+            const uint32_t a1[4] = {vx[1].x, vx[1].y, vx[1].z, vx[1].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                dst[(2 * e) * TS] = (_Float16)(bf16_lo(xw[e]) * kVScale);
-                dst[(2 * e + 1) * TS] = (_Float16)(bf16_hi(xw[e]) * kVScale);
+                const f16x2 lo = __builtin_convertvector(f32x2{bf16_lo(a0[e]), bf16_lo(a1[e])} * kVScale, f16x2);
+                const f16x2 hi = __builtin_convertvector(f32x2{bf16_hi(a0[e]), bf16_hi(a1[e])} * kVScale, f16x2);
+                *reinterpret_cast<f16x2*>(vt + (8 * w + 2 * e) * TS + t0) = lo;
+                *reinterpret_cast<f16x2*>(vt + (8 * w + 2 * e + 1) * TS + t0) = hi;
             }
         }
-        if (ONES && tid < L) vt[64 * TS + tid] = (_Float16)(tid < nvalid ? kVScale : 0.0f);
-        {   // keys: every coordinate transposed to [coordinate][token], fp16, zero past
-            // nvalid; wave w converts 16-byte slots w, w + 8, ... (lane = token)
-            for (int cs = w; cs < D / 8; cs += kWaves) {
-                uint4 x = *reinterpret_cast<const uint4*>(rk + lane * XR + 8 * cs);
-                if (lane >= nvalid) x = uint4{0u, 0u, 0u, 0u};
-                const f16x8 kx = bf16x8_to_f16(x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kT[(8 * cs + e) * TS + lane] = kx[e];
+        for (int j = 0; j < NKS; ++j) {   // keys: every coordinate to [coordinate][token]
+            const int cs = w + kWaves * j;
+            mask(kx[j][0], m0);
+            mask(kx[j][1], m1);
+            const uint32_t a0[4] = {kx[j][0].x, kx[j][0].y, kx[j][0].z, kx[j][0].w};
+            const uint32_t a1[4] = {kx[j][1].x, kx[j][1].y, kx[j][1].z, kx[j][1].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f16x2 lo = __builtin_convertvector(f32x2{bf16_lo(a0[e]), bf16_lo(a1[e])}, f16x2);
+                const f16x2 hi = __builtin_convertvector(f32x2{bf16_hi(a0[e]), bf16_hi(a1[e])}, f16x2);
+                *reinterpret_cast<f16x2*>(kT + (8 * cs + 2 * e) * TS + t0) = lo;
+                *reinterpret_cast<f16x2*>(kT + (8 * cs + 2 * e + 1) * TS + t0) = hi;
             }
-            if (tid < L) kT[D * TS + tid] = (_Float16)(tid < nvalid ? 1.0f : 0.0f);
+        }
+        {   // the constant key coordinate d (1 for the tokens, 0 past them), then
+            // coordinates d + 1 .. d + 7 (zeros): row d + w, this lane's token pair
+            const _Float16 one0 = (_Float16)(w == 0 && t0 < nvalid ? 1.0f : 0.0f);
+            const _Float16 one1 = (_Float16)(w == 0 && t0 + 1 < nvalid ? 1.0f : 0.0f);
+            *reinterpret_cast<f16x2*>(kT + (D + w) * TS + t0) = f16x2{one0, one1};
+            // the ones row of [v | 1]
+            if (ONES && w == 0)
+                *reinterpret_cast<f16x2*>(vt + 64 * TS + t0) =
+                    f16x2{(_Float16)(t0 < nvalid ? kVScale : 0.0f), (_Float16)(t0 + 1 < nvalid ? kVScale : 0.0f)};
         }
     };
 
     // update S' += K^^T . [v | 1] of this wave's rows over the sub-chunk in the tables
     auto update = [&]() {
 #pragma unroll
-        for (int kk = 0; kk < L / 32; ++kk) {
+        for (int kk = 0; kk < LU / 32; ++kk) {
             f16x8 Vop[NCT], kreg[2];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -386,15 +435,16 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         }
     };
 
-    // Windows of NSUB sub-chunks: one readout of the window's R tokens against the state
-    // before the window, then the NSUB updates.  The finalize adds the direct part of the
-    // window's earlier sub-chunks.
+    // Windows of NSUB chunks: one readout of the window's R tokens against the state
+    // before the window, then the window's updates, LU tokens each.  The finalize adds
+    // the direct part of the window's earlier chunks.
     for (int cw = a.c_begin; cw < a.c_end; cw += NSUB) {
-        const int nsub = a.c_end - cw < NSUB ? a.c_end - cw : NSUB;
-        const bool next_w = cw + NSUB < a.c_end;       // then nsub == NSUB
-        lds_barrier<0>();                  // the window's q and sub-chunk 0's k, v landed; sb written
+        const int nchw = a.c_end - cw < NSUB ? a.c_end - cw : NSUB;   // chunks of the window
+        const bool next_w = cw + NSUB < a.c_end;
+        lds_barrier<0>();           // the window's q and first k, v landed; the updates are done
 
-        // ---- q of the window to fp16 in place; tables of sub-chunk 0 ------------------------
+        // ---- fp16 state for the readout (over the previous window's tables); q to fp16 --
+        store_sb();
         {
             constexpr int NQ = (R * LY::XSLOTS + 511) / 512;
             uint4 r[NQ];
@@ -411,9 +461,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 if (sl < R * LY::XSLOTS) reinterpret_cast<f16x8*>(lds_raw + LY::qt)[sl] = h;
             }
         }
-        build_tables(cw);
         lds_barrier<63>();
-        if (nsub > 1) prefetch_kv(cw + 1);             // raw k, v are free
 
         // ---- readout: window tokens TW w .. TW w + TW - 1 over the slice's K-steps --------
         f32x4v U[MTW][NCT];
@@ -455,9 +503,9 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 }
             }
         }
-        {   // this wave's tokens lie in one sub-chunk: partials [column][token] in HBM
+        {   // this wave's tokens lie in one chunk: partials [column][token] in HBM
             const int cs = (TW * w) / L;
-            if (cs < nsub) {
+            if (cs < nchw) {
                 const int c = cw + cs;
                 float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols +
                             (TW * w) % L + 4 * g;
@@ -469,19 +517,18 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                             *reinterpret_cast<f32x4v*>(pp + gcol(16 * ct + li) * L + 16 * m) = U[m][ct] * kUScale;
             }
         }
+        lds_barrier<63>();          // every readout is done: the state copy and q are free
+        if (next_w) prefetch_q(cw + NSUB);
 
-        // ---- the window's updates -----------------------------------------------------------
-        update();
-        for (int i = 1; i < nsub; ++i) {
-            const int c = cw + i;
-            lds_barrier<0>();              // k, v of sub-chunk c landed; the update of c - 1 is done
-            if (i == 1 && next_w) prefetch_q(cw + NSUB);    // every readout of the window is done
-            build_tables(c);
+        // ---- the window's updates ----------------------------------------------------------
+        for (int cu = cw; cu < cw + nchw; cu += LU / L) {
+            if (cu > cw) lds_barrier<0>();    // k, v of this sub-chunk landed; the last update is done
+            build_tables(cu);
             lds_barrier<63>();
-            if (c + 1 < a.c_end) prefetch_kv(c + 1);        // this window's next, or the next window's first
+            // next raw k, v: this window's next sub-chunk, or the next window's first
+            if (cu + LU / L < a.c_end) prefetch_kv(cu + LU / L);
             update();
         }
-        if (next_w) store_sb();            // nsub == NSUB > 1: no wave still reads sb
     }
     __builtin_amdgcn_s_waitcnt(0);
 
