@@ -110,8 +110,9 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
 // The accumulator layout of two 16-key tiles of W^T is the B operand of the second
 // contraction when the A operand (U^T, [column][token] in LDS) lists its keys in
 // the same order: keys {4 g + r, 16 + 4 g + r} for lane group g.  Wave w owns
-// query tile w (16 tokens).  The slice partials, [column][token] per slice, are
-// summed first by all threads with 16-byte loads (the memory-bound part).
+// query tile w (16 tokens).  The slice partials ([column][token] per slice, or in
+// the MFMA scan's tile order) are summed first by all threads with 16-byte loads
+// (the memory-bound part).
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -132,7 +133,7 @@ struct FinLayout {
     static constexpr int bytes = num + L * NS * 4;
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool TILED>
 __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     using LY = FinLayout<DK, DV>;
     constexpr int L = LY::L, XR = LY::XR, TS = LY::TS, COLS = LY::COLS, NS = LY::NS;
@@ -198,11 +199,19 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
         constexpr int NI = DV * (L / 4) / 256;          // value-column items per thread
         static_assert(NI * 256 == DV * (L / 4), "whole items per thread");
         if (tid < L) num[tid * NS + DV] = 0.0f;
+        // item: 4 tokens of one value column; [column][token] order, or MFMA-tile order
+        // [token tile][column tile][lane (li, g)] (column 16 ct + li, tokens 16 tile + 4 g)
+        auto item_col = [&](int item) {
+            return TILED ? 16 * ((item / 64) % (DV / 16)) + (item % 16) : item / (L / 4);
+        };
+        auto item_tok = [&](int item) {
+            return TILED ? 16 * (item / 64 / (DV / 16)) + 4 * ((item % 64) / 16) : 4 * (item % (L / 4));
+        };
         const float* p[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int item = tid + 256 * i;
-            p[i] = part + (item / (L / 4)) * L + 4 * (item % (L / 4));
+            p[i] = part + (TILED ? 4 * item : item_col(item) * L + item_tok(item));
         }
         f32x4_t acc[NI];
 #pragma unroll
@@ -224,9 +233,9 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
                 acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride));
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int item = tid + 256 * i, col = item / (L / 4), tg = item % (L / 4);
+            const int item = tid + 256 * i, col = item_col(item), t0 = item_tok(item);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) num[(4 * tg + e) * NS + col] = acc[i][e];
+            for (int e = 0; e < 4; ++e) num[(t0 + e) * NS + col] = acc[i][e];
         }
         // normaliser column: token quad tid % 16, slices tid / 16, tid / 16 + 16, ...
         const int tg = tid % (L / 4);
@@ -298,14 +307,19 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     }
 }
 
-template <int DK, int DV>
-hipError_t launch_fin_mfma(const PrefillSegArgs& a, hipStream_t st) {
+template <int DK, int DV, bool TILED>
+hipError_t launch_fin_mfma_t(const PrefillSegArgs& a, hipStream_t st) {
     constexpr int bytes = FinLayout<DK, DV>::bytes;
-    hipError_t e = hipFuncSetAttribute((const void*)finalize_mfma_kernel<DK, DV>,
+    hipError_t e = hipFuncSetAttribute((const void*)finalize_mfma_kernel<DK, DV, TILED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((finalize_mfma_kernel<DK, DV>), dim3(a.c_end - a.c_begin, a.BH), dim3(256), bytes, st, a);
+    hipLaunchKernelGGL((finalize_mfma_kernel<DK, DV, TILED>), dim3(a.c_end - a.c_begin, a.BH), dim3(256), bytes, st, a);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_fin_mfma(const PrefillSegArgs& a, hipStream_t st) {
+    return a.partial_tiled ? launch_fin_mfma_t<DK, DV, true>(a, st) : launch_fin_mfma_t<DK, DV, false>(a, st);
 }
 
 }  // namespace
@@ -317,7 +331,8 @@ hipError_t launch_finalize(const PrefillSegArgs& a, hipStream_t st) {
         if (a.d_K == 64) return a.d_V == 64 ? launch_fin_mfma<64, 64>(a, st) : launch_fin_mfma<64, 128>(a, st);
         return a.d_V == 64 ? launch_fin_mfma<128, 64>(a, st) : launch_fin_mfma<128, 128>(a, st);
     }
-    if (a.win != 1) return hipErrorInvalidValue;   // windows come only with the MFMA scan
+    // windows and the tiled partial layout come only with the MFMA scan
+    if (a.win != 1 || a.partial_tiled) return hipErrorInvalidValue;
     const size_t lds = (size_t)finalize_lds_bytes(a.d_K, a.d_V, a.L);
     dim3 grid(a.c_end - a.c_begin, a.BH);
     if (a.bf16) {

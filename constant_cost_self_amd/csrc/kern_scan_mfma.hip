@@ -503,18 +503,27 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 }
             }
         }
-        {   // this wave's tokens lie in one chunk: partials [column][token] in HBM
+        {   // this wave's tokens lie in one chunk.  Partials in HBM, per (chunk, slice):
+            // the value columns in tile order [token tile][column tile][lane] x 16 bytes
+            // (lane (li, g): column 16 ct + li, tokens 16 tile + 4 g .. + 3), so that one
+            // store instruction writes 1 KiB contiguously; then the normaliser column,
+            // [token] (its lanes li = 0 write 16 bytes each)
             const int cs = (TW * w) / L;
             if (cs < nchw) {
                 const int c = cw + cs;
-                float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols +
-                            (TW * w) % L + 4 * g;
+                constexpr int NVT = d_V / 16;                       // value column tiles of the head
+                float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols;
 #pragma unroll
-                for (int m = 0; m < MTW; ++m)
+                for (int m = 0; m < MTW; ++m) {
+                    const int mg = ((TW * w) % L) / 16 + m;         // token tile within the chunk
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        if (ct < 4 || li == 0)
-                            *reinterpret_cast<f32x4v*>(pp + gcol(16 * ct + li) * L + 16 * m) = U[m][ct] * kUScale;
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        if (ct < 4)
+                            *reinterpret_cast<f32x4v*>(pp + ((mg * NVT + 4 * G + ct) * 64 + lane) * 4) = U[m][ct] * kUScale;
+                        else if (li == 0)
+                            *reinterpret_cast<f32x4v*>(pp + L * d_V + 16 * mg + 4 * g) = U[m][ct] * kUScale;
+                    }
+                }
             }
         }
         lds_barrier<63>();          // every readout is done: the state copy and q are free

@@ -41,7 +41,10 @@ struct PrefillSegArgs {
     const void* v;
     float* y;
     float* state;            // [BH][d_V+1][M_pad]; read if load_state, written if store_state
-    float* partial;          // [BH][c_end-c_begin][nslices][d_V+1][L] workspace
+    float* partial;          // [BH][c_end-c_begin][nslices][d_V+1][L] workspace; with
+                             // partial_tiled the d_V value columns of a (chunk, slice) block
+                             // are in MFMA-tile order instead (see kern_scan_mfma.hip)
+    bool partial_tiled;
     const uint32_t* fidx;    // packed feature indices [M_pad]
     const float* qw;         // alpha_p C_p [M_pad]
     const void* mfma_rows;   // slice tables of the MFMA scan (nullptr for the VALU scan)

@@ -338,8 +338,10 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         a.slice_feats = t->mfma.slice_feats;
         a.mfma_rows = t->mfma.d_rows;
         a.win = sata::mfma_window(d_K);
+        a.partial_tiled = true;
     } else {
         a.win = 1;
+        a.partial_tiled = false;
         a.slice_feats = sata::valu_slice_feats(d_K, d_V, L);
         if (a.slice_feats == 0) return fail(SATA_ERR_UNSUPPORTED, "no VALU slice fits LDS");
         a.nslices = (int)((t->h.M + a.slice_feats - 1) / a.slice_feats);
