@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
 // The accumulator layout of two 16-key tiles of W^T is the B operand of the second
 // contraction when the A operand (U^T, [column][token] in LDS) lists its keys in
 // the same order: keys {4 g + r, 16 + 4 g + r} for lane group g.  Wave w owns
-// query tile w (16 tokens).  The slice partials ([column][token] per slice, or in
+// query tile w (16 tokens) and keeps its direct part in registers while the slice
+// partials are summed into the LDS the q, k, v tables held.  The slice partials ([column][token] per slice, or in
 // the MFMA scan's tile order) are summed first by all threads with 16-byte loads
 // (the memory-bound part).
 // ---------------------------------------------------------------------------
@@ -126,11 +127,13 @@ struct FinLayout {
     static constexpr int TS = L + 8;                   // U^T row (fp16)
     static constexpr int COLS = DV + 1;
     static constexpr int NS = COLS + 3;                // num row (floats)
+    // q, k and [v | 1] for the direct part, then (same bytes) the sums of the partials
     static constexpr int qs = 0;
     static constexpr int ks = qs + L * XR * 2;
     static constexpr int vt = ks + L * XR * 2;
-    static constexpr int num = vt + ((COLS * TS * 2 + 15) / 16) * 16;
-    static constexpr int bytes = num + L * NS * 4;
+    static constexpr int tables = vt + ((COLS * TS * 2 + 15) / 16) * 16;
+    static constexpr int num = 0;
+    static constexpr int bytes = tables > L * NS * 4 ? tables : L * NS * 4;
 };
 
 template <int DK, int DV, bool TILED>
@@ -188,6 +191,54 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     };
     const int cw = a.c_begin + (cl / a.win) * a.win;     // first chunk of this chunk's window
     load_kv(cw);
+
+    __syncthreads();
+
+    // wave w: query tile w, over the key chunks of the window (the last one causal)
+    const int iq = 16 * w + li;                 // this lane's query token
+    f32x4_t O[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) O[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kc = cw; kc <= c; ++kc) {
+        if (kc > cw) {
+            __syncthreads();                    // the previous key chunk is consumed
+            load_kv(kc);
+            __syncthreads();
+        }
+        // S^T tiles over the 4 key tiles, then the weights
+        f16x8_t Wb[2];                          // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kd = 0; kd < DK / 32; ++kd) {
+                const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kt + li) * XR + 32 * kd + 8 * g);
+                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(qs + iq * XR + 32 * kd + 8 * g);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, st, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * kt + 4 * g + r;      // key token within chunk kc
+                const float wgt = taylor_weight(st[r], a.alpha, a.P);
+                // earlier chunks of the window are whole; chunk c is causal
+                const bool live = iq < nvalid && (kc < c || j <= iq);
+                Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)(live ? wgt : 0.0f);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = 16 * ct + li < COLS ? 16 * ct + li : DV;   // dead columns read the ones row
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 4 * g);
+                const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 16 + 4 * g);
+                const f16x8_t A = f16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Wb[kq], O[ct], 0, 0, 0);
+            }
+        }
+    }
+    // the tables are consumed: the partial sums reuse their LDS
+    __syncthreads();
 
     // slice partials: num[t][col] = sum over slices.  Value columns: DV / 16 items of 4
     // tokens per thread, all of them loaded together, 4 slices at a time.  The
@@ -248,50 +299,6 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
         for (int e = 0; e < 4; ++e) atomicAdd(&num[(4 * tg + e) * NS + DV], z[e]);
     }
     __syncthreads();
-
-    // wave w: query tile w, over the key chunks of the window (the last one causal)
-    const int iq = 16 * w + li;                 // this lane's query token
-    f32x4_t O[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) O[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kc = cw; kc <= c; ++kc) {
-        if (kc > cw) {
-            __syncthreads();                    // the previous key chunk is consumed
-            load_kv(kc);
-            __syncthreads();
-        }
-        // S^T tiles over the 4 key tiles, then the weights
-        f16x8_t Wb[2];                          // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kd = 0; kd < DK / 32; ++kd) {
-                const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kt + li) * XR + 32 * kd + 8 * g);
-                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(qs + iq * XR + 32 * kd + 8 * g);
-                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, st, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * kt + 4 * g + r;      // key token within chunk kc
-                const float wgt = taylor_weight(st[r], a.alpha, a.P);
-                // earlier chunks of the window are whole; chunk c is causal
-                const bool live = iq < nvalid && (kc < c || j <= iq);
-                Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)(live ? wgt : 0.0f);
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int row = 16 * ct + li < COLS ? 16 * ct + li : DV;   // dead columns read the ones row
-#pragma unroll
-            for (int kq = 0; kq < 2; ++kq) {
-                const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 4 * g);
-                const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + row * TS + 32 * kq + 16 + 4 * g);
-                const f16x8_t A = f16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Wb[kq], O[ct], 0, 0, 0);
-            }
-        }
-    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
