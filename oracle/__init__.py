@@ -14,7 +14,7 @@ Symmetry-Aware Taylor Approximation", as described on the blog.hotdry.top post
 "Hidden-state size and compute analysis" ([TA Size]) for the closed forms.
 
 Parity status of each function (what pins it is in tests/test_oracle_pins.py):
-  tables, features, direct, feature_form, state_rows, closed forms: pinned;
+  tables, features, direct, feature_form, state_rows, direct_grad, closed forms: pinned;
   softmax: pinned against scipy.special.softmax (a library routine); the
   Taylor-versus-softmax error it is used to report has no metric on the pages
   and is reported, not gated (parity unpinned for that report only).
@@ -79,6 +79,9 @@ def _load():
     lib.oracle_softmax.restype = None
     lib.oracle_softmax.argtypes = [dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_int, dp]
+    lib.oracle_direct_grad.restype = None
+    lib.oracle_direct_grad.argtypes = [dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -147,6 +150,23 @@ def direct(q, k, v, P: int, return_den: bool = False):
     den = np.zeros(lead + (n,), dtype=np.float64)
     _load().oracle_direct(_dp(q), _dp(k), _dp(v), heads, n, dK, dV, P, _dp(y), _dp(den))
     return (y, den) if return_den else y
+
+
+def direct_grad(q, k, v, dy, P: int):
+    """Gradients (dq, dk, dv) of L = sum dy . y for the direct form, fp64, O(n^2) per head
+    (the chain rule through y = N / D, written out pair by pair in oracle.c).
+    q, k: [..., n, dK]; v, dy: [..., n, dV]."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    lead = q.shape[:-2]
+    n, dK = q.shape[-2:]
+    dV = v.shape[-1]
+    heads = int(np.prod(lead)) if lead else 1
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    _load().oracle_direct_grad(_dp(q), _dp(k), _dp(v), _dp(dy), heads, n, dK, dV, P,
+                               _dp(dq), _dp(dk), _dp(dv))
+    return dq, dk, dv
 
 
 def direct_rows(q, k, v, P: int, heads, rows):

@@ -170,6 +170,72 @@ void oracle_direct(const double *q, const double *k, const double *v,
     }
 }
 
+/* ------------------------------------------------------------------------- */
+/* Gradients of the direct form                                               */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * For a loss L = sum_T dy_T . y_T with y the direct form above, the chain rule through
+ * y_T = N_T / D_T (N_T = sum_{t<=T} w_Tt v_t, D_T = sum_{t<=T} w_Tt, w_Tt = w(q_T.k_t))
+ * gives dL/dN_T = g_T = dy_T / D_T and dL/dD_T = h_T = -(dy_T . y_T) / D_T, so that
+ * dL/dw_Tt = c_Tt = g_T . v_t + h_T and
+ *   dv_t = sum_{T>=t} w_Tt g_T,
+ *   dq_T = sum_{t<=T} c_Tt w'(x_Tt) k_t,      dk_t = sum_{T>=t} c_Tt w'(x_Tt) q_T,
+ * with x_Tt = q_T.k_t and w'(x) = sum_{p=1}^{P-1} p alpha_p x^{p-1}.  Written out pair by
+ * pair, O(n^2) per head; heads in parallel.  q, k, dq, dk: [heads][n][dK]; v, dy, dv:
+ * [heads][n][dV].
+ */
+void oracle_direct_grad(const double *q, const double *k, const double *v, const double *dy,
+                        int64_t heads, int64_t n, int dK, int dV, int P,
+                        double *dq, double *dk, double *dv)
+{
+    double a[32];
+    for (int p = 0; p < P && p < 32; ++p) a[p] = alpha(p, dK);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t h = 0; h < heads; ++h) {
+        const double *qh = q + h * n * dK, *kh = k + h * n * dK;
+        const double *vh = v + h * n * dV, *dyh = dy + h * n * dV;
+        double *dqh = dq + h * n * dK, *dkh = dk + h * n * dK, *dvh = dv + h * n * dV;
+        double *yT = (double *)malloc((size_t)dV * sizeof(double));
+        double *gT = (double *)malloc((size_t)dV * sizeof(double));
+        for (int64_t i = 0; i < n * dK; ++i) { dqh[i] = 0.0; dkh[i] = 0.0; }
+        for (int64_t i = 0; i < n * dV; ++i) dvh[i] = 0.0;
+        for (int64_t T = 0; T < n; ++T) {
+            const double den = direct_row(qh, kh, vh, T, dK, dV, P, a, yT);
+            const double *dyT = dyh + T * dV;
+            double hT = 0.0;
+            for (int j = 0; j < dV; ++j) {
+                gT[j] = dyT[j] / den;
+                hT -= dyT[j] * yT[j];
+            }
+            hT /= den;
+            const double *qT = qh + T * dK;
+            for (int64_t t = 0; t <= T; ++t) {
+                const double *kt = kh + t * dK;
+                const double *vt = vh + t * dV;
+                double x = 0.0;
+                for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
+                double w = 0.0, wp = 0.0, xp = 1.0;
+                for (int p = 0; p < P; ++p) {
+                    w += a[p] * xp;
+                    if (p + 1 < P) wp += (p + 1) * a[p + 1] * xp;
+                    xp *= x;
+                }
+                double c = hT;
+                for (int j = 0; j < dV; ++j) c += gT[j] * vt[j];
+                for (int j = 0; j < dV; ++j) dvh[t * dV + j] += w * gT[j];
+                for (int i = 0; i < dK; ++i) {
+                    dqh[T * dK + i] += c * wp * kt[i];
+                    dkh[t * dK + i] += c * wp * qT[i];
+                }
+            }
+        }
+        free(yT);
+        free(gT);
+    }
+}
+
 /* Sampled rows of the direct form: out[r] = y of token rows[r] of head heads_of[r]
  * (q, k: [heads][n][dK], v: [heads][n][dV]); each row costs O(T (dK + dV)). */
 void oracle_direct_rows(const double *q, const double *k, const double *v,

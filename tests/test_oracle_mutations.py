@@ -44,6 +44,11 @@ def _causal_pins():
     pins.test_P1_is_cumulative_mean()
 
 
+def _grad_pins():
+    pins.test_grad_matches_finite_differences(4, 2)
+    pins.test_grad_invariant_under_value_shift()
+
+
 MUTANTS = {
     # alpha_p = 1/(p! c^p): factorial off by one
     "factorial": ("for (int s = 2; s <= p; ++s) fact *= s;",
@@ -71,6 +76,16 @@ MUTANTS = {
     # feature form: the normaliser column accumulates 1 instead of phi(k)
     "normaliser": ("S[f * cols + dV] += phik;", "S[f * cols + dV] += 1.0;",
                    _feature_form_pins),
+    # gradient: the normaliser's term h_T dropped
+    "grad_drop_h": ("            hT /= den;\n", "            hT = 0.0;\n", _grad_pins),
+    # gradient: w' with the power and the coefficient one term apart
+    "grad_wprime": ("if (p + 1 < P) wp += (p + 1) * a[p + 1] * xp;",
+                    "if (p + 1 < P) wp += (p + 1) * a[p] * xp;", _grad_pins),
+    # gradient: dk takes the key instead of the query (a transposed operand)
+    "grad_dk_operand": ("dkh[t * dK + i] += c * wp * qT[i];", "dkh[t * dK + i] += c * wp * kt[i];",
+                        _grad_pins),
+    # gradient: dv scaled by dy instead of dy / D
+    "grad_dv_scale": ("dvh[t * dV + j] += w * gT[j];", "dvh[t * dV + j] += w * dyT[j];", _grad_pins),
     # feature form: a transposed operand (v indexed by the wrong token)
     "v_index": ("S[f * cols + j] += phik * vt[j];",
                 "S[f * cols + j] += phik * v[((T + 1) % n) * dV + j];", _feature_form_pins),

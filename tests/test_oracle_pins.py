@@ -307,3 +307,69 @@ def test_bf16_rounding_is_nearest_even():
     assert vals[3] == -2.5 and vals[5] == 0.0
     assert abs(vals[4] - 3.0e-3) <= 3.0e-3 * 2 ** -8
     assert np.all((vals.view(np.uint32) & 0xFFFF) == 0)
+
+
+# --------------------------------------------------------------------------
+# Gradients of the direct form (the chain rule through y = N / D)
+# --------------------------------------------------------------------------
+
+def _loss(q, k, v, dy, P):
+    return float(np.sum(dy * oracle.direct(q, k, v, P)))
+
+
+@pytest.mark.parametrize("P,seed", [(2, 0), (3, 1), (4, 2), (5, 3)])
+def test_grad_matches_finite_differences(P, seed):
+    """Every coordinate of dq, dk, dv against central differences of L = sum dy . y,
+    computed with the forward oracle only (step 1e-5, fp64)."""
+    rng = np.random.default_rng(40 + seed)
+    n, dK, dV = 6, 3, 2
+    q, k = rng.standard_normal((n, dK)), rng.standard_normal((n, dK))
+    v, dy = rng.standard_normal((n, dV)), rng.standard_normal((n, dV))
+    dq, dk, dv = oracle.direct_grad(q, k, v, dy, P)
+    eps = 1e-5
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        for idx in np.ndindex(g.shape):
+            args = {"q": q, "k": k, "v": v}
+            plus, minus = dict(args), dict(args)
+            plus[name] = args[name].copy()
+            plus[name][idx] += eps
+            minus[name] = args[name].copy()
+            minus[name][idx] -= eps
+            fd = (_loss(plus["q"], plus["k"], plus["v"], dy, P) -
+                  _loss(minus["q"], minus["k"], minus["v"], dy, P)) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(g[idx])), (name, idx, fd, g[idx])
+
+
+def test_grad_P1_closed_form():
+    """P = 1: w = 1, y_T is the mean of v_0..v_T, so dq = dk = 0 and
+    dv_t = sum_{T>=t} dy_T / (T + 1)."""
+    rng = np.random.default_rng(50)
+    n, dK, dV = 9, 4, 3
+    q, k = rng.standard_normal((n, dK)), rng.standard_normal((n, dK))
+    v, dy = rng.standard_normal((n, dV)), rng.standard_normal((n, dV))
+    dq, dk, dv = oracle.direct_grad(q, k, v, dy, 1)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    ref = np.array([sum(dy[T] / (T + 1) for T in range(t, n)) for t in range(n)])
+    np.testing.assert_allclose(dv, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_grad_invariant_under_value_shift():
+    """Adding one vector to every v_t shifts every y_T by it, so no gradient changes."""
+    rng = np.random.default_rng(51)
+    n, dK, dV = 12, 3, 4
+    q, k = rng.standard_normal((n, dK)), rng.standard_normal((n, dK))
+    v, dy = rng.standard_normal((n, dV)), rng.standard_normal((n, dV))
+    g0 = oracle.direct_grad(q, k, v, dy, 4)
+    g1 = oracle.direct_grad(q, k, v + np.array([0.7, -1.3, 2.0, 0.25]), dy, 4)
+    for a, b in zip(g0, g1):
+        np.testing.assert_allclose(b, a, rtol=1e-9, atol=1e-11)
+
+
+def test_grad_batched_heads_independent():
+    rng = np.random.default_rng(52)
+    q, k = rng.standard_normal((2, 3, 7, 4)), rng.standard_normal((2, 3, 7, 4))
+    v, dy = rng.standard_normal((2, 3, 7, 5)), rng.standard_normal((2, 3, 7, 5))
+    g = oracle.direct_grad(q, k, v, dy, 3)
+    gh = oracle.direct_grad(q[1, 2], k[1, 2], v[1, 2], dy[1, 2], 3)
+    for a, b in zip(g, gh):
+        np.testing.assert_array_equal(a[1, 2], b)
