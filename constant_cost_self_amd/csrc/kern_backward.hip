@@ -1,0 +1,411 @@
+// kern_backward.hip -- gradients of the chunked prefill (fp32, vector ALUs, gfx950).
+//
+// For a loss with dL/dy = dy, the chain rule through y_T = N_T / D_T ([TA] "Feature maps
+// and linear attention": N_T = sum_{t<=T} w(q_T.k_t) v_t, D_T = sum_{t<=T} w(q_T.k_t))
+// gives, with u_T = [g_T | h_T], g_T = dy_T / D_T and h_T = -(dy_T . y_T) / D_T,
+// c_Tt = g_T . v_t + h_T and w'(x) = sum_{p>=1} p alpha_p x^{p-1}:
+//     dv_t = sum_{T>=t} w(q_T.k_t) g_T
+//     dq_T = sum_{t<=T} c_Tt w'(q_T.k_t) k_t
+//     dk_t = sum_{T>=t} c_Tt w'(q_T.k_t) q_T
+// In the feature form ([TA] "Feature maps and linear attention": w(q,k) =
+// sum_f qw_f phi_f(q) phi_f(k)) the parts across chunks are contractions with two
+// fixed-size states:
+//     S_T = sum_{t<=T} phi(k_t) [v_t | 1]^T     (the forward state)
+//     R_t = sum_{T>=t} qw phi(q_T) u_T^T         (its mirror, accumulated backwards)
+//     dq_T = sum_f (S[f] . u_T) d(qw_f phi_f)/dq (q_T)
+//     dk_t = sum_f (R[f] . [v_t | 1]) d phi_f/dk (k_t),     dv_t = sum_f phi_f(k_t) R[f][0:d_V]
+// and the pairs inside a chunk are taken directly.  A feature is a product of P-1
+// gathered coordinates (index d_K stands for the constant 1), so its derivative along
+// coordinate i collects, for every slot holding i, the product of the other slots.
+//
+// Kernels:
+//   bwd_u_kernel      u_T from dy, y and D (one thread per token)
+//   bwd_q_kernel      per (feature slice, head), chunks in order: a_T[f] = S[f] . u_T,
+//                     dq partials by scattering a_T[f] qw_f dphi_f into LDS, then the
+//                     update S += phi(k)^T [v | 1]
+//   bwd_kv_kernel     per (feature slice, head), chunks in reverse: b_t[f] = R[f].[v|1],
+//                     dk partials by scattering, dv partials by a readout of R, then
+//                     R += (qw phi(q))^T u
+//   bwd_fin_kernel    per (chunk, head): sum of the slice partials plus the direct part
+//                     of the chunk's pairs
+#include "launch.h"
+#include "sata_common.h"
+
+namespace sata {
+
+namespace {
+
+// LDS floats of the scan kernels: state slice, x_q, x_k, u, [v | 1], two feature
+// tables and the scatter target
+__host__ __device__ inline int64_t bwd_scan_lds_floats(int SV, int d_K, int d_V, int L) {
+    const int cols = d_V + 1, ks = d_K + 1;
+    return (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 2LL * L * SV + (int64_t)L * ks;
+}
+
+// LDS floats of the finalize: x_q, x_k, [v | 1], u, and two L x (L + 1) pair tables
+__host__ __device__ inline int64_t bwd_fin_lds_floats(int d_K, int d_V, int L) {
+    const int cols = d_V + 1;
+    return 2LL * L * d_K + 2LL * L * cols + 2LL * L * (L + 1);
+}
+
+template <typename In>
+__device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int nvalid, float* xq,
+                                  float* xk, float* uu, float* vv) {
+    using T = typename In::T;
+    const int d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1, L = a.L;
+    const T* q = static_cast<const T*>(a.q) + bh * a.n * d_K;
+    const T* k = static_cast<const T*>(a.k) + bh * a.n * d_K;
+    const T* v = static_cast<const T*>(a.v) + bh * a.n * d_V;
+    const float* u = a.u + bh * a.n * cols;
+    for (int idx = threadIdx.x; idx < L * ks; idx += kThreads) {
+        const int t = idx / ks, i = idx % ks;
+        float vq = 1.0f, vk = 1.0f;              // coordinate d_K: the constant 1
+        if (i < d_K) {
+            vq = t < nvalid ? In::load(q, (t0 + t) * d_K + i) : 0.0f;
+            vk = t < nvalid ? In::load(k, (t0 + t) * d_K + i) : 0.0f;
+        }
+        xq[idx] = vq;
+        xk[idx] = vk;
+    }
+    for (int idx = threadIdx.x; idx < L * cols; idx += kThreads) {
+        const int t = idx / cols, j = idx % cols;
+        float uv = 0.0f, vv1 = 0.0f;
+        if (t < nvalid) {
+            uv = u[(t0 + t) * cols + j];
+            vv1 = j < d_V ? In::load(v, (t0 + t) * d_V + j) : 1.0f;
+        }
+        uu[idx] = uv;
+        vv[idx] = vv1;
+    }
+}
+
+// acc[idx_s] += val * prod_{s' != s} x[idx_s'] for every slot s of a feature's packed
+// index row (LDS float atomics: several features of a thread block share coordinates)
+__device__ inline void scatter_grad(float* acc, const float* x, uint32_t packed, int nidx, float val) {
+    float xs[kMaxP];
+    int is[kMaxP];
+    for (int s = 0; s < nidx; ++s) {
+        is[s] = (packed >> (8 * s)) & 0xffu;
+        xs[s] = x[is[s]];
+    }
+    for (int s = 0; s < nidx; ++s) {
+        float prod = val;
+        for (int s2 = 0; s2 < nidx; ++s2)
+            if (s2 != s) prod *= xs[s2];
+        atomicAdd(&acc[is[s]], prod);
+    }
+}
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int slice = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int SV = a.slice_feats, L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1;
+    const int nidx = a.P - 1;
+    const int64_t F0 = (int64_t)slice * SV;
+    float* Ssl = lds;                              // [SV][cols]
+    float* xq = Ssl + SV * cols;                   // [L][ks]
+    float* xk = xq + L * ks;                       // [L][ks]
+    float* uu = xk + L * ks;                       // [L][cols]
+    float* vv = uu + L * cols;                     // [L][cols]
+    float* hat = vv + L * cols;                    // [L][SV]
+    float* gq = hat + 2 * L * SV;                  // [L][ks]
+    float* state = a.state + bh * (int64_t)cols * a.M_pad;
+
+    for (int idx = tid; idx < SV * cols; idx += kThreads) {
+        const int f = idx / cols, j = idx % cols;
+        const int64_t F = F0 + f;
+        Ssl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
+    }
+    const int nch = a.c_end - a.c_begin;
+    for (int c = a.c_begin; c < a.c_end; ++c) {
+        const int64_t t0 = (int64_t)c * L;
+        const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
+        __syncthreads();
+        load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
+        for (int idx = tid; idx < L * ks; idx += kThreads) gq[idx] = 0.0f;
+        __syncthreads();
+        // a_T[f] = S[f] . u_T against the state before the chunk
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const float* sr = Ssl + f * cols;
+            const float* ur = uu + t * cols;
+            float acc = 0.0f;
+            for (int j = 0; j < cols; ++j) acc = fmaf(sr[j], ur[j], acc);
+            hat[idx] = acc;
+        }
+        __syncthreads();
+        // dq partial: sum_f a_T[f] qw_f d phi_f / dq
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            if (F < a.M && t < nvalid) scatter_grad(gq + t * ks, xq + t * ks, a.fidx[F], nidx, hat[idx] * a.qw[F]);
+        }
+        __syncthreads();
+        float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
+        for (int idx = tid; idx < L * d_K; idx += kThreads) part[idx] = gq[(idx / d_K) * ks + idx % d_K];
+        // key features, then the update S += phi(k)^T [v | 1]
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            hat[idx] = F < a.M ? feature_value(xk + t * ks, a.fidx[F], nidx) : 0.0f;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+            const int f = idx / cols, j = idx % cols;
+            float s = 0.0f;
+            for (int t = 0; t < L; ++t) s = fmaf(hat[t * SV + f], vv[t * cols + j], s);
+            Ssl[idx] += s;
+        }
+    }
+    __syncthreads();
+    if (a.store_state) {
+        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+            const int j = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            if (F < a.M_pad) state[(int64_t)j * a.M_pad + F] = Ssl[f * cols + j];
+        }
+    }
+}
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int slice = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int SV = a.slice_feats, L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1;
+    const int nidx = a.P - 1;
+    const int64_t F0 = (int64_t)slice * SV;
+    float* Rsl = lds;                              // [SV][cols]
+    float* xq = Rsl + SV * cols;                   // [L][ks]
+    float* xk = xq + L * ks;                       // [L][ks]
+    float* uu = xk + L * ks;                       // [L][cols]
+    float* vv = uu + L * cols;                     // [L][cols]
+    float* hk = vv + L * cols;                     // [L][SV] phi(k)
+    float* hq = hk + L * SV;                       // [L][SV] qw phi(q)
+    float* gk = hq + L * SV;                       // [L][ks]
+    float* state = a.state + bh * (int64_t)cols * a.M_pad;
+
+    for (int idx = tid; idx < SV * cols; idx += kThreads) {
+        const int f = idx / cols, j = idx % cols;
+        const int64_t F = F0 + f;
+        Rsl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
+    }
+    const int nch = a.c_end - a.c_begin;
+    for (int c = a.c_end - 1; c >= a.c_begin; --c) {
+        const int64_t t0 = (int64_t)c * L;
+        const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
+        __syncthreads();
+        load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
+        for (int idx = tid; idx < L * ks; idx += kThreads) gk[idx] = 0.0f;
+        __syncthreads();
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            const bool live = F < a.M && t < nvalid;
+            hk[idx] = live ? feature_value(xk + t * ks, a.fidx[F], nidx) : 0.0f;
+            hq[idx] = live ? a.qw[F] * feature_value(xq + t * ks, a.fidx[F], nidx) : 0.0f;
+        }
+        __syncthreads();
+        const int64_t pbase = ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L;
+        // dk partial: sum_f (R[f] . [v_t | 1]) d phi_f / dk, against the chunks after c
+        for (int idx = tid; idx < L * SV; idx += kThreads) {
+            const int t = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            if (F < a.M && t < nvalid) {
+                const float* rr = Rsl + f * cols;
+                const float* vr = vv + t * cols;
+                float b = 0.0f;
+                for (int j = 0; j < cols; ++j) b = fmaf(rr[j], vr[j], b);
+                scatter_grad(gk + t * ks, xk + t * ks, a.fidx[F], nidx, b);
+            }
+        }
+        // dv partial: sum_f phi_f(k_t) R[f][j]
+        float* pv = a.part2 + pbase * d_V;
+        for (int idx = tid; idx < L * d_V; idx += kThreads) {
+            const int t = idx / d_V, j = idx % d_V;
+            const float* h = hk + t * SV;
+            float acc = 0.0f;
+            for (int f = 0; f < SV; ++f) acc = fmaf(h[f], Rsl[f * cols + j], acc);
+            pv[idx] = acc;
+        }
+        __syncthreads();
+        float* pk = a.part + pbase * d_K;
+        for (int idx = tid; idx < L * d_K; idx += kThreads) pk[idx] = gk[(idx / d_K) * ks + idx % d_K];
+        // R += (qw phi(q))^T u with the chunk's queries
+        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+            const int f = idx / cols, j = idx % cols;
+            float s = 0.0f;
+            for (int t = 0; t < L; ++t) s = fmaf(hq[t * SV + f], uu[t * cols + j], s);
+            Rsl[idx] += s;
+        }
+    }
+    __syncthreads();
+    if (a.store_state) {
+        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+            const int j = idx / SV, f = idx % SV;
+            const int64_t F = F0 + f;
+            if (F < a.M_pad) state[(int64_t)j * a.M_pad + F] = Rsl[f * cols + j];
+        }
+    }
+}
+
+// u_T = [dy_T / D_T | -(dy_T . y_T) / D_T], one thread per token
+__global__ __launch_bounds__(kThreads) void bwd_u_kernel(BwdArgs a) {
+    const int64_t tok = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (tok >= (int64_t)a.BH * a.n) return;
+    const int d_V = a.d_V, cols = d_V + 1;
+    const float inv = 1.0f / a.den[tok];
+    const float* dy = a.dy + tok * d_V;
+    const float* y = a.y + tok * d_V;
+    float* u = a.u_out + tok * cols;
+    float h = 0.0f;
+    for (int j = 0; j < d_V; ++j) {
+        u[j] = dy[j] * inv;
+        h = fmaf(dy[j], y[j], h);
+    }
+    u[d_V] = -h * inv;
+}
+
+// MODE 0: dq; MODE 1: dk and dv.  Sum of the slice partials plus the chunk's pairs.
+template <typename In, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
+    using T = typename In::T;
+    extern __shared__ float lds[];
+    const int cl = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int c = a.c_begin + cl;
+    const int tid = threadIdx.x;
+    const int L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1;
+    const int nch = a.c_end - a.c_begin;
+    const int64_t t0 = (int64_t)c * L;
+    const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
+    float* xq = lds;                     // [L][d_K]
+    float* xk = xq + L * d_K;            // [L][d_K]
+    float* vv = xk + L * d_K;            // [L][cols]: v (the last column unused)
+    float* uu = vv + L * cols;           // [L][cols]
+    float* cw = uu + L * cols;           // [L][L + 1]: c_Tt w'(x_Tt), live pairs
+    float* ww = cw + L * (L + 1);        // [L][L + 1]: w(x_Tt), live pairs
+    const T* q = static_cast<const T*>(a.q) + (bh * a.n + t0) * d_K;
+    const T* k = static_cast<const T*>(a.k) + (bh * a.n + t0) * d_K;
+    const T* v = static_cast<const T*>(a.v) + (bh * a.n + t0) * d_V;
+    const float* u = a.u + (bh * a.n + t0) * cols;
+    for (int idx = tid; idx < L * d_K; idx += kThreads) {
+        const int t = idx / d_K;
+        xq[idx] = t < nvalid ? In::load(q, idx) : 0.0f;
+        xk[idx] = t < nvalid ? In::load(k, idx) : 0.0f;
+    }
+    for (int idx = tid; idx < L * cols; idx += kThreads) {
+        const int t = idx / cols, j = idx % cols;
+        vv[idx] = (t < nvalid && j < d_V) ? In::load(v, (int64_t)t * d_V + j) : 0.0f;
+        uu[idx] = t < nvalid ? u[(int64_t)t * cols + j] : 0.0f;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < L * L; idx += kThreads) {
+        const int Tq = idx / L, t = idx % L;
+        float cv = 0.0f, wv = 0.0f;
+        if (t <= Tq && Tq < nvalid) {
+            float x = 0.0f;
+            for (int i = 0; i < d_K; ++i) x = fmaf(xq[Tq * d_K + i], xk[t * d_K + i], x);
+            // w and w' by Horner's rule
+            float w = a.alpha.a[a.P - 1], wp = 0.0f;
+            for (int p = a.P - 2; p >= 0; --p) {
+                wp = fmaf(wp, x, w);
+                w = fmaf(w, x, a.alpha.a[p]);
+            }
+            float cc = uu[Tq * cols + d_V];
+            for (int j = 0; j < d_V; ++j) cc = fmaf(uu[Tq * cols + j], vv[t * cols + j], cc);
+            cv = cc * wp;
+            wv = w;
+        }
+        cw[Tq * (L + 1) + t] = cv;
+        ww[Tq * (L + 1) + t] = wv;
+    }
+    __syncthreads();
+    const int64_t slice_stride = (int64_t)L;
+    if (MODE == 0) {
+        const float* part = a.part + ((bh * nch + cl) * (int64_t)a.nslices) * L * d_K;
+        float* dq = a.dq + (bh * a.n + t0) * d_K;
+        for (int idx = tid; idx < nvalid * d_K; idx += kThreads) {
+            const int Tq = idx / d_K, i = idx % d_K;
+            float acc = 0.0f;
+            for (int t = 0; t <= Tq; ++t) acc = fmaf(cw[Tq * (L + 1) + t], xk[t * d_K + i], acc);
+            float ps = 0.0f;
+            for (int sl = 0; sl < a.nslices; ++sl) ps += part[sl * slice_stride * d_K + idx];
+            dq[idx] = acc + ps;
+        }
+    } else {
+        const int64_t pb = (bh * nch + cl) * (int64_t)a.nslices * L;
+        const float* pk = a.part + pb * d_K;
+        const float* pv = a.part2 + pb * d_V;
+        float* dk = a.dk + (bh * a.n + t0) * d_K;
+        float* dv = a.dv + (bh * a.n + t0) * d_V;
+        for (int idx = tid; idx < nvalid * d_K; idx += kThreads) {
+            const int t = idx / d_K, i = idx % d_K;
+            float acc = 0.0f;
+            for (int Tq = t; Tq < nvalid; ++Tq) acc = fmaf(cw[Tq * (L + 1) + t], xq[Tq * d_K + i], acc);
+            float ps = 0.0f;
+            for (int sl = 0; sl < a.nslices; ++sl) ps += pk[sl * slice_stride * d_K + idx];
+            dk[idx] = acc + ps;
+        }
+        for (int idx = tid; idx < nvalid * d_V; idx += kThreads) {
+            const int t = idx / d_V, j = idx % d_V;
+            float acc = 0.0f;
+            for (int Tq = t; Tq < nvalid; ++Tq) acc = fmaf(ww[Tq * (L + 1) + t], uu[Tq * cols + j], acc);
+            float ps = 0.0f;
+            for (int sl = 0; sl < a.nslices; ++sl) ps += pv[sl * slice_stride * d_V + idx];
+            dv[idx] = acc + ps;
+        }
+    }
+}
+
+template <typename K>
+hipError_t launch_lds(K kernel, dim3 grid, size_t lds, const BwdArgs& a, hipStream_t st) {
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_slice_feats(int d_K, int d_V, int L) {
+    for (int SV = 128; SV >= 16; SV >>= 1)
+        if (bwd_scan_lds_floats(SV, d_K, d_V, L) * 4 <= 150 * 1024) return SV;
+    return 0;
+}
+
+int64_t bwd_fin_lds_bytes(int d_K, int d_V, int L) { return bwd_fin_lds_floats(d_K, d_V, L) * 4; }
+
+hipError_t launch_bwd_u(const BwdArgs& a, hipStream_t st) {
+    const int64_t toks = (int64_t)a.BH * a.n;
+    hipLaunchKernelGGL(bwd_u_kernel, dim3((unsigned)((toks + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st) {
+    const size_t lds = (size_t)bwd_scan_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
+    const dim3 grid(a.nslices, a.BH);
+    return a.bf16 ? launch_lds(bwd_q_kernel<InBF16>, grid, lds, a, st) : launch_lds(bwd_q_kernel<InF32>, grid, lds, a, st);
+}
+
+hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
+    const size_t lds = (size_t)bwd_scan_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
+    const dim3 grid(a.nslices, a.BH);
+    return a.bf16 ? launch_lds(bwd_kv_kernel<InBF16>, grid, lds, a, st) : launch_lds(bwd_kv_kernel<InF32>, grid, lds, a, st);
+}
+
+hipError_t launch_bwd_fin(const BwdArgs& a, int mode, hipStream_t st) {
+    const size_t lds = (size_t)bwd_fin_lds_bytes(a.d_K, a.d_V, a.L);
+    const dim3 grid(a.c_end - a.c_begin, a.BH);
+    if (mode == 0)
+        return a.bf16 ? launch_lds(bwd_fin_kernel<InBF16, 0>, grid, lds, a, st)
+                      : launch_lds(bwd_fin_kernel<InF32, 0>, grid, lds, a, st);
+    return a.bf16 ? launch_lds(bwd_fin_kernel<InBF16, 1>, grid, lds, a, st)
+                  : launch_lds(bwd_fin_kernel<InF32, 1>, grid, lds, a, st);
+}
+
+}  // namespace sata

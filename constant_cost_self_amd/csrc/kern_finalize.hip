@@ -97,6 +97,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
         const int t = idx / d_V, j = idx % d_V;
         y[idx] = num[t * cols + j] / num[t * cols + d_V];
     }
+    if (a.den)
+        for (int t = tid; t < nvalid; t += kThreads) a.den[bh * a.n + t0 + t] = num[t * cols + d_V];
 }
 
 // ---------------------------------------------------------------------------
@@ -338,6 +340,10 @@ hipError_t launch_finalize(const PrefillSegArgs& a, hipStream_t st) {
         if (a.d_K == 64) return a.d_V == 64 ? launch_fin_mfma<64, 64>(a, st) : launch_fin_mfma<64, 128>(a, st);
         return a.d_V == 64 ? launch_fin_mfma<128, 64>(a, st) : launch_fin_mfma<128, 128>(a, st);
     }
+    return launch_finalize_fp32(a, st);
+}
+
+hipError_t launch_finalize_fp32(const PrefillSegArgs& a, hipStream_t st) {
     // windows and the tiled partial layout come only with the MFMA scan
     if (a.win != 1 || a.partial_tiled) return hipErrorInvalidValue;
     const size_t lds = (size_t)finalize_lds_bytes(a.d_K, a.d_V, a.L);

@@ -45,6 +45,7 @@ struct PrefillSegArgs {
                              // partial_tiled the d_V value columns of a (chunk, slice) block
                              // are in MFMA-tile order instead (see kern_scan_mfma.hip)
     bool partial_tiled;
+    float* den;              // nullable: the fp32 finalize writes D_T of every row here
     const uint32_t* fidx;    // packed feature indices [M_pad]
     const float* qw;         // alpha_p C_p [M_pad]
     const void* mfma_rows;   // slice tables of the MFMA scan (nullptr for the VALU scan)
@@ -66,5 +67,41 @@ hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st);
 // Intra-chunk part + reduction of the slice partials + normalisation -> y.
 int64_t finalize_lds_bytes(int d_K, int d_V, int L);
 hipError_t launch_finalize(const PrefillSegArgs& a, hipStream_t st);
+// The fp32 finalize whatever the input type (the backward's forward recompute); writes
+// the normaliser D_T of every row to a.den when it is non-null.
+hipError_t launch_finalize_fp32(const PrefillSegArgs& a, hipStream_t st);
+
+// Backward of the chunked prefill, one segment [c_begin, c_end) of chunks.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* dy;         // [BH][n][d_V]
+    const float* y;          // [BH][n][d_V] forward output
+    const float* den;        // [BH][n] forward normaliser D_T
+    const float* u;          // [BH][n][d_V+1]: dy / D, then -(dy . y) / D
+    float* u_out;            // where bwd_u_kernel writes u (the same buffer)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* state;            // S (dq pass) or R (dk, dv pass) carrier [BH][d_V+1][M_pad]
+    float* part;             // dq or dk slice partials [BH][c_end-c_begin][nslices][L][d_K]
+    float* part2;            // dv slice partials [BH][c_end-c_begin][nslices][L][d_V]
+    const uint32_t* fidx;
+    const float* qw;
+    Alpha alpha;
+    int64_t M, M_pad;
+    int BH, n, d_K, d_V, P, L;
+    int nslices, slice_feats;
+    int c_begin, c_end;
+    int load_state, store_state;
+    bool bf16;
+};
+int bwd_slice_feats(int d_K, int d_V, int L);
+int64_t bwd_fin_lds_bytes(int d_K, int d_V, int L);
+hipError_t launch_bwd_u(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_fin(const BwdArgs& a, int mode, hipStream_t st);   // 0: dq; 1: dk, dv
 
 }  // namespace sata

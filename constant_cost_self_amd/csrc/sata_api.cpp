@@ -11,6 +11,9 @@
 //   caller's state buffer (or a workspace copy when the caller passed none).
 // Decode: one streaming read-modify-write kernel over the state, then a per-head
 //   reduction of the partial readouts.
+// Backward: a fp32 forward recompute (y and the normaliser of every row), then the
+//   gradient scans of kern_backward.hip: dq with the forward state in chunk order,
+//   dk and dv with its mirror in reverse chunk order.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -391,6 +394,138 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
     }
+    return SATA_OK;
+}
+
+int sata_prefill_backward(const sata_tables* tc, const void* q, const void* k, const void* v,
+                          const float* dy, float* dq, float* dk, float* dv, int B, int H, int n,
+                          int d_K, int d_V, int P, int chunk, sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!q || !k || !v || !dy || !dq || !dk || !dv)
+        return fail(SATA_ERR_ARG, "q, k, v, dy, dq, dk and dv must be non-NULL");
+    if (B < 1 || H < 1 || n < 1) return fail(SATA_ERR_ARG, "need B, H, n >= 1 (got %d %d %d)", B, H, n);
+    int rc = check_sizes(d_K, d_V, P);
+    if (rc) return rc;
+    if (d_K != t->h.d_K || P != t->h.P)
+        return fail(SATA_ERR_ARG, "handle built for d_K=%d P=%d, call has d_K=%d P=%d",
+                    t->h.d_K, t->h.P, d_K, P);
+    if (in_dtype != SATA_F32 && in_dtype != SATA_BF16)
+        return fail(SATA_ERR_ARG, "unknown input dtype %d", (int)in_dtype);
+    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 16, 32, 64 or 128 (got %d)", chunk);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int L = chunk;
+    const int SVf = sata::valu_slice_feats(d_K, d_V, L), SVb = sata::bwd_slice_feats(d_K, d_V, L);
+    if (sata::finalize_lds_bytes(d_K, d_V, L) > 160 * 1024 || sata::bwd_fin_lds_bytes(d_K, d_V, L) > 160 * 1024 ||
+        SVf == 0 || SVb == 0)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk=%d is too large for the backward at d_K=%d, d_V=%d", chunk,
+                    d_K, d_V);
+    if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    rc = check_device(t);
+    if (rc) return rc;
+
+    const bool bf16 = in_dtype == SATA_BF16;
+    const int BH = B * H, cols = d_V + 1;
+    const int nchunks = (int)(((int64_t)n + L - 1) / L);
+    const int64_t M = t->h.M, M_pad = t->h.M_pad;
+    const int nslf = (int)((M + SVf - 1) / SVf), nslb = (int)((M + SVb - 1) / SVb);
+    auto r256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    const int64_t y_b = r256((int64_t)BH * n * d_V * 4), den_b = r256((int64_t)BH * n * 4);
+    const int64_t u_b = r256((int64_t)BH * n * cols * 4), st_b = r256((int64_t)BH * cols * M_pad * 4);
+    const int64_t fixed = y_b + den_b + u_b + st_b;
+    int64_t per_chunk = (int64_t)BH * nslf * L * cols * 4;                    // forward recompute
+    const int64_t per_q = (int64_t)BH * nslb * L * d_K * 4;
+    const int64_t per_kv = (int64_t)BH * nslb * L * (d_K + d_V) * 4;
+    if (per_q > per_chunk) per_chunk = per_q;
+    if (per_kv > per_chunk) per_chunk = per_kv;
+    int64_t seg = nchunks;
+    if (fixed + per_chunk * seg > t->ws_limit) {
+        seg = (t->ws_limit - fixed) / per_chunk;
+        if (seg < 1) seg = 1;
+        const int64_t ns = (nchunks + seg - 1) / seg;
+        seg = (nchunks + ns - 1) / ns;
+    }
+    const int nseg = (int)((nchunks + seg - 1) / seg);
+
+    std::lock_guard<std::mutex> lock(t->mu);
+    hipStream_t st = (hipStream_t)stream;
+    rc = ensure_ws(t, (size_t)(fixed + per_chunk * seg), st);
+    if (rc) return rc;
+    char* base = (char*)t->ws;
+    float* y_ws = (float*)base;
+    float* den_ws = (float*)(base + y_b);
+    float* u_ws = (float*)(base + y_b + den_b);
+    float* carrier = (float*)(base + y_b + den_b + u_b);
+    float* part = (float*)(base + fixed);
+    hipEvent_t ev = t->timer.begin(st);
+
+    // forward recompute in fp32: y and the normaliser D of every row
+    sata::PrefillSegArgs a{};
+    a.q = q; a.k = k; a.v = v; a.y = y_ws; a.den = den_ws;
+    a.fidx = t->d_fidx;
+    a.qw = t->d_qw;
+    for (int p = 0; p < P; ++p) a.alpha.a[p] = (float)t->h.alpha[p];
+    a.M = M; a.M_pad = M_pad;
+    a.BH = BH; a.n = n; a.d_K = d_K; a.d_V = d_V; a.P = P; a.L = L;
+    a.bf16 = bf16;
+    a.win = 1;
+    a.partial_tiled = false;
+    a.slice_feats = SVf;
+    a.nslices = nslf;
+    a.partial = part;
+    a.state = carrier;
+    hipError_t e = hipSuccess;
+    for (int s = 0; s < nseg && e == hipSuccess; ++s) {
+        a.c_begin = (int)(s * seg);
+        a.c_end = (int)((s + 1) * seg < nchunks ? (s + 1) * seg : nchunks);
+        a.load_state = s > 0 ? 1 : 0;
+        a.store_state = s < nseg - 1 ? 1 : 0;
+        e = sata::launch_scan_valu(a, st);
+        if (e == hipSuccess) e = sata::launch_finalize_fp32(a, st);
+    }
+    // u = [dy / D | -(dy . y) / D]
+    sata::BwdArgs b{};
+    b.q = q; b.k = k; b.v = v;
+    b.dy = dy; b.y = y_ws; b.den = den_ws; b.u = u_ws; b.u_out = u_ws;
+    b.dq = dq; b.dk = dk; b.dv = dv;
+    b.state = carrier;
+    b.fidx = t->d_fidx;
+    b.qw = t->d_qw;
+    b.alpha = a.alpha;
+    b.M = M; b.M_pad = M_pad;
+    b.BH = BH; b.n = n; b.d_K = d_K; b.d_V = d_V; b.P = P; b.L = L;
+    b.nslices = nslb;
+    b.slice_feats = SVb;
+    b.bf16 = bf16;
+    if (e == hipSuccess) e = sata::launch_bwd_u(b, st);
+    // dq: chunks in order, the forward state S carried between segments
+    b.part = part;
+    b.part2 = nullptr;
+    for (int s = 0; s < nseg && e == hipSuccess; ++s) {
+        b.c_begin = (int)(s * seg);
+        b.c_end = (int)((s + 1) * seg < nchunks ? (s + 1) * seg : nchunks);
+        b.load_state = s > 0 ? 1 : 0;
+        b.store_state = s < nseg - 1 ? 1 : 0;
+        e = sata::launch_bwd_q(b, st);
+        if (e == hipSuccess) e = sata::launch_bwd_fin(b, 0, st);
+    }
+    // dk, dv: chunks in reverse, the mirror state R carried between segments
+    for (int s = nseg - 1; s >= 0 && e == hipSuccess; --s) {
+        b.c_begin = (int)(s * seg);
+        b.c_end = (int)((s + 1) * seg < nchunks ? (s + 1) * seg : nchunks);
+        b.part = part;
+        b.part2 = part + (int64_t)BH * (b.c_end - b.c_begin) * nslb * L * d_K;
+        b.load_state = s < nseg - 1 ? 1 : 0;
+        b.store_state = s > 0 ? 1 : 0;
+        e = sata::launch_bwd_kv(b, st);
+        if (e == hipSuccess) e = sata::launch_bwd_fin(b, 1, st);
+    }
+    t->timer.end(SATA_KERNEL_BACKWARD, ev, st);
+    if (e != hipSuccess) return fail(SATA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return SATA_OK;
 }
 

@@ -26,10 +26,10 @@ SATA_ERR_OOM = -5
 
 EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "sata_tables_free", "sata_feature_dim",
             "sata_state_stride", "sata_state_bytes", "sata_prefill", "sata_decode_step",
-            "sata_decode_step_pool",
+            "sata_decode_step_pool", "sata_prefill_backward",
             "sata_last_error", "sata_set_workspace_limit", "sata_set_timing",
             "sata_read_timing")
-KERNELS = ("scan", "finalize", "decode", "decode_reduce")
+KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward")
 
 _lib = None
 
@@ -73,6 +73,9 @@ def load():
     lib.sata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.sata_decode_step_pool.restype = i32
     lib.sata_decode_step_pool.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.sata_prefill_backward.restype = i32
+    lib.sata_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                          i32, i32, i32, i32, vp]
     lib.sata_last_error.restype = ctypes.c_char_p
     lib.sata_last_error.argtypes = []
     lib.sata_set_workspace_limit.restype = i32
@@ -224,6 +227,18 @@ def sata_prefill(t: Tables, q, k, v, y, state=None, *, chunk: int = 64,
     _check(load().sata_prefill(t.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(state),
                                B, H, n, d_K, d_V, t.P, chunk, _dtype_code(q), flags,
                                _stream(stream)))
+
+
+def sata_prefill_backward(t: Tables, q, k, v, dy, dq, dk, dv, *, chunk: int = 64, stream=None):
+    """Gradients of the causal prefill for dL/dy = dy.  q, k, v as for sata_prefill;
+    dy: fp32 [B, H, n, d_V]; dq, dk: fp32 [B, H, n, d_K] and dv: fp32 [B, H, n, d_V],
+    written."""
+    _need(q, k, v, dy, dq, dk, dv)
+    B, H, n, d_K = q.shape
+    d_V = v.shape[-1]
+    _check(load().sata_prefill_backward(t.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), B, H, n, d_K, d_V, t.P, chunk,
+                                        _dtype_code(q), _stream(stream)))
 
 
 def sata_decode_step(t: Tables, state, q, k, v, y, *, stream=None):

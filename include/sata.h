@@ -172,6 +172,32 @@ int sata_decode_step_pool(const sata_tables *t, float *state_pool, int64_t pool_
                           const void *v, float *y, int H, int d_K, int d_V, int P,
                           sata_dtype in_dtype, void *stream);
 
+/*
+ * Gradients of the causal prefill: for a loss with dL/dy = dy, the gradients dq, dk, dv
+ * of the y that sata_prefill computes from q, k, v (empty prefix; no state in or out).
+ * With y_T = N_T / D_T ([TA] "Feature maps and linear attention": N_T = sum_{t<=T}
+ * w(q_T.k_t) v_t, D_T = sum_{t<=T} w(q_T.k_t)), g_T = dy_T / D_T, h_T = -(dy_T . y_T) / D_T,
+ * c_Tt = g_T . v_t + h_T and w'(x) = sum_{p>=1} p alpha_p x^{p-1}:
+ *     dv_t = sum_{T>=t} w(q_T.k_t) g_T,
+ *     dq_T = sum_{t<=T} c_Tt w'(q_T.k_t) k_t,     dk_t = sum_{T>=t} c_Tt w'(q_T.k_t) q_T.
+ * The pages give the forward only; these are its derivatives.  The call recomputes the
+ * forward in fp32 and then runs two chunked scans over fixed-size states: the forward
+ * state for dq, and its mirror sum_{T>=t} alpha C phi(q_T) u_T^T (u = [g | h]) in reverse
+ * chunk order for dk and dv; pairs inside a chunk are taken directly.  Arithmetic is fp32
+ * on the vector ALUs for either input type.
+ *
+ * q, k, v  [B][H][n][d_K or d_V], in_dtype (as for sata_prefill)
+ * dy       fp32 [B][H][n][d_V]
+ * dq, dk   fp32 [B][H][n][d_K] (written);  dv: fp32 [B][H][n][d_V] (written)
+ * Errors: as sata_prefill; SATA_ERR_UNSUPPORTED when the chunk's tables do not fit LDS
+ * (chunk 128 with d_K or d_V above 64, chunk 64 at d_K = d_V = 128).  The handle's
+ * workspace holds y, D, u and the slice partials (segments of whole chunks under the cap).
+ */
+int sata_prefill_backward(const sata_tables *t, const void *q, const void *k, const void *v,
+                          const float *dy, float *dq, float *dk, float *dv, int B, int H,
+                          int n, int d_K, int d_V, int P, int chunk, sata_dtype in_dtype,
+                          void *stream);
+
 /* The calling thread's last error message ("" if none). */
 const char *sata_last_error(void);
 
@@ -197,7 +223,8 @@ enum {
     SATA_KERNEL_FINALIZE = 1,      /* intra-chunk part, reduction, y             */
     SATA_KERNEL_DECODE = 2,        /* decode state read-modify-write             */
     SATA_KERNEL_DECODE_REDUCE = 3, /* decode per-head reduction, y               */
-    SATA_NUM_KERNELS = 4
+    SATA_KERNEL_BACKWARD = 4,      /* one sata_prefill_backward call, all kernels */
+    SATA_NUM_KERNELS = 5
 };
 int sata_set_timing(sata_tables *t, int enable);
 int sata_read_timing(sata_tables *t, double *ms, int64_t *count);

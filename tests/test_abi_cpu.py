@@ -201,3 +201,45 @@ def test_decode_pool_argument_errors(host_tables, kw, code):
 
 def test_decode_pool_null_handle():
     assert _decode_pool(None) == sata.SATA_ERR_ARG
+
+
+def _backward(t, **kw):
+    args = dict(q=A, k=A, v=A, dy=A, dq=A, dk=A, dv=A, B=1, H=2, n=100, d_K=8, d_V=8, P=4,
+                chunk=16, dtype=sata.SATA_F32)
+    args.update(kw)
+    lib = sata.load()
+    return lib.sata_prefill_backward(t.handle if t else None, args["q"] or None, args["k"], args["v"],
+                                     args["dy"] or None, args["dq"], args["dk"], args["dv"] or None,
+                                     args["B"], args["H"], args["n"], args["d_K"], args["d_V"],
+                                     args["P"], args["chunk"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), sata.SATA_ERR_ARG),                       # valid args, but host-only handle
+    (dict(q=0), sata.SATA_ERR_ARG),
+    (dict(dy=0), sata.SATA_ERR_ARG),
+    (dict(dv=0), sata.SATA_ERR_ARG),
+    (dict(n=0), sata.SATA_ERR_ARG),
+    (dict(H=0), sata.SATA_ERR_ARG),
+    (dict(d_K=16), sata.SATA_ERR_ARG),                 # handle mismatch
+    (dict(d_V=129), sata.SATA_ERR_UNSUPPORTED),
+    (dict(chunk=48), sata.SATA_ERR_UNSUPPORTED),
+    (dict(dtype=7), sata.SATA_ERR_ARG),
+    (dict(dk=A + 4), sata.SATA_ERR_ALIGN),
+])
+def test_backward_argument_errors(host_tables, kw, code):
+    assert _backward(host_tables, **kw) == code
+    assert sata.last_error() != ""
+
+
+def test_backward_rejects_chunk_too_large_for_lds():
+    t = sata.sata_tables_build_host(128, 4)
+    try:
+        assert _backward(t, d_K=128, d_V=128, chunk=128) == sata.SATA_ERR_UNSUPPORTED
+        assert "too large" in sata.last_error()
+    finally:
+        t.close()
+
+
+def test_backward_null_handle():
+    assert _backward(None) == sata.SATA_ERR_ARG

@@ -1,0 +1,112 @@
+"""GPU parity of the prefill backward (sata_prefill_backward) against the oracle's
+gradients of the direct form (oracle.direct_grad, fp64 on the stored input values).
+
+Metric: for each head, max |g_gpu - g_ref| / max(max |g_ref|, 1e-3 max |dy|) over the whole
+gradient tensor of that head.  A per-row normalisation is undefined here (dq and dk of a
+one-token sequence are 0 in exact arithmetic, since y_0 = v_0), hence the whole tensor and
+the floor tied to the size of dy.  The backward computes in fp32 for both input types;
+TOL_GRAD bounds fp32 rounding over sums of up to n pairs and M features."""
+import numpy as np
+import pytest
+
+from gpu_helpers import inputs, oracle, sata, say, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def grad_err(g_gpu, g_ref, dy) -> float:
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    a = g_gpu.reshape(-1, g_ref.shape[-2] * g_ref.shape[-1])
+    b = g_ref.reshape(a.shape)
+    floor = 1e-3 * np.max(np.abs(dy.reshape(a.shape[0], -1)), axis=1)
+    num = np.max(np.abs(a - b), axis=1)
+    den = np.maximum(np.max(np.abs(b), axis=1), floor)
+    return float(np.max(num / den))
+
+
+def run_backward(torch, t, x, dtype, dy, chunk):
+    q, k, v = upload(x, dtype)
+    B, H, n, d_K = q.shape
+    d_V = v.shape[-1]
+    dyt = torch.from_numpy(np.ascontiguousarray(dy, dtype=np.float32)).to("cuda:0")
+    dq = torch.full((B, H, n, d_K), float("nan"), device="cuda:0", dtype=torch.float32)
+    dk = torch.full_like(dq, float("nan"))
+    dv = torch.full((B, H, n, d_V), float("nan"), device="cuda:0", dtype=torch.float32)
+    sata.sata_prefill_backward(t, q, k, v, dyt, dq, dk, dv, chunk=chunk)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def check(torch, dK, dV, P, n, chunk, dtype, B=1, H=2, sigma=0.5, seed=0, tol=TOL_GRAD):
+    x = inputs.draw((B, H, n, dK), (B, H, n, dV), dtype, sigma, 1.0, seed)
+    dy = np.random.default_rng(seed + 100).standard_normal((B, H, n, dV)).astype(np.float32)
+    t = sata.sata_tables_build(dK, P)
+    try:
+        got = run_backward(torch, t, x, dtype, dy, chunk)
+    finally:
+        t.close()
+    ref = oracle.direct_grad(x["q"], x["k"], x["v"], dy, P)
+    errs = [grad_err(g, r, dy) for g, r in zip(got, ref)]
+    say("  backward d_K=%d d_V=%d P=%d n=%d chunk=%d %s: dq %.2e dk %.2e dv %.2e" %
+        (dK, dV, P, n, chunk, dtype, *errs))
+    for name, e in zip(("dq", "dk", "dv"), errs):
+        assert e <= tol, (name, e)
+    return got
+
+
+def test_backward_tiny_f32(torch_cuda):
+    check(torch_cuda, 8, 8, 4, 256, 16, "f32", sigma=1.0)
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 17, 100])
+def test_backward_short_and_ragged(torch_cuda, n):
+    check(torch_cuda, 8, 8, 4, n, 16, "f32", sigma=1.0, seed=n)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5])
+def test_backward_term_counts(torch_cuda, P):
+    got = check(torch_cuda, 6, 5, P, 90, 32, "f32", sigma=0.8, seed=10 + P)
+    if P == 1:                                   # w = 1: y does not depend on q or k
+        assert np.all(got[0] == 0.0) and np.all(got[1] == 0.0)
+
+
+def test_backward_unequal_dims(torch_cuda):
+    check(torch_cuda, 12, 20, 3, 130, 32, "f32", sigma=0.6, seed=7)
+
+
+def test_backward_mid_shape_bf16(torch_cuda):
+    """d = 64, P = 4 (47905 features) with bf16 inputs and a ragged last chunk."""
+    check(torch_cuda, 64, 64, 4, 200, 64, "bf16", H=2, sigma=0.5, seed=3)
+
+
+def test_backward_wide_heads_bf16(torch_cuda):
+    """d = 128 (366145 features), chunk 32."""
+    check(torch_cuda, 128, 128, 4, 70, 32, "bf16", H=1, sigma=0.35, seed=4)
+
+
+def test_backward_segmented_equals_single(torch_cuda):
+    """A small workspace cap splits the backward into segments that carry the forward
+    state and its mirror: the result equals one segment to fp32 rounding."""
+    torch = torch_cuda
+    x = inputs.draw((1, 2, 300, 8), (1, 2, 300, 8), "f32", 1.0, 1.0, 5)
+    dy = np.random.default_rng(6).standard_normal((1, 2, 300, 8)).astype(np.float32)
+    t = sata.sata_tables_build(8, 4)
+    try:
+        one = run_backward(torch, t, x, "f32", dy, 16)
+        t.set_workspace_limit(78 << 10)          # 4 segments of 5 chunks
+        seg = run_backward(torch, t, x, "f32", dy, 16)
+    finally:
+        t.close()
+    for a, b in zip(one, seg):
+        d = float(np.max(np.abs(a - b)) / np.max(np.abs(a)))
+        say("  segmented vs single: %.2e" % d)
+        assert d <= 1e-5
