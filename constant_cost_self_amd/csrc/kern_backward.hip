@@ -39,7 +39,7 @@ namespace {
 // tables and the scatter target
 __host__ __device__ inline int64_t bwd_scan_lds_floats(int SV, int d_K, int d_V, int L) {
     const int cols = d_V + 1, ks = d_K + 1;
-    return (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 2LL * L * SV + (int64_t)L * ks;
+    return (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3LL * L * SV + (int64_t)L * ks;
 }
 
 // LDS floats of the finalize: x_q, x_k, [v | 1], u, and two L x (L + 1) pair tables
@@ -57,7 +57,7 @@ __device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int 
     const T* k = static_cast<const T*>(a.k) + bh * a.n * d_K;
     const T* v = static_cast<const T*>(a.v) + bh * a.n * d_V;
     const float* u = a.u + bh * a.n * cols;
-    for (int idx = threadIdx.x; idx < L * ks; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < L * ks; idx += kScanThreads) {
         const int t = idx / ks, i = idx % ks;
         float vq = 1.0f, vk = 1.0f;              // coordinate d_K: the constant 1
         if (i < d_K) {
@@ -67,7 +67,7 @@ __device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int 
         xq[idx] = vq;
         xk[idx] = vk;
     }
-    for (int idx = threadIdx.x; idx < L * cols; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < L * cols; idx += kScanThreads) {
         const int t = idx / cols, j = idx % cols;
         float uv = 0.0f, vv1 = 0.0f;
         if (t < nvalid) {
@@ -97,7 +97,7 @@ __device__ inline void scatter_grad(float* acc, const float* x, uint32_t packed,
 }
 
 template <typename In>
-__global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y;
@@ -110,11 +110,11 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs a) {
     float* xk = xq + L * ks;                       // [L][ks]
     float* uu = xk + L * ks;                       // [L][cols]
     float* vv = uu + L * cols;                     // [L][cols]
-    float* hat = vv + L * cols;                    // [L][SV]
-    float* gq = hat + 2 * L * SV;                  // [L][ks]
+    float* hat = vv + L * cols;                    // [SV][L] a_T, then [L][SV] phi(k)
+    float* gq = hat + 3 * L * SV;                  // [L][ks] (the layout of bwd_kv_kernel)
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
 
-    for (int idx = tid; idx < SV * cols; idx += kThreads) {
+    for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
         const int64_t F = F0 + f;
         Ssl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
@@ -125,44 +125,33 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs a) {
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
         load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
-        for (int idx = tid; idx < L * ks; idx += kThreads) gq[idx] = 0.0f;
+        for (int idx = tid; idx < L * ks; idx += kScanThreads) gq[idx] = 0.0f;
         __syncthreads();
-        // a_T[f] = S[f] . u_T against the state before the chunk
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
-            const int t = idx / SV, f = idx % SV;
-            const float* sr = Ssl + f * cols;
-            const float* ur = uu + t * cols;
-            float acc = 0.0f;
-            for (int j = 0; j < cols; ++j) acc = fmaf(sr[j], ur[j], acc);
-            hat[idx] = acc;
-        }
+        // a_T[f] = S[f] . u_T against the state before the chunk, stored [f][t]
+        lds_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols, [&](int t, int f, float c) { hat[f * L + t] = c; });
         __syncthreads();
-        // dq partial: sum_f a_T[f] qw_f d phi_f / dq
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
-            const int t = idx / SV, f = idx % SV;
+        // dq partial: sum_f a_T[f] qw_f d phi_f / dq.  The lanes of a wave take one feature
+        // for consecutive tokens, so their LDS atomics hit distinct rows of gq.
+        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
+            const int f = idx / L, t = idx % L;
             const int64_t F = F0 + f;
             if (F < a.M && t < nvalid) scatter_grad(gq + t * ks, xq + t * ks, a.fidx[F], nidx, hat[idx] * a.qw[F]);
         }
         __syncthreads();
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
-        for (int idx = tid; idx < L * d_K; idx += kThreads) part[idx] = gq[(idx / d_K) * ks + idx % d_K];
+        for (int idx = tid; idx < L * d_K; idx += kScanThreads) part[idx] = gq[(idx / d_K) * ks + idx % d_K];
         // key features, then the update S += phi(k)^T [v | 1]
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
+        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             hat[idx] = F < a.M ? feature_value(xk + t * ks, a.fidx[F], nidx) : 0.0f;
         }
         __syncthreads();
-        for (int idx = tid; idx < SV * cols; idx += kThreads) {
-            const int f = idx / cols, j = idx % cols;
-            float s = 0.0f;
-            for (int t = 0; t < L; ++t) s = fmaf(hat[t * SV + f], vv[t * cols + j], s);
-            Ssl[idx] += s;
-        }
+        lds_gemm<kScanThreads>(SV, cols, L, hat, 1, SV, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {
-        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+        for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
             const int j = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             if (F < a.M_pad) state[(int64_t)j * a.M_pad + F] = Ssl[f * cols + j];
@@ -171,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs a) {
 }
 
 template <typename In>
-__global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y;
@@ -186,10 +175,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs a) {
     float* vv = uu + L * cols;                     // [L][cols]
     float* hk = vv + L * cols;                     // [L][SV] phi(k)
     float* hq = hk + L * SV;                       // [L][SV] qw phi(q)
-    float* gk = hq + L * SV;                       // [L][ks]
+    float* bb = hq + L * SV;                       // [SV][L] R[f] . [v_t | 1]
+    float* gk = bb + L * SV;                       // [L][ks]
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
 
-    for (int idx = tid; idx < SV * cols; idx += kThreads) {
+    for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
         const int64_t F = F0 + f;
         Rsl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
@@ -200,9 +190,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs a) {
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
         load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
-        for (int idx = tid; idx < L * ks; idx += kThreads) gk[idx] = 0.0f;
+        for (int idx = tid; idx < L * ks; idx += kScanThreads) gk[idx] = 0.0f;
         __syncthreads();
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
+        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             const bool live = F < a.M && t < nvalid;
@@ -211,41 +201,28 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs a) {
         }
         __syncthreads();
         const int64_t pbase = ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L;
-        // dk partial: sum_f (R[f] . [v_t | 1]) d phi_f / dk, against the chunks after c
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
-            const int t = idx / SV, f = idx % SV;
-            const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) {
-                const float* rr = Rsl + f * cols;
-                const float* vr = vv + t * cols;
-                float b = 0.0f;
-                for (int j = 0; j < cols; ++j) b = fmaf(rr[j], vr[j], b);
-                scatter_grad(gk + t * ks, xk + t * ks, a.fidx[F], nidx, b);
-            }
-        }
-        // dv partial: sum_f phi_f(k_t) R[f][j]
+        // b_t[f] = R[f] . [v_t | 1] and the dv partial sum_f phi_f(k_t) R[f][j], against
+        // the chunks after c
+        lds_gemm<kScanThreads>(L, SV, cols, vv, cols, 1, Rsl, 1, cols, [&](int t, int f, float c) { bb[f * L + t] = c; });
         float* pv = a.part2 + pbase * d_V;
-        for (int idx = tid; idx < L * d_V; idx += kThreads) {
-            const int t = idx / d_V, j = idx % d_V;
-            const float* h = hk + t * SV;
-            float acc = 0.0f;
-            for (int f = 0; f < SV; ++f) acc = fmaf(h[f], Rsl[f * cols + j], acc);
-            pv[idx] = acc;
+        lds_gemm<kScanThreads>(L, d_V, SV, hk, SV, 1, Rsl, cols, 1, [&](int t, int j, float c) { pv[t * d_V + j] = c; });
+        __syncthreads();
+        // dk partial: sum_f b_t[f] d phi_f / dk (bb is [f][t]: a wave's atomics hit
+        // distinct token rows of gk)
+        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
+            const int f = idx / L, t = idx % L;
+            const int64_t F = F0 + f;
+            if (F < a.M && t < nvalid) scatter_grad(gk + t * ks, xk + t * ks, a.fidx[F], nidx, bb[idx]);
         }
         __syncthreads();
         float* pk = a.part + pbase * d_K;
-        for (int idx = tid; idx < L * d_K; idx += kThreads) pk[idx] = gk[(idx / d_K) * ks + idx % d_K];
+        for (int idx = tid; idx < L * d_K; idx += kScanThreads) pk[idx] = gk[(idx / d_K) * ks + idx % d_K];
         // R += (qw phi(q))^T u with the chunk's queries
-        for (int idx = tid; idx < SV * cols; idx += kThreads) {
-            const int f = idx / cols, j = idx % cols;
-            float s = 0.0f;
-            for (int t = 0; t < L; ++t) s = fmaf(hq[t * SV + f], uu[t * cols + j], s);
-            Rsl[idx] += s;
-        }
+        lds_gemm<kScanThreads>(SV, cols, L, hq, 1, SV, uu, cols, 1, [&](int f, int j, float c) { Rsl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {
-        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+        for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
             const int j = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             if (F < a.M_pad) state[(int64_t)j * a.M_pad + F] = Rsl[f * cols + j];
@@ -363,10 +340,10 @@ __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
 }
 
 template <typename K>
-hipError_t launch_lds(K kernel, dim3 grid, size_t lds, const BwdArgs& a, hipStream_t st) {
+hipError_t launch_lds(K kernel, dim3 grid, int threads, size_t lds, const BwdArgs& a, hipStream_t st) {
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, st, a);
     return hipGetLastError();
 }
 
@@ -389,23 +366,25 @@ hipError_t launch_bwd_u(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st) {
     const size_t lds = (size_t)bwd_scan_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
     const dim3 grid(a.nslices, a.BH);
-    return a.bf16 ? launch_lds(bwd_q_kernel<InBF16>, grid, lds, a, st) : launch_lds(bwd_q_kernel<InF32>, grid, lds, a, st);
+    return a.bf16 ? launch_lds(bwd_q_kernel<InBF16>, grid, kScanThreads, lds, a, st)
+                  : launch_lds(bwd_q_kernel<InF32>, grid, kScanThreads, lds, a, st);
 }
 
 hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
     const size_t lds = (size_t)bwd_scan_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
     const dim3 grid(a.nslices, a.BH);
-    return a.bf16 ? launch_lds(bwd_kv_kernel<InBF16>, grid, lds, a, st) : launch_lds(bwd_kv_kernel<InF32>, grid, lds, a, st);
+    return a.bf16 ? launch_lds(bwd_kv_kernel<InBF16>, grid, kScanThreads, lds, a, st)
+                  : launch_lds(bwd_kv_kernel<InF32>, grid, kScanThreads, lds, a, st);
 }
 
 hipError_t launch_bwd_fin(const BwdArgs& a, int mode, hipStream_t st) {
     const size_t lds = (size_t)bwd_fin_lds_bytes(a.d_K, a.d_V, a.L);
     const dim3 grid(a.c_end - a.c_begin, a.BH);
     if (mode == 0)
-        return a.bf16 ? launch_lds(bwd_fin_kernel<InBF16, 0>, grid, lds, a, st)
-                      : launch_lds(bwd_fin_kernel<InF32, 0>, grid, lds, a, st);
-    return a.bf16 ? launch_lds(bwd_fin_kernel<InBF16, 1>, grid, lds, a, st)
-                  : launch_lds(bwd_fin_kernel<InF32, 1>, grid, lds, a, st);
+        return a.bf16 ? launch_lds(bwd_fin_kernel<InBF16, 0>, grid, kThreads, lds, a, st)
+                      : launch_lds(bwd_fin_kernel<InF32, 0>, grid, kThreads, lds, a, st);
+    return a.bf16 ? launch_lds(bwd_fin_kernel<InBF16, 1>, grid, kThreads, lds, a, st)
+                  : launch_lds(bwd_fin_kernel<InF32, 1>, grid, kThreads, lds, a, st);
 }
 
 }  // namespace sata

@@ -25,7 +25,7 @@ __host__ __device__ inline int64_t valu_lds_floats(int SV, int d_K, int d_V, int
 }
 
 template <typename In>
-__global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
+__global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs a) {
     using T = typename In::T;
     extern __shared__ float lds[];
     const int slice = blockIdx.x;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
     const T* v = static_cast<const T*>(a.v) + bh * a.n * d_V;
     float* state = a.state ? a.state + bh * (int64_t)cols * a.M_pad : nullptr;
 
-    for (int idx = tid; idx < SV * cols; idx += kThreads) {
+    for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
         const int64_t F = F0 + f;
         Ssl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
         const int64_t t0 = (int64_t)c * L;
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
-        for (int idx = tid; idx < L * (d_K + 1); idx += kThreads) {
+        for (int idx = tid; idx < L * (d_K + 1); idx += kScanThreads) {
             const int t = idx / (d_K + 1), i = idx % (d_K + 1);
             float vq = 1.0f, vk = 1.0f;
             if (i < d_K) {
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
             xq[idx] = vq;
             xk[idx] = vk;
         }
-        for (int idx = tid; idx < L * cols; idx += kThreads) {
+        for (int idx = tid; idx < L * cols; idx += kScanThreads) {
             const int t = idx / cols, j = idx % cols;
             float u = 0.0f;
             if (t < nvalid) u = j < d_V ? In::load(v, (t0 + t) * d_V + j) : 1.0f;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
         }
         __syncthreads();
         // weighted query features of the slice
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
+        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             hat[idx] = F < a.M ? a.qw[F] * feature_value(xq + t * (d_K + 1), a.fidx[F], nidx)
@@ -85,32 +85,21 @@ __global__ __launch_bounds__(kThreads) void scan_valu_kernel(PrefillSegArgs a) {
         // readout against the state of the chunks before c
         float* part = a.partial +
                       (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * cols;
-        for (int idx = tid; idx < L * cols; idx += kThreads) {
-            const int t = idx / cols, j = idx % cols;
-            const float* h = hat + t * SV;
-            float acc = 0.0f;
-            for (int f = 0; f < SV; ++f) acc = fmaf(h[f], Ssl[f * cols + j], acc);
-            part[j * L + t] = acc;
-        }
+        lds_gemm<kScanThreads>(L, cols, SV, hat, SV, 1, Ssl, cols, 1, [&](int t, int j, float c) { part[j * L + t] = c; });
         __syncthreads();
         // key features of the slice
-        for (int idx = tid; idx < L * SV; idx += kThreads) {
+        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             hat[idx] = F < a.M ? feature_value(xk + t * (d_K + 1), a.fidx[F], nidx) : 0.0f;
         }
         __syncthreads();
         // state update with the chunk
-        for (int idx = tid; idx < SV * cols; idx += kThreads) {
-            const int f = idx / cols, j = idx % cols;
-            float s = 0.0f;
-            for (int t = 0; t < L; ++t) s = fmaf(hat[t * SV + f], us[t * cols + j], s);
-            Ssl[idx] += s;
-        }
+        lds_gemm<kScanThreads>(SV, cols, L, hat, 1, SV, us, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {
-        for (int idx = tid; idx < SV * cols; idx += kThreads) {
+        for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
             const int j = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             if (F < a.M_pad) state[(int64_t)j * a.M_pad + F] = Ssl[f * cols + j];
@@ -133,12 +122,12 @@ hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st) {
         hipError_t e = hipFuncSetAttribute((const void*)scan_valu_kernel<InBF16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(scan_valu_kernel<InBF16>, grid, dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL(scan_valu_kernel<InBF16>, grid, dim3(kScanThreads), lds, st, a);
     } else {
         hipError_t e = hipFuncSetAttribute((const void*)scan_valu_kernel<InF32>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(scan_valu_kernel<InF32>, grid, dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL(scan_valu_kernel<InF32>, grid, dim3(kScanThreads), lds, st, a);
     }
     return hipGetLastError();
 }

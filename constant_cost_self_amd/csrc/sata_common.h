@@ -49,4 +49,57 @@ __device__ inline float taylor_weight(float x, const Alpha& al, int P) {
 
 __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+constexpr int kScanThreads = 512;    // block size of the fp32 scan kernels (2 waves per SIMD)
+
+// C(m, n) = sum_{k < K} A(m, k) B(k, n) for m < Mo, n < No, with A(m, k) = A[m sam + k sak]
+// and B(k, n) = B[k sbk + n sbn] in LDS, by the NT threads of a block; out(m, n, c)
+// receives each result.  Every 64 x 64 output block is split into register tiles of
+// TM x 4 (TM = 1024 / NT): thread tid = 16 mt + nt owns rows mt + (NT / 16) i and columns
+// nt + 16 j.  Per k it reads TM values of A and 4 of B for 4 TM FMAs; the 16 threads of
+// a row read 16 consecutive columns of B.
+template <int NT, typename Out>
+__device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, int sak, const float* B,
+                                int sbk, int sbn, Out out) {
+    static_assert(NT == 256 || NT == 512, "16 columns of threads, 64 rows per block");
+    constexpr int TM = 1024 / NT, RS = NT / 16;
+    const int mt = threadIdx.x >> 4, nt = threadIdx.x & 15;
+    for (int mb = 0; mb < Mo; mb += 64)
+        for (int nb = 0; nb < No; nb += 64) {
+            float acc[TM][4];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+            int mi[TM], nj[4];
+            bool mv[TM], nv[4];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                mi[i] = mb + mt + RS * i;
+                mv[i] = mi[i] < Mo;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                nj[j] = nb + nt + 16 * j;
+                nv[j] = nj[j] < No;
+            }
+#pragma unroll 2
+            for (int k = 0; k < K; ++k) {
+                float a[TM], b[4];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) a[i] = mv[i] ? A[mi[i] * sam + k * sak] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = nv[j] ? B[k * sbk + nj[j] * sbn] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (mv[i] && nv[j]) out(mi[i], nj[j], acc[i][j]);
+        }
+}
+
 }  // namespace sata
