@@ -247,6 +247,17 @@ __global__ __launch_bounds__(kThreads) void bwd_u_kernel(BwdArgs a) {
     u[d_V] = -h * inv;
 }
 
+// sum over the slices of one partial entry: 8 independent loads in flight per thread
+__device__ inline float slice_sum(const float* p, int64_t stride, int nslices) {
+    float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    int sl = 0;
+    for (; sl + 8 <= nslices; sl += 8)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] += __builtin_nontemporal_load(p + (sl + u) * stride);
+    for (; sl < nslices; ++sl) s[0] += __builtin_nontemporal_load(p + sl * stride);
+    return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
 // MODE 0: dq; MODE 1: dk and dv.  Sum of the slice partials plus the chunk's pairs.
 template <typename In, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
@@ -310,9 +321,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
             const int Tq = idx / d_K, i = idx % d_K;
             float acc = 0.0f;
             for (int t = 0; t <= Tq; ++t) acc = fmaf(cw[Tq * (L + 1) + t], xk[t * d_K + i], acc);
-            float ps = 0.0f;
-            for (int sl = 0; sl < a.nslices; ++sl) ps += part[sl * slice_stride * d_K + idx];
-            dq[idx] = acc + ps;
+            dq[idx] = acc + slice_sum(part + idx, slice_stride * d_K, a.nslices);
         }
     } else {
         const int64_t pb = (bh * nch + cl) * (int64_t)a.nslices * L;
@@ -324,17 +333,13 @@ __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
             const int t = idx / d_K, i = idx % d_K;
             float acc = 0.0f;
             for (int Tq = t; Tq < nvalid; ++Tq) acc = fmaf(cw[Tq * (L + 1) + t], xq[Tq * d_K + i], acc);
-            float ps = 0.0f;
-            for (int sl = 0; sl < a.nslices; ++sl) ps += pk[sl * slice_stride * d_K + idx];
-            dk[idx] = acc + ps;
+            dk[idx] = acc + slice_sum(pk + idx, slice_stride * d_K, a.nslices);
         }
         for (int idx = tid; idx < nvalid * d_V; idx += kThreads) {
             const int t = idx / d_V, j = idx % d_V;
             float acc = 0.0f;
             for (int Tq = t; Tq < nvalid; ++Tq) acc = fmaf(ww[Tq * (L + 1) + t], uu[Tq * cols + j], acc);
-            float ps = 0.0f;
-            for (int sl = 0; sl < a.nslices; ++sl) ps += pv[sl * slice_stride * d_V + idx];
-            dv[idx] = acc + ps;
+            dv[idx] = acc + slice_sum(pv + idx, slice_stride * d_V, a.nslices);
         }
     }
 }
