@@ -63,8 +63,18 @@ __device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, 
     static_assert(NT == 256 || NT == 512, "16 columns of threads, 64 rows per block");
     constexpr int TM = 1024 / NT, RS = NT / 16;
     const int mt = threadIdx.x >> 4, nt = threadIdx.x & 15;
+    // a few columns past the last whole block of 64 (the normaliser column of [v | 1]):
+    // one thread per output, so that they do not cost a whole block of tiles
+    const int rem = No % 64 <= 4 && No >= 64 ? No % 64 : 0;
+    const int Nt = No - rem;
+    for (int idx = threadIdx.x; idx < Mo * rem; idx += NT) {
+        const int m = idx / rem, n = Nt + idx % rem;
+        float c = 0.0f;
+        for (int k = 0; k < K; ++k) c = fmaf(A[m * sam + k * sak], B[k * sbk + n * sbn], c);
+        out(m, n, c);
+    }
     for (int mb = 0; mb < Mo; mb += 64)
-        for (int nb = 0; nb < No; nb += 64) {
+        for (int nb = 0; nb < Nt; nb += 64) {
             float acc[TM][4];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -80,7 +90,7 @@ __device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 nj[j] = nb + nt + 16 * j;
-                nv[j] = nj[j] < No;
+                nv[j] = nj[j] < Nt;
             }
 #pragma unroll 2
             for (int k = 0; k < K; ++k) {
