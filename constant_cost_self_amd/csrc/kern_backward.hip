@@ -52,30 +52,27 @@ template <typename In>
 __device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int nvalid, float* xq,
                                   float* xk, float* uu, float* vv) {
     using T = typename In::T;
-    const int d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1, L = a.L;
-    const T* q = static_cast<const T*>(a.q) + bh * a.n * d_K;
-    const T* k = static_cast<const T*>(a.k) + bh * a.n * d_K;
-    const T* v = static_cast<const T*>(a.v) + bh * a.n * d_V;
-    const float* u = a.u + bh * a.n * cols;
-    for (int idx = threadIdx.x; idx < L * ks; idx += kScanThreads) {
-        const int t = idx / ks, i = idx % ks;
-        float vq = 1.0f, vk = 1.0f;              // coordinate d_K: the constant 1
-        if (i < d_K) {
-            vq = t < nvalid ? In::load(q, (t0 + t) * d_K + i) : 0.0f;
-            vk = t < nvalid ? In::load(k, (t0 + t) * d_K + i) : 0.0f;
-        }
-        xq[idx] = vq;
-        xk[idx] = vk;
+    const int d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1, L = a.L, uc = a.ucols;
+    load_rows<In, kScanThreads>(static_cast<const T*>(a.q) + bh * a.n * d_K, t0, nvalid, L, d_K, xq, ks);
+    load_rows<In, kScanThreads>(static_cast<const T*>(a.k) + bh * a.n * d_K, t0, nvalid, L, d_K, xk, ks);
+    load_rows<In, kScanThreads>(static_cast<const T*>(a.v) + bh * a.n * d_V, t0, nvalid, L, d_V, vv, cols);
+    // u rows are padded to uc floats (a multiple of 4): 16-byte loads
+    const float* u = a.u + (bh * a.n + t0) * uc;
+    const int pr = uc / 4;
+    for (int idx = threadIdx.x; idx < L * pr; idx += kScanThreads) {
+        const int t = idx / pr, c = idx % pr;
+        float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (t < nvalid) x = *reinterpret_cast<const float4*>(u + (int64_t)t * uc + 4 * c);
+        const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * c + e < cols) uu[t * cols + 4 * c + e] = xv[e];
     }
-    for (int idx = threadIdx.x; idx < L * cols; idx += kScanThreads) {
-        const int t = idx / cols, j = idx % cols;
-        float uv = 0.0f, vv1 = 0.0f;
-        if (t < nvalid) {
-            uv = u[(t0 + t) * cols + j];
-            vv1 = j < d_V ? In::load(v, (t0 + t) * d_V + j) : 1.0f;
-        }
-        uu[idx] = uv;
-        vv[idx] = vv1;
+    // coordinate d_K is the constant 1; the last column of [v | 1] is 1 for the tokens
+    for (int t = threadIdx.x; t < L; t += kScanThreads) {
+        xq[t * ks + d_K] = 1.0f;
+        xk[t * ks + d_K] = 1.0f;
+        vv[t * cols + d_V] = t < nvalid ? 1.0f : 0.0f;
     }
 }
 
@@ -234,11 +231,11 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
 __global__ __launch_bounds__(kThreads) void bwd_u_kernel(BwdArgs a) {
     const int64_t tok = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (tok >= (int64_t)a.BH * a.n) return;
-    const int d_V = a.d_V, cols = d_V + 1;
+    const int d_V = a.d_V;
     const float inv = 1.0f / a.den[tok];
     const float* dy = a.dy + tok * d_V;
     const float* y = a.y + tok * d_V;
-    float* u = a.u_out + tok * cols;
+    float* u = a.u_out + tok * a.ucols;
     float h = 0.0f;
     for (int j = 0; j < d_V; ++j) {
         u[j] = dy[j] * inv;
@@ -280,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
     const T* q = static_cast<const T*>(a.q) + (bh * a.n + t0) * d_K;
     const T* k = static_cast<const T*>(a.k) + (bh * a.n + t0) * d_K;
     const T* v = static_cast<const T*>(a.v) + (bh * a.n + t0) * d_V;
-    const float* u = a.u + (bh * a.n + t0) * cols;
+    const float* u = a.u + (bh * a.n + t0) * a.ucols;
     for (int idx = tid; idx < L * d_K; idx += kThreads) {
         const int t = idx / d_K;
         xq[idx] = t < nvalid ? In::load(q, idx) : 0.0f;
@@ -289,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
     for (int idx = tid; idx < L * cols; idx += kThreads) {
         const int t = idx / cols, j = idx % cols;
         vv[idx] = (t < nvalid && j < d_V) ? In::load(v, (int64_t)t * d_V + j) : 0.0f;
-        uu[idx] = t < nvalid ? u[(int64_t)t * cols + j] : 0.0f;
+        uu[idx] = t < nvalid ? u[(int64_t)t * a.ucols + j] : 0.0f;
     }
     __syncthreads();
     for (int idx = tid; idx < L * L; idx += kThreads) {

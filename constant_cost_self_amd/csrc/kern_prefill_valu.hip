@@ -57,21 +57,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         const int64_t t0 = (int64_t)c * L;
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
-        for (int idx = tid; idx < L * (d_K + 1); idx += kScanThreads) {
-            const int t = idx / (d_K + 1), i = idx % (d_K + 1);
-            float vq = 1.0f, vk = 1.0f;
-            if (i < d_K) {
-                vq = t < nvalid ? In::load(q, (t0 + t) * d_K + i) : 0.0f;
-                vk = t < nvalid ? In::load(k, (t0 + t) * d_K + i) : 0.0f;
-            }
-            xq[idx] = vq;
-            xk[idx] = vk;
-        }
-        for (int idx = tid; idx < L * cols; idx += kScanThreads) {
-            const int t = idx / cols, j = idx % cols;
-            float u = 0.0f;
-            if (t < nvalid) u = j < d_V ? In::load(v, (t0 + t) * d_V + j) : 1.0f;
-            us[idx] = u;
+        load_rows<In, kScanThreads>(q, t0, nvalid, L, d_K, xq, d_K + 1);
+        load_rows<In, kScanThreads>(k, t0, nvalid, L, d_K, xk, d_K + 1);
+        load_rows<In, kScanThreads>(v, t0, nvalid, L, d_V, us, cols);
+        for (int t = tid; t < L; t += kScanThreads) {      // coordinate d_K == 1; u = [v | 1]
+            xq[t * (d_K + 1) + d_K] = 1.0f;
+            xk[t * (d_K + 1) + d_K] = 1.0f;
+            us[t * cols + d_V] = t < nvalid ? 1.0f : 0.0f;
         }
         __syncthreads();
         // weighted query features of the slice

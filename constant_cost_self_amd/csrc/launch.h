@@ -79,7 +79,8 @@ struct BwdArgs {
     const float* dy;         // [BH][n][d_V]
     const float* y;          // [BH][n][d_V] forward output
     const float* den;        // [BH][n] forward normaliser D_T
-    const float* u;          // [BH][n][d_V+1]: dy / D, then -(dy . y) / D
+    const float* u;          // [BH][n][ucols]: dy / D, then -(dy . y) / D, then padding
+    int ucols;               // d_V + 1 rounded up to a multiple of 4
     float* u_out;            // where bwd_u_kernel writes u (the same buffer)
     float* dq;
     float* dk;

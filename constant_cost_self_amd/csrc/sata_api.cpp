@@ -435,7 +435,8 @@ int sata_prefill_backward(const sata_tables* tc, const void* q, const void* k, c
     const int nslf = (int)((M + SVf - 1) / SVf), nslb = (int)((M + SVb - 1) / SVb);
     auto r256 = [](int64_t b) { return (b + 255) / 256 * 256; };
     const int64_t y_b = r256((int64_t)BH * n * d_V * 4), den_b = r256((int64_t)BH * n * 4);
-    const int64_t u_b = r256((int64_t)BH * n * cols * 4), st_b = r256((int64_t)BH * cols * M_pad * 4);
+    const int ucols = (cols + 3) / 4 * 4;
+    const int64_t u_b = r256((int64_t)BH * n * ucols * 4), st_b = r256((int64_t)BH * cols * M_pad * 4);
     const int64_t fixed = y_b + den_b + u_b + st_b;
     int64_t per_chunk = (int64_t)BH * nslf * L * cols * 4;                    // forward recompute
     const int64_t per_q = (int64_t)BH * nslb * L * d_K * 4;
@@ -490,7 +491,7 @@ int sata_prefill_backward(const sata_tables* tc, const void* q, const void* k, c
     // u = [dy / D | -(dy . y) / D]
     sata::BwdArgs b{};
     b.q = q; b.k = k; b.v = v;
-    b.dy = dy; b.y = y_ws; b.den = den_ws; b.u = u_ws; b.u_out = u_ws;
+    b.dy = dy; b.y = y_ws; b.den = den_ws; b.u = u_ws; b.u_out = u_ws; b.ucols = ucols;
     b.dq = dq; b.dk = dk; b.dv = dv;
     b.state = carrier;
     b.fidx = t->d_fidx;

@@ -51,6 +51,45 @@ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) 
 
 constexpr int kScanThreads = 512;    // block size of the fp32 scan kernels (2 waves per SIMD)
 
+// dst[t * ds + i] = src[(row0 + t) * d + i] as fp32 for t < L, i < d; rows t >= nvalid are
+// zero.  16-byte loads when a row is a whole number of 16-byte pieces (the base is
+// 16-byte aligned), else one element per load.  All NT threads of the block take part.
+template <typename In, int NT>
+__device__ inline void load_rows(const typename In::T* src, int64_t row0, int nvalid, int L, int d,
+                                 float* dst, int ds) {
+    using T = typename In::T;
+    constexpr int VE = 16 / sizeof(T);
+    if ((d * (int)sizeof(T)) % 16 == 0) {
+        const int pr = d / VE;                                  // 16-byte pieces per row
+        for (int idx = threadIdx.x; idx < L * pr; idx += NT) {
+            const int t = idx / pr, c = idx % pr;
+            float* o = dst + t * ds + c * VE;
+            if (t < nvalid) {
+                const uint4 x = *reinterpret_cast<const uint4*>(src + (row0 + t) * d + c * VE);
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                if (sizeof(T) == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o[2 * e] = __uint_as_float(w[e] << 16);
+                        o[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(w[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) o[e] = 0.0f;
+            }
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < L * d; idx += NT) {
+            const int t = idx / d, i = idx % d;
+            dst[t * ds + i] = t < nvalid ? In::load(src, (row0 + t) * d + i) : 0.0f;
+        }
+    }
+}
+
 // C(m, n) = sum_{k < K} A(m, k) B(k, n) for m < Mo, n < No, with A(m, k) = A[m sam + k sak]
 // and B(k, n) = B[k sbk + n sbn] in LDS, by the NT threads of a block; out(m, n, c)
 // receives each result.  Every 64 x 64 output block is split into register tiles of
