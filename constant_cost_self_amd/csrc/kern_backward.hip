@@ -39,7 +39,7 @@ namespace {
 // tables and the scatter target
 __host__ __device__ inline int64_t bwd_scan_lds_floats(int SV, int d_K, int d_V, int L) {
     const int cols = d_V + 1, ks = d_K + 1;
-    return (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3LL * L * SV + (int64_t)L * ks;
+    return (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3LL * L * SV + (int64_t)L * ks + 2LL * SV;
 }
 
 // LDS floats of the finalize: x_q, x_k, [v | 1], u, and two L x (L + 1) pair tables
@@ -76,6 +76,16 @@ __device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int 
     }
 }
 
+// the slice's packed index rows and query weights, copied to LDS once per block (the
+// tables are M_pad long: padding rows have weight 0 and an all-sentinel index row)
+__device__ inline void stage_slice(const BwdArgs& a, int64_t F0, int SV, uint32_t* sfi, float* sqw) {
+    for (int f = threadIdx.x; f < SV; f += kScanThreads) {
+        const int64_t F = F0 + f;
+        sfi[f] = F < a.M_pad ? a.fidx[F] : 0u;
+        sqw[f] = F < a.M_pad ? a.qw[F] : 0.0f;
+    }
+}
+
 // acc[idx_s] += val * prod_{s' != s} x[idx_s'] for every slot s of a feature's packed
 // index row (LDS float atomics: several features of a thread block share coordinates)
 __device__ inline void scatter_grad(float* acc, const float* x, uint32_t packed, int nidx, float val) {
@@ -109,7 +119,10 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     float* vv = uu + L * cols;                     // [L][cols]
     float* hat = vv + L * cols;                    // [SV][L] a_T, then [L][SV] phi(k)
     float* gq = hat + 3 * L * SV;                  // [L][ks] (the layout of bwd_kv_kernel)
+    uint32_t* sfi = reinterpret_cast<uint32_t*>(gq + L * ks);   // [SV] packed indices
+    float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
+    stage_slice(a, F0, SV, sfi, sqw);
 
     for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
@@ -132,7 +145,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int f = idx / L, t = idx % L;
             const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) scatter_grad(gq + t * ks, xq + t * ks, a.fidx[F], nidx, hat[idx] * a.qw[F]);
+            if (F < a.M && t < nvalid) scatter_grad(gq + t * ks, xq + t * ks, sfi[f], nidx, hat[idx] * sqw[f]);
         }
         __syncthreads();
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
@@ -141,7 +154,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? feature_value(xk + t * ks, a.fidx[F], nidx) : 0.0f;
+            hat[idx] = F < a.M ? feature_value(xk + t * ks, sfi[f], nidx) : 0.0f;
         }
         __syncthreads();
         lds_gemm<kScanThreads>(SV, cols, L, hat, 1, SV, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
@@ -174,7 +187,10 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
     float* hq = hk + L * SV;                       // [L][SV] qw phi(q)
     float* bb = hq + L * SV;                       // [SV][L] R[f] . [v_t | 1]
     float* gk = bb + L * SV;                       // [L][ks]
+    uint32_t* sfi = reinterpret_cast<uint32_t*>(gk + L * ks);   // [SV] packed indices
+    float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
+    stage_slice(a, F0, SV, sfi, sqw);
 
     for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
@@ -193,8 +209,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             const bool live = F < a.M && t < nvalid;
-            hk[idx] = live ? feature_value(xk + t * ks, a.fidx[F], nidx) : 0.0f;
-            hq[idx] = live ? a.qw[F] * feature_value(xq + t * ks, a.fidx[F], nidx) : 0.0f;
+            hk[idx] = live ? feature_value(xk + t * ks, sfi[f], nidx) : 0.0f;
+            hq[idx] = live ? sqw[f] * feature_value(xq + t * ks, sfi[f], nidx) : 0.0f;
         }
         __syncthreads();
         const int64_t pbase = ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L;
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int f = idx / L, t = idx % L;
             const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) scatter_grad(gk + t * ks, xk + t * ks, a.fidx[F], nidx, bb[idx]);
+            if (F < a.M && t < nvalid) scatter_grad(gk + t * ks, xk + t * ks, sfi[f], nidx, bb[idx]);
         }
         __syncthreads();
         float* pk = a.part + pbase * d_K;

@@ -21,7 +21,7 @@ namespace {
 
 __host__ __device__ inline int64_t valu_lds_floats(int SV, int d_K, int d_V, int L) {
     const int cols = d_V + 1;
-    return (int64_t)SV * cols + 2LL * L * (d_K + 1) + (int64_t)L * cols + (int64_t)L * SV;
+    return (int64_t)SV * cols + 2LL * L * (d_K + 1) + (int64_t)L * cols + (int64_t)L * SV + 2LL * SV;
 }
 
 template <typename In>
@@ -40,6 +40,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
     float* xk = xq + L * (d_K + 1);                // [L][d_K+1]
     float* us = xk + L * (d_K + 1);                // [L][cols]
     float* hat = us + L * cols;                    // [L][SV]
+    uint32_t* sfi = reinterpret_cast<uint32_t*>(hat + L * SV);   // [SV] packed indices
+    float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights
+    for (int f = tid; f < SV; f += kScanThreads) {   // tables are M_pad long (padding: weight 0)
+        const int64_t F = F0 + f;
+        sfi[f] = F < a.M_pad ? a.fidx[F] : 0u;
+        sqw[f] = F < a.M_pad ? a.qw[F] : 0.0f;
+    }
 
     const T* q = static_cast<const T*>(a.q) + bh * a.n * d_K;
     const T* k = static_cast<const T*>(a.k) + bh * a.n * d_K;
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? a.qw[F] * feature_value(xq + t * (d_K + 1), a.fidx[F], nidx)
+            hat[idx] = F < a.M ? sqw[f] * feature_value(xq + t * (d_K + 1), sfi[f], nidx)
                                : 0.0f;
         }
         __syncthreads();
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? feature_value(xk + t * (d_K + 1), a.fidx[F], nidx) : 0.0f;
+            hat[idx] = F < a.M ? feature_value(xk + t * (d_K + 1), sfi[f], nidx) : 0.0f;
         }
         __syncthreads();
         // state update with the chunk
