@@ -87,30 +87,34 @@ __device__ inline void stage_slice(const BwdArgs& a, int64_t F0, int SV, uint32_
 }
 
 // acc[idx_s] += val * prod_{s' != s} x[idx_s'] for every slot s of a feature's packed
-// index row (LDS float atomics: several features of a thread block share coordinates)
-__device__ inline void scatter_grad(float* acc, const float* x, uint32_t packed, int nidx, float val) {
-    float xs[kMaxP];
-    int is[kMaxP];
-    for (int s = 0; s < nidx; ++s) {
+// index row (LDS float atomics: several features of a thread block share coordinates);
+// NIDX = P - 1 slots, unrolled
+template <int NIDX>
+__device__ inline void scatter_grad(float* acc, const float* x, uint32_t packed, float val) {
+    float xs[NIDX > 0 ? NIDX : 1];
+    int is[NIDX > 0 ? NIDX : 1];
+#pragma unroll
+    for (int s = 0; s < NIDX; ++s) {
         is[s] = (packed >> (8 * s)) & 0xffu;
         xs[s] = x[is[s]];
     }
-    for (int s = 0; s < nidx; ++s) {
+#pragma unroll
+    for (int s = 0; s < NIDX; ++s) {
         float prod = val;
-        for (int s2 = 0; s2 < nidx; ++s2)
+#pragma unroll
+        for (int s2 = 0; s2 < NIDX; ++s2)
             if (s2 != s) prod *= xs[s2];
         atomicAdd(&acc[is[s]], prod);
     }
 }
 
-template <typename In>
+template <typename In, int NIDX>
 __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int SV = a.slice_feats, L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1;
-    const int nidx = a.P - 1;
     const int64_t F0 = (int64_t)slice * SV;
     float* Ssl = lds;                              // [SV][cols]
     float* xq = Ssl + SV * cols;                   // [L][ks]
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int f = idx / L, t = idx % L;
             const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) scatter_grad(gq + t * ks, xq + t * ks, sfi[f], nidx, hat[idx] * sqw[f]);
+            if (F < a.M && t < nvalid) scatter_grad<NIDX>(gq + t * ks, xq + t * ks, sfi[f], hat[idx] * sqw[f]);
         }
         __syncthreads();
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? feature_value(xk + t * ks, sfi[f], nidx) : 0.0f;
+            hat[idx] = F < a.M ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
         }
         __syncthreads();
         lds_gemm<kScanThreads>(SV, cols, L, hat, 1, SV, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
@@ -169,14 +173,13 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     }
 }
 
-template <typename In>
+template <typename In, int NIDX>
 __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int SV = a.slice_feats, L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1;
-    const int nidx = a.P - 1;
     const int64_t F0 = (int64_t)slice * SV;
     float* Rsl = lds;                              // [SV][cols]
     float* xq = Rsl + SV * cols;                   // [L][ks]
@@ -209,8 +212,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             const bool live = F < a.M && t < nvalid;
-            hk[idx] = live ? feature_value(xk + t * ks, sfi[f], nidx) : 0.0f;
-            hq[idx] = live ? sqw[f] * feature_value(xq + t * ks, sfi[f], nidx) : 0.0f;
+            hk[idx] = live ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
+            hq[idx] = live ? sqw[f] * feature_value_n<NIDX>(xq + t * ks, sfi[f]) : 0.0f;
         }
         __syncthreads();
         const int64_t pbase = ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int f = idx / L, t = idx % L;
             const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) scatter_grad(gk + t * ks, xk + t * ks, sfi[f], nidx, bb[idx]);
+            if (F < a.M && t < nvalid) scatter_grad<NIDX>(gk + t * ks, xk + t * ks, sfi[f], bb[idx]);
         }
         __syncthreads();
         float* pk = a.part + pbase * d_K;
@@ -381,19 +384,30 @@ hipError_t launch_bwd_u(const BwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st) {
+template <int NIDX>
+hipError_t launch_bwd_scans(const BwdArgs& a, bool kv, hipStream_t st) {
     const size_t lds = (size_t)bwd_scan_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
     const dim3 grid(a.nslices, a.BH);
-    return a.bf16 ? launch_lds(bwd_q_kernel<InBF16>, grid, kScanThreads, lds, a, st)
-                  : launch_lds(bwd_q_kernel<InF32>, grid, kScanThreads, lds, a, st);
+    if (kv)
+        return a.bf16 ? launch_lds(bwd_kv_kernel<InBF16, NIDX>, grid, kScanThreads, lds, a, st)
+                      : launch_lds(bwd_kv_kernel<InF32, NIDX>, grid, kScanThreads, lds, a, st);
+    return a.bf16 ? launch_lds(bwd_q_kernel<InBF16, NIDX>, grid, kScanThreads, lds, a, st)
+                  : launch_lds(bwd_q_kernel<InF32, NIDX>, grid, kScanThreads, lds, a, st);
 }
 
-hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
-    const size_t lds = (size_t)bwd_scan_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
-    const dim3 grid(a.nslices, a.BH);
-    return a.bf16 ? launch_lds(bwd_kv_kernel<InBF16>, grid, kScanThreads, lds, a, st)
-                  : launch_lds(bwd_kv_kernel<InF32>, grid, kScanThreads, lds, a, st);
+hipError_t launch_bwd_scan(const BwdArgs& a, bool kv, hipStream_t st) {
+    switch (a.P - 1) {                 // slots per feature
+        case 0: return launch_bwd_scans<0>(a, kv, st);
+        case 1: return launch_bwd_scans<1>(a, kv, st);
+        case 2: return launch_bwd_scans<2>(a, kv, st);
+        case 3: return launch_bwd_scans<3>(a, kv, st);
+        default: return launch_bwd_scans<4>(a, kv, st);
+    }
 }
+
+hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st) { return launch_bwd_scan(a, false, st); }
+
+hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) { return launch_bwd_scan(a, true, st); }
 
 hipError_t launch_bwd_fin(const BwdArgs& a, int mode, hipStream_t st) {
     const size_t lds = (size_t)bwd_fin_lds_bytes(a.d_K, a.d_V, a.L);

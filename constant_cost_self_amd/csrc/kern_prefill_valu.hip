@@ -24,7 +24,7 @@ __host__ __device__ inline int64_t valu_lds_floats(int SV, int d_K, int d_V, int
     return (int64_t)SV * cols + 2LL * L * (d_K + 1) + (int64_t)L * cols + (int64_t)L * SV + 2LL * SV;
 }
 
-template <typename In>
+template <typename In, int NIDX>
 __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs a) {
     using T = typename In::T;
     extern __shared__ float lds[];
@@ -32,7 +32,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int SV = a.slice_feats, L = a.L, d_K = a.d_K, d_V = a.d_V, cols = d_V + 1;
-    const int nidx = a.P - 1;
     const int64_t F0 = (int64_t)slice * SV;
 
     float* Ssl = lds;                              // [SV][cols]
@@ -77,7 +76,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? sqw[f] * feature_value(xq + t * (d_K + 1), sfi[f], nidx)
+            hat[idx] = F < a.M ? sqw[f] * feature_value_n<NIDX>(xq + t * (d_K + 1), sfi[f])
                                : 0.0f;
         }
         __syncthreads();
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? feature_value(xk + t * (d_K + 1), sfi[f], nidx) : 0.0f;
+            hat[idx] = F < a.M ? feature_value_n<NIDX>(xk + t * (d_K + 1), sfi[f]) : 0.0f;
         }
         __syncthreads();
         // state update with the chunk
@@ -114,21 +113,29 @@ int valu_slice_feats(int d_K, int d_V, int L) {
     return 0;
 }
 
-hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st) {
+namespace {
+
+template <int NIDX>
+hipError_t launch_scan_valu_n(const PrefillSegArgs& a, hipStream_t st) {
     const size_t lds = (size_t)valu_lds_floats(a.slice_feats, a.d_K, a.d_V, a.L) * 4;
     dim3 grid(a.nslices, a.BH);
-    if (a.bf16) {
-        hipError_t e = hipFuncSetAttribute((const void*)scan_valu_kernel<InBF16>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(scan_valu_kernel<InBF16>, grid, dim3(kScanThreads), lds, st, a);
-    } else {
-        hipError_t e = hipFuncSetAttribute((const void*)scan_valu_kernel<InF32>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(scan_valu_kernel<InF32>, grid, dim3(kScanThreads), lds, st, a);
-    }
+    auto kernel = a.bf16 ? scan_valu_kernel<InBF16, NIDX> : scan_valu_kernel<InF32, NIDX>;
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, grid, dim3(kScanThreads), lds, st, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st) {
+    switch (a.P - 1) {                 // slots per feature
+        case 0: return launch_scan_valu_n<0>(a, st);
+        case 1: return launch_scan_valu_n<1>(a, st);
+        case 2: return launch_scan_valu_n<2>(a, st);
+        case 3: return launch_scan_valu_n<3>(a, st);
+        default: return launch_scan_valu_n<4>(a, st);
+    }
 }
 
 }  // namespace sata

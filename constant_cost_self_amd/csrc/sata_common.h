@@ -40,6 +40,15 @@ __device__ inline float feature_value(const float* x, uint32_t packed, int nidx)
     return prod;
 }
 
+// feature_value with the slot count known at compile time (fully unrolled gathers)
+template <int NIDX>
+__device__ inline float feature_value_n(const float* x, uint32_t packed) {
+    float prod = 1.0f;
+#pragma unroll
+    for (int s = 0; s < NIDX; ++s) prod *= x[(packed >> (8 * s)) & 0xffu];
+    return prod;
+}
+
 // Truncated kernel w(x) = sum_{p<P} alpha_p x^p by Horner's rule.
 __device__ inline float taylor_weight(float x, const Alpha& al, int P) {
     float w = al.a[P - 1];
