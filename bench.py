@@ -13,6 +13,11 @@ its own stream: achieved = algorithmic work per launch / mean launch time.
                 (the forward FLOPs/token closed form of the method), peak = bf16 MFMA
                 2.5 PFLOP/s.
   decode:       bytes = 8 (d_V + 1) M per head (fp32 state read + write), peak 8 TB/s.
+  backward:     (sata_prefill_backward on the Mid shape, fp32 on the vector ALUs)
+                flops = B H n [forward closed form + 2 M (4 (d_V + 1) + d_V)]: the fp32
+                forward recompute plus the five state contractions of the gradient
+                scans (S . u, S update, R . [v|1], phi(k) R, R update); peak = fp32
+                vector 157.3 TFLOP/s.
 cpu_baseline: the fp64 oracle's fixed-size-state form, timed on the host's cores
 on a bounded sample (one head, the first --cpu-tokens tokens).
 Prints one JSON line on stdout; progress goes to stderr.
@@ -32,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
+VALU_FP32_PEAK_TFLOPS = 157.3
 
 
 def log(msg):
@@ -133,6 +139,41 @@ def bench_decode(steps, warmup, prefill_chunk=64):
     return wall, tim, bytes_per_step, w
 
 
+def backward_flops_per_token(d_K, d_V, P):
+    M = math.comb(d_K + P - 1, P - 1)
+    return flops_per_token(d_K, d_V, P) + 2.0 * M * (4 * (d_V + 1) + d_V)
+
+
+def bench_backward(steps, warmup):
+    import numpy as np
+    import torch
+    from constant_cost_self_amd import inputs, sata
+
+    w = inputs.MID
+    log("backward: %s shape B=%d H=%d n=%d d=%d" % (w.name, w.B, w.H, w.n, w.d_K))
+    x = inputs.prefill_inputs(w)
+    q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
+    dy = to_dev(np.random.default_rng(7).standard_normal((w.B, w.H, w.n, w.d_V)).astype(np.float32), "f32")
+    dq = torch.empty((w.B, w.H, w.n, w.d_K), device="cuda:0", dtype=torch.float32)
+    dk = torch.empty_like(dq)
+    dv = torch.empty((w.B, w.H, w.n, w.d_V), device="cuda:0", dtype=torch.float32)
+    t = sata.sata_tables_build(w.d_K, w.P)
+    t.set_timing(True)
+    for i in range(warmup):
+        sata.sata_prefill_backward(t, q, k, v, dy, dq, dk, dv, chunk=w.chunk)
+    torch.cuda.synchronize()
+    t.read_timing()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sata.sata_prefill_backward(t, q, k, v, dy, dq, dk, dv, chunk=w.chunk)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tim = t.read_timing()
+    log("  backward %d steps: %.3f s; kernels %s" % (steps, wall, tim))
+    t.close()
+    return wall, tim, w
+
+
 def cpu_baseline(w, ntok):
     """The oracle's fixed-size-state form on head (0, 0), first ntok tokens."""
     import oracle
@@ -164,7 +205,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--backward-steps", type=int, default=3)
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one part only (for profiler runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB, 3 times (calibrates the "
@@ -194,6 +237,11 @@ def main():
         print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4}))
         return
     w = inputs.WORKLOADS[args.workload]
+    if args.only == "backward":
+        bwall, btim, bw = bench_backward(args.backward_steps, 1)
+        print(json.dumps({"backward_ms": btim["backward"][0] / btim["backward"][1],
+                          "backward_step_ms": bwall / args.backward_steps * 1e3}))
+        return
     if args.only == "decode":
         dwall, dtim, dbytes, dw = bench_decode(args.decode_steps, args.decode_warmup)
         dk_ms, dk_n = dtim["decode"]
@@ -257,6 +305,23 @@ def main():
                          "ms_per_launch": dk_ms / dk_n,
                          "algorithmic_bytes_per_launch": dbytes},
             "reduce_ms_per_step": dtim["decode_reduce"][0] / max(dtim["decode_reduce"][1], 1),
+        }
+
+    if not args.no_backward and args.only is None:
+        bwall, btim, bw = bench_backward(args.backward_steps, 1)
+        b_ms, b_n = btim["backward"]
+        bflops = backward_flops_per_token(bw.d_K, bw.d_V, bw.P) * bw.B * bw.H * bw.n
+        b_tflops = bflops / (b_ms / b_n * 1e-3) / 1e12
+        out["backward"] = {
+            "workload": "prefill backward (dq, dk, dv for dL/dy = dy): B=%d H=%d n=%d d_K=d_V=%d "
+                        "P=%d chunk=%d, %s q,k,v, fp32 dy; fp32 arithmetic" %
+                        (bw.B, bw.H, bw.n, bw.d_K, bw.P, bw.chunk, bw.dtype),
+            "value": bw.B * bw.n / (bwall / args.backward_steps), "unit": "tokens/s",
+            "steps": args.backward_steps, "ms_per_step": bwall / args.backward_steps * 1e3,
+            "roofline": {"bound": "alu", "achieved": b_tflops, "peak": VALU_FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": b_tflops / VALU_FP32_PEAK_TFLOPS,
+                         "traffic": None, "kernel": "prefill backward (all kernels of one call)",
+                         "ms_per_launch": b_ms / b_n, "algorithmic_flops_per_launch": bflops},
         }
 
     if not args.no_cpu and args.only is None:
