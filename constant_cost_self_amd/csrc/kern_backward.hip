@@ -35,11 +35,17 @@ namespace sata {
 
 namespace {
 
-// LDS floats of the scan kernels: state slice, x_q, x_k, u, [v | 1], two feature
-// tables and the scatter target
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kMaxSlots = 4;                       // P - 1 gathered slots per feature, P <= 5
+
+// LDS floats of the scan kernels: state slice, x_q, x_k, u, [v | 1], three feature tables,
+// the gradient rows, the slice's index rows and weights, then the scatter plan (entries of
+// two words, coordinate offsets, wave ranges) at an even offset
 __host__ __device__ inline int64_t bwd_scan_lds_floats(int SV, int d_K, int d_V, int L) {
     const int cols = d_V + 1, ks = d_K + 1;
-    return (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3LL * L * SV + (int64_t)L * ks + 2LL * SV;
+    int64_t base = (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3LL * L * SV + (int64_t)L * ks + 2LL * SV;
+    base += base & 1;
+    return base + 2LL * kMaxSlots * SV + (d_K + 1) + (kScanWaves + 1);
 }
 
 // LDS floats of the finalize: x_q, x_k, [v | 1], u, and two L x (L + 1) pair tables
@@ -86,25 +92,106 @@ __device__ inline void stage_slice(const BwdArgs& a, int64_t F0, int SV, uint32_
     }
 }
 
-// acc[idx_s] += val * prod_{s' != s} x[idx_s'] for every slot s of a feature's packed
-// index row (LDS float atomics: several features of a thread block share coordinates);
-// NIDX = P - 1 slots, unrolled
+// Scatter plan of a slice, built once per block.  When coordinate i fills m of the slots of
+// feature f, d phi_f / d x_i = m x_i^(m-1) prod(other slots), so the slice's gradient along i
+// sums one entry per feature holding i.  The entries are grouped by coordinate (the
+// constant-1 slot has no gradient) and the coordinates are split into one contiguous range
+// per wave with about equal entry counts.  A wave then sums every (token, coordinate) of its
+// range in one lane's register and writes it once: no two waves write one place, and no LDS
+// atomics are needed.
+// Entry: x = feature | coordinate << 16 | m << 24 | (last entry of its coordinate) << 31,
+//        y = the other NIDX - 1 slots (one copy of the coordinate taken out), 8 bits each.
 template <int NIDX>
-__device__ inline void scatter_grad(float* acc, const float* x, uint32_t packed, float val) {
-    float xs[NIDX > 0 ? NIDX : 1];
-    int is[NIDX > 0 ? NIDX : 1];
+__device__ inline void build_plan(const BwdArgs& a, int64_t F0, int SV, const uint32_t* sfi, uint2* ent,
+                                  int* off, int* wave_begin) {
+    const int tid = threadIdx.x, d_K = a.d_K;
+    const int nf = (int)((a.M - F0) < SV ? (a.M - F0) : SV);     // live features of the slice
+    __syncthreads();                                              // sfi is written by other waves
+    if (tid < d_K) {
+        int cnt = 0;
+        for (int f = 0; f < nf; ++f) {
+            bool has = false;
 #pragma unroll
-    for (int s = 0; s < NIDX; ++s) {
-        is[s] = (packed >> (8 * s)) & 0xffu;
-        xs[s] = x[is[s]];
+            for (int sl = 0; sl < NIDX; ++sl) has |= ((sfi[f] >> (8 * sl)) & 0xffu) == (uint32_t)tid;
+            cnt += has;
+        }
+        off[tid + 1] = cnt;
     }
+    __syncthreads();
+    if (tid == 0) {
+        off[0] = 0;
+        for (int i = 0; i < d_K; ++i) off[i + 1] += off[i];
+        const int64_t E = off[d_K];
+        int w = 1;
+        wave_begin[0] = 0;
+        for (int i = 0; i < d_K; ++i)
+            while (w < kScanWaves && (int64_t)off[i + 1] * kScanWaves >= w * E) wave_begin[w++] = off[i + 1];
+        for (; w <= kScanWaves; ++w) wave_begin[w] = (int)E;
+    }
+    __syncthreads();
+    if (tid < d_K) {
+        int pos = off[tid];
+        const int end = off[tid + 1];
+        for (int f = 0; f < nf; ++f) {
+            uint32_t m = 0, others = 0;
+            int no = 0;
 #pragma unroll
-    for (int s = 0; s < NIDX; ++s) {
-        float prod = val;
+            for (int sl = 0; sl < NIDX; ++sl) {
+                const uint32_t c = (sfi[f] >> (8 * sl)) & 0xffu;
+                if (c == (uint32_t)tid && m++ == 0) continue;
+                others |= c << (8 * no++);
+            }
+            if (m) {
+                const uint32_t last = pos + 1 == end ? 1u << 31 : 0u;
+                ent[pos++] = make_uint2((uint32_t)f | (uint32_t)tid << 16 | m << 24 | last, others);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// g[t][i] = sum over the plan entries (f, i) of this wave's coordinate range of
+// coef[f][t] m prod(other slots of x_t), lanes over tokens; rows t >= nvalid are written 0.
+// Entries are taken four at a time, all LDS reads of a group issued before its sums.
+template <int NIDX>
+__device__ inline void scatter_planned(float* __restrict__ g, const float* __restrict__ x,
+                                       const float* __restrict__ coef, const uint2* __restrict__ ent,
+                                       const int* __restrict__ wave_begin, int L, int ks, int nvalid) {
+    constexpr int U = 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e0 = wave_begin[w], e1 = wave_begin[w + 1];
+    for (int tb = 0; tb < L; tb += 64) {
+        const int t = tb + lane;
+        const int tt = t < L ? t : L - 1;
+        const float* xr = x + tt * ks;
+        const float* cr = coef + tt;
+        float acc = 0.0f;
+        for (int e = e0; e < e1; e += U) {
+            uint32_t ex[U], ey[U];
+            float p[U];
 #pragma unroll
-        for (int s2 = 0; s2 < NIDX; ++s2)
-            if (s2 != s) prod *= xs[s2];
-        atomicAdd(&acc[is[s]], prod);
+            for (int u = 0; u < U; ++u) {
+                const uint2 en = ent[e + u < e1 ? e + u : e1 - 1];
+                ex[u] = __builtin_amdgcn_readfirstlane(en.x);
+                ey[u] = __builtin_amdgcn_readfirstlane(en.y);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = cr[(int)(ex[u] & 0xffffu) * L] * (float)((ex[u] >> 24) & 7u);
+#pragma unroll
+                for (int sl = 0; sl < NIDX - 1; ++sl) p[u] *= xr[(ey[u] >> (8 * sl)) & 0xffu];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (e + u < e1) {
+                    acc += p[u];
+                    if (ex[u] >> 31) {
+                        if (t < L) g[t * ks + ((ex[u] >> 16) & 0xffu)] = t < nvalid ? acc : 0.0f;
+                        acc = 0.0f;
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -125,8 +212,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     float* gq = hat + 3 * L * SV;                  // [L][ks] (the layout of bwd_kv_kernel)
     uint32_t* sfi = reinterpret_cast<uint32_t*>(gq + L * ks);   // [SV] packed indices
     float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
+    uint2* ent = reinterpret_cast<uint2*>(lds + ((sqw + SV - lds + 1) & ~int64_t(1)));  // plan
+    int* off = reinterpret_cast<int*>(ent + kMaxSlots * SV);
+    int* wave_begin = off + d_K + 1;
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
     stage_slice(a, F0, SV, sfi, sqw);
+    build_plan<NIDX>(a, F0, SV, sfi, ent, off, wave_begin);
 
     for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
@@ -141,16 +232,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
         for (int idx = tid; idx < L * ks; idx += kScanThreads) gq[idx] = 0.0f;
         __syncthreads();
-        // a_T[f] = S[f] . u_T against the state before the chunk, stored [f][t]
-        lds_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols, [&](int t, int f, float c) { hat[f * L + t] = c; });
+        // qw_f a_T[f], a_T[f] = S[f] . u_T against the state before the chunk, stored [f][t]
+        lds_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols,
+                               [&](int t, int f, float c) { hat[f * L + t] = c * sqw[f]; });
         __syncthreads();
-        // dq partial: sum_f a_T[f] qw_f d phi_f / dq.  The lanes of a wave take one feature
-        // for consecutive tokens, so their LDS atomics hit distinct rows of gq.
-        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
-            const int f = idx / L, t = idx % L;
-            const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) scatter_grad<NIDX>(gq + t * ks, xq + t * ks, sfi[f], hat[idx] * sqw[f]);
-        }
+        // dq partial: sum_f qw_f a_T[f] d phi_f / dq
+        scatter_planned<NIDX>(gq, xq, hat, ent, wave_begin, L, ks, nvalid);
         __syncthreads();
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
         for (int idx = tid; idx < L * d_K; idx += kScanThreads) part[idx] = gq[(idx / d_K) * ks + idx % d_K];
@@ -192,8 +279,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
     float* gk = bb + L * SV;                       // [L][ks]
     uint32_t* sfi = reinterpret_cast<uint32_t*>(gk + L * ks);   // [SV] packed indices
     float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
+    uint2* ent = reinterpret_cast<uint2*>(lds + ((sqw + SV - lds + 1) & ~int64_t(1)));  // plan
+    int* off = reinterpret_cast<int*>(ent + kMaxSlots * SV);
+    int* wave_begin = off + d_K + 1;
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
     stage_slice(a, F0, SV, sfi, sqw);
+    build_plan<NIDX>(a, F0, SV, sfi, ent, off, wave_begin);
 
     for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
@@ -223,13 +314,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
         float* pv = a.part2 + pbase * d_V;
         lds_gemm<kScanThreads>(L, d_V, SV, hk, SV, 1, Rsl, cols, 1, [&](int t, int j, float c) { pv[t * d_V + j] = c; });
         __syncthreads();
-        // dk partial: sum_f b_t[f] d phi_f / dk (bb is [f][t]: a wave's atomics hit
-        // distinct token rows of gk)
-        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
-            const int f = idx / L, t = idx % L;
-            const int64_t F = F0 + f;
-            if (F < a.M && t < nvalid) scatter_grad<NIDX>(gk + t * ks, xk + t * ks, sfi[f], bb[idx]);
-        }
+        // dk partial: sum_f b_t[f] d phi_f / dk
+        scatter_planned<NIDX>(gk, xk, bb, ent, wave_begin, L, ks, nvalid);
         __syncthreads();
         float* pk = a.part + pbase * d_K;
         for (int idx = tid; idx < L * d_K; idx += kScanThreads) pk[idx] = gk[(idx / d_K) * ks + idx % d_K];

@@ -110,3 +110,9 @@ def test_backward_segmented_equals_single(torch_cuda):
         d = float(np.max(np.abs(a - b)) / np.max(np.abs(a)))
         say("  segmented vs single: %.2e" % d)
         assert d <= 1e-5
+
+
+@pytest.mark.parametrize("dK,dV,P", [(100, 20, 3), (96, 96, 4)])
+def test_backward_coordinates_past_one_wave(torch_cuda, dK, dV, P):
+    """d_K > 64: the slice's gradient plan is built by more than one wave of threads."""
+    check(torch_cuda, dK, dV, P, 70, 32, "f32", H=1, sigma=0.4, seed=dK)
