@@ -38,12 +38,17 @@ namespace {
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kMaxSlots = 4;                       // P - 1 gathered slots per feature, P <= 5
 
+// LDS floats of a feature table: [L][SV + 1] or [SV][L + 1] (row strides of 1 modulo 64
+// floats for the matrix-core loads)
+__host__ __device__ inline int64_t bwd_table_floats(int SV, int L) { return (int64_t)(L + 1) * (SV + 1); }
+
 // LDS floats of the scan kernels: state slice, x_q, x_k, u, [v | 1], three feature tables,
 // the gradient rows, the slice's index rows and weights, then the scatter plan (entries of
 // two words, coordinate offsets, wave ranges) at an even offset
 __host__ __device__ inline int64_t bwd_scan_lds_floats(int SV, int d_K, int d_V, int L) {
     const int cols = d_V + 1, ks = d_K + 1;
-    int64_t base = (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3LL * L * SV + (int64_t)L * ks + 2LL * SV;
+    int64_t base = (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3 * bwd_table_floats(SV, L) +
+                   (int64_t)L * ks + 2LL * SV;
     base += base & 1;
     return base + 2LL * kMaxSlots * SV + (d_K + 1) + (kScanWaves + 1);
 }
@@ -151,12 +156,12 @@ __device__ inline void build_plan(const BwdArgs& a, int64_t F0, int SV, const ui
 }
 
 // g[t][i] = sum over the plan entries (f, i) of this wave's coordinate range of
-// coef[f][t] m prod(other slots of x_t), lanes over tokens; rows t >= nvalid are written 0.
+// coef[f cs + t] m prod(other slots of x_t), lanes over tokens; rows t >= nvalid are written 0.
 // Entries are taken four at a time, all LDS reads of a group issued before its sums.
 template <int NIDX>
 __device__ inline void scatter_planned(float* __restrict__ g, const float* __restrict__ x,
                                        const float* __restrict__ coef, const uint2* __restrict__ ent,
-                                       const int* __restrict__ wave_begin, int L, int ks, int nvalid) {
+                                       const int* __restrict__ wave_begin, int L, int cs, int ks, int nvalid) {
     constexpr int U = 4;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int e0 = wave_begin[w], e1 = wave_begin[w + 1];
@@ -177,7 +182,7 @@ __device__ inline void scatter_planned(float* __restrict__ g, const float* __res
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                p[u] = cr[(int)(ex[u] & 0xffffu) * L] * (float)((ex[u] >> 24) & 7u);
+                p[u] = cr[(int)(ex[u] & 0xffffu) * cs] * (float)((ex[u] >> 24) & 7u);
 #pragma unroll
                 for (int sl = 0; sl < NIDX - 1; ++sl) p[u] *= xr[(ey[u] >> (8 * sl)) & 0xffu];
             }
@@ -208,8 +213,9 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     float* xk = xq + L * ks;                       // [L][ks]
     float* uu = xk + L * ks;                       // [L][cols]
     float* vv = uu + L * cols;                     // [L][cols]
-    float* hat = vv + L * cols;                    // [SV][L] a_T, then [L][SV] phi(k)
-    float* gq = hat + 3 * L * SV;                  // [L][ks] (the layout of bwd_kv_kernel)
+    const int LP = L + 1, SVP = SV + 1;
+    float* hat = vv + L * cols;                    // [SV][LP] qw a_T, then [L][SVP] phi(k)
+    float* gq = hat + 3 * bwd_table_floats(SV, L); // [L][ks] (the layout of bwd_kv_kernel)
     uint32_t* sfi = reinterpret_cast<uint32_t*>(gq + L * ks);   // [SV] packed indices
     float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
     uint2* ent = reinterpret_cast<uint2*>(lds + ((sqw + SV - lds + 1) & ~int64_t(1)));  // plan
@@ -233,11 +239,11 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * ks; idx += kScanThreads) gq[idx] = 0.0f;
         __syncthreads();
         // qw_f a_T[f], a_T[f] = S[f] . u_T against the state before the chunk, stored [f][t]
-        lds_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols,
-                               [&](int t, int f, float c) { hat[f * L + t] = c * sqw[f]; });
+        mfma_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols,
+                                [&](int t, int f, float c) { hat[f * LP + t] = c * sqw[f]; });
         __syncthreads();
         // dq partial: sum_f qw_f a_T[f] d phi_f / dq
-        scatter_planned<NIDX>(gq, xq, hat, ent, wave_begin, L, ks, nvalid);
+        scatter_planned<NIDX>(gq, xq, hat, ent, wave_begin, L, LP, ks, nvalid);
         __syncthreads();
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
         for (int idx = tid; idx < L * d_K; idx += kScanThreads) part[idx] = gq[(idx / d_K) * ks + idx % d_K];
@@ -245,10 +251,10 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
+            hat[t * SVP + f] = F < a.M ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
         }
         __syncthreads();
-        lds_gemm<kScanThreads>(SV, cols, L, hat, 1, SV, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
+        mfma_gemm<kScanThreads>(SV, cols, L, hat, 1, SVP, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {
@@ -273,10 +279,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
     float* xk = xq + L * ks;                       // [L][ks]
     float* uu = xk + L * ks;                       // [L][cols]
     float* vv = uu + L * cols;                     // [L][cols]
-    float* hk = vv + L * cols;                     // [L][SV] phi(k)
-    float* hq = hk + L * SV;                       // [L][SV] qw phi(q)
-    float* bb = hq + L * SV;                       // [SV][L] R[f] . [v_t | 1]
-    float* gk = bb + L * SV;                       // [L][ks]
+    const int LP = L + 1, SVP = SV + 1;
+    const int64_t TAB = bwd_table_floats(SV, L);
+    float* hk = vv + L * cols;                     // [L][SVP] phi(k)
+    float* hq = hk + TAB;                          // [L][SVP] qw phi(q)
+    float* bb = hq + TAB;                          // [SV][LP] R[f] . [v_t | 1]
+    float* gk = bb + TAB;                          // [L][ks]
     uint32_t* sfi = reinterpret_cast<uint32_t*>(gk + L * ks);   // [SV] packed indices
     float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
     uint2* ent = reinterpret_cast<uint2*>(lds + ((sqw + SV - lds + 1) & ~int64_t(1)));  // plan
@@ -303,24 +311,24 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
             const bool live = F < a.M && t < nvalid;
-            hk[idx] = live ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
-            hq[idx] = live ? sqw[f] * feature_value_n<NIDX>(xq + t * ks, sfi[f]) : 0.0f;
+            hk[t * SVP + f] = live ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
+            hq[t * SVP + f] = live ? sqw[f] * feature_value_n<NIDX>(xq + t * ks, sfi[f]) : 0.0f;
         }
         __syncthreads();
         const int64_t pbase = ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L;
         // b_t[f] = R[f] . [v_t | 1] and the dv partial sum_f phi_f(k_t) R[f][j], against
         // the chunks after c
-        lds_gemm<kScanThreads>(L, SV, cols, vv, cols, 1, Rsl, 1, cols, [&](int t, int f, float c) { bb[f * L + t] = c; });
+        mfma_gemm<kScanThreads>(L, SV, cols, vv, cols, 1, Rsl, 1, cols, [&](int t, int f, float c) { bb[f * LP + t] = c; });
         float* pv = a.part2 + pbase * d_V;
-        lds_gemm<kScanThreads>(L, d_V, SV, hk, SV, 1, Rsl, cols, 1, [&](int t, int j, float c) { pv[t * d_V + j] = c; });
+        mfma_gemm<kScanThreads>(L, d_V, SV, hk, SVP, 1, Rsl, cols, 1, [&](int t, int j, float c) { pv[t * d_V + j] = c; });
         __syncthreads();
         // dk partial: sum_f b_t[f] d phi_f / dk
-        scatter_planned<NIDX>(gk, xk, bb, ent, wave_begin, L, ks, nvalid);
+        scatter_planned<NIDX>(gk, xk, bb, ent, wave_begin, L, LP, ks, nvalid);
         __syncthreads();
         float* pk = a.part + pbase * d_K;
         for (int idx = tid; idx < L * d_K; idx += kScanThreads) pk[idx] = gk[(idx / d_K) * ks + idx % d_K];
         // R += (qw phi(q))^T u with the chunk's queries
-        lds_gemm<kScanThreads>(SV, cols, L, hq, 1, SV, uu, cols, 1, [&](int f, int j, float c) { Rsl[f * cols + j] += c; });
+        mfma_gemm<kScanThreads>(SV, cols, L, hq, 1, SVP, uu, cols, 1, [&](int f, int j, float c) { Rsl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {

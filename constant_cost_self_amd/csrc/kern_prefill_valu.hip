@@ -21,7 +21,7 @@ namespace {
 
 __host__ __device__ inline int64_t valu_lds_floats(int SV, int d_K, int d_V, int L) {
     const int cols = d_V + 1;
-    return (int64_t)SV * cols + 2LL * L * (d_K + 1) + (int64_t)L * cols + (int64_t)L * SV + 2LL * SV;
+    return (int64_t)SV * cols + 2LL * L * (d_K + 1) + (int64_t)L * cols + (int64_t)L * (SV + 1) + 2LL * SV;
 }
 
 template <typename In, int NIDX>
@@ -38,8 +38,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
     float* xq = Ssl + SV * cols;                   // [L][d_K+1], coordinate d_K == 1
     float* xk = xq + L * (d_K + 1);                // [L][d_K+1]
     float* us = xk + L * (d_K + 1);                // [L][cols]
-    float* hat = us + L * cols;                    // [L][SV]
-    uint32_t* sfi = reinterpret_cast<uint32_t*>(hat + L * SV);   // [SV] packed indices
+    const int SVP = SV + 1;                        // row stride of 1 modulo 64 floats
+    float* hat = us + L * cols;                    // [L][SVP]
+    uint32_t* sfi = reinterpret_cast<uint32_t*>(hat + L * SVP);  // [SV] packed indices
     float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights
     for (int f = tid; f < SV; f += kScanThreads) {   // tables are M_pad long (padding: weight 0)
         const int64_t F = F0 + f;
@@ -76,24 +77,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? sqw[f] * feature_value_n<NIDX>(xq + t * (d_K + 1), sfi[f])
-                               : 0.0f;
+            hat[t * SVP + f] = F < a.M ? sqw[f] * feature_value_n<NIDX>(xq + t * (d_K + 1), sfi[f])
+                                       : 0.0f;
         }
         __syncthreads();
         // readout against the state of the chunks before c
         float* part = a.partial +
                       (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * cols;
-        lds_gemm<kScanThreads>(L, cols, SV, hat, SV, 1, Ssl, cols, 1, [&](int t, int j, float c) { part[j * L + t] = c; });
+        mfma_gemm<kScanThreads>(L, cols, SV, hat, SVP, 1, Ssl, cols, 1, [&](int t, int j, float c) { part[j * L + t] = c; });
         __syncthreads();
         // key features of the slice
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;
-            hat[idx] = F < a.M ? feature_value_n<NIDX>(xk + t * (d_K + 1), sfi[f]) : 0.0f;
+            hat[t * SVP + f] = F < a.M ? feature_value_n<NIDX>(xk + t * (d_K + 1), sfi[f]) : 0.0f;
         }
         __syncthreads();
         // state update with the chunk
-        lds_gemm<kScanThreads>(SV, cols, L, hat, 1, SV, us, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
+        mfma_gemm<kScanThreads>(SV, cols, L, hat, 1, SVP, us, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {

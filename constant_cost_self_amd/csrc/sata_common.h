@@ -160,4 +160,45 @@ __device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, 
         }
 }
 
+// The same contraction on the matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands and
+// accumulation), by the NT threads of a block.  A wave computes 16 x 16 output tiles, tile
+// w, w + NT/64, ...  In step j of a tile the 16 lanes of group g = lane / 16 take
+// k = g KQ + j (KQ = ceil(K / 4)): lane i + 16 g holds A(m0 + i, k) and B(k, n0 + i), and
+// register r of the accumulator is C(m0 + 4 g + r, n0 + i).  With row strides of 1 modulo
+// 64 floats (65, 129, L + 1, SV + 1) the 64 lanes of a load hit 64 different LDS banks.
+// Steps alternate between two accumulators so that consecutive MFMAs are independent.
+template <int NT, typename Out>
+__device__ inline void mfma_gemm(int Mo, int No, int K, const float* A, int sam, int sak, const float* B,
+                                 int sbk, int sbn, Out out) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int tiles_n = (No + 15) / 16, tiles = (Mo + 15) / 16 * tiles_n;
+    const int KQ = (K + 3) / 4;
+    for (int tile = w; tile < tiles; tile += NW) {
+        const int m0 = tile / tiles_n * 16, n0 = tile % tiles_n * 16;
+        const bool mv = m0 + i < Mo, nv = n0 + i < No;
+        const float* Ap = A + (mv ? m0 + i : 0) * sam;
+        const float* Bp = B + (nv ? n0 + i : 0) * sbn;
+        const int kb = g * KQ;
+        const int kl = K - kb < KQ ? K - kb : KQ;          // live steps of this lane group
+        f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < KQ; j += 2) {
+            const bool v0 = j < kl, v1 = j + 1 < kl;
+            const float a0 = (mv && v0) ? Ap[(kb + j) * sak] : 0.0f;
+            const float b0 = (nv && v0) ? Bp[(kb + j) * sbk] : 0.0f;
+            const float a1 = (mv && v1) ? Ap[(kb + j + 1) * sak] : 0.0f;
+            const float b1 = (nv && v1) ? Bp[(kb + j + 1) * sbk] : 0.0f;
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc1, 0, 0, 0);
+        }
+        const f32x4 acc = acc0 + acc1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * g + r;
+            if (m < Mo && nv) out(m, n0 + i, acc[r]);
+        }
+    }
+}
+
 }  // namespace sata
