@@ -157,42 +157,49 @@ __device__ inline void build_plan(const BwdArgs& a, int64_t F0, int SV, const ui
 
 // g[t][i] = sum over the plan entries (f, i) of this wave's coordinate range of
 // coef[f cs + t] m prod(other slots of x_t), lanes over tokens; rows t >= nvalid are written 0.
-// Entries are taken four at a time, all LDS reads of a group issued before its sums.
+// The wave's entries come in batches of 64, one per lane, and are read out of the lanes by
+// index (the range is uniform over the wave); then eight entries at a time, all their LDS
+// reads issued before their sums.
 template <int NIDX>
 __device__ inline void scatter_planned(float* __restrict__ g, const float* __restrict__ x,
                                        const float* __restrict__ coef, const uint2* __restrict__ ent,
                                        const int* __restrict__ wave_begin, int L, int cs, int ks, int nvalid) {
-    constexpr int U = 4;
+    constexpr int U = 8;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int e0 = wave_begin[w], e1 = wave_begin[w + 1];
+    const int e0 = __builtin_amdgcn_readfirstlane(wave_begin[w]);
+    const int e1 = __builtin_amdgcn_readfirstlane(wave_begin[w + 1]);
     for (int tb = 0; tb < L; tb += 64) {
         const int t = tb + lane;
         const int tt = t < L ? t : L - 1;
         const float* xr = x + tt * ks;
         const float* cr = coef + tt;
         float acc = 0.0f;
-        for (int e = e0; e < e1; e += U) {
-            uint32_t ex[U], ey[U];
-            float p[U];
+        for (int eb = e0; eb < e1; eb += 64) {
+            const int ne = e1 - eb < 64 ? e1 - eb : 64;
+            const uint2 mine = ent[eb + (lane < ne ? lane : ne - 1)];
+            for (int j = 0; j < ne; j += U) {
+                uint32_t ex[U], ey[U];
+                float p[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint2 en = ent[e + u < e1 ? e + u : e1 - 1];
-                ex[u] = __builtin_amdgcn_readfirstlane(en.x);
-                ey[u] = __builtin_amdgcn_readfirstlane(en.y);
-            }
+                for (int u = 0; u < U; ++u) {
+                    const int jj = j + u < ne ? j + u : ne - 1;
+                    ex[u] = __builtin_amdgcn_readlane(mine.x, jj);
+                    ey[u] = __builtin_amdgcn_readlane(mine.y, jj);
+                }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                p[u] = cr[(int)(ex[u] & 0xffffu) * cs] * (float)((ex[u] >> 24) & 7u);
+                for (int u = 0; u < U; ++u) {
+                    p[u] = cr[(int)(ex[u] & 0xffffu) * cs] * (float)((ex[u] >> 24) & 7u);
 #pragma unroll
-                for (int sl = 0; sl < NIDX - 1; ++sl) p[u] *= xr[(ey[u] >> (8 * sl)) & 0xffu];
-            }
+                    for (int sl = 0; sl < NIDX - 1; ++sl) p[u] *= xr[(ey[u] >> (8 * sl)) & 0xffu];
+                }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (e + u < e1) {
-                    acc += p[u];
-                    if (ex[u] >> 31) {
-                        if (t < L) g[t * ks + ((ex[u] >> 16) & 0xffu)] = t < nvalid ? acc : 0.0f;
-                        acc = 0.0f;
+                for (int u = 0; u < U; ++u) {
+                    if (j + u < ne) {
+                        acc += p[u];
+                        if (ex[u] >> 31) {
+                            if (t < L) g[t * ks + ((ex[u] >> 16) & 0xffu)] = t < nvalid ? acc : 0.0f;
+                            acc = 0.0f;
+                        }
                     }
                 }
             }

@@ -167,6 +167,7 @@ __device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, 
 // register r of the accumulator is C(m0 + 4 g + r, n0 + i).  With row strides of 1 modulo
 // 64 floats (65, 129, L + 1, SV + 1) the 64 lanes of a load hit 64 different LDS banks.
 // Steps alternate between two accumulators so that consecutive MFMAs are independent.
+// K >= 1.
 template <int NT, typename Out>
 __device__ inline void mfma_gemm(int Mo, int No, int K, const float* A, int sam, int sak, const float* B,
                                  int sbk, int sbn, Out out) {
@@ -178,19 +179,40 @@ __device__ inline void mfma_gemm(int Mo, int No, int K, const float* A, int sam,
     for (int tile = w; tile < tiles; tile += NW) {
         const int m0 = tile / tiles_n * 16, n0 = tile % tiles_n * 16;
         const bool mv = m0 + i < Mo, nv = n0 + i < No;
-        const float* Ap = A + (mv ? m0 + i : 0) * sam;
-        const float* Bp = B + (nv ? n0 + i : 0) * sbn;
+        const float* Ap = A + (mv ? m0 + i : Mo - 1) * sam;
+        const float* Bp = B + (nv ? n0 + i : No - 1) * sbn;
         const int kb = g * KQ;
         const int kl = K - kb < KQ ? K - kb : KQ;          // live steps of this lane group
+        // loads from clamped (always valid) positions: rows of A past Mo and columns of B past
+        // No only reach outputs that are dropped, and a dead step is zeroed on the A side
+        // alone; no branches, so the next four steps are loaded before the MFMAs
+        auto ld = [&](const float* p, int st, int j) {
+            const int k = kb + j < K ? kb + j : K - 1;
+            return p[k * st];
+        };
         f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int j = 0; j < KQ; j += 2) {
-            const bool v0 = j < kl, v1 = j + 1 < kl;
-            const float a0 = (mv && v0) ? Ap[(kb + j) * sak] : 0.0f;
-            const float b0 = (nv && v0) ? Bp[(kb + j) * sbk] : 0.0f;
-            const float a1 = (mv && v1) ? Ap[(kb + j + 1) * sak] : 0.0f;
-            const float b1 = (nv && v1) ? Bp[(kb + j + 1) * sbk] : 0.0f;
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc1, 0, 0, 0);
+        float ra[4], rb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            ra[u] = u < kl ? ld(Ap, sak, u) : 0.0f;
+            rb[u] = ld(Bp, sbk, u);
+        }
+        for (int j = 0; j < KQ; j += 4) {
+            float na[4], nb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                na[u] = j + 4 + u < kl ? ld(Ap, sak, j + 4 + u) : 0.0f;
+                nb[u] = ld(Bp, sbk, j + 4 + u);
+            }
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[0], rb[0], acc0, 0, 0, 0);
+            if (j + 1 < KQ) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[1], rb[1], acc1, 0, 0, 0);
+            if (j + 2 < KQ) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[2], rb[2], acc0, 0, 0, 0);
+            if (j + 3 < KQ) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[3], rb[3], acc1, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ra[u] = na[u];
+                rb[u] = nb[u];
+            }
         }
         const f32x4 acc = acc0 + acc1;
 #pragma unroll
