@@ -13,11 +13,11 @@ its own stream: achieved = algorithmic work per launch / mean launch time.
                 (the forward FLOPs/token closed form of the method), peak = bf16 MFMA
                 2.5 PFLOP/s.
   decode:       bytes = 8 (d_V + 1) M per head (fp32 state read + write), peak 8 TB/s.
-  backward:     (sata_prefill_backward on the Mid shape, fp32 on the vector ALUs)
-                flops = B H n [forward closed form + 2 M (4 (d_V + 1) + d_V)]: the fp32
-                forward recompute plus the five state contractions of the gradient
-                scans (S . u, S update, R . [v|1], phi(k) R, R update); peak = fp32
-                vector 157.3 TFLOP/s.
+  backward:     (sata_prefill_backward on the Mid shape, fp32 arithmetic, the state
+                contractions on the matrix cores) flops = B H n [forward closed form +
+                2 M (4 (d_V + 1) + d_V)]: the fp32 forward recompute plus the five state
+                contractions of the gradient scans (S . u, S update, R . [v|1], phi(k) R,
+                R update); peak = fp32 dense MFMA 157.3 TFLOP/s.
 cpu_baseline: the fp64 oracle's fixed-size-state form, timed on the host's cores
 on a bounded sample (one head, the first --cpu-tokens tokens).
 Prints one JSON line on stdout; progress goes to stderr.
@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
-VALU_FP32_PEAK_TFLOPS = 157.3
+MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
 def log(msg):
@@ -318,8 +318,8 @@ def main():
                         (bw.B, bw.H, bw.n, bw.d_K, bw.P, bw.chunk, bw.dtype),
             "value": bw.B * bw.n / (bwall / args.backward_steps), "unit": "tokens/s",
             "steps": args.backward_steps, "ms_per_step": bwall / args.backward_steps * 1e3,
-            "roofline": {"bound": "alu", "achieved": b_tflops, "peak": VALU_FP32_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": b_tflops / VALU_FP32_PEAK_TFLOPS,
+            "roofline": {"bound": "mfma", "achieved": b_tflops, "peak": MFMA_FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": b_tflops / MFMA_FP32_PEAK_TFLOPS,
                          "traffic": None, "kernel": "prefill backward (all kernels of one call)",
                          "ms_per_launch": b_ms / b_n, "algorithmic_flops_per_launch": bflops},
         }
