@@ -116,3 +116,26 @@ def test_backward_segmented_equals_single(torch_cuda):
 def test_backward_coordinates_past_one_wave(torch_cuda, dK, dV, P):
     """d_K > 64: the slice's gradient plan is built by more than one wave of threads."""
     check(torch_cuda, dK, dV, P, 70, 32, "f32", H=1, sigma=0.4, seed=dK)
+
+
+def test_backward_mid_full_size(torch_cuda):
+    """The benchmark's backward workload at full size (B=1 H=8 n=4096 d=64 P=4, chunk 64, bf16
+    inputs, dy drawn with seed 7, the default workspace cap: two segments), in the launch
+    configuration the benchmark times; the oracle checks three of the eight heads whole."""
+    torch = torch_cuda
+    w = inputs.MID
+    x = inputs.prefill_inputs(w)
+    dy = np.random.default_rng(7).standard_normal((w.B, w.H, w.n, w.d_V)).astype(np.float32)
+    t = sata.sata_tables_build(w.d_K, w.P)
+    try:
+        got = run_backward(torch, t, x, w.dtype, dy, w.chunk)
+    finally:
+        t.close()
+    heads = [0, 3, 7]
+    ref = oracle.direct_grad(x["q"][:, heads], x["k"][:, heads], x["v"][:, heads], dy[:, heads], w.P)
+    errs = [grad_err(g[:, heads], r, dy[:, heads]) for g, r in zip(got, ref)]
+    say("  backward full Mid, heads %s: dq %.2e dk %.2e dv %.2e" % (heads, *errs))
+    for name, e in zip(("dq", "dk", "dv"), errs):
+        assert e <= TOL_GRAD, (name, e)
+    for g in got:
+        assert np.all(np.isfinite(g))
