@@ -183,35 +183,68 @@ __device__ inline void mfma_gemm(int Mo, int No, int K, const float* A, int sam,
         const float* Bp = B + (nv ? n0 + i : No - 1) * sbn;
         const int kb = g * KQ;
         const int kl = K - kb < KQ ? K - kb : KQ;          // live steps of this lane group
-        // loads from clamped (always valid) positions: rows of A past Mo and columns of B past
-        // No only reach outputs that are dropped, and a dead step is zeroed on the A side
-        // alone; no branches, so the next four steps are loaded before the MFMAs
-        auto ld = [&](const float* p, int st, int j) {
-            const int k = kb + j < K ? kb + j : K - 1;
-            return p[k * st];
-        };
+        // steps live in every lane group, in whole groups of four: no clamps, one address
+        // add per load
+        const int jm = (K - 3 * KQ > 0 ? K - 3 * KQ : 0) & ~3;
         f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-        float ra[4], rb[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            ra[u] = u < kl ? ld(Ap, sak, u) : 0.0f;
-            rb[u] = ld(Bp, sbk, u);
-        }
-        for (int j = 0; j < KQ; j += 4) {
-            float na[4], nb[4];
+        const float* pa = Ap + kb * sak;
+        const float* pb = Bp + kb * sbk;
+        // two register sets take turns, so the next group's operands are loaded before this
+        // group's MFMAs without copies between them
+        auto ld4 = [&](float* ra, float* rb) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                na[u] = j + 4 + u < kl ? ld(Ap, sak, j + 4 + u) : 0.0f;
-                nb[u] = ld(Bp, sbk, j + 4 + u);
+                ra[u] = pa[u * sak];
+                rb[u] = pb[u * sbk];
             }
+            pa += 4 * sak;
+            pb += 4 * sbk;
+        };
+        auto mma4 = [&](const float* ra, const float* rb) {
             acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[0], rb[0], acc0, 0, 0, 0);
-            if (j + 1 < KQ) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[1], rb[1], acc1, 0, 0, 0);
-            if (j + 2 < KQ) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[2], rb[2], acc0, 0, 0, 0);
-            if (j + 3 < KQ) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[3], rb[3], acc1, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[1], rb[1], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[2], rb[2], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[3], rb[3], acc1, 0, 0, 0);
+        };
+        // (the loop body has no branches, so the compiler can wait for the older set alone)
+        float xa[4], xb[4], ya[4], yb[4];
+        if (jm > 0) {
+            ld4(xa, xb);                                 // group 0
+            int j = 0;
+            for (; j + 12 <= jm; j += 8) {               // groups j + 4 and j + 8 exist
+                ld4(ya, yb);
+                __builtin_amdgcn_sched_barrier(0);       // keep each group's loads ahead
+                mma4(xa, xb);
+                __builtin_amdgcn_sched_barrier(0);
+                ld4(xa, xb);
+                __builtin_amdgcn_sched_barrier(0);
+                mma4(ya, yb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (j + 8 <= jm) {                           // groups j and j + 4 remain
+                ld4(ya, yb);
+                mma4(xa, xb);
+                mma4(ya, yb);
+            } else {                                     // group j remains
+                mma4(xa, xb);
+            }
+        }
+        // the rest (at most 7 steps): loads from clamped, always valid positions, all issued
+        // first; rows of A past Mo and columns of B past No only reach outputs that are
+        // dropped, and a dead step is zeroed on the A side alone
+        if (jm < KQ) {
+            float ta[8], tb[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ra[u] = na[u];
-                rb[u] = nb[u];
+            for (int u = 0; u < 8; ++u) {
+                const int j = jm + u;
+                const int k = kb + j < K ? kb + j : K - 1;
+                ta[u] = j < kl ? Ap[k * sak] : 0.0f;
+                tb[u] = Bp[k * sbk];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u += 2) {
+                if (jm + u < KQ) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[u], tb[u], acc0, 0, 0, 0);
+                if (jm + u + 1 < KQ) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[u + 1], tb[u + 1], acc1, 0, 0, 0);
             }
         }
         const f32x4 acc = acc0 + acc1;
