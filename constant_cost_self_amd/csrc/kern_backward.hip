@@ -50,7 +50,7 @@ __host__ __device__ inline int64_t bwd_scan_lds_floats(int SV, int d_K, int d_V,
     int64_t base = (int64_t)SV * cols + 2LL * L * ks + 2LL * L * cols + 3 * bwd_table_floats(SV, L) +
                    (int64_t)L * ks + 2LL * SV;
     base += base & 1;
-    return base + 2LL * kMaxSlots * SV + (d_K + 1) + (kScanWaves + 1);
+    return base + 2LL * kMaxSlots * SV + (d_K + 1) + (kScanWaves + 1) + kScanWaves;
 }
 
 // LDS floats of the finalize: x_q, x_k, [v | 1], u, and two L x (L + 1) pair tables
@@ -100,15 +100,20 @@ __device__ inline void stage_slice(const BwdArgs& a, int64_t F0, int SV, uint32_
 // Scatter plan of a slice, built once per block.  When coordinate i fills m of the slots of
 // feature f, d phi_f / d x_i = m x_i^(m-1) prod(other slots), so the slice's gradient along i
 // sums one entry per feature holding i.  The entries are grouped by coordinate (the
-// constant-1 slot has no gradient) and the coordinates are split into one contiguous range
-// per wave with about equal entry counts.  A wave then sums every (token, coordinate) of its
-// range in one lane's register and writes it once: no two waves write one place, and no LDS
-// atomics are needed.
-// Entry: x = feature | coordinate << 16 | m << 24 | (last entry of its coordinate) << 31,
+// constant-1 slot has no gradient) and split into eight equal ranges, one per wave (one
+// coordinate of a slice can hold every feature, so ranges of whole coordinates would leave
+// waves idle).  A wave sums each run of one coordinate in its range, for every token, in one
+// lane's register and writes it once.  The run that holds a coordinate's first entry is
+// written into the gradient rows; a wave whose range starts inside a coordinate writes that
+// first run to its own carry row instead, and the copy-out adds the carries: no two waves
+// write one place, and no LDS atomics are needed.
+// Entry: x = feature | coordinate << 16 | m << 24 | (first entry of its coordinate) << 30
+//            | (last entry of its coordinate) << 31,
 //        y = the other NIDX - 1 slots (one copy of the coordinate taken out), 8 bits each.
+// carry_coord[w]: the coordinate of wave w's carry row, or -1.
 template <int NIDX>
 __device__ inline void build_plan(const BwdArgs& a, int64_t F0, int SV, const uint32_t* sfi, uint2* ent,
-                                  int* off, int* wave_begin) {
+                                  int* off, int* wave_begin, int* carry_coord) {
     const int tid = threadIdx.x, d_K = a.d_K;
     const int nf = (int)((a.M - F0) < SV ? (a.M - F0) : SV);     // live features of the slice
     __syncthreads();                                              // sfi is written by other waves
@@ -126,12 +131,8 @@ __device__ inline void build_plan(const BwdArgs& a, int64_t F0, int SV, const ui
     if (tid == 0) {
         off[0] = 0;
         for (int i = 0; i < d_K; ++i) off[i + 1] += off[i];
-        const int64_t E = off[d_K];
-        int w = 1;
-        wave_begin[0] = 0;
-        for (int i = 0; i < d_K; ++i)
-            while (w < kScanWaves && (int64_t)off[i + 1] * kScanWaves >= w * E) wave_begin[w++] = off[i + 1];
-        for (; w <= kScanWaves; ++w) wave_begin[w] = (int)E;
+        const int E = off[d_K];
+        for (int w = 0; w <= kScanWaves; ++w) wave_begin[w] = E * w / kScanWaves;
     }
     __syncthreads();
     if (tid < d_K) {
@@ -147,23 +148,31 @@ __device__ inline void build_plan(const BwdArgs& a, int64_t F0, int SV, const ui
                 others |= c << (8 * no++);
             }
             if (m) {
+                const uint32_t first = pos == off[tid] ? 1u << 30 : 0u;
                 const uint32_t last = pos + 1 == end ? 1u << 31 : 0u;
-                ent[pos++] = make_uint2((uint32_t)f | (uint32_t)tid << 16 | m << 24 | last, others);
+                ent[pos++] = make_uint2((uint32_t)f | (uint32_t)tid << 16 | m << 24 | first | last, others);
             }
         }
     }
     __syncthreads();
+    if (tid < kScanWaves) {
+        const int e = wave_begin[tid];
+        carry_coord[tid] = (e < wave_begin[tid + 1] && !((ent[e].x >> 30) & 1u)) ? (int)((ent[e].x >> 16) & 0xffu) : -1;
+    }
+    __syncthreads();
 }
 
-// g[t][i] = sum over the plan entries (f, i) of this wave's coordinate range of
-// coef[f cs + t] m prod(other slots of x_t), lanes over tokens; rows t >= nvalid are written 0.
+// g[t][i] = sum over the plan entries (f, i) of this wave's range of coef[f cs + t] m prod(other
+// slots of x_t), lanes over tokens; rows t >= nvalid are written 0.  A first run that continues
+// the previous wave's coordinate goes to carry[w L + t] instead.
 // The wave's entries come in batches of 64, one per lane, and are read out of the lanes by
 // index (the range is uniform over the wave); then eight entries at a time, all their LDS
 // reads issued before their sums.
 template <int NIDX>
 __device__ inline void scatter_planned(float* __restrict__ g, const float* __restrict__ x,
                                        const float* __restrict__ coef, const uint2* __restrict__ ent,
-                                       const int* __restrict__ wave_begin, int L, int cs, int ks, int nvalid) {
+                                       const int* __restrict__ wave_begin, const int* __restrict__ carry_coord,
+                                       float* __restrict__ carry, int L, int cs, int ks, int nvalid) {
     constexpr int U = 8;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int e0 = __builtin_amdgcn_readfirstlane(wave_begin[w]);
@@ -174,6 +183,7 @@ __device__ inline void scatter_planned(float* __restrict__ g, const float* __res
         const float* xr = x + tt * ks;
         const float* cr = coef + tt;
         float acc = 0.0f;
+        bool owner = __builtin_amdgcn_readfirstlane(carry_coord[w]) < 0;
         for (int eb = e0; eb < e1; eb += 64) {
             const int ne = e1 - eb < 64 ? e1 - eb : 64;
             const uint2 mine = ent[eb + (lane < ne ? lane : ne - 1)];
@@ -196,13 +206,45 @@ __device__ inline void scatter_planned(float* __restrict__ g, const float* __res
                 for (int u = 0; u < U; ++u) {
                     if (j + u < ne) {
                         acc += p[u];
-                        if (ex[u] >> 31) {
-                            if (t < L) g[t * ks + ((ex[u] >> 16) & 0xffu)] = t < nvalid ? acc : 0.0f;
+                        if ((ex[u] >> 31) || eb + j + u + 1 == e1) {     // end of a run
+                            const float r = t < nvalid ? acc : 0.0f;
+                            if (t < L) {
+                                if (owner) g[t * ks + ((ex[u] >> 16) & 0xffu)] = r;
+                                else carry[w * L + t] = r;
+                            }
+                            owner = true;
                             acc = 0.0f;
                         }
                     }
                 }
             }
+        }
+    }
+}
+
+// part[t][i] = g[t][i] plus the carry rows of coordinate i (t < L, i < d_K), all threads.
+// Columns without a carry are copied by the first loop (uniform compares, no extra loads);
+// each carried column is written once by the second, from the first wave that carries it
+// (the waves carrying one coordinate are consecutive).
+__device__ inline void copy_grad_rows(float* part, const float* g, const float* carry, const int* carry_coord,
+                                      int L, int d_K, int ks) {
+    int cc[kScanWaves];
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) cc[w] = __builtin_amdgcn_readfirstlane(carry_coord[w]);
+    for (int idx = threadIdx.x; idx < L * d_K; idx += kScanThreads) {
+        const int t = idx / d_K, i = idx % d_K;
+        bool carried = false;
+#pragma unroll
+        for (int w = 1; w < kScanWaves; ++w) carried |= cc[w] == i;
+        if (!carried) part[idx] = g[t * ks + i];
+    }
+    for (int idx = threadIdx.x; idx < (kScanWaves - 1) * L; idx += kScanThreads) {
+        const int w = 1 + idx / L, t = idx % L;
+        const int c = carry_coord[w];
+        if (c >= 0 && carry_coord[w - 1] != c) {
+            float v = g[t * ks + c];
+            for (int w2 = w; w2 < kScanWaves && carry_coord[w2] == c; ++w2) v += carry[w2 * L + t];
+            part[t * d_K + c] = v;
         }
     }
 }
@@ -228,9 +270,10 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     uint2* ent = reinterpret_cast<uint2*>(lds + ((sqw + SV - lds + 1) & ~int64_t(1)));  // plan
     int* off = reinterpret_cast<int*>(ent + kMaxSlots * SV);
     int* wave_begin = off + d_K + 1;
+    int* carry_coord = wave_begin + kScanWaves + 1;
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
     stage_slice(a, F0, SV, sfi, sqw);
-    build_plan<NIDX>(a, F0, SV, sfi, ent, off, wave_begin);
+    build_plan<NIDX>(a, F0, SV, sfi, ent, off, wave_begin, carry_coord);
 
     for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
@@ -250,10 +293,11 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
                                 [&](int t, int f, float c) { hat[f * LP + t] = c * sqw[f]; });
         __syncthreads();
         // dq partial: sum_f qw_f a_T[f] d phi_f / dq
-        scatter_planned<NIDX>(gq, xq, hat, ent, wave_begin, L, LP, ks, nvalid);
+        float* carry = hat + bwd_table_floats(SV, L);      // [waves][L] in the unused second table
+        scatter_planned<NIDX>(gq, xq, hat, ent, wave_begin, carry_coord, carry, L, LP, ks, nvalid);
         __syncthreads();
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
-        for (int idx = tid; idx < L * d_K; idx += kScanThreads) part[idx] = gq[(idx / d_K) * ks + idx % d_K];
+        copy_grad_rows(part, gq, carry, carry_coord, L, d_K, ks);
         // key features, then the update S += phi(k)^T [v | 1]
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
@@ -297,9 +341,10 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
     uint2* ent = reinterpret_cast<uint2*>(lds + ((sqw + SV - lds + 1) & ~int64_t(1)));  // plan
     int* off = reinterpret_cast<int*>(ent + kMaxSlots * SV);
     int* wave_begin = off + d_K + 1;
+    int* carry_coord = wave_begin + kScanWaves + 1;
     float* state = a.state + bh * (int64_t)cols * a.M_pad;
     stage_slice(a, F0, SV, sfi, sqw);
-    build_plan<NIDX>(a, F0, SV, sfi, ent, off, wave_begin);
+    build_plan<NIDX>(a, F0, SV, sfi, ent, off, wave_begin, carry_coord);
 
     for (int idx = tid; idx < SV * cols; idx += kScanThreads) {
         const int f = idx / cols, j = idx % cols;
@@ -330,10 +375,11 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
         mfma_gemm<kScanThreads>(L, d_V, SV, hk, SVP, 1, Rsl, cols, 1, [&](int t, int j, float c) { pv[t * d_V + j] = c; });
         __syncthreads();
         // dk partial: sum_f b_t[f] d phi_f / dk
-        scatter_planned<NIDX>(gk, xk, bb, ent, wave_begin, L, LP, ks, nvalid);
+        // the carry rows take the key-feature table, which the dv partial has finished with
+        scatter_planned<NIDX>(gk, xk, bb, ent, wave_begin, carry_coord, hk, L, LP, ks, nvalid);
         __syncthreads();
         float* pk = a.part + pbase * d_K;
-        for (int idx = tid; idx < L * d_K; idx += kScanThreads) pk[idx] = gk[(idx / d_K) * ks + idx % d_K];
+        copy_grad_rows(pk, gk, hk, carry_coord, L, d_K, ks);
         // R += (qw phi(q))^T u with the chunk's queries
         mfma_gemm<kScanThreads>(SV, cols, L, hq, 1, SVP, uu, cols, 1, [&](int f, int j, float c) { Rsl[f * cols + j] += c; });
     }
