@@ -59,6 +59,44 @@ __host__ __device__ inline int64_t bwd_fin_lds_floats(int d_K, int d_V, int L) {
     return 2LL * L * d_K + 2LL * L * cols + 2LL * L * (L + 1);
 }
 
+// The chunk's q, k, v and u rows staged in registers (see RowStage).
+template <typename In>
+struct ChunkStage {
+    RowStage<In, kScanThreads, 2> q, k, v;
+    RowStage<InF32, kScanThreads, 3> u;
+    __device__ static bool fits(const BwdArgs& a) {
+        return RowStage<In, kScanThreads, 2>::fits(a.L, a.d_K) && RowStage<In, kScanThreads, 2>::fits(a.L, a.d_V) &&
+               RowStage<InF32, kScanThreads, 3>::fits(a.L, a.ucols);
+    }
+    __device__ void issue(const BwdArgs& a, int64_t bh, int c) {
+        using T = typename In::T;
+        const int64_t t0 = (int64_t)c * a.L;
+        const int nvalid = (int)((a.n - t0) < a.L ? (a.n - t0) : a.L);
+        q.issue(static_cast<const T*>(a.q) + bh * a.n * a.d_K, t0, nvalid, a.L, a.d_K);
+        k.issue(static_cast<const T*>(a.k) + bh * a.n * a.d_K, t0, nvalid, a.L, a.d_K);
+        v.issue(static_cast<const T*>(a.v) + bh * a.n * a.d_V, t0, nvalid, a.L, a.d_V);
+        u.issue(a.u + bh * a.n * a.ucols, t0, nvalid, a.L, a.ucols);
+    }
+    __device__ void commit(const BwdArgs& a, float* xq, float* xk, float* uu, float* vv) const {
+        const int cols = a.d_V + 1, ks = a.d_K + 1;
+        q.commit(xq, ks, a.L, a.d_K, a.d_K);
+        k.commit(xk, ks, a.L, a.d_K, a.d_K);
+        v.commit(vv, cols, a.L, a.d_V, a.d_V);
+        u.commit(uu, cols, a.L, a.ucols, cols);
+    }
+};
+
+// coordinate d_K is the constant 1; the last column of [v | 1] is 1 for the tokens
+__device__ inline void chunk_constants(const BwdArgs& a, int nvalid, float* xq, float* xk, float* vv) {
+    const int d_K = a.d_K, d_V = a.d_V, cols = d_V + 1, ks = d_K + 1;
+    for (int t = threadIdx.x; t < a.L; t += kScanThreads) {
+        xq[t * ks + d_K] = 1.0f;
+        xk[t * ks + d_K] = 1.0f;
+        vv[t * cols + d_V] = t < nvalid ? 1.0f : 0.0f;
+    }
+}
+
+// The chunk's rows straight from global memory (when they do not fit a ChunkStage).
 template <typename In>
 __device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int nvalid, float* xq,
                                   float* xk, float* uu, float* vv) {
@@ -78,12 +116,6 @@ __device__ inline void load_chunk(const BwdArgs& a, int64_t bh, int64_t t0, int 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (4 * c + e < cols) uu[t * cols + 4 * c + e] = xv[e];
-    }
-    // coordinate d_K is the constant 1; the last column of [v | 1] is 1 for the tokens
-    for (int t = threadIdx.x; t < L; t += kScanThreads) {
-        xq[t * ks + d_K] = 1.0f;
-        xk[t * ks + d_K] = 1.0f;
-        vv[t * cols + d_V] = t < nvalid ? 1.0f : 0.0f;
     }
 }
 
@@ -281,13 +313,19 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         Ssl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
     }
     const int nch = a.c_end - a.c_begin;
+    ChunkStage<In> stage;
+    const bool staged = ChunkStage<In>::fits(a);
+    if (staged) stage.issue(a, bh, a.c_begin);
     for (int c = a.c_begin; c < a.c_end; ++c) {
         const int64_t t0 = (int64_t)c * L;
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
-        load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
+        if (staged) stage.commit(a, xq, xk, uu, vv);
+        else load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
+        chunk_constants(a, nvalid, xq, xk, vv);
         for (int idx = tid; idx < L * ks; idx += kScanThreads) gq[idx] = 0.0f;
         __syncthreads();
+        if (staged && c + 1 < a.c_end) stage.issue(a, bh, c + 1);     // in flight during this chunk
         // qw_f a_T[f], a_T[f] = S[f] . u_T against the state before the chunk, stored [f][t]
         mfma_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols,
                                 [&](int t, int f, float c) { hat[f * LP + t] = c * sqw[f]; });
@@ -352,13 +390,19 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
         Rsl[idx] = (a.load_state && F < a.M_pad) ? state[(int64_t)j * a.M_pad + F] : 0.0f;
     }
     const int nch = a.c_end - a.c_begin;
+    ChunkStage<In> stage;
+    const bool staged = ChunkStage<In>::fits(a);
+    if (staged) stage.issue(a, bh, a.c_end - 1);
     for (int c = a.c_end - 1; c >= a.c_begin; --c) {
         const int64_t t0 = (int64_t)c * L;
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
-        load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
+        if (staged) stage.commit(a, xq, xk, uu, vv);
+        else load_chunk<In>(a, bh, t0, nvalid, xq, xk, uu, vv);
+        chunk_constants(a, nvalid, xq, xk, vv);
         for (int idx = tid; idx < L * ks; idx += kScanThreads) gk[idx] = 0.0f;
         __syncthreads();
+        if (staged && c > a.c_begin) stage.issue(a, bh, c - 1);      // in flight during this chunk
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;
             const int64_t F = F0 + f;

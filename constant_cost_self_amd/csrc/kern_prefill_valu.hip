@@ -60,19 +60,38 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
     }
 
     const int nch = a.c_end - a.c_begin;
+    // the next chunk's rows are loaded into registers while this chunk is computed
+    using Stage = RowStage<In, kScanThreads, 2>;
+    Stage sq, sk, sv;
+    const bool staged = Stage::fits(L, d_K) && Stage::fits(L, d_V);
+    auto issue = [&](int c) {
+        const int64_t t0 = (int64_t)c * L;
+        const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
+        sq.issue(q, t0, nvalid, L, d_K);
+        sk.issue(k, t0, nvalid, L, d_K);
+        sv.issue(v, t0, nvalid, L, d_V);
+    };
+    if (staged) issue(a.c_begin);
     for (int c = a.c_begin; c < a.c_end; ++c) {
         const int64_t t0 = (int64_t)c * L;
         const int nvalid = (int)((a.n - t0) < L ? (a.n - t0) : L);
         __syncthreads();
-        load_rows<In, kScanThreads>(q, t0, nvalid, L, d_K, xq, d_K + 1);
-        load_rows<In, kScanThreads>(k, t0, nvalid, L, d_K, xk, d_K + 1);
-        load_rows<In, kScanThreads>(v, t0, nvalid, L, d_V, us, cols);
+        if (staged) {
+            sq.commit(xq, d_K + 1, L, d_K, d_K);
+            sk.commit(xk, d_K + 1, L, d_K, d_K);
+            sv.commit(us, cols, L, d_V, d_V);
+        } else {
+            load_rows<In, kScanThreads>(q, t0, nvalid, L, d_K, xq, d_K + 1);
+            load_rows<In, kScanThreads>(k, t0, nvalid, L, d_K, xk, d_K + 1);
+            load_rows<In, kScanThreads>(v, t0, nvalid, L, d_V, us, cols);
+        }
         for (int t = tid; t < L; t += kScanThreads) {      // coordinate d_K == 1; u = [v | 1]
             xq[t * (d_K + 1) + d_K] = 1.0f;
             xk[t * (d_K + 1) + d_K] = 1.0f;
             us[t * cols + d_V] = t < nvalid ? 1.0f : 0.0f;
         }
         __syncthreads();
+        if (staged && c + 1 < a.c_end) issue(c + 1);        // in flight during this chunk
         // weighted query features of the slice
         for (int idx = tid; idx < L * SV; idx += kScanThreads) {
             const int t = idx / SV, f = idx % SV;

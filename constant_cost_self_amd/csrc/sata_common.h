@@ -99,6 +99,52 @@ __device__ inline void load_rows(const typename In::T* src, int64_t row0, int nv
     }
 }
 
+// The rows of one chunk held in registers between their global load and their LDS write,
+// so that the next chunk's loads are in flight while the current chunk is computed.  A
+// thread holds up to MAXP 16-byte pieces (piece idx = tid + p NT of the L x pr pieces, row
+// idx / pr); fits() says whether the rows are whole 16-byte pieces that MAXP pieces per
+// thread cover, and the caller loads with load_rows otherwise.  Rows t >= nvalid are zero.
+template <typename In, int NT, int MAXP>
+struct RowStage {
+    using T = typename In::T;
+    static constexpr int VE = 16 / sizeof(T);
+    uint4 r[MAXP];
+    __device__ static bool fits(int L, int d) {
+        return (d * (int)sizeof(T)) % 16 == 0 && L * (d / VE) <= MAXP * NT;
+    }
+    __device__ void issue(const T* src, int64_t row0, int nvalid, int L, int d) {
+        const int pr = d / VE;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const int idx = threadIdx.x + p * NT, t = idx / pr, c = idx % pr;
+            r[p] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < L * pr && t < nvalid) r[p] = *reinterpret_cast<const uint4*>(src + (row0 + t) * d + c * VE);
+        }
+    }
+    // dst[t * ds + i] for the first dcols elements of each row
+    __device__ void commit(float* dst, int ds, int L, int d, int dcols) const {
+        const int pr = d / VE;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const int idx = threadIdx.x + p * NT, t = idx / pr, c = idx % pr;
+            if (idx >= L * pr) continue;
+            float* o = dst + t * ds + c * VE;
+            const uint32_t w[4] = {r[p].x, r[p].y, r[p].z, r[p].w};
+            if (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (c * VE + 2 * e < dcols) o[2 * e] = __uint_as_float(w[e] << 16);
+                    if (c * VE + 2 * e + 1 < dcols) o[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c * VE + e < dcols) o[e] = __uint_as_float(w[e]);
+            }
+        }
+    }
+};
+
 // C(m, n) = sum_{k < K} A(m, k) B(k, n) for m < Mo, n < No, with A(m, k) = A[m sam + k sak]
 // and B(k, n) = B[k sbk + n sbn] in LDS, by the NT threads of a block; out(m, n, c)
 // receives each result.  Every 64 x 64 output block is split into register tiles of
