@@ -337,10 +337,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
         copy_grad_rows(part, gq, carry, carry_coord, L, d_K, ks);
         // key features, then the update S += phi(k)^T [v | 1]
-        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
-            const int t = idx / SV, f = idx % SV;
-            const int64_t F = F0 + f;
-            hat[t * SVP + f] = F < a.M ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
+        {   // a thread owns feature tid % SV (a power of two) for tokens tid / SV + k NT / SV
+            const int f = tid & (SV - 1);
+            const bool live = F0 + f < a.M;
+            const uint32_t fi = sfi[f];
+            for (int t = tid / SV; t < L; t += kScanThreads / SV)
+                hat[t * SVP + f] = live ? feature_value_n<NIDX>(xk + t * ks, fi) : 0.0f;
         }
         __syncthreads();
         mfma_gemm<kScanThreads>(SV, cols, L, hat, 1, SVP, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
@@ -403,12 +405,16 @@ __global__ __launch_bounds__(kScanThreads) void bwd_kv_kernel(BwdArgs a) {
         for (int idx = tid; idx < L * ks; idx += kScanThreads) gk[idx] = 0.0f;
         __syncthreads();
         if (staged && c > a.c_begin) stage.issue(a, bh, c - 1);      // in flight during this chunk
-        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
-            const int t = idx / SV, f = idx % SV;
-            const int64_t F = F0 + f;
-            const bool live = F < a.M && t < nvalid;
-            hk[t * SVP + f] = live ? feature_value_n<NIDX>(xk + t * ks, sfi[f]) : 0.0f;
-            hq[t * SVP + f] = live ? sqw[f] * feature_value_n<NIDX>(xq + t * ks, sfi[f]) : 0.0f;
+        {   // a thread owns feature tid % SV (a power of two) for tokens tid / SV + k NT / SV
+            const int f = tid & (SV - 1);
+            const bool fl = F0 + f < a.M;
+            const uint32_t fi = sfi[f];
+            const float w = sqw[f];
+            for (int t = tid / SV; t < L; t += kScanThreads / SV) {
+                const bool live = fl && t < nvalid;
+                hk[t * SVP + f] = live ? feature_value_n<NIDX>(xk + t * ks, fi) : 0.0f;
+                hq[t * SVP + f] = live ? w * feature_value_n<NIDX>(xq + t * ks, fi) : 0.0f;
+            }
         }
         __syncthreads();
         const int64_t pbase = ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L;
@@ -561,6 +567,7 @@ hipError_t launch_lds(K kernel, dim3 grid, int threads, size_t lds, const BwdArg
 
 }  // namespace
 
+// a power of two no larger than the block (the feature loops rely on it)
 int bwd_slice_feats(int d_K, int d_V, int L) {
     for (int SV = 128; SV >= 16; SV >>= 1)
         if (bwd_scan_lds_floats(SV, d_K, d_V, L) * 4 <= 150 * 1024) return SV;

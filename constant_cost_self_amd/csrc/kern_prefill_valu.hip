@@ -93,12 +93,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         __syncthreads();
         if (staged && c + 1 < a.c_end) issue(c + 1);        // in flight during this chunk
         // weighted query features of the slice
-        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
-            const int t = idx / SV, f = idx % SV;
-            const int64_t F = F0 + f;
-            hat[t * SVP + f] = F < a.M ? sqw[f] * feature_value_n<NIDX>(xq + t * (d_K + 1), sfi[f])
-                                       : 0.0f;
-        }
+        // (a thread owns feature tid % SV, a power of two, for tokens tid / SV + k NT / SV)
+        const int fo = tid & (SV - 1);
+        const bool flive = F0 + fo < a.M;
+        const uint32_t fi = sfi[fo];
+        const float fw = sqw[fo];
+        for (int t = tid / SV; t < L; t += kScanThreads / SV)
+            hat[t * SVP + fo] = flive ? fw * feature_value_n<NIDX>(xq + t * (d_K + 1), fi) : 0.0f;
         __syncthreads();
         // readout against the state of the chunks before c
         float* part = a.partial +
@@ -106,11 +107,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
         mfma_gemm<kScanThreads>(L, cols, SV, hat, SVP, 1, Ssl, cols, 1, [&](int t, int j, float c) { part[j * L + t] = c; });
         __syncthreads();
         // key features of the slice
-        for (int idx = tid; idx < L * SV; idx += kScanThreads) {
-            const int t = idx / SV, f = idx % SV;
-            const int64_t F = F0 + f;
-            hat[t * SVP + f] = F < a.M ? feature_value_n<NIDX>(xk + t * (d_K + 1), sfi[f]) : 0.0f;
-        }
+        for (int t = tid / SV; t < L; t += kScanThreads / SV)
+            hat[t * SVP + fo] = flive ? feature_value_n<NIDX>(xk + t * (d_K + 1), fi) : 0.0f;
         __syncthreads();
         // state update with the chunk
         mfma_gemm<kScanThreads>(SV, cols, L, hat, 1, SVP, us, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
@@ -127,6 +125,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_valu_kernel(PrefillSegArgs 
 
 }  // namespace
 
+// a power of two no larger than the block (the feature loops rely on it)
 int valu_slice_feats(int d_K, int d_V, int L) {
     for (int SV = 256; SV >= 16; SV >>= 1)
         if (valu_lds_floats(SV, d_K, d_V, L) * 4 <= 96 * 1024) return SV;
