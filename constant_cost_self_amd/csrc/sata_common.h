@@ -207,26 +207,32 @@ __device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, 
 }
 
 // The same contraction on the matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands and
-// accumulation), by the NT threads of a block.  A wave computes 16 x 16 output tiles, tile
-// w, w + NT/64, ...  In step j of a tile the 16 lanes of group g = lane / 16 take
+// accumulation), by the NT threads of a block.  A wave computes units of two 16 x 16 output
+// tiles side by side (rows m0.., columns n0.. and n0 + 16..), which share the A operand:
+// unit w, w + NT/64, ...  In step j of a unit the 16 lanes of group g = lane / 16 take
 // k = g KQ + j (KQ = ceil(K / 4)): lane i + 16 g holds A(m0 + i, k) and B(k, n0 + i), and
-// register r of the accumulator is C(m0 + 4 g + r, n0 + i).  With row strides of 1 modulo
-// 64 floats (65, 129, L + 1, SV + 1) the 64 lanes of a load hit 64 different LDS banks.
-// Steps alternate between two accumulators so that consecutive MFMAs are independent.
-// K >= 1.
+// register r of a tile's accumulator is C(m0 + 4 g + r, n0 + i).  With row strides of 1
+// modulo 64 floats (65, 129, L + 1, SV + 1) the 64 lanes of a load hit 64 different LDS
+// banks.  A last column past whole pairs of tiles (the normaliser of [v | 1], No = 32 q + 1)
+// is a dot product per row on the vector ALUs instead of a unit of its own.  K >= 1.
 template <int NT, typename Out>
 __device__ inline void mfma_gemm(int Mo, int No, int K, const float* A, int sam, int sak, const float* B,
                                  int sbk, int sbn, Out out) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i = lane & 15, g = lane >> 4;
-    const int tiles_n = (No + 15) / 16, tiles = (Mo + 15) / 16 * tiles_n;
+    const int rem = (No % 32 == 1 && No > 32) ? 1 : 0;
+    const int Nm = No - rem;
+    const int pairs_n = (Nm + 31) / 32, units = (Mo + 15) / 16 * pairs_n;
     const int KQ = (K + 3) / 4;
-    for (int tile = w; tile < tiles; tile += NW) {
-        const int m0 = tile / tiles_n * 16, n0 = tile % tiles_n * 16;
-        const bool mv = m0 + i < Mo, nv = n0 + i < No;
+    for (int unit = w; unit < units; unit += NW) {
+        const int m0 = unit / pairs_n * 16, n0 = unit % pairs_n * 32;
+        const bool mv = m0 + i < Mo, nv0 = n0 + i < Nm, nv1 = n0 + 16 + i < Nm;
+        // rows of A past Mo and columns of B past Nm are read from valid places and only
+        // reach outputs that are dropped
         const float* Ap = A + (mv ? m0 + i : Mo - 1) * sam;
-        const float* Bp = B + (nv ? n0 + i : No - 1) * sbn;
+        const float* Bp0 = B + (nv0 ? n0 + i : Nm - 1) * sbn;
+        const float* Bp1 = B + (nv1 ? n0 + 16 + i : Nm - 1) * sbn;
         const int kb = g * KQ;
         const int kl = K - kb < KQ ? K - kb : KQ;          // live steps of this lane group
         // steps live in every lane group, in whole groups of four: no clamps, one address
@@ -234,70 +240,93 @@ __device__ inline void mfma_gemm(int Mo, int No, int K, const float* A, int sam,
         const int jm = (K - 3 * KQ > 0 ? K - 3 * KQ : 0) & ~3;
         f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
         const float* pa = Ap + kb * sak;
-        const float* pb = Bp + kb * sbk;
+        const float* pb0 = Bp0 + kb * sbk;
+        const float* pb1 = Bp1 + kb * sbk;
         // two register sets take turns, so the next group's operands are loaded before this
         // group's MFMAs without copies between them
-        auto ld4 = [&](float* ra, float* rb) {
+        auto ld4 = [&](float* ra, float* rb0, float* rb1) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 ra[u] = pa[u * sak];
-                rb[u] = pb[u * sbk];
+                rb0[u] = pb0[u * sbk];
+                rb1[u] = pb1[u * sbk];
             }
             pa += 4 * sak;
-            pb += 4 * sbk;
+            pb0 += 4 * sbk;
+            pb1 += 4 * sbk;
         };
-        auto mma4 = [&](const float* ra, const float* rb) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[0], rb[0], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[1], rb[1], acc1, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[2], rb[2], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[3], rb[3], acc1, 0, 0, 0);
+        auto mma4 = [&](const float* ra, const float* rb0, const float* rb1) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[u], rb0[u], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[u], rb1[u], acc1, 0, 0, 0);
+            }
         };
         // (the loop body has no branches, so the compiler can wait for the older set alone)
-        float xa[4], xb[4], ya[4], yb[4];
+        float xa[4], xb0[4], xb1[4], ya[4], yb0[4], yb1[4];
         if (jm > 0) {
-            ld4(xa, xb);                                 // group 0
+            ld4(xa, xb0, xb1);                           // group 0
             int j = 0;
             for (; j + 12 <= jm; j += 8) {               // groups j + 4 and j + 8 exist
-                ld4(ya, yb);
+                ld4(ya, yb0, yb1);
                 __builtin_amdgcn_sched_barrier(0);       // keep each group's loads ahead
-                mma4(xa, xb);
+                mma4(xa, xb0, xb1);
                 __builtin_amdgcn_sched_barrier(0);
-                ld4(xa, xb);
+                ld4(xa, xb0, xb1);
                 __builtin_amdgcn_sched_barrier(0);
-                mma4(ya, yb);
+                mma4(ya, yb0, yb1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (j + 8 <= jm) {                           // groups j and j + 4 remain
-                ld4(ya, yb);
-                mma4(xa, xb);
-                mma4(ya, yb);
+                ld4(ya, yb0, yb1);
+                mma4(xa, xb0, xb1);
+                mma4(ya, yb0, yb1);
             } else {                                     // group j remains
-                mma4(xa, xb);
+                mma4(xa, xb0, xb1);
             }
         }
         // the rest (at most 7 steps): loads from clamped, always valid positions, all issued
-        // first; rows of A past Mo and columns of B past No only reach outputs that are
-        // dropped, and a dead step is zeroed on the A side alone
+        // first; a dead step is zeroed on the A side alone
         if (jm < KQ) {
-            float ta[8], tb[8];
+            float ta[8], tb0[8], tb1[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = jm + u;
                 const int k = kb + j < K ? kb + j : K - 1;
                 ta[u] = j < kl ? Ap[k * sak] : 0.0f;
-                tb[u] = Bp[k * sbk];
+                tb0[u] = Bp0[k * sbk];
+                tb1[u] = Bp1[k * sbk];
             }
 #pragma unroll
-            for (int u = 0; u < 8; u += 2) {
-                if (jm + u < KQ) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[u], tb[u], acc0, 0, 0, 0);
-                if (jm + u + 1 < KQ) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[u + 1], tb[u + 1], acc1, 0, 0, 0);
+            for (int u = 0; u < 8; ++u) {
+                if (jm + u < KQ) {
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[u], tb0[u], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[u], tb1[u], acc1, 0, 0, 0);
+                }
             }
         }
-        const f32x4 acc = acc0 + acc1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 4 * g + r;
-            if (m < Mo && nv) out(m, n0 + i, acc[r]);
+            if (m < Mo) {
+                if (nv0) out(m, n0 + i, acc0[r]);
+                if (nv1) out(m, n0 + 16 + i, acc1[r]);
+            }
+        }
+    }
+    if (rem) {
+        // C(m, Nm) for every row: 8 lanes per row, each summing every 8th k, then the 8 partial
+        // sums of a row added across its lanes
+        const float* Bc = B + Nm * sbn;
+        for (int base = 0; base < Mo * 8; base += NT) {
+            const int idx = base + threadIdx.x, m = idx >> 3, sub = idx & 7;
+            const int mm = m < Mo ? m : Mo - 1;
+            float c = 0.0f;
+            for (int k = sub; k < K; k += 8) c = fmaf(A[mm * sam + k * sak], Bc[k * sbk], c);
+            c += __shfl_xor(c, 1, 64);
+            c += __shfl_xor(c, 2, 64);
+            c += __shfl_xor(c, 4, 64);
+            if (sub == 0 && m < Mo) out(m, Nm, c);
         }
     }
 }
