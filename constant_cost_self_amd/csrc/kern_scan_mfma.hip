@@ -214,9 +214,13 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int slice = blockIdx.x;
-    const int64_t bh = blockIdx.y;
+    const int64_t bh = blockIdx.y / a.nsub;
+    const int sub = blockIdx.y % a.nsub;
     constexpr int d_V = DV, cols = DV + 1;
-    const int nch = a.c_end - a.c_begin;
+    const int nch = a.c_end - a.c_begin;       // chunks of the partial buffer
+    // the chunks this block scans: its sub-segment (the whole range when nsub = 1)
+    const int cb = a.c_begin + sub * a.sub_chunks;
+    const int ce = a.nsub > 1 && cb + a.sub_chunks < a.c_end ? cb + a.sub_chunks : a.c_end;
     const int row_s = slice * kRowsPerSlice;                 // first row of the slice
     const int lb_w = rt.wave_lblock[slice * kWaves + w];     // l-block of this wave's update rows
     // global column of local column j of this group (local 64 is the normaliser)
@@ -225,7 +229,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + bh * (int64_t)a.n * D;
     const uint16_t* k = static_cast<const uint16_t*>(a.k) + bh * (int64_t)a.n * D;
     const uint16_t* v = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.n * d_V;
-    float* state = a.state ? a.state + bh * (int64_t)cols * a.M_pad : nullptr;
+    float* state = a.state ? a.state + (bh * a.nsub + sub) * (int64_t)cols * a.M_pad : nullptr;
 
     // tokens of [c L, c L + len) that exist
     auto nvalid_of = [&](int c, int len) {
@@ -233,7 +237,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         return (int)(r < len ? r : len);
     };
     // tokens of [c L, c L + LU) that belong to the segment (the update stops at its end)
-    const int64_t seg_end = (int64_t)a.c_end * L < a.n ? (int64_t)a.c_end * L : a.n;
+    const int64_t seg_end = (int64_t)ce * L < a.n ? (int64_t)ce * L : a.n;
     auto nupd_of = [&](int c) {
         const int64_t r = seg_end - (int64_t)c * L;
         return (int)(r < LU ? r : LU);
@@ -253,8 +257,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         *reinterpret_cast<uint4*>(row) = uint4{0x3f80u, 0u, 0u, 0u};
     }
     // the first window's q and first sub-chunk's k, v in flight while the state is set up
-    prefetch_q(a.c_begin);
-    prefetch_kv(a.c_begin);
+    if (!a.update_only) prefetch_q(cb);
+    prefetch_kv(cb);
 
     // readout constants of the slice's rows (K-step s covers rows 4 s .. 4 s + 3, lane group
     // g row 4 s + g), in LDS: the parent coordinates as byte offsets in a q row (10 bits
@@ -438,10 +442,11 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     // Windows of NSUB chunks: one readout of the window's R tokens against the state
     // before the window, then the window's updates, LU tokens each.  The finalize adds
     // the direct part of the window's earlier chunks.
-    for (int cw = a.c_begin; cw < a.c_end; cw += NSUB) {
-        const int nchw = a.c_end - cw < NSUB ? a.c_end - cw : NSUB;   // chunks of the window
-        const bool next_w = cw + NSUB < a.c_end;
+    for (int cw = cb; cw < ce; cw += NSUB) {
+        const int nchw = ce - cw < NSUB ? ce - cw : NSUB;             // chunks of the window
+        const bool next_w = cw + NSUB < ce;
         lds_barrier<0>();           // the window's q and first k, v landed; the updates are done
+        if (!a.update_only) {
 
         // ---- fp16 state for the readout (over the previous window's tables); q to fp16 --
         store_sb();
@@ -528,6 +533,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         }
         lds_barrier<63>();          // every readout is done: the state copy and q are free
         if (next_w) prefetch_q(cw + NSUB);
+        }   // readout
 
         // ---- the window's updates ----------------------------------------------------------
         for (int cu = cw; cu < cw + nchw; cu += LU / L) {
@@ -535,7 +541,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             build_tables(cu);
             lds_barrier<63>();
             // next raw k, v: this window's next sub-chunk, or the next window's first
-            if (cu + LU / L < a.c_end) prefetch_kv(cu + LU / L);
+            if (cu + LU / L < ce) prefetch_kv(cu + LU / L);
             update();
         }
     }
@@ -580,8 +586,8 @@ hipError_t launch_t(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st
     hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, G, NPC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, G, NPC>), dim3(a.nslices, a.BH), dim3(512), LY::bytes, st,
-                       a, rt);
+    hipLaunchKernelGGL((scan_mfma_kernel<D, DV, G, NPC>), dim3(a.nslices, a.BH * a.nsub), dim3(512), LY::bytes,
+                       st, a, rt);
     return hipGetLastError();
 }
 
@@ -643,6 +649,30 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
 void free_mfma_tables(MfmaTables& m) {
     if (m.d_rows) (void)hipFree(m.d_rows);
     m = MfmaTables();
+}
+
+namespace {
+__global__ __launch_bounds__(kThreads) void state_prefix_kernel(float* __restrict__ states, const float* __restrict__ init,
+                                                                float* __restrict__ final, int nsub, int64_t per_state) {
+    const int64_t bh = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= per_state) return;
+    float acc = init ? init[bh * per_state + e] : 0.0f;
+    float* s = states + bh * nsub * per_state + e;
+    for (int i = 0; i < nsub; ++i) {
+        const float x = s[i * per_state];
+        s[i * per_state] = acc;
+        acc += x;
+    }
+    if (final) final[bh * per_state + e] = acc;
+}
+}  // namespace
+
+hipError_t launch_state_prefix(float* states, const float* init, float* final, int BH, int nsub,
+                               int64_t per_state, hipStream_t st) {
+    dim3 grid((unsigned)((per_state + kThreads - 1) / kThreads), (unsigned)BH);
+    hipLaunchKernelGGL(state_prefix_kernel, grid, dim3(kThreads), 0, st, states, init, final, nsub, per_state);
+    return hipGetLastError();
 }
 
 int mfma_window(int d_K) { return d_K == 64 ? Layout<64, 5>::NSUB : Layout<128, 5>::NSUB; }

@@ -58,7 +58,20 @@ struct PrefillSegArgs {
                              // window's first chunk c_begin + win * floor((c - c_begin) / win)
     int load_state, store_state;
     bool bf16;
+    // Two-level form (MFMA scan only): the chunks [c_begin, c_end) are cut into nsub
+    // sub-segments of sub_chunks chunks (a multiple of win), scanned in parallel, each from
+    // its own state: state holds [BH][nsub][d_V+1][M_pad].  nsub = 1: one segment, state
+    // [BH][d_V+1][M_pad].  update_only: no readout and no partials, only the state updates.
+    int nsub = 1, sub_chunks = 0;
+    bool update_only = false;
 };
+
+// Two-level prefill: replaces the nsub local states of every head, [BH][nsub][per_state],
+// by the state each sub-segment starts from (exclusive prefix sums, starting from init, which
+// is [BH][per_state] or zero when null), and writes the total to final when non-null (final
+// may equal init).
+hipError_t launch_state_prefix(float* states, const float* init, float* final, int BH, int nsub,
+                               int64_t per_state, hipStream_t st);
 
 // VALU fp32 scan: slice_feats features per block, chosen by valu_slice_feats().
 int valu_slice_feats(int d_K, int d_V, int L);

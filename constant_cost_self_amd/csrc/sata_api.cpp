@@ -96,6 +96,8 @@ struct sata_tables {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     int64_t ws_limit = kDefaultWorkspace;
+    int cus = 0;                      // compute units of the device
+    int split = 0;                    // two-level prefill: 0 automatic, 1 never, k >= 2 forced
 };
 
 namespace {
@@ -188,7 +190,8 @@ int sata_tables_build(int d_K, int P, sata_tables** out) {
         delete t;
         return fail(SATA_ERR_ARG, "table construction failed for d_K=%d P=%d", d_K, P);
     }
-    if (hipGetDevice(&t->device) != hipSuccess) {
+    if (hipGetDevice(&t->device) != hipSuccess ||
+        hipDeviceGetAttribute(&t->cus, hipDeviceAttributeMultiprocessorCount, t->device) != hipSuccess) {
         delete t;
         return fail(SATA_ERR_HIP, "hipGetDevice failed");
     }
@@ -282,6 +285,15 @@ int sata_read_timing(sata_tables* t, double* ms, int64_t* count) {
     return rc;
 }
 
+int sata_set_prefill_split(sata_tables* t, int nsub) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (nsub < 0 || nsub > 4096) return fail(SATA_ERR_ARG, "split must be in [0, 4096] (got %d)", nsub);
+    std::lock_guard<std::mutex> lock(t->mu);
+    t->split = nsub;
+    return SATA_OK;
+}
+
 int sata_set_workspace_limit(sata_tables* t, int64_t bytes) {
     clear_err();
     if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
@@ -355,6 +367,64 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     hipStream_t st = (hipStream_t)stream;
     const int64_t per_chunk = (int64_t)BH * a.nslices * L * cols * 4;
     const int64_t state_b = (int64_t)BH * cols * t->h.M_pad * 4;
+
+    // Two-level form (the state recurrence as a prefix over segments, [TA] "Hardware
+    // optimisation path"): when the slices of all heads leave compute units idle, the
+    // sequence is cut into nsub sub-segments of whole readout windows.  Their local states
+    // are accumulated in parallel (update-only scan), turned into each sub-segment's
+    // starting state by a prefix sum, and the sub-segments are then scanned in parallel from
+    // those states.  Same sums as one segment, in another order.
+    if (use_mfma && t->split != 1) {
+        const int64_t nwin = (nchunks + a.win - 1) / a.win;
+        int64_t nsub = 1;
+        if (t->split >= 2) {
+            nsub = t->split;
+        } else {
+            const int64_t wgs = (int64_t)BH * a.nslices;            // workgroups of one scan launch
+            nsub = wgs < t->cus ? t->cus / wgs : 1;
+            if (nsub > nwin / 4) nsub = nwin / 4;                   // at least 4 windows each
+        }
+        if (nsub > nwin) nsub = nwin;
+        int64_t sub_chunks = nchunks;
+        if (nsub >= 2) {
+            sub_chunks = (nwin + nsub - 1) / nsub * a.win;
+            nsub = (nchunks + sub_chunks - 1) / sub_chunks;         // no empty sub-segment
+        }
+        const int64_t need = per_chunk * nchunks + state_b * nsub;
+        if (nsub >= 2 && BH * nsub <= 65535 && need <= t->ws_limit) {
+            rc = ensure_ws(t, (size_t)need, st);
+            if (rc) return rc;
+            a.partial = (float*)t->ws;
+            float* starts = (float*)((char*)t->ws + per_chunk * nchunks);
+            a.c_begin = 0;
+            a.c_end = nchunks;
+            a.nsub = (int)nsub;
+            a.sub_chunks = (int)sub_chunks;
+            a.state = starts;
+            hipEvent_t ev = t->timer.begin(st);
+            a.update_only = true;                   // local states from zero
+            a.load_state = 0;
+            a.store_state = 1;
+            hipError_t e = sata::launch_scan_mfma(a, t->mfma, st);
+            if (e == hipSuccess)
+                e = sata::launch_state_prefix(starts, cont ? state : nullptr, state, BH, (int)nsub,
+                                              (int64_t)cols * t->h.M_pad, st);
+            a.update_only = false;                  // readouts and partials from the starts
+            a.load_state = 1;
+            a.store_state = 0;
+            if (e == hipSuccess) e = sata::launch_scan_mfma(a, t->mfma, st);
+            t->timer.end(SATA_KERNEL_SCAN, ev, st);
+            if (e != hipSuccess)
+                return fail(SATA_ERR_HIP, "two-level scan launch failed: %s", hipGetErrorString(e));
+            ev = t->timer.begin(st);
+            e = sata::launch_finalize(a, st);
+            t->timer.end(SATA_KERNEL_FINALIZE, ev, st);
+            if (e != hipSuccess)
+                return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
+            return SATA_OK;
+        }
+    }
+
     int64_t seg = nchunks;
     if (per_chunk * seg > t->ws_limit) {
         seg = (t->ws_limit - (state ? 0 : state_b)) / per_chunk;

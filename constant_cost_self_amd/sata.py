@@ -27,7 +27,7 @@ SATA_ERR_OOM = -5
 EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "sata_tables_free", "sata_feature_dim",
             "sata_state_stride", "sata_state_bytes", "sata_prefill", "sata_decode_step",
             "sata_decode_step_pool", "sata_prefill_backward",
-            "sata_last_error", "sata_set_workspace_limit", "sata_set_timing",
+            "sata_last_error", "sata_set_workspace_limit", "sata_set_prefill_split", "sata_set_timing",
             "sata_read_timing")
 KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward")
 
@@ -80,6 +80,8 @@ def load():
     lib.sata_last_error.argtypes = []
     lib.sata_set_workspace_limit.restype = i32
     lib.sata_set_workspace_limit.argtypes = [vp, i64]
+    lib.sata_set_prefill_split.restype = i32
+    lib.sata_set_prefill_split.argtypes = [vp, i32]
     lib.sata_set_timing.restype = i32
     lib.sata_set_timing.argtypes = [vp, i32]
     lib.sata_read_timing.restype = i32
@@ -174,6 +176,10 @@ class Tables:
 
     def set_workspace_limit(self, nbytes: int):
         _check(load().sata_set_workspace_limit(self.handle, nbytes))
+
+    def set_prefill_split(self, nsub: int):
+        """Sub-segments of the two-level prefill: 0 automatic, 1 never, k >= 2 forced."""
+        _check(load().sata_set_prefill_split(self.handle, nsub))
 
     def set_timing(self, enable: bool):
         _check(load().sata_set_timing(self.handle, 1 if enable else 0))

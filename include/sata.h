@@ -133,6 +133,14 @@ int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
  *        the state of a prefix that precedes these n tokens; y then attends to
  *        that prefix too.  Without the flag the prefix is empty.
  * stream hipStream_t (NULL = default stream)
+ *
+ * Two-level form (bf16 matrix-core path only): when the slices of all B x H heads
+ * leave compute units idle (few heads), the sequence is cut into sub-segments of
+ * whole readout windows whose local states are summed in parallel, turned into
+ * each sub-segment's starting state by a prefix sum, and then scanned in parallel
+ * from those states ([TA] "Hardware optimisation path": the recurrence as a
+ * parallel prefix).  The results equal the one-segment scan up to rounding.
+ * sata_set_prefill_split chooses when it is used.
  */
 int sata_prefill(const sata_tables *t, const void *q, const void *k, const void *v,
                  float *y, float *state, int B, int H, int n, int d_K, int d_V,
@@ -208,6 +216,18 @@ const char *sata_last_error(void);
  * matrix-core path, 1 otherwise).  0 restores the default (32 GiB).
  */
 int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
+
+/*
+ * Optional: sub-segments of the two-level prefill.  0 (the default): automatic,
+ * used when B H times the number of feature slices is at most half the device's
+ * compute units, with at least 4 readout windows per sub-segment; 1: never;
+ * k >= 2: k sub-segments (fewer when the sequence has fewer readout windows)
+ * whenever the matrix-core path runs.  The two-level form needs workspace for
+ * the partials of the whole sequence plus one state per sub-segment; beyond the
+ * workspace cap the one-level form runs.  Errors: SATA_ERR_ARG for a NULL handle
+ * or k outside [0, 4096].
+ */
+int sata_set_prefill_split(sata_tables *t, int nsub);
 
 /*
  * Kernel timing.  With timing enabled, every kernel launch of the handle is

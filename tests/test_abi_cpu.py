@@ -170,6 +170,15 @@ def test_workspace_limit_argument(host_tables):
         host_tables.set_workspace_limit(-1)
 
 
+def test_prefill_split_argument(host_tables):
+    for k in (0, 1, 2, 7, 4096):
+        host_tables.set_prefill_split(k)
+    for k in (-1, 4097):
+        with pytest.raises(sata.SataError):
+            host_tables.set_prefill_split(k)
+    assert sata.load().sata_set_prefill_split(None, 2) == sata.SATA_ERR_ARG
+
+
 def _decode_pool(t, **kw):
     args = dict(pool=A, pool_size=3, slots=A, count=2, q=A, k=A, v=A, y=A, H=2, d_K=8, d_V=8, P=4,
                 dtype=sata.SATA_F32)

@@ -1,0 +1,132 @@
+"""GPU parity of the two-level prefill (sub-segments of the sequence scanned in parallel
+from prefix-summed starting states) against the fp64 oracle, and against the one-level
+scan.  Bars as in test_gpu_parity: y within 2e-2 (bf16 inputs, fp32 state) as max over
+rows of max_j |y - y_ref| / max_j |y_ref|; the final state by the same bound per column."""
+import time
+
+import numpy as np
+import pytest
+
+from gpu_helpers import (TOL_BF16, inputs, max_row_err, new_state, oracle, prefill, sample_feature_rows,
+                         sampled_state_err, say, sata, state_col_err, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _draw(n, d, H, seed):
+    return inputs.draw((1, H, n, d), (1, H, n, d), "bf16", 0.5, 1.0, seed)
+
+
+@pytest.mark.parametrize("d,nsub,n", [(64, 2, 2000), (64, 3, 2000), (64, 5, 1234), (64, 8, 300),
+                                      (128, 3, 700), (128, 2, 129)])
+def test_two_level_matches_oracle(torch_cuda, d, nsub, n):
+    """Forced sub-segments (ragged last chunk, a last sub-segment shorter than the others,
+    more sub-segments asked for than the sequence has windows): y and the final state."""
+    say("two-level d=%d nsub=%d n=%d" % (d, nsub, n))
+    x = _draw(n, d, 2, 40 + nsub + d)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(d, 4)
+    t.set_prefill_split(nsub)
+    S = new_state(1, 2, d, d, 4)
+    y = prefill(t, q, k, v, 64, S)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    err = max_row_err(y.cpu().numpy(), ref)
+    say("  y err %.3e" % err)
+    assert err <= TOL_BF16
+    M = oracle.feature_dim(d, 4)
+    rows = sample_feature_rows(M, 200, n)
+    S_ref = oracle.state_rows(x["k"][0, 1], x["v"][0, 1], 4, rows)
+    Sg = S[0, 1].cpu().numpy()
+    serr = sampled_state_err(Sg, S_ref, rows)
+    say("  state err %.3e" % serr)
+    assert serr <= TOL_BF16
+    assert np.all(Sg[:, M:] == 0.0), "padding of the state must stay zero"
+    t.close()
+
+
+def test_two_level_continue_from_state(torch_cuda):
+    """The first sub-segment starts from the caller's state (prefix of 700 tokens)."""
+    say("two-level prefill(700) + prefill(1300, continue, nsub=3)")
+    n1, n2 = 700, 1300
+    x = _draw(n1 + n2, 64, 1, 50)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(64, 4)
+    S = new_state(1, 1, 64, 64, 4)
+    prefill(t, q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(), 64, S)
+    t.set_prefill_split(3)
+    y2 = prefill(t, q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous(),
+                 64, S, continue_state=True)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    err = max_row_err(y2.cpu().numpy(), ref[:, :, n1:])
+    say("  y err %.3e" % err)
+    assert err <= TOL_BF16
+    _, S_ref = oracle.feature_form(None, x["k"][0, 0], x["v"][0, 0], 4, want_y=False)
+    M = S_ref.shape[1]
+    assert state_col_err(S[0, 0].cpu().numpy()[:, :M], S_ref) <= TOL_BF16
+    t.close()
+
+
+def test_two_level_equals_one_level(torch_cuda):
+    """Same sums in another order: the two forms agree far inside the oracle bar."""
+    say("two-level vs one-level, d=64 n=3000")
+    n = 3000
+    x = _draw(n, 64, 1, 60)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(64, 4)
+    t.set_prefill_split(1)
+    S1 = new_state(1, 1, 64, 64, 4)
+    y1 = prefill(t, q, k, v, 64, S1)
+    t.set_prefill_split(4)
+    S2 = new_state(1, 1, 64, 64, 4)
+    y2 = prefill(t, q, k, v, 64, S2)
+    torch_cuda.cuda.synchronize()
+    dy = max_row_err(y2.cpu().numpy(), y1.cpu().numpy().astype(np.float64))
+    a, b = S1[0, 0].cpu().numpy().astype(np.float64), S2[0, 0].cpu().numpy()
+    ds = state_col_err(b, a)
+    say("  y diff %.3e state diff %.3e" % (dy, ds))
+    assert dy <= 2e-3 and ds <= 1e-5
+    t.close()
+
+
+def test_two_level_automatic_long_single_head(torch_cuda):
+    """One head of 16384 tokens leaves most compute units idle: the automatic choice takes
+    the two-level form.  Sampled rows of y and of the state against the oracle; the time of
+    both forms is printed."""
+    n = 16384
+    say("automatic two-level, B=H=1 n=%d d=64" % n)
+    x = _draw(n, 64, 1, 70)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(64, 4)
+    S = new_state(1, 1, 64, 64, 4)
+    times = {}
+    for split in (1, 0):
+        t.set_prefill_split(split)
+        prefill(t, q, k, v, 64, S)                     # warm-up
+        torch_cuda.cuda.synchronize()
+        t0 = time.perf_counter()
+        y = prefill(t, q, k, v, 64, S)
+        torch_cuda.cuda.synchronize()
+        times[split] = (time.perf_counter() - t0) * 1e3
+    say("  one-level %.2f ms, automatic %.2f ms" % (times[1], times[0]))
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 8191, 8192, n - 1],
+                                     np.random.default_rng(1).choice(n, 40, replace=False)]))
+    ref = oracle.direct_rows(x["q"], x["k"], x["v"], 4, np.zeros_like(rows), rows)
+    err = max_row_err(y[0, 0].cpu().numpy()[rows], ref)
+    say("  sampled y err %.3e" % err)
+    assert err <= TOL_BF16
+    M = oracle.feature_dim(64, 4)
+    frows = sample_feature_rows(M, 100, 2)
+    S_ref = oracle.state_rows(x["k"][0, 0], x["v"][0, 0], 4, frows)
+    serr = sampled_state_err(S[0, 0].cpu().numpy(), S_ref, frows)
+    say("  sampled state err %.3e" % serr)
+    assert serr <= TOL_BF16
+    t.close()
