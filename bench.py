@@ -13,6 +13,9 @@ its own stream: achieved = algorithmic work per launch / mean launch time.
                 (the forward FLOPs/token closed form of the method), peak = bf16 MFMA
                 2.5 PFLOP/s.
   decode:       bytes = 8 (d_V + 1) M per head (fp32 state read + write), peak 8 TB/s.
+  two_level:    one head of 65536 tokens (too few slices to fill the CUs): the automatic
+                two-level prefill against the one-level scan; flops as for prefill, over
+                the scan time (both passes and the prefix sum).
   backward:     (sata_prefill_backward on the Mid shape, fp32 arithmetic, the state
                 contractions on the matrix cores) flops = B H n [forward closed form +
                 2 M (4 (d_V + 1) + d_V)]: the fp32 forward recompute plus the five state
@@ -144,6 +147,36 @@ def backward_flops_per_token(d_K, d_V, P):
     return flops_per_token(d_K, d_V, P) + 2.0 * M * (4 * (d_V + 1) + d_V)
 
 
+def bench_two_level(steps, n=65536):
+    """One head (B=H=1) of n tokens, d=64 P=4 bf16: the one-level scan against the automatic
+    choice (the two-level form, since one head's slices fill under half of the CUs)."""
+    import numpy as np
+    import torch
+    from constant_cost_self_amd import inputs, sata
+
+    x = inputs.draw((1, 1, n, 64), (1, 1, n, 64), "bf16", 0.5, 1.0, 0)
+    q, k, v = (to_dev(x[s], "bf16") for s in ("q", "k", "v"))
+    y = torch.empty((1, 1, n, 64), device="cuda:0", dtype=torch.float32)
+    t = sata.sata_tables_build(64, 4)
+    t.set_timing(True)
+    out = {}
+    for split in (1, 0):
+        t.set_prefill_split(split)
+        sata.sata_prefill(t, q, k, v, y, None, chunk=64)
+        torch.cuda.synchronize()
+        t.read_timing()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            sata.sata_prefill(t, q, k, v, y, None, chunk=64)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        tim = t.read_timing()
+        out[split] = (wall, tim["scan"][0] / steps)
+    t.close()
+    log("  two-level: one head n=%d: one-level %.3f ms, automatic %.3f ms" % (n, out[1][0] * 1e3, out[0][0] * 1e3))
+    return out
+
+
 def bench_backward(steps, warmup):
     import numpy as np
     import torch
@@ -207,6 +240,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-two-level", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one part only (for profiler runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
@@ -305,6 +339,21 @@ def main():
                          "ms_per_launch": dk_ms / dk_n,
                          "algorithmic_bytes_per_launch": dbytes},
             "reduce_ms_per_step": dtim["decode_reduce"][0] / max(dtim["decode_reduce"][1], 1),
+        }
+
+    if not args.no_two_level and args.only is None:
+        n2 = 65536
+        tl = bench_two_level(5, n2)
+        fl = flops_per_token(64, 64, 4) * n2
+        out["two_level"] = {
+            "workload": "prefill of one head (B=H=1) n=%d d_K=d_V=64 P=4 chunk=64, bf16: the automatic "
+                        "two-level form (sub-segments scanned in parallel) against one level" % n2,
+            "value": n2 / tl[0][0], "unit": "tokens/s", "ms_per_step": tl[0][0] * 1e3,
+            "one_level_ms_per_step": tl[1][0] * 1e3, "speedup": tl[1][0] / tl[0][0],
+            "roofline": {"bound": "mfma", "achieved": fl / (tl[0][1] * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fl / (tl[0][1] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "traffic": None, "kernel": "prefill scan (both passes and the prefix sum)",
+                         "ms_per_launch": tl[0][1], "algorithmic_flops_per_launch": fl},
         }
 
     if not args.no_backward and args.only is None:
