@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
     float* uu = xk + L * ks;                       // [L][cols]
     float* vv = uu + L * cols;                     // [L][cols]
     const int LP = L + 1, SVP = SV + 1;
-    float* hat = vv + L * cols;                    // [SV][LP] qw a_T, then [L][SVP] phi(k)
+    float* hat = vv + L * cols;                    // [SV][LP] qw a_T; two more tables follow
     float* gq = hat + 3 * bwd_table_floats(SV, L); // [L][ks] (the layout of bwd_kv_kernel)
     uint32_t* sfi = reinterpret_cast<uint32_t*>(gq + L * ks);   // [SV] packed indices
     float* sqw = reinterpret_cast<float*>(sfi + SV);             // [SV] query weights, 0 past M
@@ -330,22 +330,23 @@ __global__ __launch_bounds__(kScanThreads) void bwd_q_kernel(BwdArgs a) {
         mfma_gemm<kScanThreads>(L, SV, cols, uu, cols, 1, Ssl, 1, cols,
                                 [&](int t, int f, float c) { hat[f * LP + t] = c * sqw[f]; });
         __syncthreads();
-        // dq partial: sum_f qw_f a_T[f] d phi_f / dq
-        float* carry = hat + bwd_table_floats(SV, L);      // [waves][L] in the unused second table
+        // dq partial: sum_f qw_f a_T[f] d phi_f / dq, and in the same phase the key features
+        // (third table) for the update
+        float* carry = hat + bwd_table_floats(SV, L);      // [waves][L] in the second table
+        float* hk = hat + 2 * bwd_table_floats(SV, L);     // [L][SVP] phi(k)
         scatter_planned<NIDX>(gq, xq, hat, ent, wave_begin, carry_coord, carry, L, LP, ks, nvalid);
-        __syncthreads();
-        float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
-        copy_grad_rows(part, gq, carry, carry_coord, L, d_K, ks);
-        // key features, then the update S += phi(k)^T [v | 1]
         {   // a thread owns feature tid % SV (a power of two) for tokens tid / SV + k NT / SV
             const int f = tid & (SV - 1);
             const bool live = F0 + f < a.M;
             const uint32_t fi = sfi[f];
             for (int t = tid / SV; t < L; t += kScanThreads / SV)
-                hat[t * SVP + f] = live ? feature_value_n<NIDX>(xk + t * ks, fi) : 0.0f;
+                hk[t * SVP + f] = live ? feature_value_n<NIDX>(xk + t * ks, fi) : 0.0f;
         }
         __syncthreads();
-        mfma_gemm<kScanThreads>(SV, cols, L, hat, 1, SVP, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
+        float* part = a.part + (((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L) * d_K;
+        copy_grad_rows(part, gq, carry, carry_coord, L, d_K, ks);
+        // the update S += phi(k)^T [v | 1]
+        mfma_gemm<kScanThreads>(SV, cols, L, hk, 1, SVP, vv, cols, 1, [&](int f, int j, float c) { Ssl[f * cols + j] += c; });
     }
     __syncthreads();
     if (a.store_state) {
