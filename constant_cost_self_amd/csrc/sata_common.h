@@ -146,70 +146,11 @@ struct RowStage {
 };
 
 // C(m, n) = sum_{k < K} A(m, k) B(k, n) for m < Mo, n < No, with A(m, k) = A[m sam + k sak]
-// and B(k, n) = B[k sbk + n sbn] in LDS, by the NT threads of a block; out(m, n, c)
-// receives each result.  Every 64 x 64 output block is split into register tiles of
-// TM x 4 (TM = 1024 / NT): thread tid = 16 mt + nt owns rows mt + (NT / 16) i and columns
-// nt + 16 j.  Per k it reads TM values of A and 4 of B for 4 TM FMAs; the 16 threads of
-// a row read 16 consecutive columns of B.
-template <int NT, typename Out>
-__device__ inline void lds_gemm(int Mo, int No, int K, const float* A, int sam, int sak, const float* B,
-                                int sbk, int sbn, Out out) {
-    static_assert(NT == 256 || NT == 512, "16 columns of threads, 64 rows per block");
-    constexpr int TM = 1024 / NT, RS = NT / 16;
-    const int mt = threadIdx.x >> 4, nt = threadIdx.x & 15;
-    // a few columns past the last whole block of 64 (the normaliser column of [v | 1]):
-    // one thread per output, so that they do not cost a whole block of tiles
-    const int rem = No % 64 <= 4 && No >= 64 ? No % 64 : 0;
-    const int Nt = No - rem;
-    for (int idx = threadIdx.x; idx < Mo * rem; idx += NT) {
-        const int m = idx / rem, n = Nt + idx % rem;
-        float c = 0.0f;
-        for (int k = 0; k < K; ++k) c = fmaf(A[m * sam + k * sak], B[k * sbk + n * sbn], c);
-        out(m, n, c);
-    }
-    for (int mb = 0; mb < Mo; mb += 64)
-        for (int nb = 0; nb < Nt; nb += 64) {
-            float acc[TM][4];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-            int mi[TM], nj[4];
-            bool mv[TM], nv[4];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                mi[i] = mb + mt + RS * i;
-                mv[i] = mi[i] < Mo;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                nj[j] = nb + nt + 16 * j;
-                nv[j] = nj[j] < Nt;
-            }
-#pragma unroll 2
-            for (int k = 0; k < K; ++k) {
-                float a[TM], b[4];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) a[i] = mv[i] ? A[mi[i] * sam + k * sak] : 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = nv[j] ? B[k * sbk + nj[j] * sbn] : 0.0f;
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (mv[i] && nv[j]) out(mi[i], nj[j], acc[i][j]);
-        }
-}
-
-// The same contraction on the matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands and
-// accumulation), by the NT threads of a block.  A wave computes units of two 16 x 16 output
-// tiles side by side (rows m0.., columns n0.. and n0 + 16..), which share the A operand:
-// unit w, w + NT/64, ...  In step j of a unit the 16 lanes of group g = lane / 16 take
+// and B(k, n) = B[k sbk + n sbn] in LDS, on the matrix cores (v_mfma_f32_16x16x4_f32: fp32
+// operands and accumulation), by the NT threads of a block; out(m, n, c) receives each
+// result.  A wave computes units of two 16 x 16 output tiles side by side (rows m0..,
+// columns n0.. and n0 + 16..), which share the A operand: unit w, w + NT/64, ...
+// In step j of a unit the 16 lanes of group g = lane / 16 take
 // k = g KQ + j (KQ = ceil(K / 4)): lane i + 16 g holds A(m0 + i, k) and B(k, n0 + i), and
 // register r of a tile's accumulator is C(m0 + 4 g + r, n0 + i).  With row strides of 1
 // modulo 64 floats (65, 129, L + 1, SV + 1) the 64 lanes of a load hit 64 different LDS
