@@ -1,4 +1,4 @@
-// kern_backward.hip -- gradients of the chunked prefill (fp32, vector ALUs, gfx950).
+// kern_backward.hip -- gradients of the chunked prefill (fp32, gfx950).
 //
 // For a loss with dL/dy = dy, the chain rule through y_T = N_T / D_T ([TA] "Feature maps
 // and linear attention": N_T = sum_{t<=T} w(q_T.k_t) v_t, D_T = sum_{t<=T} w(q_T.k_t))
@@ -28,6 +28,8 @@
 //                     R += (qw phi(q))^T u
 //   bwd_fin_kernel    per (chunk, head): sum of the slice partials plus the direct part
 //                     of the chunk's pairs
+// The state contractions run on the matrix cores with fp32 operands (mfma_gemm); the
+// scatter follows a per-slice plan (build_plan) instead of atomics.
 #include "launch.h"
 #include "sata_common.h"
 

@@ -1,4 +1,4 @@
-// kern_prefill_valu.hip -- fp32 chunked prefill scan on the vector ALUs (gfx950).
+// kern_prefill_valu.hip -- fp32 chunked prefill scan (gfx950).
 //
 // The inter-chunk half of the chunked prefill ([TA] "Feature maps and linear
 // attention": the state recurrence evaluated chunk by chunk).  A block owns one
@@ -9,9 +9,10 @@
 //     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
 // The readout of every slice is written as a partial sum ([column][token] within
 // the chunk); the finalize kernel adds
-// the partials of all slices to the intra-chunk part.  Arithmetic is fp32 on the
-// VALU: this is the path for fp32 inputs and for sizes the MFMA scan does not
-// cover.  Tokens past n in the last chunk get u = 0 and so never enter the state.
+// the partials of all slices to the intra-chunk part.  Arithmetic is fp32 (the two
+// contractions on the matrix cores with fp32 operands, mfma_gemm): this is the path for
+// fp32 inputs and for sizes the fp16-operand MFMA scan does not cover.  Tokens past n in
+// the last chunk get u = 0 and so never enter the state.
 #include "launch.h"
 #include "sata_common.h"
 

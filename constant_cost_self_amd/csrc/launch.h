@@ -73,7 +73,7 @@ struct PrefillSegArgs {
 hipError_t launch_state_prefix(float* states, const float* init, float* final, int BH, int nsub,
                                int64_t per_state, hipStream_t st);
 
-// VALU fp32 scan: slice_feats features per block, chosen by valu_slice_feats().
+// fp32 scan: slice_feats features per block, chosen by valu_slice_feats().
 int valu_slice_feats(int d_K, int d_V, int L);
 hipError_t launch_scan_valu(const PrefillSegArgs& a, hipStream_t st);
 

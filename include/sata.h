@@ -192,7 +192,7 @@ int sata_decode_step_pool(const sata_tables *t, float *state_pool, int64_t pool_
  * forward in fp32 and then runs two chunked scans over fixed-size states: the forward
  * state for dq, and its mirror sum_{T>=t} alpha C phi(q_T) u_T^T (u = [g | h]) in reverse
  * chunk order for dk and dv; pairs inside a chunk are taken directly.  Arithmetic is fp32
- * on the vector ALUs for either input type.
+ * for either input type (state contractions on the matrix cores with fp32 operands).
  *
  * q, k, v  [B][H][n][d_K or d_V], in_dtype (as for sata_prefill)
  * dy       fp32 [B][H][n][d_V]
