@@ -242,57 +242,95 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     // the tables are consumed: the partial sums reuse their LDS
     __syncthreads();
 
-    // slice partials: num[t][col] = sum over slices.  Value columns: DV / 16 items of 4
-    // tokens per thread, all of them loaded together, 4 slices at a time.  The
-    // normaliser column (16 items) is split over 16 slice groups, one per thread, and
+    // slice partials: num[t][col] = sum over slices.  Value columns: items of 16 bytes per
+    // thread, all of them loaded together, several slices at a time (16 loads in flight).
+    // The normaliser column (16 items) is split over 16 slice groups, one per thread, and
     // summed with LDS atomics, so that no thread walks the slices alone at the end.
     {
-        const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * L * COLS;
-        const int64_t stride = (int64_t)L * COLS;
-        constexpr int NI = DV * (L / 4) / 256;          // value-column items per thread
-        static_assert(NI * 256 == DV * (L / 4), "whole items per thread");
+        const int64_t stride = TILED ? tiled_partial_floats(L, DV) : (int64_t)L * COLS;
+        const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * stride;
         if (tid < L) num[tid * NS + DV] = 0.0f;
-        // item: 4 tokens of one value column; [column][token] order, or MFMA-tile order
-        // [token tile][column tile][lane (li, g)] (column 16 ct + li, tokens 16 tile + 4 g)
-        auto item_col = [&](int item) {
-            return TILED ? 16 * ((item / 64) % (DV / 16)) + (item % 16) : item / (L / 4);
-        };
-        auto item_tok = [&](int item) {
-            return TILED ? 16 * (item / 64 / (DV / 16)) + 4 * ((item % 64) / 16) : 4 * (item % (L / 4));
-        };
-        const float* p[NI];
+        if constexpr (TILED) {
+            // items of 8 fp16: [token tile][tile pair][lane (li, g)], tokens 16 tile + 4 g + r,
+            // columns 32 pair + li (halves r) and 32 pair + 16 + li (halves 4 + r)
+            constexpr int NVP = DV / 32, NI = L * DV / 8 / 256, SB = 16 / NI;
+            static_assert(NI * 256 * 8 == L * DV && SB * NI == 16, "whole items per thread");
+            const float* p[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int item = tid + 256 * i;
-            p[i] = part + (TILED ? 4 * item : item_col(item) * L + item_tok(item));
-        }
-        f32x4_t acc[NI];
+            for (int i = 0; i < NI; ++i) p[i] = part + 4 * (tid + 256 * i);
+            f32x4_t acc[NI][2];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        int sl = 0;
-        for (; sl + 4 <= a.nslices; sl += 4) {
-            f32x4_t x[4][NI];
+            for (int i = 0; i < NI; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            auto add = [&](f32x4_t* ac, f32x4_t raw) {
+                const f16x8_t h = __builtin_bit_cast(f16x8_t, raw);
+                ac[0] += f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+                ac[1] += f32x4_t{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+            };
+            int sl = 0;
+            for (; sl + SB <= a.nslices; sl += SB) {
+                f32x4_t x[SB][NI];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < SB; ++u)
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+                        x[u][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + (sl + u) * stride));
+#pragma unroll
+                for (int u = 0; u < SB; ++u)
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) add(acc[i], x[u][i]);
+            }
+            for (; sl < a.nslices; ++sl)
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
-                    x[u][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + (sl + u) * stride));
+                    add(acc[i], __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride)));
 #pragma unroll
-            for (int i = 0; i < NI; ++i) acc[i] += (x[0][i] + x[1][i]) + (x[2][i] + x[3][i]);
-        }
-        for (; sl < a.nslices; ++sl)
+            for (int i = 0; i < NI; ++i) {
+                const int item = tid + 256 * i, ln = item % 64, pr = (item / 64) % NVP, tt = item / 64 / NVP;
+                const int col = 32 * pr + (ln & 15), t0 = 16 * tt + 4 * (ln >> 4);
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
-                acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride));
+                for (int e = 0; e < 4; ++e) {
+                    num[(t0 + e) * NS + col] = acc[i][0][e] * (1.0f / kPartialScale);
+                    num[(t0 + e) * NS + col + 16] = acc[i][1][e] * (1.0f / kPartialScale);
+                }
+            }
+        } else {
+            // items of 4 tokens of one value column, [column][token]
+            constexpr int NI = DV * (L / 4) / 256;
+            static_assert(NI * 256 == DV * (L / 4), "whole items per thread");
+            const float* p[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int item = tid + 256 * i, col = item_col(item), t0 = item_tok(item);
+            for (int i = 0; i < NI; ++i) {
+                const int item = tid + 256 * i;
+                p[i] = part + (item / (L / 4)) * L + 4 * (item % (L / 4));
+            }
+            f32x4_t acc[NI];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) num[(t0 + e) * NS + col] = acc[i][e];
+            for (int i = 0; i < NI; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            int sl = 0;
+            for (; sl + 4 <= a.nslices; sl += 4) {
+                f32x4_t x[4][NI];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+                        x[u][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + (sl + u) * stride));
+#pragma unroll
+                for (int i = 0; i < NI; ++i) acc[i] += (x[0][i] + x[1][i]) + (x[2][i] + x[3][i]);
+            }
+            for (; sl < a.nslices; ++sl)
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride));
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int item = tid + 256 * i, col = item / (L / 4), t0 = 4 * (item % (L / 4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) num[(t0 + e) * NS + col] = acc[i][e];
+            }
         }
         // normaliser column: token quad tid % 16, slices tid / 16, tid / 16 + 16, ...
         const int tg = tid % (L / 4);
-        const float* pz = part + DV * L + 4 * tg;
+        const float* pz = part + (TILED ? L * DV / 2 : L * DV) + 4 * tg;
         f32x4_t z = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         for (int s2 = tid / (L / 4); s2 < a.nslices; s2 += 256 / (L / 4))
             z += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pz + s2 * stride));

@@ -508,25 +508,30 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 }
             }
         }
-        {   // this wave's tokens lie in one chunk.  Partials in HBM, per (chunk, slice):
-            // the value columns in tile order [token tile][column tile][lane] x 16 bytes
-            // (lane (li, g): column 16 ct + li, tokens 16 tile + 4 g .. + 3), so that one
-            // store instruction writes 1 KiB contiguously; then the normaliser column,
-            // [token] (its lanes li = 0 write 16 bytes each)
+        {   // this wave's tokens lie in one chunk.  Partials in HBM, per (chunk, slice), in
+            // the tiled layout (launch.h): a lane's accumulators of two adjacent column tiles
+            // as one 16-byte store of fp16, so that one store instruction writes 1 KiB
+            // contiguously; then the normaliser column in fp32, [token] (its lanes li = 0
+            // write 16 bytes each)
             const int cs = (TW * w) / L;
             if (cs < nchw) {
                 const int c = cw + cs;
-                constexpr int NVT = d_V / 16;                       // value column tiles of the head
-                float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * (int64_t)L * cols;
+                constexpr int NVP = d_V / 32;                       // value column-tile pairs of the head
+                constexpr float ps = kUScale * kPartialScale;
+                float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * tiled_partial_floats(L, d_V);
+                _Float16* ph = reinterpret_cast<_Float16*>(pp);
 #pragma unroll
                 for (int m = 0; m < MTW; ++m) {
                     const int mg = ((TW * w) % L) / 16 + m;         // token tile within the chunk
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        if (ct < 4)
-                            *reinterpret_cast<f32x4v*>(pp + ((mg * NVT + 4 * G + ct) * 64 + lane) * 4) = U[m][ct] * kUScale;
-                        else if (li == 0)
-                            *reinterpret_cast<f32x4v*>(pp + L * d_V + 16 * mg + 4 * g) = U[m][ct] * kUScale;
+                    for (int cp = 0; cp < 2; ++cp) {
+                        const f32x4v lo = U[m][2 * cp] * ps, hi = U[m][2 * cp + 1] * ps;
+                        const f16x8 h = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+                                         (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+                        *reinterpret_cast<f16x8*>(ph + ((mg * NVP + 2 * G + cp) * 64 + lane) * 8) = h;
+                    }
+                    if constexpr (ONES) {
+                        if (li == 0) *reinterpret_cast<f32x4v*>(pp + L * d_V / 2 + 16 * mg + 4 * g) = U[m][NCT - 1] * kUScale;
                     }
                 }
             }

@@ -41,9 +41,9 @@ struct PrefillSegArgs {
     const void* v;
     float* y;
     float* state;            // [BH][d_V+1][M_pad]; read if load_state, written if store_state
-    float* partial;          // [BH][c_end-c_begin][nslices][d_V+1][L] workspace; with
-                             // partial_tiled the d_V value columns of a (chunk, slice) block
-                             // are in MFMA-tile order instead (see kern_scan_mfma.hip)
+    float* partial;          // [BH][c_end-c_begin][nslices] blocks of slice partials: fp32
+                             // [d_V+1][L]; with partial_tiled the matrix-core layout of
+                             // tiled_partial_floats(L, d_V) floats (below)
     bool partial_tiled;
     float* den;              // nullable: the fp32 finalize writes D_T of every row here
     const uint32_t* fidx;    // packed feature indices [M_pad]
@@ -65,6 +65,14 @@ struct PrefillSegArgs {
     int nsub = 1, sub_chunks = 0;
     bool update_only = false;
 };
+
+// Slice partials of the matrix-core scan, one block per (head, chunk, slice): the d_V value
+// columns as fp16 times kPartialScale, in tile-pair order [token tile][pair of 16-column
+// tiles][lane] x 16 bytes (lane (li, g): tokens 16 tile + 4 g .. + 3, halves 0-3 column
+// 32 pair + li, halves 4-7 column 32 pair + 16 + li), then the normaliser column as L fp32
+// values.  The power-of-two scale keeps partials up to 65504 / kPartialScale in range.
+constexpr float kPartialScale = 1.0f / 256.0f;
+__host__ __device__ constexpr int64_t tiled_partial_floats(int L, int d_V) { return (int64_t)L * d_V / 2 + L; }
 
 // Two-level prefill: replaces the nsub local states of every head, [BH][nsub][per_state],
 // by the state each sub-segment starts from (exclusive prefix sums, starting from init, which

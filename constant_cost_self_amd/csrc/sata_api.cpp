@@ -365,7 +365,8 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
 
     std::lock_guard<std::mutex> lock(t->mu);
     hipStream_t st = (hipStream_t)stream;
-    const int64_t per_chunk = (int64_t)BH * a.nslices * L * cols * 4;
+    const int64_t per_chunk = (int64_t)BH * a.nslices * 4 *
+                              (a.partial_tiled ? sata::tiled_partial_floats(L, d_V) : (int64_t)L * cols);
     const int64_t state_b = (int64_t)BH * cols * t->h.M_pad * 4;
 
     // Two-level form (the state recurrence as a prefix over segments, [TA] "Hardware
