@@ -52,6 +52,24 @@ def test_two_level_matches_oracle(torch_cuda, d, nsub, n):
     t.close()
 
 
+@pytest.mark.parametrize("P", [2, 3, 5])
+def test_two_level_term_counts(torch_cuda, P):
+    """Other term counts (another parent depth in the scan's operand building)."""
+    n = 1100
+    say("two-level d=64 P=%d nsub=3 n=%d" % (P, n))
+    x = _draw(n, 64, 1, 80 + P)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(64, P)
+    t.set_prefill_split(3)
+    y = prefill(t, q, k, v, 64)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], P)
+    err = max_row_err(y.cpu().numpy(), ref)
+    say("  y err %.3e" % err)
+    assert err <= TOL_BF16
+    t.close()
+
+
 def test_two_level_continue_from_state(torch_cuda):
     """The first sub-segment starts from the caller's state (prefix of 700 tokens)."""
     say("two-level prefill(700) + prefill(1300, continue, nsub=3)")
