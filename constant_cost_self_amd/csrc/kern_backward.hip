@@ -474,6 +474,40 @@ __device__ inline float slice_sum(const float* p, int64_t stride, int nslices) {
     return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
+// sum over the slices of four consecutive partial entries (16-byte aligned): 8 independent
+// 16-byte loads in flight per thread
+__device__ inline f32x4 slice_sum4(const float* p, int64_t stride, int nslices) {
+    f32x4 s[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    int sl = 0;
+    for (; sl + 8 <= nslices; sl += 8)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + (sl + u) * stride));
+    for (; sl < nslices; ++sl) s[0] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + sl * stride));
+    return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
+// out[r][c] (r < nvalid, c < d; row stride d) = the chunk's pair sum plus the slice partials,
+// four consecutive columns per thread with 16-byte loads and stores when d is a multiple of 4,
+// else one column.  pair(r, c) returns the pair sum of one entry.
+template <typename Pair>
+__device__ inline void fin_rows(float* out, const float* part, int64_t pstride, int nslices, int nvalid, int d,
+                                Pair pair) {
+    if (d % 4 == 0) {
+        for (int q4 = threadIdx.x; q4 < nvalid * d / 4; q4 += kThreads) {
+            const int idx = 4 * q4, r = idx / d, c = idx % d;
+            f32x4 v = slice_sum4(part + idx, pstride, nslices);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += pair(r, c + e);
+            *reinterpret_cast<f32x4*>(out + idx) = v;
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < nvalid * d; idx += kThreads)
+            out[idx] = pair(idx / d, idx % d) + slice_sum(part + idx, pstride, nslices);
+    }
+}
+
 // MODE 0: dq; MODE 1: dk and dv.  Sum of the slice partials plus the chunk's pairs.
 template <typename In, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
@@ -533,30 +567,27 @@ __global__ __launch_bounds__(kThreads) void bwd_fin_kernel(BwdArgs a) {
     if (MODE == 0) {
         const float* part = a.part + ((bh * nch + cl) * (int64_t)a.nslices) * L * d_K;
         float* dq = a.dq + (bh * a.n + t0) * d_K;
-        for (int idx = tid; idx < nvalid * d_K; idx += kThreads) {
-            const int Tq = idx / d_K, i = idx % d_K;
+        fin_rows(dq, part, slice_stride * d_K, a.nslices, nvalid, d_K, [&](int Tq, int i) {
             float acc = 0.0f;
             for (int t = 0; t <= Tq; ++t) acc = fmaf(cw[Tq * (L + 1) + t], xk[t * d_K + i], acc);
-            dq[idx] = acc + slice_sum(part + idx, slice_stride * d_K, a.nslices);
-        }
+            return acc;
+        });
     } else {
         const int64_t pb = (bh * nch + cl) * (int64_t)a.nslices * L;
         const float* pk = a.part + pb * d_K;
         const float* pv = a.part2 + pb * d_V;
         float* dk = a.dk + (bh * a.n + t0) * d_K;
         float* dv = a.dv + (bh * a.n + t0) * d_V;
-        for (int idx = tid; idx < nvalid * d_K; idx += kThreads) {
-            const int t = idx / d_K, i = idx % d_K;
+        fin_rows(dk, pk, slice_stride * d_K, a.nslices, nvalid, d_K, [&](int t, int i) {
             float acc = 0.0f;
             for (int Tq = t; Tq < nvalid; ++Tq) acc = fmaf(cw[Tq * (L + 1) + t], xq[Tq * d_K + i], acc);
-            dk[idx] = acc + slice_sum(pk + idx, slice_stride * d_K, a.nslices);
-        }
-        for (int idx = tid; idx < nvalid * d_V; idx += kThreads) {
-            const int t = idx / d_V, j = idx % d_V;
+            return acc;
+        });
+        fin_rows(dv, pv, slice_stride * d_V, a.nslices, nvalid, d_V, [&](int t, int j) {
             float acc = 0.0f;
             for (int Tq = t; Tq < nvalid; ++Tq) acc = fmaf(ww[Tq * (L + 1) + t], uu[Tq * cols + j], acc);
-            dv[idx] = acc + slice_sum(pv + idx, slice_stride * d_V, a.nslices);
-        }
+            return acc;
+        });
     }
 }
 
