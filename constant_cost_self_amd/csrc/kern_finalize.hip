@@ -72,24 +72,30 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(PrefillSegArgs a) {
     }
     __syncthreads();
     const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * L * cols;
-    for (int idx = tid; idx < L * cols; idx += kThreads) {
-        const int j = idx / L, T_ = idx % L;      // token fastest: coalesced partial reads
-        const float* wr = W + T_ * (L + 1);
-        float acc = 0.0f;
-        for (int s = 0; s <= T_; ++s) acc = fmaf(wr[s], us[s * cols + j], acc);
-        // slice partials: read once, four independent sums to keep loads in flight
-        const float* p = part + j * L + T_;           // partials are [column][token]
-        const int64_t stride = (int64_t)L * cols;
-        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-        int sl = 0;
-        for (; sl + 4 <= a.nslices; sl += 4) {
-            a0 += __builtin_nontemporal_load(p + (sl + 0) * stride);
-            a1 += __builtin_nontemporal_load(p + (sl + 1) * stride);
-            a2 += __builtin_nontemporal_load(p + (sl + 2) * stride);
-            a3 += __builtin_nontemporal_load(p + (sl + 3) * stride);
+    const int64_t stride = (int64_t)L * cols;
+    // four tokens T0 .. T0 + 3 of one column per thread (L is a multiple of 4): the slice
+    // partials ([column][token]) with 16-byte loads, 8 slices in flight
+    for (int q4 = tid; q4 < L * cols / 4; q4 += kThreads) {
+        const int idx = 4 * q4, j = idx / L, T0 = idx % L;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s <= T0 + 3; ++s) {
+            const float u = us[s * cols + j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (s <= T0 + e) acc[e] = fmaf(W[(T0 + e) * (L + 1) + s], u, acc[e]);
         }
-        for (; sl < a.nslices; ++sl) a0 += __builtin_nontemporal_load(p + sl * stride);
-        num[T_ * cols + j] = acc + ((a0 + a1) + (a2 + a3));
+        const float* p = part + idx;
+        f32x4 ps[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ps[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        int sl = 0;
+        for (; sl + 8 <= a.nslices; sl += 8)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ps[u] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + (sl + u) * stride));
+        for (; sl < a.nslices; ++sl) ps[0] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + sl * stride));
+        const f32x4 sum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[(T0 + e) * cols + j] = acc[e] + sum[e];
     }
     __syncthreads();
     float* y = a.y + (bh * a.n + t0) * d_V;
