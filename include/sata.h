@@ -134,6 +134,16 @@ int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
  *        that prefix too.  Without the flag the prefix is empty.
  * stream hipStream_t (NULL = default stream)
  *
+ * Precision: bf16 inputs with d_K, d_V in {64, 128}, P >= 2 and chunk 64 take the
+ * matrix-core path: contractions with fp16 operands (the bf16 values converted exactly,
+ * power-of-two scales) and fp32 accumulation, the state in fp32, and the per-slice partial
+ * readouts of the value columns stored in fp16 (times 2^-8; the normaliser's in fp32).  Its
+ * per-row error against the exact attention is about 1e-3 on the benchmark shapes.  Its range
+ * limits: |sum_t phi_f(k_t) [v_t | 1]| < 1.6e7 for every feature and column (e.g. n max|v|
+ * for the constant feature), |q_i| up to about 16, and one slice's share of a numerator
+ * below 1.7e7; beyond them y becomes NaN rather than silently wrong.  All other cases take
+ * the fp32 path (errors of fp32 rounding, no such limits).
+ *
  * Two-level form (bf16 matrix-core path only): when the slices of all B x H heads
  * leave compute units idle (few heads), the sequence is cut into sub-segments of
  * whole readout windows whose local states are summed in parallel, turned into
