@@ -148,3 +148,26 @@ def test_two_level_automatic_long_single_head(torch_cuda):
     say("  sampled state err %.3e" % serr)
     assert serr <= TOL_BF16
     t.close()
+
+
+def test_two_level_falls_back_under_a_small_workspace_cap(torch_cuda):
+    """The two-level form needs the whole sequence's partials: under a small cap the one-level
+    scan runs in segments instead, with the same results."""
+    n = 2000
+    say("two-level asked for under an 8 MiB workspace cap, n=%d" % n)
+    x = _draw(n, 64, 1, 90)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(64, 4)
+    t.set_prefill_split(4)
+    t.set_workspace_limit(8 << 20)
+    S = new_state(1, 1, 64, 64, 4)
+    y = prefill(t, q, k, v, 64, S)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], 4)
+    err = max_row_err(y.cpu().numpy(), ref)
+    say("  y err %.3e" % err)
+    assert err <= TOL_BF16
+    _, S_ref = oracle.feature_form(None, x["k"][0, 0], x["v"][0, 0], 4, want_y=False)
+    M = S_ref.shape[1]
+    assert state_col_err(S[0, 0].cpu().numpy()[:, :M], S_ref) <= TOL_BF16
+    t.close()
