@@ -385,3 +385,24 @@ def test_mfma_wide_continue_and_segmented(torch_cuda):
     say("  segmented rel diffs y %.2e state %.2e" % (d13, dS))
     assert d13 <= 1e-5 and dS <= 1e-5
     t.close()
+
+
+def test_mfma_range_limit_gives_nan_not_wrong_values(torch_cuda):
+    """Past the documented range of the matrix-core path (the constant feature's row of the
+    state reaches n max|v|: here 8192 t, beyond 1.6e7 after 2048 tokens) the readout overflows
+    in fp16 and y is not finite; below it y is right.  With v constant the exact y is v."""
+    n = 4096
+    say("mfma range limit: v = 8192, n = %d" % n)
+    x = _bf16_64(n, 1, 1, 50)
+    x["v"][...] = 8192.0
+    q, k, v = upload(x, "bf16")
+    t = _tables(64, 4)
+    y = prefill(t, q, k, v, 64)
+    torch_cuda.cuda.synchronize()
+    yn = y[0, 0].cpu().numpy()
+    finite = np.isfinite(yn).all(axis=-1)
+    say("  finite rows: %d of %d (first non-finite %s)" % (finite.sum(), n, np.argmin(finite) if not finite.all() else "-"))
+    assert finite[:1024].all()
+    assert np.max(np.abs(yn[:1024] - 8192.0)) / 8192.0 <= TOL_BF16
+    assert not finite[2304:].any()
+    t.close()
