@@ -115,13 +115,13 @@ def test_two_level_equals_one_level(torch_cuda):
     t.close()
 
 
-def test_two_level_automatic_long_single_head(torch_cuda):
-    """One head of 16384 tokens leaves most compute units idle: the automatic choice takes
-    the two-level form.  Sampled rows of y and of the state against the oracle; the time of
-    both forms is printed."""
-    n = 16384
+@pytest.mark.parametrize("n", [16384, 65536])
+def test_two_level_automatic_long_single_head(torch_cuda, n):
+    """One head leaves most compute units idle: the automatic choice takes the two-level form
+    (n = 65536 is the benchmark's two-level workload, drawn as the benchmark draws it).
+    Sampled rows of y and of the state against the oracle; the time of both forms is printed."""
     say("automatic two-level, B=H=1 n=%d d=64" % n)
-    x = _draw(n, 64, 1, 70)
+    x = _draw(n, 64, 1, 70) if n != 65536 else inputs.draw((1, 1, n, 64), (1, 1, n, 64), "bf16", 0.5, 1.0, 0)
     q, k, v = upload(x, "bf16")
     t = sata.sata_tables_build(64, 4)
     S = new_state(1, 1, 64, 64, 4)
@@ -135,7 +135,7 @@ def test_two_level_automatic_long_single_head(torch_cuda):
         torch_cuda.cuda.synchronize()
         times[split] = (time.perf_counter() - t0) * 1e3
     say("  one-level %.2f ms, automatic %.2f ms" % (times[1], times[0]))
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 8191, 8192, n - 1],
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 8191, 8192, n // 2 - 1, n // 2, n - 1],
                                      np.random.default_rng(1).choice(n, 40, replace=False)]))
     ref = oracle.direct_rows(x["q"], x["k"], x["v"], 4, np.zeros_like(rows), rows)
     err = max_row_err(y[0, 0].cpu().numpy()[rows], ref)
