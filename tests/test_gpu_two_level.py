@@ -171,3 +171,31 @@ def test_two_level_falls_back_under_a_small_workspace_cap(torch_cuda):
     M = S_ref.shape[1]
     assert state_col_err(S[0, 0].cpu().numpy()[:, :M], S_ref) <= TOL_BF16
     t.close()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_two_level_sweep_against_one_level(torch_cuda, case):
+    """Seeded awkward shapes (sequence lengths around window boundaries, sub-segment counts
+    that do not divide the windows): the two forms agree on y and the final state."""
+    rng = np.random.default_rng(1000 + case)
+    d = int(rng.choice([64, 128]))
+    win = 4 if d == 64 else 2
+    n = int(64 * win * rng.integers(2, 9) + rng.integers(-70, 70))
+    nsub = int(rng.integers(2, 7))
+    say("two-level sweep: d=%d n=%d nsub=%d" % (d, n, nsub))
+    x = _draw(n, d, 1, 2000 + case)
+    q, k, v = upload(x, "bf16")
+    t = sata.sata_tables_build(d, 4)
+    out = []
+    for split in (1, nsub):
+        t.set_prefill_split(split)
+        S = new_state(1, 1, d, d, 4)
+        y = prefill(t, q, k, v, 64, S)
+        torch_cuda.cuda.synchronize()
+        out.append((y[0, 0].cpu().numpy().astype(np.float64), S[0, 0].cpu().numpy().astype(np.float64)))
+    t.close()
+    dy = max_row_err(out[1][0], out[0][0])
+    ds = state_col_err(out[1][1], out[0][1])
+    say("  y diff %.3e state diff %.3e" % (dy, ds))
+    assert np.all(np.isfinite(out[1][0]))
+    assert dy <= 2e-3 and ds <= 1e-5
