@@ -406,3 +406,30 @@ def test_mfma_range_limit_gives_nan_not_wrong_values(torch_cuda):
     assert np.max(np.abs(yn[:1024] - 8192.0)) / 8192.0 <= TOL_BF16
     assert not finite[2304:].any()
     t.close()
+
+
+@pytest.mark.parametrize("d,P", [(64, 2), (64, 3), (64, 5), (128, 3)])
+def test_mfma_term_counts_prefill_then_decode(torch_cuda, d, P):
+    """The matrix-core prefill (one level) at other term counts (another parent depth in the
+    operand building), then decode steps on its state, against the oracle."""
+    torch = torch_cuda
+    n1, steps = 700, 3
+    say("mfma bf16 d=%d P=%d: prefill(%d) + %d decode steps" % (d, P, n1, steps))
+    x = inputs.draw((1, 2, n1 + steps, d), (1, 2, n1 + steps, d), "bf16", 0.5 if d == 64 else 0.35, 1.0, 60 + P)
+    q, k, v = upload(x, "bf16")
+    t = _tables(d, P)
+    t.set_prefill_split(1)
+    S = new_state(1, 2, d, d, P)
+    y1 = prefill(t, q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(), 64, S)
+    ys = []
+    for T in range(n1, n1 + steps):
+        y = torch.empty((1, 2, d), device="cuda:0")
+        sata.sata_decode_step(t, S, q[:, :, T].contiguous(), k[:, :, T].contiguous(), v[:, :, T].contiguous(), y)
+        ys.append(y.cpu().numpy())
+    torch.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], P)
+    e1 = max_row_err(y1.cpu().numpy(), ref[:, :, :n1])
+    e2 = max_row_err(np.stack(ys, axis=2), ref[:, :, n1:])
+    say("  prefill y err %.3e, decode y err %.3e" % (e1, e2))
+    assert e1 <= TOL_BF16 and e2 <= TOL_BF16
+    t.close()
