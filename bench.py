@@ -236,7 +236,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--no-backward", action="store_true")
