@@ -13,6 +13,8 @@ its own stream: achieved = algorithmic work per launch / mean launch time.
                 (the forward FLOPs/token closed form of the method), peak = bf16 MFMA
                 2.5 PFLOP/s.
   decode:       bytes = 8 (d_V + 1) M per head (fp32 state read + write), peak 8 TB/s.
+  decode_pool:  the same step in its serving form: 16 of a pool of 24 prefilled sequences,
+                at seeded scattered slots; bytes and peak as for decode (active heads only).
   two_level:    one head of 65536 tokens (too few slices to fill the CUs): the automatic
                 two-level prefill against the one-level scan; flops as for prefill, over
                 the scan time (both passes and the prefix sum).
@@ -28,6 +30,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -140,6 +143,48 @@ def bench_decode(steps, warmup, prefill_chunk=64):
     M = math.comb(w.d_K + w.P - 1, w.P - 1)
     bytes_per_step = 8.0 * (w.d_V + 1) * M * w.B * w.H
     return wall, tim, bytes_per_step, w
+
+
+def bench_decode_pool(steps, warmup, pool_size=24, active=16, prefill_chunk=64):
+    """Serving-style decode: a preallocated pool of pool_size sequence states (the decode
+    workload's heads and sizes, each prefilled with its tokens), stepping a ragged batch of
+    `active` sequences whose states sit at seeded, scattered slots of the pool."""
+    import numpy as np
+    import torch
+    from constant_cost_self_amd import inputs, sata
+
+    w = dataclasses.replace(inputs.DECODE, B=pool_size)
+    log("decode pool: prefilling %d tokens for %dx%d heads" % (w.n, w.B, w.H))
+    x = inputs.prefill_inputs(w)
+    q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
+    t = sata.sata_tables_build(w.d_K, w.P)
+    Mp = sata.sata_state_stride(w.d_K, w.P)
+    pool = torch.zeros((pool_size, w.H, w.d_V + 1, Mp), device="cuda:0", dtype=torch.float32)
+    y = torch.empty((w.B, w.H, w.n, w.d_V), device="cuda:0", dtype=torch.float32)
+    sata.sata_prefill(t, q, k, v, y, pool, chunk=prefill_chunk)
+    del q, k, v, y, x
+    slots_h = np.random.default_rng(5).permutation(pool_size)[:active].astype(np.int32)
+    slots = torch.from_numpy(slots_h).to("cuda:0")
+    s = inputs.decode_inputs(w, warmup + steps, seed=2, B=active)
+    qs, ks, vs = (to_dev(s[c], w.dtype) for c in ("q", "k", "v"))
+    yd = torch.empty((active, w.H, w.d_V), device="cuda:0", dtype=torch.float32)
+    torch.cuda.synchronize()
+    t.set_timing(True)
+    for i in range(warmup):
+        sata.sata_decode_step_pool(t, pool, slots, qs[i], ks[i], vs[i], yd)
+    torch.cuda.synchronize()
+    t.read_timing()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        sata.sata_decode_step_pool(t, pool, slots, qs[i], ks[i], vs[i], yd)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tim = t.read_timing()
+    log("  decode pool %d steps: %.3f s; kernels %s" % (steps, wall, tim))
+    t.close()
+    M = math.comb(w.d_K + w.P - 1, w.P - 1)
+    bytes_per_step = 8.0 * (w.d_V + 1) * M * active * w.H
+    return wall, tim, bytes_per_step, w, slots_h
 
 
 def backward_flops_per_token(d_K, d_V, P):
@@ -339,6 +384,23 @@ def main():
                          "ms_per_launch": dk_ms / dk_n,
                          "algorithmic_bytes_per_launch": dbytes},
             "reduce_ms_per_step": dtim["decode_reduce"][0] / max(dtim["decode_reduce"][1], 1),
+        }
+
+    if not args.no_decode and args.only is None:
+        pwall, ptim, pbytes, pw, pslots = bench_decode_pool(args.decode_steps, args.decode_warmup)
+        pk_ms, pk_n = ptim["decode"]
+        pk_gbs = pbytes / (pk_ms / pk_n * 1e-3) / 1e9
+        out["decode_pool"] = {
+            "workload": "serving-style decode step: %d of %d pooled sequences (slots %s) x %d heads, "
+                        "d_K=d_V=%d, P=%d, fp32 states prefilled with %d tokens, %s q,k,v" %
+                        (len(pslots), pw.B, ",".join(str(int(v)) for v in pslots), pw.H, pw.d_K,
+                         pw.P, pw.n, pw.dtype),
+            "value": pbytes * args.decode_steps / pwall / 1e9, "unit": "GB/s",
+            "steps": args.decode_steps, "ms_per_step": pwall / args.decode_steps * 1e3,
+            "roofline": {"bound": "hbm", "achieved": pk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": pk_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "decode state read-modify-write (pool form)",
+                         "ms_per_launch": pk_ms / pk_n, "algorithmic_bytes_per_launch": pbytes},
         }
 
     if not args.no_two_level and args.only is None:
