@@ -141,7 +141,9 @@ struct FinLayout {
     static constexpr int vt = ks + L * XR * 2;
     static constexpr int tables = vt + ((COLS * TS * 2 + 15) / 16) * 16;
     static constexpr int num = 0;
-    static constexpr int bytes = tables > L * NS * 4 ? tables : L * NS * 4;
+    static constexpr int zs = num + L * NS * 4;        // normaliser partial sums [16 groups][L]
+    static constexpr int sums_end = zs + 16 * L * 4;
+    static constexpr int bytes = tables > sums_end ? tables : sums_end;
 };
 
 template <int DK, int DV, bool TILED>
@@ -250,12 +252,11 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
 
     // slice partials: num[t][col] = sum over slices.  Value columns: items of 16 bytes per
     // thread, all of them loaded together, several slices at a time (16 loads in flight).
-    // The normaliser column (16 items) is split over 16 slice groups, one per thread, and
-    // summed with LDS atomics, so that no thread walks the slices alone at the end.
+    // The normaliser column (16 items) is split over 16 slice groups, one per thread, so
+    // that no thread walks the slices alone at the end; the groups' sums are added in order.
     {
         const int64_t stride = TILED ? tiled_partial_floats(L, DV) : (int64_t)L * COLS;
         const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * stride;
-        if (tid < L) num[tid * NS + DV] = 0.0f;
         if constexpr (TILED) {
             // items of 8 fp16: [token tile][tile pair][lane (li, g)], tokens 16 tile + 4 g + r,
             // columns 32 pair + li (halves r) and 32 pair + 16 + li (halves 4 + r)
@@ -334,15 +335,22 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
                 for (int e = 0; e < 4; ++e) num[(t0 + e) * NS + col] = acc[i][e];
             }
         }
-        // normaliser column: token quad tid % 16, slices tid / 16, tid / 16 + 16, ...
-        const int tg = tid % (L / 4);
+        // normaliser column: token quad tid % 16, slices tid / 16, tid / 16 + 16, ...; the 16
+        // slice groups are then added in a fixed order (no atomics: y is reproducible)
+        const int tg = tid % (L / 4), sg = tid / (L / 4);
         const float* pz = part + (TILED ? L * DV / 2 : L * DV) + 4 * tg;
         f32x4_t z = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int s2 = tid / (L / 4); s2 < a.nslices; s2 += 256 / (L / 4))
+        for (int s2 = sg; s2 < a.nslices; s2 += 256 / (L / 4))
             z += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pz + s2 * stride));
-        __syncthreads();                              // the normaliser column is zeroed
+        float* zs = reinterpret_cast<float*>(fl + LY::zs);
+        *reinterpret_cast<f32x4_t*>(zs + sg * L + 4 * tg) = z;
+        __syncthreads();
+        if (tid < L) {
+            float acc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(&num[(4 * tg + e) * NS + DV], z[e]);
+            for (int i = 0; i < 256 / (L / 4); ++i) acc += zs[i * L + tid];
+            num[tid * NS + DV] = acc;
+        }
     }
     __syncthreads();
 #pragma unroll

@@ -682,9 +682,18 @@ hipError_t launch_state_prefix(float* states, const float* init, float* final, i
 
 int mfma_window(int d_K) { return d_K == 64 ? Layout<64, 5>::NSUB : Layout<128, 5>::NSUB; }
 
+bool mfma_shape(bool bf16, int d_K, int d_V, int P, int L) {
+    return bf16 && P >= 2 && P <= 5 && (d_V == 64 || d_V == 128) && (d_K == 64 || d_K == 128) && L == kL;
+}
+
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L) {
-    return m.ok && bf16 && d_K == m.d_K && P == m.P && P >= 2 && P <= 5 && (d_V == 64 || d_V == 128) &&
-           (d_K == 64 || d_K == 128) && L == kL;
+    return m.ok && d_K == m.d_K && P == m.P && mfma_shape(bf16, d_K, d_V, P, L);
+}
+
+int mfma_slice_count(const HostTables& h) {
+    MfmaHostRows r;
+    if (!build_mfma_rows(h, r)) return 0;
+    return r.nrows / kRowsPerSlice;
 }
 
 hipError_t launch_scan_mfma(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {

@@ -81,9 +81,9 @@ struct KernelTimer {
     }
 };
 
-// Default cap on the slice-partial workspace of one prefill call (about 11% of the
-// 288 GB of an MI355X); a call that needs more runs in segments of whole chunks.
-constexpr int64_t kDefaultWorkspace = 32LL << 30;
+// Default cap on the workspace of one call (about 5.6% of the 288 GB of an MI355X); a
+// prefill whose slice partials need more runs in segments of whole readout windows.
+constexpr int64_t kDefaultWorkspace = 16LL << 30;
 
 struct sata_tables {
     sata::HostTables h;
@@ -96,8 +96,9 @@ struct sata_tables {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     int64_t ws_limit = kDefaultWorkspace;
-    int cus = 0;                      // compute units of the device
+    int cus = 0;                      // compute units of the device (256 assumed host-only)
     int split = 0;                    // two-level prefill: 0 automatic, 1 never, k >= 2 forced
+    int mfma_slices = 0;              // feature slices of the matrix-core scan (0: not its shape)
 };
 
 namespace {
@@ -152,6 +153,116 @@ int check_sizes(int d_K, int d_V, int P) {
         return fail(SATA_ERR_UNSUPPORTED,
                     "unsupported sizes d_K=%d d_V=%d P=%d (need 1..128, 1..128, 1..5)", d_K,
                     d_V, P);
+    return SATA_OK;
+}
+
+// How a prefill of these sizes runs: which scan, how the feature axis is sliced, how the
+// sequence is cut (two-level sub-segments, or segments of whole readout windows under the
+// workspace cap) and the workspace that takes.
+struct PrefillPlan {
+    bool mfma = false;
+    int win = 1;                 // chunks per readout window
+    int nslices = 0, slice_feats = 0;
+    int nchunks = 0;
+    int64_t per_chunk = 0;       // slice-partial bytes of one chunk of every head
+    int64_t state_b = 0;         // bytes of one state per head, all heads
+    int nsub = 1, sub_chunks = 0; // two-level form when nsub >= 2
+    int seg = 0, nseg = 1;       // one-level form: segments of seg chunks
+    int64_t ws_bytes = 0;
+};
+
+// Segment length of the one-level form: whole readout windows (a segment starts a new
+// window, so results do not depend on the segmentation), at least one window, segments of
+// nearly equal length (each boundary stores and reloads the state of every slice), and
+// per_chunk * seg + carrier <= limit whenever one window fits.
+int64_t segment_chunks(int64_t nchunks, int64_t win, int64_t per_chunk, int64_t carrier,
+                       int64_t limit) {
+    if (per_chunk * nchunks <= limit) return nchunks;
+    int64_t seg = (limit - carrier) / per_chunk;
+    seg -= seg % win;
+    if (seg < win) seg = win;                          // one window even above the cap
+    if (seg >= nchunks) return nchunks;
+    const int64_t ns = (nchunks + seg - 1) / seg;
+    const int64_t even = (nchunks + ns - 1) / ns;      // <= seg, since ns segments of seg cover
+    return (even + win - 1) / win * win;               // whole windows, still <= seg
+}
+
+int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, bool bf16,
+                 bool has_state, bool cont, PrefillPlan& pl) {
+    const int d_K = t->h.d_K, P = t->h.P, L = chunk, cols = d_V + 1;
+    const int64_t BH = (int64_t)B * H;
+    pl = PrefillPlan();
+    pl.nchunks = (int)(((int64_t)n + L - 1) / L);
+    pl.mfma = t->mfma_slices > 0 && sata::mfma_shape(bf16, d_K, d_V, P, L);
+    if (pl.mfma) {
+        pl.nslices = t->mfma_slices;
+        pl.slice_feats = sata::kRowsPerSlice * 8;
+        pl.win = sata::mfma_window(d_K);
+    } else {
+        pl.win = 1;
+        pl.slice_feats = sata::valu_slice_feats(d_K, d_V, L);
+        if (pl.slice_feats == 0) return fail(SATA_ERR_UNSUPPORTED, "no fp32 scan slice fits LDS");
+        pl.nslices = (int)((t->h.M + pl.slice_feats - 1) / pl.slice_feats);
+    }
+    pl.per_chunk = BH * pl.nslices * 4 *
+                   (pl.mfma ? sata::tiled_partial_floats(L, d_V) : (int64_t)L * cols);
+    pl.state_b = BH * cols * t->h.M_pad * 4;
+    const int64_t limit = t->ws_limit;
+
+    // Two-level form: when the slices of all heads leave compute units idle, the sequence
+    // is cut into nsub sub-segments of whole readout windows (at least 4 windows each).
+    if (pl.mfma && t->split != 1) {
+        const int64_t nwin = (pl.nchunks + pl.win - 1) / pl.win;
+        int64_t nsub = 1;
+        if (t->split >= 2) {
+            nsub = t->split;
+        } else {
+            const int64_t cus = t->cus > 0 ? t->cus : 256;
+            const int64_t wgs = BH * pl.nslices;                   // workgroups of one scan launch
+            nsub = wgs < cus ? cus / wgs : 1;
+            if (nsub > nwin / 4) nsub = nwin / 4;
+        }
+        if (nsub > nwin) nsub = nwin;
+        int64_t sub_chunks = pl.nchunks;
+        if (nsub >= 2) {
+            sub_chunks = (nwin + nsub - 1) / nsub * pl.win;
+            nsub = (pl.nchunks + sub_chunks - 1) / sub_chunks;     // no empty sub-segment
+        }
+        const int64_t need = pl.per_chunk * pl.nchunks + pl.state_b * nsub;
+        if (nsub >= 2 && BH * nsub <= 65535 && need <= limit) {
+            pl.nsub = (int)nsub;
+            pl.sub_chunks = (int)sub_chunks;
+            pl.seg = pl.nchunks;
+            pl.nseg = 1;
+            pl.ws_bytes = need;
+            return SATA_OK;
+        }
+    }
+    (void)cont;
+    const int64_t carrier = has_state ? 0 : pl.state_b;
+    pl.seg = (int)segment_chunks(pl.nchunks, pl.win, pl.per_chunk, carrier, limit);
+    pl.nseg = (pl.nchunks + pl.seg - 1) / pl.seg;
+    pl.ws_bytes = pl.per_chunk * pl.seg + (!has_state && pl.nseg > 1 ? pl.state_b : 0);
+    return SATA_OK;
+}
+
+// Checks shared by sata_prefill and the workspace query (no pointer is dereferenced).
+int check_prefill_sizes(const sata_tables* t, int B, int H, int n, int d_K, int d_V, int P,
+                        int chunk, sata_dtype in_dtype) {
+    if (B < 1 || H < 1 || n < 1) return fail(SATA_ERR_ARG, "need B, H, n >= 1 (got %d %d %d)", B, H, n);
+    int rc = check_sizes(d_K, d_V, P);
+    if (rc) return rc;
+    if (d_K != t->h.d_K || P != t->h.P)
+        return fail(SATA_ERR_ARG, "handle built for d_K=%d P=%d, call has d_K=%d P=%d",
+                    t->h.d_K, t->h.P, d_K, P);
+    if (in_dtype != SATA_F32 && in_dtype != SATA_BF16)
+        return fail(SATA_ERR_ARG, "unknown input dtype %d", (int)in_dtype);
+    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 16, 32, 64 or 128 (got %d)", chunk);
+    if (sata::finalize_lds_bytes(d_K, d_V, chunk) > 160 * 1024)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk=%d is too large for d_K=%d, d_V=%d", chunk,
+                    d_K, d_V);
+    if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
     return SATA_OK;
 }
 
@@ -211,6 +322,7 @@ int sata_tables_build(int d_K, int P, sata_tables** out) {
         sata_tables_free(t);
         return fail(rc, "MFMA slice tables failed");
     }
+    t->mfma_slices = t->mfma.ok ? t->mfma.nslices : 0;
     *out = t;
     return SATA_OK;
 }
@@ -228,6 +340,7 @@ int sata_tables_build_host(int d_K, int P, sata_tables** out) {
         return fail(SATA_ERR_ARG, "table construction failed for d_K=%d P=%d", d_K, P);
     }
     t->device = -1;
+    t->mfma_slices = sata::mfma_slice_count(t->h);
     *out = t;
     return SATA_OK;
 }
@@ -303,6 +416,48 @@ int sata_set_workspace_limit(sata_tables* t, int64_t bytes) {
     return SATA_OK;
 }
 
+int sata_prefill_workspace(const sata_tables* t, int B, int H, int n, int d_K, int d_V, int P,
+                           int chunk, sata_dtype in_dtype, int flags, int with_state,
+                           int64_t* bytes, int* segments, int* subsegments) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!bytes) return fail(SATA_ERR_ARG, "bytes is NULL");
+    int rc = check_prefill_sizes(t, B, H, n, d_K, d_V, P, chunk, in_dtype);
+    if (rc) return rc;
+    if (flags & ~SATA_PREFILL_CONTINUE) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
+    const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0;
+    if (cont && !with_state) return fail(SATA_ERR_ARG, "SATA_PREFILL_CONTINUE needs a state buffer");
+    sata_tables* tm = const_cast<sata_tables*>(t);
+    std::lock_guard<std::mutex> lock(tm->mu);
+    PrefillPlan pl;
+    rc = plan_prefill(t, B, H, n, d_V, chunk, in_dtype == SATA_BF16, with_state != 0, cont, pl);
+    if (rc) return rc;
+    *bytes = pl.ws_bytes;
+    if (segments) *segments = pl.nseg;
+    if (subsegments) *subsegments = pl.nsub;
+    return SATA_OK;
+}
+
+int sata_decode_workspace(const sata_tables* t, int B, int H, int d_V, int64_t* bytes) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!bytes) return fail(SATA_ERR_ARG, "bytes is NULL");
+    if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
+    if (d_V < 1 || d_V > sata::kMaxD) return fail(SATA_ERR_UNSUPPORTED, "d_V=%d outside 1..128", d_V);
+    *bytes = sata::decode_partial_floats(B * H, d_V, t->h.M_pad) * 4;
+    return SATA_OK;
+}
+
+int sata_reserve_workspace(sata_tables* t, int64_t bytes, void* stream) {
+    clear_err();
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (bytes < 0) return fail(SATA_ERR_ARG, "negative size");
+    int rc = check_device(t);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(t->mu);
+    return ensure_ws(t, (size_t)bytes, (hipStream_t)stream);
+}
+
 int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void* v, float* y,
                  float* state, int B, int H, int n, int d_K, int d_V, int P, int chunk,
                  sata_dtype in_dtype, int flags, void* stream) {
@@ -310,32 +465,23 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     sata_tables* t = const_cast<sata_tables*>(tc);
     if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
     if (!q || !k || !v || !y) return fail(SATA_ERR_ARG, "q, k, v and y must be non-NULL");
-    if (B < 1 || H < 1 || n < 1) return fail(SATA_ERR_ARG, "need B, H, n >= 1 (got %d %d %d)", B, H, n);
-    int rc = check_sizes(d_K, d_V, P);
+    int rc = check_prefill_sizes(t, B, H, n, d_K, d_V, P, chunk, in_dtype);
     if (rc) return rc;
-    if (d_K != t->h.d_K || P != t->h.P)
-        return fail(SATA_ERR_ARG, "handle built for d_K=%d P=%d, call has d_K=%d P=%d",
-                    t->h.d_K, t->h.P, d_K, P);
-    if (in_dtype != SATA_F32 && in_dtype != SATA_BF16)
-        return fail(SATA_ERR_ARG, "unknown input dtype %d", (int)in_dtype);
-    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
-        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 16, 32, 64 or 128 (got %d)", chunk);
     if (flags & ~SATA_PREFILL_CONTINUE) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
     const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0;
     if (cont && !state) return fail(SATA_ERR_ARG, "SATA_PREFILL_CONTINUE needs a state buffer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
         (state && !aligned16(state)))
         return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-    if (sata::finalize_lds_bytes(d_K, d_V, chunk) > 160 * 1024)
-        return fail(SATA_ERR_UNSUPPORTED, "chunk=%d is too large for d_K=%d, d_V=%d", chunk,
-                    d_K, d_V);
-    if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
     rc = check_device(t);
     if (rc) return rc;
 
+    std::lock_guard<std::mutex> lock(t->mu);
+    PrefillPlan pl;
+    rc = plan_prefill(t, B, H, n, d_V, chunk, in_dtype == SATA_BF16, state != nullptr, cont, pl);
+    if (rc) return rc;
     const bool bf16 = in_dtype == SATA_BF16;
     const int BH = B * H, L = chunk, cols = d_V + 1;
-    const int nchunks = (int)(((int64_t)n + L - 1) / L);
 
     sata::PrefillSegArgs a{};
     a.q = q; a.k = k; a.v = v; a.y = y;
@@ -346,116 +492,64 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     a.M_pad = t->h.M_pad;
     a.BH = BH; a.n = n; a.d_K = d_K; a.d_V = d_V; a.P = P; a.L = L;
     a.bf16 = bf16;
+    a.nslices = pl.nslices;
+    a.slice_feats = pl.slice_feats;
+    a.win = pl.win;
+    a.partial_tiled = pl.mfma;
+    a.mfma_rows = pl.mfma ? t->mfma.d_rows : nullptr;
 
-    const bool use_mfma = sata::mfma_supported(t->mfma, bf16, d_K, d_V, P, L);
-    if (use_mfma) {
-        a.nslices = t->mfma.nslices;
-        a.slice_feats = t->mfma.slice_feats;
-        a.mfma_rows = t->mfma.d_rows;
-        a.win = sata::mfma_window(d_K);
-        a.partial_tiled = true;
-    } else {
-        a.win = 1;
-        a.partial_tiled = false;
-        a.slice_feats = sata::valu_slice_feats(d_K, d_V, L);
-        if (a.slice_feats == 0) return fail(SATA_ERR_UNSUPPORTED, "no VALU slice fits LDS");
-        a.nslices = (int)((t->h.M + a.slice_feats - 1) / a.slice_feats);
-        a.mfma_rows = nullptr;
-    }
-
-    std::lock_guard<std::mutex> lock(t->mu);
     hipStream_t st = (hipStream_t)stream;
-    const int64_t per_chunk = (int64_t)BH * a.nslices * 4 *
-                              (a.partial_tiled ? sata::tiled_partial_floats(L, d_V) : (int64_t)L * cols);
-    const int64_t state_b = (int64_t)BH * cols * t->h.M_pad * 4;
-
-    // Two-level form (the state recurrence as a prefix over segments, [TA] "Hardware
-    // optimisation path"): when the slices of all heads leave compute units idle, the
-    // sequence is cut into nsub sub-segments of whole readout windows.  Their local states
-    // are accumulated in parallel (update-only scan), turned into each sub-segment's
-    // starting state by a prefix sum, and the sub-segments are then scanned in parallel from
-    // those states.  Same sums as one segment, in another order.
-    if (use_mfma && t->split != 1) {
-        const int64_t nwin = (nchunks + a.win - 1) / a.win;
-        int64_t nsub = 1;
-        if (t->split >= 2) {
-            nsub = t->split;
-        } else {
-            const int64_t wgs = (int64_t)BH * a.nslices;            // workgroups of one scan launch
-            nsub = wgs < t->cus ? t->cus / wgs : 1;
-            if (nsub > nwin / 4) nsub = nwin / 4;                   // at least 4 windows each
-        }
-        if (nsub > nwin) nsub = nwin;
-        int64_t sub_chunks = nchunks;
-        if (nsub >= 2) {
-            sub_chunks = (nwin + nsub - 1) / nsub * a.win;
-            nsub = (nchunks + sub_chunks - 1) / sub_chunks;         // no empty sub-segment
-        }
-        const int64_t need = per_chunk * nchunks + state_b * nsub;
-        if (nsub >= 2 && BH * nsub <= 65535 && need <= t->ws_limit) {
-            rc = ensure_ws(t, (size_t)need, st);
-            if (rc) return rc;
-            a.partial = (float*)t->ws;
-            float* starts = (float*)((char*)t->ws + per_chunk * nchunks);
-            a.c_begin = 0;
-            a.c_end = nchunks;
-            a.nsub = (int)nsub;
-            a.sub_chunks = (int)sub_chunks;
-            a.state = starts;
-            hipEvent_t ev = t->timer.begin(st);
-            a.update_only = true;                   // local states from zero
-            a.load_state = 0;
-            a.store_state = 1;
-            hipError_t e = sata::launch_scan_mfma(a, t->mfma, st);
-            if (e == hipSuccess)
-                e = sata::launch_state_prefix(starts, cont ? state : nullptr, state, BH, (int)nsub,
-                                              (int64_t)cols * t->h.M_pad, st);
-            a.update_only = false;                  // readouts and partials from the starts
-            a.load_state = 1;
-            a.store_state = 0;
-            if (e == hipSuccess) e = sata::launch_scan_mfma(a, t->mfma, st);
-            t->timer.end(SATA_KERNEL_SCAN, ev, st);
-            if (e != hipSuccess)
-                return fail(SATA_ERR_HIP, "two-level scan launch failed: %s", hipGetErrorString(e));
-            ev = t->timer.begin(st);
-            e = sata::launch_finalize(a, st);
-            t->timer.end(SATA_KERNEL_FINALIZE, ev, st);
-            if (e != hipSuccess)
-                return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
-            return SATA_OK;
-        }
-    }
-
-    int64_t seg = nchunks;
-    if (per_chunk * seg > t->ws_limit) {
-        seg = (t->ws_limit - (state ? 0 : state_b)) / per_chunk;
-        if (seg < a.win) seg = a.win;            // at least one readout window
-        // equal segments: every segment boundary stores and reloads the state, so no
-        // segment should be much shorter than the others
-        const int64_t ns = (nchunks + seg - 1) / seg;
-        seg = (nchunks + ns - 1) / ns;
-        // whole readout windows per segment: a segment starts a new window, so the
-        // windows (and the results) do not depend on the segmentation
-        seg -= seg % a.win;
-    }
-    const int nseg = (int)((nchunks + seg - 1) / seg);
-    float* carrier = state;
-    size_t need = (size_t)(per_chunk * seg);
-    if (!state && nseg > 1) need += (size_t)state_b;
-    rc = ensure_ws(t, need, st);
+    rc = ensure_ws(t, (size_t)pl.ws_bytes, st);
     if (rc) return rc;
-    a.partial = (float*)t->ws;
-    if (!carrier && nseg > 1) carrier = (float*)((char*)t->ws + per_chunk * seg);
-    a.state = carrier;
 
-    for (int s = 0; s < nseg; ++s) {
-        a.c_begin = (int)(s * seg);
-        a.c_end = (int)((s + 1) * seg < nchunks ? (s + 1) * seg : nchunks);
-        a.load_state = (s > 0 || cont) ? 1 : 0;
-        a.store_state = (s < nseg - 1 || state) ? 1 : 0;
+    if (pl.nsub >= 2) {
+        // Two-level form (the state recurrence as a prefix over segments, [TA] "Hardware
+        // optimisation path"): the local states of the sub-segments are accumulated in
+        // parallel (update-only scan), turned into each sub-segment's starting state by a
+        // prefix sum, and the sub-segments are then scanned in parallel from those states.
+        // Same sums as one segment, in another order.
+        a.partial = (float*)t->ws;
+        float* starts = (float*)((char*)t->ws + pl.per_chunk * pl.nchunks);
+        a.c_begin = 0;
+        a.c_end = pl.nchunks;
+        a.nsub = pl.nsub;
+        a.sub_chunks = pl.sub_chunks;
+        a.state = starts;
         hipEvent_t ev = t->timer.begin(st);
-        hipError_t e = use_mfma ? sata::launch_scan_mfma(a, t->mfma, st)
-                                : sata::launch_scan_valu(a, st);
+        a.update_only = true;                   // local states from zero
+        a.load_state = 0;
+        a.store_state = 1;
+        hipError_t e = sata::launch_scan_mfma(a, t->mfma, st);
+        if (e == hipSuccess)
+            e = sata::launch_state_prefix(starts, cont ? state : nullptr, state, BH, pl.nsub,
+                                          (int64_t)cols * t->h.M_pad, st);
+        a.update_only = false;                  // readouts and partials from the starts
+        a.load_state = 1;
+        a.store_state = 0;
+        if (e == hipSuccess) e = sata::launch_scan_mfma(a, t->mfma, st);
+        t->timer.end(SATA_KERNEL_SCAN, ev, st);
+        if (e != hipSuccess)
+            return fail(SATA_ERR_HIP, "two-level scan launch failed: %s", hipGetErrorString(e));
+        ev = t->timer.begin(st);
+        e = sata::launch_finalize(a, st);
+        t->timer.end(SATA_KERNEL_FINALIZE, ev, st);
+        if (e != hipSuccess)
+            return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
+        return SATA_OK;
+    }
+
+    a.partial = (float*)t->ws;
+    float* carrier = state;
+    if (!carrier && pl.nseg > 1) carrier = (float*)((char*)t->ws + pl.per_chunk * pl.seg);
+    a.state = carrier;
+    for (int s = 0; s < pl.nseg; ++s) {
+        a.c_begin = s * pl.seg;
+        a.c_end = (s + 1) * pl.seg < pl.nchunks ? (s + 1) * pl.seg : pl.nchunks;
+        a.load_state = (s > 0 || cont) ? 1 : 0;
+        a.store_state = (s < pl.nseg - 1 || state) ? 1 : 0;
+        hipEvent_t ev = t->timer.begin(st);
+        hipError_t e = pl.mfma ? sata::launch_scan_mfma(a, t->mfma, st)
+                               : sata::launch_scan_valu(a, st);
         t->timer.end(SATA_KERNEL_SCAN, ev, st);
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));

@@ -48,7 +48,12 @@ struct MfmaTables {
 
 int build_mfma_tables(const HostTables& h, MfmaTables& m);
 void free_mfma_tables(MfmaTables& m);
+// Shapes the matrix-core scan serves (bf16 inputs, d_K and d_V in {64, 128}, 2 <= P <= 5,
+// chunk 64), whatever the tables.
+bool mfma_shape(bool bf16, int d_K, int d_V, int P, int L);
 bool mfma_supported(const MfmaTables& m, bool bf16, int d_K, int d_V, int P, int L);
+// Feature slices of the matrix-core scan for these host tables (0 if it does not apply).
+int mfma_slice_count(const HostTables& h);
 // Chunks per readout window of the MFMA scan (the finalize's direct part spans the window).
 int mfma_window(int d_K);
 hipError_t launch_scan_mfma(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st);

@@ -28,7 +28,8 @@ EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "s
             "sata_state_stride", "sata_state_bytes", "sata_prefill", "sata_decode_step",
             "sata_decode_step_pool", "sata_prefill_backward",
             "sata_last_error", "sata_set_workspace_limit", "sata_set_prefill_split", "sata_set_timing",
-            "sata_read_timing")
+            "sata_read_timing", "sata_prefill_workspace", "sata_decode_workspace",
+            "sata_reserve_workspace")
 KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward")
 
 _lib = None
@@ -84,6 +85,14 @@ def load():
     lib.sata_set_prefill_split.argtypes = [vp, i32]
     lib.sata_set_timing.restype = i32
     lib.sata_set_timing.argtypes = [vp, i32]
+    lib.sata_prefill_workspace.restype = i32
+    lib.sata_prefill_workspace.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                           ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                           ctypes.POINTER(i32)]
+    lib.sata_decode_workspace.restype = i32
+    lib.sata_decode_workspace.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i64)]
+    lib.sata_reserve_workspace.restype = i32
+    lib.sata_reserve_workspace.argtypes = [vp, i64, vp]
     lib.sata_read_timing.restype = i32
     lib.sata_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
@@ -180,6 +189,27 @@ class Tables:
     def set_prefill_split(self, nsub: int):
         """Sub-segments of the two-level prefill: 0 automatic, 1 never, k >= 2 forced."""
         _check(load().sata_set_prefill_split(self.handle, nsub))
+
+    def prefill_workspace(self, B: int, H: int, n: int, d_V: int, *, chunk: int = 64,
+                          dtype: int = SATA_BF16, continue_state: bool = False,
+                          with_state: bool = True):
+        """(workspace bytes, one-level segments, two-level sub-segments) of a prefill."""
+        nb = ctypes.c_int64()
+        seg = ctypes.c_int()
+        sub = ctypes.c_int()
+        _check(load().sata_prefill_workspace(self.handle, B, H, n, self.d_K, d_V, self.P, chunk,
+                                             dtype, SATA_PREFILL_CONTINUE if continue_state else 0,
+                                             1 if with_state else 0, ctypes.byref(nb),
+                                             ctypes.byref(seg), ctypes.byref(sub)))
+        return nb.value, seg.value, sub.value
+
+    def decode_workspace(self, B: int, H: int, d_V: int) -> int:
+        nb = ctypes.c_int64()
+        _check(load().sata_decode_workspace(self.handle, B, H, d_V, ctypes.byref(nb)))
+        return nb.value
+
+    def reserve_workspace(self, nbytes: int, stream=None):
+        _check(load().sata_reserve_workspace(self.handle, nbytes, _stream(stream)))
 
     def set_timing(self, enable: bool):
         _check(load().sata_set_timing(self.handle, 1 if enable else 0))

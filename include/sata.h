@@ -40,12 +40,18 @@
  *   Causality.  Row T attends to t <= T (inclusive); the decode step adds the new
  *     token to the state before reading it out.
  *   Streams.  Work is enqueued on `stream` (a hipStream_t, NULL = default stream)
- *     and returns without waiting; no call synchronises the host.
+ *     and returns without waiting; apart from workspace growth (below) no call
+ *     synchronises the host.
  *   Ownership.  The caller owns q, k, v, y and the state.  The library owns the
  *     tables handle (host and device copies) and a scratch workspace held by the
  *     handle, grown on demand and released by sata_tables_free.  Calls that share
  *     one handle must not overlap in time (issue them on one stream, or use one
  *     handle per stream): they share that workspace.
+ *   Workspace growth.  A call that needs more workspace than the handle holds waits
+ *     for its stream (hipStreamSynchronize), frees the old buffer and allocates a
+ *     larger one; that is the only host synchronisation of the compute calls.  Size
+ *     it beforehand with sata_prefill_workspace / sata_decode_workspace and
+ *     sata_reserve_workspace to keep every later call free of it.
  *   Errors.  Every int-returning call returns SATA_OK (0) or a negative code and
  *     never aborts; sata_last_error() gives the calling thread's last message.
  *     Arguments are checked before anything is enqueued, so on an argument error
@@ -221,11 +227,34 @@ const char *sata_last_error(void);
 
 /*
  * Optional: cap (bytes) on the workspace a handle may hold; prefill splits the
- * sequence into segments of whole chunks to stay under it (a segment holds at
- * least one readout window: 4 chunks at d_K = 64, 2 at d_K = 128 on the bf16
- * matrix-core path, 1 otherwise).  0 restores the default (32 GiB).
+ * sequence into segments of whole readout windows to stay under it (a segment holds
+ * at least one window: 4 chunks at d_K = 64, 2 at d_K = 128 on the bf16 matrix-core
+ * path, 1 otherwise, even when one window alone exceeds the cap).  0 restores the
+ * default (16 GiB).
  */
 int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
+
+/*
+ * Workspace that sata_prefill with these arguments would use under the handle's
+ * current cap, and how it would cut the sequence; no device work, so a host-only
+ * handle serves too.  with_state: nonzero if the call passes a state buffer.
+ * *bytes receives the workspace bytes; *segments (nullable) the number of segments
+ * of the one-level scan; *subsegments (nullable) the sub-segments of the two-level
+ * form (1 when it is not used).  Errors: those of sata_prefill's size checks.
+ */
+int sata_prefill_workspace(const sata_tables *t, int B, int H, int n, int d_K, int d_V,
+                           int P, int chunk, sata_dtype in_dtype, int flags, int with_state,
+                           int64_t *bytes, int *segments, int *subsegments);
+
+/* Workspace bytes of sata_decode_step (or the pool form with count = B) for B x H heads. */
+int sata_decode_workspace(const sata_tables *t, int B, int H, int d_V, int64_t *bytes);
+
+/*
+ * Grow the handle's workspace to at least `bytes` now (growth waits for `stream`,
+ * see "Workspace growth"), so that later calls needing at most that much neither
+ * allocate nor synchronise.  SATA_ERR_OOM if the allocation fails.
+ */
+int sata_reserve_workspace(sata_tables *t, int64_t bytes, void *stream);
 
 /*
  * Optional: sub-segments of the two-level prefill.  0 (the default): automatic,

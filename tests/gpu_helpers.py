@@ -1,7 +1,9 @@
 """Helpers for the GPU parity tests: upload seeded inputs, call the C ABI through
-the binding, compare with the oracle by the per-row normalised metric."""
+the binding, compare with the oracle by the per-row normalised metric (y) and by
+the per-degree-block metric (states)."""
 from __future__ import annotations
 
+import math
 import sys
 
 import numpy as np
@@ -47,32 +49,63 @@ def max_row_err(y_gpu, y_ref) -> float:
     return float(np.max(oracle.row_rel_err(np.asarray(y_gpu, dtype=np.float64), y_ref)))
 
 
-def state_col_err(S_gpu, S_ref) -> float:
-    """max over columns j of max_f |dS[j,f]| / max_f |S_ref[j,f]|; S as [cols, M]."""
-    S_gpu = np.asarray(S_gpu, dtype=np.float64)
-    num = np.max(np.abs(S_gpu - S_ref), axis=1)
-    den = np.max(np.abs(S_ref), axis=1)
-    return float(np.max(num / np.where(den > 0, den, 1.0)))
+def feature_degrees(d_K: int, P: int) -> np.ndarray:
+    """Degree p of every feature f of the concatenated order p = 0 .. P-1 (block sizes
+    binom(d_K + p - 1, p))."""
+    return np.repeat(np.arange(P), [math.comb(d_K + p - 1, p) for p in range(P)])
 
 
-def sample_feature_rows(M: int, count: int, seed: int) -> np.ndarray:
-    """Rows of the state to check: the first few (p = 0 and degree-1 features), the
-    last two, and `count` drawn at random."""
+def _block_err(got, ref, deg, P) -> float:
+    """got, ref: [rows, cols]; per degree block and column, max |got - ref| over the block's
+    rows / max |ref| over them; the max over blocks and columns."""
+    worst = 0.0
+    for p in range(P):
+        sel = deg == p
+        if not sel.any():
+            continue
+        num = np.max(np.abs(got[sel] - ref[sel]), axis=0)
+        den = np.max(np.abs(ref[sel]), axis=0)
+        worst = max(worst, float(np.max(num / np.where(den > 0, den, 1.0))))
+    return worst
+
+
+def state_col_err(S_gpu, S_ref, d_K: int, P: int) -> float:
+    """State bar, per Taylor term: for every degree block p (the rows of M_p) and column j,
+    max_f |dS[j, f]| / max_f |S_ref[j, f]| over the block's features; the max over blocks
+    and columns.  S as [cols, M or M_pad] (padding columns are ignored here; callers check
+    that they are zero).  A block's own scale is the reference, so an error in the small
+    high-degree rows cannot hide under the large p = 0 row."""
+    deg = feature_degrees(d_K, P)
+    M = deg.size
+    got = np.asarray(S_gpu, dtype=np.float64)[:, :M].T
+    ref = np.asarray(S_ref, dtype=np.float64)[:, :M].T
+    return _block_err(got, ref, deg, P)
+
+
+def sample_feature_rows(d_K: int, P: int, count: int, seed: int) -> np.ndarray:
+    """Rows of the state to check, stratified by degree: the first and last row of every
+    degree block and about count / P rows drawn at random within each block."""
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 2, 3, M - 2, M - 1]
-    return np.unique(np.concatenate([fixed, rng.choice(M, size=count, replace=False)]))
+    sizes = [math.comb(d_K + p - 1, p) for p in range(P)]
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    picks = []
+    for p in range(P):
+        lo, hi = int(offs[p]), int(offs[p + 1])
+        picks += [lo, hi - 1]
+        k = min(hi - lo, max(count // P, 1))
+        picks += list(lo + rng.choice(hi - lo, size=k, replace=False))
+    return np.unique(np.asarray(picks, dtype=np.int64))
 
 
-def sampled_state_err(S_gpu, S_ref_rows, rows) -> float:
-    """The state bound on sampled rows: S_gpu is one head's [cols, M_pad] state,
-    S_ref_rows[r, j] = S[rows[r], j] from the oracle.  max over columns j of
-    max_r |dS| / max_r |S_ref| (row 0, the largest row, is always sampled)."""
+def sampled_state_err(S_gpu, S_ref_rows, rows, d_K: int, P: int) -> float:
+    """The state bar on sampled rows: S_gpu is one head's [cols, M_pad] state,
+    S_ref_rows[r, j] = S[rows[r], j] from the oracle; per degree block of the sampled rows
+    and column, max |dS| / max |S_ref| (see state_col_err)."""
+    deg = feature_degrees(d_K, P)[np.asarray(rows)]
     got = np.asarray(S_gpu, dtype=np.float64)[:, rows].T
-    num = np.max(np.abs(got - S_ref_rows), axis=0)
-    den = np.max(np.abs(S_ref_rows), axis=0)
-    return float(np.max(num / np.where(den > 0, den, 1.0)))
+    return _block_err(got, np.asarray(S_ref_rows, dtype=np.float64), deg, P)
 
 
 __all__ = ["inputs", "oracle", "sata", "TOL_BF16", "TOL_F32", "say", "dev_tensor", "upload",
            "prefill", "new_state", "max_row_err", "state_col_err", "sample_feature_rows",
-           "sampled_state_err"]
+           "sampled_state_err", "feature_degrees"]
