@@ -3,9 +3,14 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|mid|wide]
 
 One step = one chunked prefill (tables already built) of the workload with the
-final state written.  value = prefill tokens/s (B*n/t).  In the same run the
-batched decode step (16 sequences x 32 heads, d=64, P=4, fp32 states prefilled
-with 1024 tokens) is timed over 256 steps and reported as state GB/s.
+final state written.  value = prefill tokens/s (B*n/t) of --workload (long).  In the
+same run: the prefill of the other two workloads (mid, wide; *_prefill), the batched
+decode step (16 sequences x 32 heads, d=64, P=4, fp32 states prefilled with 1024
+tokens) over 256 steps and the wide-head decode step (32 heads, d=128, states
+prefilled with 16384 tokens) over 128 steps, both reported as state GB/s; and the
+measured ceilings (ceilings: an in-place read-modify-write sweep over the decode
+state's 6.4 GB, back-to-back fp16 MFMA), against which each roofline also gives
+frac_of_measured_ceiling.
 
 Rooflines come from HIP events recorded by libsata around each kernel launch on
 its own stream: achieved = algorithmic work per launch / mean launch time.
@@ -24,7 +29,10 @@ its own stream: achieved = algorithmic work per launch / mean launch time.
                 contractions of the gradient scans (S . u, S update, R . [v|1], phi(k) R,
                 R update); peak = fp32 dense MFMA 157.3 TFLOP/s.
 cpu_baseline: the fp64 oracle's fixed-size-state form, timed on the host's cores
-on a bounded sample (one head, the first --cpu-tokens tokens).
+on a bounded sample (one head, the first --cpu-tokens tokens); beside it the oracle's
+Taylor-versus-exact-softmax error report (taylor_vs_softmax: per-row max and median for
+P = 1..5 on one head of each of mid, long and wide; all rows of mid, --softmax-rows rows
+spread over the others).
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -106,15 +114,114 @@ def bench_prefill(w, steps, warmup):
     tim = t.read_timing()
     log("  timed %d steps: %.3f s; kernels %s" % (steps, wall, tim))
     t.close()
+    del q, k, v, y, state
+    torch.cuda.empty_cache()
     return wall, tim
 
 
-def bench_decode(steps, warmup, prefill_chunk=64):
+def prefill_record(w, steps, wall, tim, ceil_tflops):
+    """The JSON object of one prefill leg: tokens/s and the scan kernel's roofline."""
+    F = flops_per_token(w.d_K, w.d_V, w.P)
+    scan_ms, scan_n = tim["scan"]
+    alg_total = F * w.B * w.H * w.n * steps
+    scan_tflops = alg_total / scan_n / (scan_ms / scan_n * 1e-3) / 1e12
+    step_tflops = alg_total / wall / 1e12
+    return {
+        "workload": "%s prefill: B=%d H=%d n=%d d_K=%d d_V=%d P=%d chunk=%d %s inputs, fp32 state"
+                    % (w.name, w.B, w.H, w.n, w.d_K, w.d_V, w.P, w.chunk, w.dtype),
+        "value": w.B * w.n / (wall / steps), "unit": "tokens/s", "steps": steps,
+        "ms_per_step": wall / steps * 1e3,
+        "token_heads_per_s": w.B * w.H * w.n / (wall / steps),
+        "roofline": {"bound": "mfma", "achieved": scan_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": scan_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "frac_of_measured_ceiling": scan_tflops / ceil_tflops if ceil_tflops else None,
+                     "traffic": traffic_from_profiles("prefill_scan_" + w.name),
+                     "kernel": "prefill scan", "launches": scan_n, "ms_per_launch": scan_ms / scan_n,
+                     "algorithmic_flops_per_launch": alg_total / scan_n},
+        "step": {"tflops": step_tflops, "frac_mfma": step_tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "kernels_ms_per_step": {k: v[0] / steps for k, v in tim.items() if v[1]}},
+    }
+
+
+def decode_record(w, steps, wall, tim, nbytes, ceil_gbs, label):
+    dk_ms, dk_n = tim["decode"]
+    kern_gbs = nbytes / (dk_ms / dk_n * 1e-3) / 1e9
+    return {
+        "workload": "%s: %d sequences x %d heads, d_K=%d d_V=%d, P=%d, fp32 states (%.3f GB) "
+                    "prefilled with %d tokens, %s q,k,v" % (label, w.B, w.H, w.d_K, w.d_V, w.P,
+                                                          nbytes / 2e9, w.n, w.dtype),
+        "value": nbytes * steps / wall / 1e9, "unit": "GB/s", "steps": steps,
+        "ms_per_step": wall / steps * 1e3,
+        "seq_tokens_per_s": w.B * steps / wall,
+        "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kern_gbs / HBM_PEAK_GBS,
+                     "frac_of_measured_ceiling": kern_gbs / ceil_gbs if ceil_gbs else None,
+                     "traffic": traffic_from_profiles("decode_step" if w.d_K == 64 else "decode_step_" + w.name),
+                     "kernel": "decode state read-modify-write",
+                     "ms_per_launch": dk_ms / dk_n, "algorithmic_bytes_per_launch": nbytes},
+        "reduce_ms_per_step": tim["decode_reduce"][0] / max(tim["decode_reduce"][1], 1),
+    }
+
+
+def measure_ceilings(rmw_bytes):
+    """Measured ceilings on this device (probe library): the in-place read-modify-write of
+    rmw_bytes in one linear sweep (GB/s of read + write traffic), and back-to-back fp16 MFMA
+    (TFLOP/s) at the prefill scan's occupancy.  Timed with torch events on torch's stream,
+    where the probes are launched."""
+    import ctypes
+    import torch
+    from constant_cost_self_amd import build as hb
+
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    lib.probe_rmw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    lib.probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    st = torch.cuda.current_stream()
+    n = int(rmw_bytes // 16 * 4)
+    buf = torch.randn(n, device="cuda:0", dtype=torch.float32)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def rmw():
+        assert lib.probe_rmw(buf.data_ptr(), n, 1.0000001, -1e-7, st.cuda_stream) == 0
+    ms = timed(rmw, 10)
+    rmw_gbs = 8.0 * n / (ms * 1e-3) / 1e9
+    del buf
+    blocks, iters = 4096, 2048
+    out = torch.empty(blocks * 512, device="cuda:0", dtype=torch.float32)
+
+    def mm():
+        assert lib.probe_mfma(out.data_ptr(), blocks, iters, st.cuda_stream) == 0
+    ms2 = timed(mm, 5)
+    mfma_tflops = blocks * 8 * 4 * iters * 16384 / (ms2 * 1e-3) / 1e12
+    del out
+    torch.cuda.empty_cache()
+    log("ceilings: read-modify-write %.0f GB/s over %.2f GB; fp16 MFMA %.0f TFLOP/s" %
+        (rmw_gbs, 8.0 * n / 1e9, mfma_tflops))
+    return {"hbm_rmw": {"value": rmw_gbs, "unit": "GB/s", "frac_of_peak": rmw_gbs / HBM_PEAK_GBS,
+                        "bytes_per_launch": 8.0 * n, "ms_per_launch": ms,
+                        "probe": "in-place x = a x + b over %.2f GB (the decode workload's state size), "
+                                 "one 16-byte non-temporal load and store per thread" % (4.0 * n / 1e9)},
+            "mfma_f16": {"value": mfma_tflops, "unit": "TFLOP/s",
+                         "frac_of_peak": mfma_tflops / MFMA_BF16_PEAK_TFLOPS, "ms_per_launch": ms2,
+                         "probe": "%d workgroups x 8 waves, 4 independent chains of "
+                                  "v_mfma_f32_16x16x32_f16 x %d per wave" % (blocks, iters)}}
+
+
+def bench_decode(w, steps, warmup, prefill_chunk=64):
+    """Decode steps over all B x H heads of workload w, states prefilled with its w.n tokens."""
     import torch
     from constant_cost_self_amd import inputs, sata
 
-    w = inputs.DECODE
-    log("decode: prefilling %d tokens for %dx%d heads" % (w.n, w.B, w.H))
+    log("decode %s: prefilling %d tokens for %dx%d heads" % (w.name, w.n, w.B, w.H))
     x = inputs.prefill_inputs(w)
     q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
     t = sata.sata_tables_build(w.d_K, w.P)
@@ -140,9 +247,11 @@ def bench_decode(steps, warmup, prefill_chunk=64):
     tim = t.read_timing()
     log("  decode %d steps: %.3f s; kernels %s" % (steps, wall, tim))
     t.close()
+    del state
+    torch.cuda.empty_cache()
     M = math.comb(w.d_K + w.P - 1, w.P - 1)
     bytes_per_step = 8.0 * (w.d_V + 1) * M * w.B * w.H
-    return wall, tim, bytes_per_step, w
+    return wall, tim, bytes_per_step
 
 
 def bench_decode_pool(steps, warmup, pool_size=24, active=16, prefill_chunk=64):
@@ -252,8 +361,40 @@ def bench_backward(steps, warmup):
     return wall, tim, w
 
 
-def cpu_baseline(w, ntok):
-    """The oracle's fixed-size-state form on head (0, 0), first ntok tokens."""
+def taylor_vs_softmax(nrows):
+    """The truncation error the pages describe as close to float16 resolution at P = 4: per-row
+    max_j |y_taylor - y_softmax| / max_j |y_softmax| of the oracle's truncated-kernel attention
+    against its exact causal softmax, for one head drawn by each workload's recipe (its own
+    input scale and length): every row of a Mid head (n = 4096), nrows rows spread over a Long
+    head (n = 65536) and over a Wide head (n = 16384).  P = 1 .. 5.  Reported, not gated: the
+    pages give no metric."""
+    import numpy as np
+    import oracle
+    from constant_cost_self_amd import inputs
+
+    out = {}
+    for w in (inputs.MID, inputs.LONG, inputs.WIDE):
+        x = inputs.prefill_inputs(w, B=1, H=1)
+        q, k, v = x["q"][0, 0], x["k"][0, 0], x["v"][0, 0]
+        if w.n <= 4096:
+            rows = np.arange(w.n)
+        else:
+            rows = np.unique(np.linspace(0, w.n - 1, nrows).astype(np.int64))
+        heads = np.zeros_like(rows)
+        ys = oracle.softmax_rows(q[None], k[None], v[None], heads, rows)
+        rec = {"d_K": w.d_K, "sigma_qk": w.sigma_qk, "n": w.n, "rows": int(rows.size)}
+        for P in (1, 2, 3, 4, 5):
+            e = oracle.row_rel_err(oracle.direct_rows(q[None], k[None], v[None], P, heads, rows), ys)
+            rec["P=%d" % P] = {"max": float(np.max(e)), "median": float(np.median(e))}
+        out[w.name] = rec
+        log("  taylor vs softmax, %s: P=4 max %.2e median %.2e" % (w.name, rec["P=4"]["max"],
+                                                                   rec["P=4"]["median"]))
+    return out
+
+
+def cpu_baseline(w, ntok, softmax_rows):
+    """The oracle's fixed-size-state form on head (0, 0), first ntok tokens; and, beside it,
+    the oracle's Taylor-versus-softmax error report."""
     import oracle
     from constant_cost_self_amd import inputs
 
@@ -264,12 +405,15 @@ def cpu_baseline(w, ntok):
     oracle.feature_form(q, k, v, w.P)
     dt = time.perf_counter() - t0
     heads_per_token = w.H            # a token of the workload spans all H heads of a batch row
-    return {"value": ntok / dt / heads_per_token, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "fp64 oracle, fixed-size-state form (state update + readout per token), "
-                      "head (0,0) of the %s workload, first %d tokens, %.1f s; scaled to tokens "
-                      "of all %d heads" % (w.name, ntok, dt, w.H),
-            "seconds": dt}
+    rec = {"value": ntok / dt / heads_per_token, "unit": "tokens/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": "fp64 oracle, fixed-size-state form (state update + readout per token), "
+                     "head (0,0) of the %s workload, first %d tokens, %.1f s; scaled to tokens "
+                     "of all %d heads" % (w.name, ntok, dt, w.H),
+           "seconds": dt}
+    if softmax_rows:
+        rec["taylor_vs_softmax"] = taylor_vs_softmax(softmax_rows)
+    return rec
 
 
 def main():
@@ -281,7 +425,11 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip the prefill legs of the workloads other than --workload")
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--softmax-rows", type=int, default=512)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--no-backward", action="store_true")
@@ -322,69 +470,60 @@ def main():
                           "backward_step_ms": bwall / args.backward_steps * 1e3}))
         return
     if args.only == "decode":
-        dwall, dtim, dbytes, dw = bench_decode(args.decode_steps, args.decode_warmup)
+        dw = inputs.DECODE if w.d_K == 64 else inputs.WIDE
+        dwall, dtim, dbytes = bench_decode(dw, args.decode_steps, args.decode_warmup)
         dk_ms, dk_n = dtim["decode"]
         print(json.dumps({"decode_kernel_gbs": dbytes / (dk_ms / dk_n * 1e-3) / 1e9,
                           "decode_step_ms": dwall / args.decode_steps * 1e3}))
         return
 
+    ceil = None
+    if not args.no_ceilings and args.only is None:
+        M = math.comb(inputs.DECODE.d_K + inputs.DECODE.P - 1, inputs.DECODE.P - 1)
+        ceil = measure_ceilings(4.0 * (inputs.DECODE.d_V + 1) * M * inputs.DECODE.B * inputs.DECODE.H)
+    ceil_tflops = ceil["mfma_f16"]["value"] if ceil else None
+    ceil_gbs = ceil["hbm_rmw"]["value"] if ceil else None
+
     wall, tim = bench_prefill(w, args.steps, args.warmup)
-    tokens = w.B * w.n
-    ms_per_step = wall / args.steps * 1e3
-    F = flops_per_token(w.d_K, w.d_V, w.P)
-    scan_ms, scan_n = tim["scan"]
-    alg_flops_total = F * w.B * w.H * w.n * args.steps
-    scan_tflops = alg_flops_total / scan_n / (scan_ms / scan_n * 1e-3) / 1e12
-    step_tflops = alg_flops_total / wall / 1e12
-    traffic = traffic_from_profiles("prefill_scan_" + w.name)
+    rec = prefill_record(w, args.steps, wall, tim, ceil_tflops)
     out = {
         "metric": "prefill tokens/s (d=64,P=4) + decode state GB/s; % of MFMA/HBM peak",
-        "value": tokens / (wall / args.steps),
+        "value": rec["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded i.i.d. Gaussian q,k,v; no dataset, no weights)",
-        "config": {"workload": "%s prefill: B=%d H=%d n=%d d_K=%d d_V=%d P=%d chunk=%d %s inputs, "
-                               "fp32 state" % (w.name, w.B, w.H, w.n, w.d_K, w.d_V, w.P, w.chunk,
-                                                w.dtype),
+        "config": {"workload": rec["workload"],
                    "B": w.B, "H": w.H, "n": w.n, "d_K": w.d_K, "d_V": w.d_V, "P": w.P,
                    "chunk": w.chunk},
-        "roofline": {"bound": "mfma", "achieved": scan_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": scan_tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic, "kernel": "prefill scan",
-                     "launches": scan_n, "ms_per_launch": scan_ms / scan_n,
-                     "algorithmic_flops_per_launch": alg_flops_total / scan_n},
-        "prefill_step": {"tflops": step_tflops, "frac_mfma": step_tflops / MFMA_BF16_PEAK_TFLOPS,
-                         "token_heads_per_s": w.B * w.H * w.n / (wall / args.steps),
-                         "kernels_ms_per_step": {k: v[0] / args.steps for k, v in tim.items()}},
+        "roofline": rec["roofline"],
+        "prefill_step": dict(rec["step"], token_heads_per_s=rec["token_heads_per_s"]),
     }
+    if ceil:
+        out["ceilings"] = ceil
+
+    if not args.no_other_prefill and args.only is None:
+        for ow in (inputs.MID, inputs.LONG, inputs.WIDE):
+            if ow.name == w.name:
+                continue
+            steps = 20 if ow is inputs.MID else args.steps
+            owall, otim = bench_prefill(ow, steps, args.warmup)
+            out[ow.name + "_prefill"] = prefill_record(ow, steps, owall, otim, ceil_tflops)
 
     if not args.no_decode and args.only is None:
-        dwall, dtim, dbytes, dw = bench_decode(args.decode_steps, args.decode_warmup)
-        dk_ms, dk_n = dtim["decode"]
-        kern_gbs = dbytes / (dk_ms / dk_n * 1e-3) / 1e9
-        step_gbs = dbytes * args.decode_steps / dwall / 1e9
-        out["decode"] = {
-            "workload": "decode step: %d sequences x %d heads, d_K=d_V=%d, P=%d, fp32 states "
-                        "(%.3f GB) prefilled with %d tokens, %s q,k,v" %
-                        (dw.B, dw.H, dw.d_K, dw.P, dbytes / 2e9, dw.n, dw.dtype),
-            "value": step_gbs, "unit": "GB/s", "steps": args.decode_steps,
-            "ms_per_step": dwall / args.decode_steps * 1e3,
-            "seq_tokens_per_s": dw.B * args.decode_steps / dwall,
-            "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": kern_gbs / HBM_PEAK_GBS,
-                         "traffic": traffic_from_profiles("decode_step"),
-                         "kernel": "decode state read-modify-write",
-                         "ms_per_launch": dk_ms / dk_n,
-                         "algorithmic_bytes_per_launch": dbytes},
-            "reduce_ms_per_step": dtim["decode_reduce"][0] / max(dtim["decode_reduce"][1], 1),
-        }
+        dwall, dtim, dbytes = bench_decode(inputs.DECODE, args.decode_steps, args.decode_warmup)
+        out["decode"] = decode_record(inputs.DECODE, args.decode_steps, dwall, dtim, dbytes, ceil_gbs,
+                                      "decode step")
+        wsteps = inputs.WIDE_DECODE_STEPS
+        wwall, wtim, wbytes = bench_decode(inputs.WIDE, wsteps, args.decode_warmup)
+        out["wide_decode"] = decode_record(inputs.WIDE, wsteps, wwall, wtim, wbytes, ceil_gbs,
+                                           "wide-head decode step")
 
     if not args.no_decode and args.only is None:
         pwall, ptim, pbytes, pw, pslots = bench_decode_pool(args.decode_steps, args.decode_warmup)
@@ -398,7 +537,9 @@ def main():
             "value": pbytes * args.decode_steps / pwall / 1e9, "unit": "GB/s",
             "steps": args.decode_steps, "ms_per_step": pwall / args.decode_steps * 1e3,
             "roofline": {"bound": "hbm", "achieved": pk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": pk_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": pk_gbs / HBM_PEAK_GBS,
+                         "frac_of_measured_ceiling": pk_gbs / ceil_gbs if ceil_gbs else None,
+                         "traffic": None,
                          "kernel": "decode state read-modify-write (pool form)",
                          "ms_per_launch": pk_ms / pk_n, "algorithmic_bytes_per_launch": pbytes},
         }
@@ -437,7 +578,7 @@ def main():
 
     if not args.no_cpu and args.only is None:
         log("cpu baseline: oracle on %d tokens" % args.cpu_tokens)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens, args.softmax_rows)
 
     print(json.dumps(out), flush=True)
 

@@ -3,7 +3,8 @@
     python -m constant_cost_self_amd.build
 
 Compiles every source under csrc/ for --offload-arch=gfx950 into
-constant_cost_self_amd/_lib/libsata.so.  Packed fp32 VALU instructions are
+constant_cost_self_amd/_lib/libsata.so, and the benchmark's ceiling probes
+(probe/ceilings.hip) into constant_cost_self_amd/_lib/libsata_ceilings.so.  Packed fp32 VALU instructions are
 disabled for all device code.
 """
 from __future__ import annotations
@@ -18,6 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libsata.so")
+PROBE_SRC = os.path.join(HERE, "probe", "ceilings.hip")
+PROBE_LIB = os.path.join(LIBDIR, "libsata_ceilings.so")
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
@@ -51,6 +54,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # the benchmark's ceiling probes: a library of their own, not linked into libsata
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", "-shared", "-x", "hip", PROBE_SRC, "-o", tmp] + FLAGS
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

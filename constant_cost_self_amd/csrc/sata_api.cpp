@@ -81,9 +81,13 @@ struct KernelTimer {
     }
 };
 
-// Default cap on the workspace of one call (about 5.6% of the 288 GB of an MI355X); a
-// prefill whose slice partials need more runs in segments of whole readout windows.
-constexpr int64_t kDefaultWorkspace = 16LL << 30;
+// Default cap on the workspace of one call (about 11% of the 288 GB of an MI355X); a
+// prefill whose slice partials need more runs in segments of whole readout windows.  Each
+// segment boundary stores and reloads every head's state and restarts every workgroup:
+// measured on the Long prefill (4 x 16 heads of 65536 tokens) 2 segments under this cap
+// against 4 under 16 GiB cost 98.9 against 103.7 ms, on the Wide one (32 heads, d = 128)
+// 4 segments against 7 cost 260 against 317 ms.  sata_prefill_workspace reports the need.
+constexpr int64_t kDefaultWorkspace = 32LL << 30;
 
 struct sata_tables {
     sata::HostTables h;

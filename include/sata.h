@@ -230,7 +230,8 @@ const char *sata_last_error(void);
  * sequence into segments of whole readout windows to stay under it (a segment holds
  * at least one window: 4 chunks at d_K = 64, 2 at d_K = 128 on the bf16 matrix-core
  * path, 1 otherwise, even when one window alone exceeds the cap).  0 restores the
- * default (16 GiB).
+ * default (32 GiB: the bf16 Long prefill, 4 x 16 heads of 65536 tokens, takes about
+ * 31 GB of it in 2 segments; query the need with sata_prefill_workspace).
  */
 int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
 

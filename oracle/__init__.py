@@ -15,7 +15,7 @@ Symmetry-Aware Taylor Approximation", as described on the blog.hotdry.top post
 
 Parity status of each function (what pins it is in tests/test_oracle_pins.py):
   tables, features, direct, feature_form, state_rows, direct_grad, closed forms: pinned;
-  softmax: pinned against scipy.special.softmax (a library routine); the
+  softmax, softmax_rows: pinned against scipy.special.softmax (a library routine); the
   Taylor-versus-softmax error it is used to report has no metric on the pages
   and is reported, not gated (parity unpinned for that report only).
 """
@@ -79,6 +79,9 @@ def _load():
     lib.oracle_softmax.restype = None
     lib.oracle_softmax.argtypes = [dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_int, dp]
+    lib.oracle_softmax_rows.restype = None
+    lib.oracle_softmax_rows.argtypes = [dp, dp, dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                        i64p, i64p, ctypes.c_int64, dp]
     lib.oracle_direct_grad.restype = None
     lib.oracle_direct_grad.argtypes = [dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp]
@@ -238,6 +241,29 @@ def softmax(q, k, v):
     y = np.zeros(lead + (n, dV), dtype=np.float64)
     _load().oracle_softmax(_dp(q), _dp(k), _dp(v), heads, n, dK, dV, _dp(y))
     return y
+
+
+def softmax_rows(q, k, v, heads, rows):
+    """Sampled rows of the exact causal softmax, fp64: out[r] = y[heads[r], rows[r]].
+    q, k: [heads, n, dK]; v: [heads, n, dV] (leading dims flattened)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, dK = q.shape[-2:]
+    dV = v.shape[-1]
+    q = q.reshape(-1, n, dK)
+    k = k.reshape(-1, n, dK)
+    v = v.reshape(-1, n, dV)
+    heads = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if heads.shape != rows.shape or heads.ndim != 1:
+        raise ValueError("heads and rows must be 1-D of one length")
+    if heads.size and (heads.min() < 0 or heads.max() >= q.shape[0] or rows.min() < 0
+                       or rows.max() >= n):
+        raise ValueError("sampled head or row out of range")
+    out = np.zeros((rows.shape[0], dV), dtype=np.float64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    _load().oracle_softmax_rows(_dp(q), _dp(k), _dp(v), n, dK, dV, heads.ctypes.data_as(i64p),
+                                rows.ctypes.data_as(i64p), rows.shape[0], _dp(out))
+    return out
 
 
 def num_threads() -> int:

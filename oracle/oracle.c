@@ -410,37 +410,57 @@ int oracle_state_rows(const double *k, const double *v, int64_t n, int dK, int d
 /*
  * y_T = sum_{t<=T} exp(q_T.k_t / c) v_t / sum_{t<=T} exp(q_T.k_t / c), c = sqrt(dK)
  * ([TA Taylor]: the exponential kernel being expanded).  The row maximum is
- * subtracted before exponentiating; it cancels in the quotient.
+ * subtracted before exponentiating; it cancels in the quotient.  One row T of one
+ * head (qh, kh: [n][dK], vh: [n][dV]).
  */
+static void softmax_row(const double *qh, const double *kh, const double *vh, int64_t T,
+                        int dK, int dV, double *yT)
+{
+    const double c = sqrt((double)dK);
+    const double *qT = qh + T * dK;
+    double mx = -INFINITY;
+    for (int64_t t = 0; t <= T; ++t) {
+        const double *kt = kh + t * dK;
+        double x = 0.0;
+        for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
+        if (x / c > mx) mx = x / c;
+    }
+    double den = 0.0;
+    for (int j = 0; j < dV; ++j) yT[j] = 0.0;
+    for (int64_t t = 0; t <= T; ++t) {
+        const double *kt = kh + t * dK;
+        const double *vt = vh + t * dV;
+        double x = 0.0;
+        for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
+        double e = exp(x / c - mx);
+        den += e;
+        for (int j = 0; j < dV; ++j) yT[j] += e * vt[j];
+    }
+    for (int j = 0; j < dV; ++j) yT[j] /= den;
+}
+
+/* Exact causal softmax attention of every row of every head. */
 void oracle_softmax(const double *q, const double *k, const double *v,
                     int64_t heads, int64_t n, int dK, int dV, double *y)
 {
-    const double c = sqrt((double)dK);
 #pragma omp parallel for collapse(2) schedule(dynamic, 16)
-    for (int64_t h = 0; h < heads; ++h) {
-        for (int64_t T = 0; T < n; ++T) {
-            const double *qT = q + (h * n + T) * dK;
-            double *yT = y + (h * n + T) * dV;
-            double mx = -INFINITY;
-            for (int64_t t = 0; t <= T; ++t) {
-                const double *kt = k + (h * n + t) * dK;
-                double x = 0.0;
-                for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
-                if (x / c > mx) mx = x / c;
-            }
-            double den = 0.0;
-            for (int j = 0; j < dV; ++j) yT[j] = 0.0;
-            for (int64_t t = 0; t <= T; ++t) {
-                const double *kt = k + (h * n + t) * dK;
-                const double *vt = v + (h * n + t) * dV;
-                double x = 0.0;
-                for (int i = 0; i < dK; ++i) x += qT[i] * kt[i];
-                double e = exp(x / c - mx);
-                den += e;
-                for (int j = 0; j < dV; ++j) yT[j] += e * vt[j];
-            }
-            for (int j = 0; j < dV; ++j) yT[j] /= den;
-        }
+    for (int64_t h = 0; h < heads; ++h)
+        for (int64_t T = 0; T < n; ++T)
+            softmax_row(q + h * n * dK, k + h * n * dK, v + h * n * dV, T, dK, dV,
+                        y + (h * n + T) * dV);
+}
+
+/* Sampled rows of the exact softmax attention: out[r] = y of token rows[r] of head
+ * heads_of[r]; each row costs O(T (dK + dV)). */
+void oracle_softmax_rows(const double *q, const double *k, const double *v,
+                         int64_t n, int dK, int dV,
+                         const int64_t *heads_of, const int64_t *rows, int64_t nr, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nr; ++r) {
+        const int64_t h = heads_of[r];
+        softmax_row(q + h * n * dK, k + h * n * dK, v + h * n * dV, rows[r], dK, dV,
+                    out + r * dV);
     }
 }
 

@@ -185,6 +185,23 @@ def test_large_P_converges_to_softmax():
     assert all(b < a for a, b in zip(errs, errs[1:])), errs
 
 
+def test_softmax_rows_against_scipy_and_the_full_form():
+    """Sampled softmax rows: scipy.special.softmax over each sampled causal row (several
+    heads, first and last rows included), and the same rows of oracle.softmax."""
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((3, 40, 6)) * 0.7
+    k = rng.standard_normal((3, 40, 6)) * 0.7
+    v = rng.standard_normal((3, 40, 4))
+    hs = np.array([0, 0, 1, 2, 2, 1])
+    ts = np.array([0, 39, 17, 5, 39, 38])
+    got = oracle.softmax_rows(q, k, v, hs, ts)
+    c = math.sqrt(6)
+    for r, (h, t) in enumerate(zip(hs, ts)):
+        s = q[h, t] @ k[h, :t + 1].T / c
+        np.testing.assert_allclose(got[r], scipy.special.softmax(s) @ v[h, :t + 1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got, oracle.softmax(q, k, v)[hs, ts], rtol=1e-14, atol=1e-14)
+
+
 def test_affine_equivariance_in_v():
     q, k, v = _rand(30, 8, 4, 0.5, 6)
     y = oracle.direct(q, k, v, 4)

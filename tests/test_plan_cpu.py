@@ -61,10 +61,10 @@ def test_advisor_shapes_do_not_crash(handles):
     assert nseg >= 1 and nbytes > 0
     t.set_workspace_limit(0)
     nbytes, nseg, nsub = t.prefill_workspace(128, 64, 560, 64)
-    # 9 chunks of 8192 heads: one readout window (4 chunks) alone exceeds the 16 GiB cap, so
-    # the segments are single windows
+    # 9 chunks of 8192 heads: one readout window (4 chunks) fits the 32 GiB cap, two do not,
+    # so the segments are single windows
     per_chunk = nbytes // 4
-    assert nseg == 3 and nbytes == 4 * per_chunk and 4 * per_chunk > 16 << 30
+    assert nseg == 3 and nbytes == 4 * per_chunk and 8 * per_chunk > 32 << 30
 
 
 def test_carrier_counted_without_caller_state(handles):
