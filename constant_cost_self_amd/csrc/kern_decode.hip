@@ -25,10 +25,38 @@
 // Pool form ([HW] "The fixed-size hidden state of SATA attention": the state's memory
 // is allocated up front and requests share the device in turns): batch entry b uses
 // the state in slot slots[b] of a preallocated pool instead of state b.
+#include <mutex>
+
 #include "launch.h"
 #include "sata_common.h"
 
 namespace sata {
+
+// Fixed scratch of the allocation-free decode step: the partial readouts of one call, in a
+// file-scope device array that each GPU holds until the process ends.  Host code must not
+// pass `scratch` itself to a kernel (on the host it is only a stand-in symbol): its device
+// address is taken once per device with hipGetSymbolAddress and that address is used.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(int device, float** ptr) {
+    *ptr = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
 namespace {
 

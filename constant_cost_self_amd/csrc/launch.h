@@ -32,6 +32,10 @@ int decode_blocks(int64_t M_pad);
 // Floats of decode workspace (per-wave partial readouts) for BH heads.
 int64_t decode_partial_floats(int BH, int d_V, int64_t M_pad);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);         // state RMW + partials
+// Bytes of the fixed device scratch of the allocation-free decode step, and its device
+// address on `device` (the current device; taken once per device, no allocation).
+constexpr int64_t kNoAllocScratchBytes = 16LL << 20;
+hipError_t noalloc_scratch(int device, float** ptr);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);  // partials -> y
 
 // One segment [c_begin, c_end) of chunks of a chunked prefill.

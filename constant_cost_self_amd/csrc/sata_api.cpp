@@ -703,11 +703,12 @@ int sata_prefill_backward(const sata_tables* tc, const void* q, const void* k, c
 
 namespace {
 
-// Decode step shared by the dense and the pool forms: BH = batch entries x H heads;
-// slots == NULL for the dense form.
+// Decode step shared by the dense, the pool and the allocation-free forms: BH = batch
+// entries x H heads; slots == NULL for the dense forms; noalloc: the partial readouts go to
+// the fixed device scratch, and nothing is allocated (no workspace, no timing events).
 int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool, const void* q,
                 const void* k, const void* v, float* y, int B, int H, int d_K, int d_V, int P,
-                sata_dtype in_dtype, void* stream) {
+                sata_dtype in_dtype, void* stream, bool noalloc = false) {
     int rc = check_sizes(d_K, d_V, P);
     if (rc) return rc;
     if (d_K != t->h.d_K || P != t->h.P)
@@ -718,6 +719,12 @@ int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool
     if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
         return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    const int64_t part_bytes = sata::decode_partial_floats(B * H, d_V, t->h.M_pad) * 4;
+    if (noalloc && part_bytes > sata::kNoAllocScratchBytes)
+        return fail(SATA_ERR_UNSUPPORTED,
+                    "the allocation-free decode step holds %lld bytes of partials; B=%d H=%d "
+                    "d_V=%d needs %lld", (long long)sata::kNoAllocScratchBytes, B, H, d_V,
+                    (long long)part_bytes);
     rc = check_device(t);
     if (rc) return rc;
 
@@ -734,9 +741,18 @@ int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool
     a.pool = pool;
     a.H = H;
 
-    std::lock_guard<std::mutex> lock(t->mu);
     hipStream_t st = (hipStream_t)stream;
-    rc = ensure_ws(t, (size_t)sata::decode_partial_floats(a.BH, d_V, a.M_pad) * 4, st);
+    if (noalloc) {
+        hipError_t e = sata::noalloc_scratch(t->device, &a.partial);
+        if (e != hipSuccess)
+            return fail(SATA_ERR_HIP, "address of the decode scratch: %s", hipGetErrorString(e));
+        e = sata::launch_decode(a, st);
+        if (e == hipSuccess) e = sata::launch_decode_reduce(a, st);
+        if (e != hipSuccess) return fail(SATA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+        return SATA_OK;
+    }
+    std::lock_guard<std::mutex> lock(t->mu);
+    rc = ensure_ws(t, (size_t)part_bytes, st);
     if (rc) return rc;
     a.partial = (float*)t->ws;
     hipEvent_t ev = t->timer.begin(st);
@@ -765,6 +781,18 @@ int sata_decode_step(const sata_tables* tc, float* state, const void* q, const v
         return fail(SATA_ERR_ARG, "state, q, k, v and y must be non-NULL");
     if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
     return decode_impl(t, state, nullptr, 0, q, k, v, y, B, H, d_K, d_V, P, in_dtype, stream);
+}
+
+int sata_decode_step_noalloc(const sata_tables* tc, float* state, const void* q, const void* k,
+                             const void* v, float* y, int B, int H, int d_K, int d_V, int P,
+                             sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!state || !q || !k || !v || !y)
+        return fail(SATA_ERR_ARG, "state, q, k, v and y must be non-NULL");
+    if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
+    return decode_impl(t, state, nullptr, 0, q, k, v, y, B, H, d_K, d_V, P, in_dtype, stream, true);
 }
 
 int sata_decode_step_pool(const sata_tables* tc, float* state_pool, int64_t pool_size,

@@ -29,7 +29,7 @@ EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "s
             "sata_decode_step_pool", "sata_prefill_backward",
             "sata_last_error", "sata_set_workspace_limit", "sata_set_prefill_split", "sata_set_timing",
             "sata_read_timing", "sata_prefill_workspace", "sata_decode_workspace",
-            "sata_reserve_workspace")
+            "sata_reserve_workspace", "sata_decode_step_noalloc")
 KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward")
 
 _lib = None
@@ -72,6 +72,8 @@ def load():
                                  i32, i32, vp]
     lib.sata_decode_step.restype = i32
     lib.sata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.sata_decode_step_noalloc.restype = i32
+    lib.sata_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.sata_decode_step_pool.restype = i32
     lib.sata_decode_step_pool.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.sata_prefill_backward.restype = i32
@@ -285,6 +287,16 @@ def sata_decode_step(t: Tables, state, q, k, v, y, *, stream=None):
     d_V = v.shape[-1]
     _check(load().sata_decode_step(t.handle, _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(y),
                                    B, H, d_K, d_V, t.P, _dtype_code(q), _stream(stream)))
+
+
+def sata_decode_step_noalloc(t: Tables, state, q, k, v, y, *, stream=None):
+    """sata_decode_step without any allocation (partials in the library's fixed 16 MiB
+    device scratch; calls overlapping on one GPU race)."""
+    _need(state, q, k, v, y)
+    B, H, d_K = q.shape
+    d_V = v.shape[-1]
+    _check(load().sata_decode_step_noalloc(t.handle, _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(y),
+                                           B, H, d_K, d_V, t.P, _dtype_code(q), _stream(stream)))
 
 
 def sata_decode_step_pool(t: Tables, pool, slots, q, k, v, y, *, stream=None):

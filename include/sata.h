@@ -197,6 +197,22 @@ int sata_decode_step_pool(const sata_tables *t, float *state_pool, int64_t pool_
                           sata_dtype in_dtype, void *stream);
 
 /*
+ * The decode step for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same computation and
+ * kernels as sata_decode_step, but the partial readouts go to a fixed device array of
+ * 16 MiB that the library holds on each GPU it runs on until the process ends, instead of
+ * the handle's workspace.  The call allocates nothing (no workspace, no timing events).
+ * Limit: B x H x (d_V + 1) x ceil(M_pad / 2048) x 16 bytes <= 16 MiB (e.g. 512 heads at
+ * d_K = d_V = 64, P = 4; 32 heads at d_K = d_V = 128, P = 4); larger batches return
+ * SATA_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU shares that
+ * array, so calls that overlap in time on one GPU (several streams, threads or handles)
+ * race; issue them in order.  Errors otherwise as sata_decode_step.
+ */
+int sata_decode_step_noalloc(const sata_tables *t, float *state, const void *q,
+                             const void *k, const void *v, float *y, int B, int H,
+                             int d_K, int d_V, int P, sata_dtype in_dtype, void *stream);
+
+/*
  * Gradients of the causal prefill: for a loss with dL/dy = dy, the gradients dq, dk, dv
  * of the y that sata_prefill computes from q, k, v (empty prefix; no state in or out).
  * With y_T = N_T / D_T ([TA] "Feature maps and linear attention": N_T = sum_{t<=T}
