@@ -88,6 +88,9 @@ def to_dev(a, dtype):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
+WORKSPACE_CAP = 0          # bytes; 0 = the library's default (--workspace-gib)
+
+
 def bench_prefill(w, steps, warmup):
     import torch
     from constant_cost_self_amd import inputs, sata
@@ -97,9 +100,13 @@ def bench_prefill(w, steps, warmup):
     q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
     del x
     t = sata.sata_tables_build(w.d_K, w.P)
+    t.set_workspace_limit(WORKSPACE_CAP)
     Mp = sata.sata_state_stride(w.d_K, w.P)
     y = torch.empty((w.B, w.H, w.n, w.d_V), device="cuda:0", dtype=torch.float32)
     state = torch.empty((w.B, w.H, w.d_V + 1, Mp), device="cuda:0", dtype=torch.float32)
+    nbytes, nseg, nsub = t.prefill_workspace(w.B, w.H, w.n, w.d_V, chunk=w.chunk,
+                                             dtype=sata.SATA_BF16 if w.dtype == "bf16" else sata.SATA_F32)
+    log("  plan: %d segment(s), %d sub-segment(s), workspace %.2f GB" % (nseg, nsub, nbytes / 1e9))
     t.set_timing(True)
     for i in range(warmup):
         sata.sata_prefill(t, q, k, v, y, state, chunk=w.chunk)
@@ -428,6 +435,8 @@ def main():
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the prefill legs of the workloads other than --workload")
     ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--workspace-gib", type=float, default=0.0,
+                    help="workspace cap of the prefill legs (0: the library's default)")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--softmax-rows", type=int, default=512)
     ap.add_argument("--no-cpu", action="store_true")
@@ -450,6 +459,8 @@ def main():
     import torch
     from constant_cost_self_amd import inputs, sata
 
+    global WORKSPACE_CAP
+    WORKSPACE_CAP = int(args.workspace_gib * (1 << 30))
     sata.load()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -96,7 +96,8 @@ struct Layout {
     // state load/store staging (outside the chunk loop) aliases the fp16 state area
     static constexpr int IO = 68;                                   // floats per feature row
     static constexpr int io_rows = kWaves * 16;                     // one tile per wave per phase
-    static_assert(io_rows * IO * 4 <= 4 * KS * 64 * 16, "state staging size");
+    static constexpr int cf = sb + io_rows * IO * 4;                // [512] canonical index, [512] factor
+    static_assert(cf + kRowsPerSlice * 8 * 8 <= 4 * KS * 64 * 16, "state staging size");
     static_assert(qt % 16 == 0 && rawk % 16 == 0 && rawv % 16 == 0 && kT % 16 == 0 && ri % 16 == 0,
                   "16-byte alignment of LDS regions");
     static_assert((R * XSLOTS) % 64 == 0 && (LU * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
@@ -301,20 +302,48 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[T][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    // State I/O at the segment's ends goes through LDS, one update tile per wave at a time.
+    // The slice's canonical feature index and key-side factor per kernel feature are staged
+    // in LDS first; consecutive threads then take consecutive kernel features of one column
+    // (mostly consecutive canonical features: few cache lines per wave), and every thread
+    // issues all its loads before it writes any of them.
+    constexpr int NIO = (LY::io_rows * NCL + 511) / 512, IOB = 6;
+    int32_t* cf_idx = reinterpret_cast<int32_t*>(lds_raw + LY::cf);
+    float* cf_fac = reinterpret_cast<float*>(lds_raw + LY::cf) + kRowsPerSlice * 8;
+    // kernel feature (within the slice) of staging row fr of update tile T
+    auto kf_of = [](int T, int fr) {
+        const int ww = fr / 16, rho = fr % 16;
+        return (8 * ww + 4 * (T >> 1) + (rho >> 2)) * 8 + 4 * (T & 1) + (rho & 3);
+    };
     if (a.load_state) {
-        // through LDS, one tile per wave at a time: plain gather loop, then a register
-        // fill with compile-time indices
+        const int fi = row_s * 8 + tid;
+        cf_idx[tid] = rt.canon[fi];
+        cf_fac[tid] = kfactor(rt.kscale[fi]) * kVScale;
+    }
+    if (a.load_state) {
         float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             __syncthreads();
-            for (int idx = tid; idx < LY::io_rows * NCL; idx += 512) {
-                const int fr = idx / NCL, j = idx % NCL;
-                const int ww = fr / 16, rho = fr % 16;
-                const int fi = (row_s + 8 * ww + 4 * (T >> 1) + (rho >> 2)) * 8 + 4 * (T & 1) + (rho & 3);
-                const int F = rt.canon[fi];
-                io[fr * LY::IO + j] =
-                    F >= 0 ? kfactor(rt.kscale[fi]) * kVScale * state[(int64_t)gcol(j) * a.M_pad + F] : 0.0f;
+            // batches of IOB loads in flight per thread
+            for (int i0 = 0; i0 < NIO; i0 += IOB) {
+                float vals[IOB];
+#pragma unroll
+                for (int i = 0; i < IOB; ++i) {
+                    const int idx = tid + 512 * (i0 + i);
+                    float x = 0.0f;
+                    if (idx < LY::io_rows * NCL) {
+                        const int j = idx / LY::io_rows, kf = kf_of(T, idx % LY::io_rows);
+                        const int F = cf_idx[kf];
+                        if (F >= 0) x = state[(int64_t)gcol(j) * a.M_pad + F] * cf_fac[kf];
+                    }
+                    vals[i] = x;
+                }
+#pragma unroll
+                for (int i = 0; i < IOB; ++i) {
+                    const int idx = tid + 512 * (i0 + i);
+                    if (idx < LY::io_rows * NCL) io[(idx % LY::io_rows) * LY::IO + idx / LY::io_rows] = vals[i];
+                }
             }
             __syncthreads();
 #pragma unroll
@@ -553,8 +582,15 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     __builtin_amdgcn_s_waitcnt(0);
 
     if (a.store_state) {
-        // through LDS as for the load; S = S' / (2^-8 c)
+        // through LDS as for the load; S = S' / (2^-8 c).  The window loop has reused the
+        // staging area: stage the canonical indices and factors again.
         float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
+        __syncthreads();
+        {
+            const int fi = row_s * 8 + tid;
+            cf_idx[tid] = rt.canon[fi];
+            cf_fac[tid] = kfactor(rt.kscale[fi]) * kVScale;
+        }
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             __syncthreads();
@@ -566,13 +602,14 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                     if (j < LY::IO) io[(w * 16 + 4 * g + r) * LY::IO + j] = S[T][ct][r];
                 }
             __syncthreads();
-            for (int idx = tid; idx < LY::io_rows * NCL; idx += 512) {
-                const int fr = idx / NCL, j = idx % NCL;
-                const int ww = fr / 16, rho = fr % 16;
-                const int fi = (row_s + 8 * ww + 4 * (T >> 1) + (rho >> 2)) * 8 + 4 * (T & 1) + (rho & 3);
-                const int F = rt.canon[fi];
-                if (F >= 0)
-                    state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / (kfactor(rt.kscale[fi]) * kVScale);
+#pragma unroll 4
+            for (int i = 0; i < NIO; ++i) {
+                const int idx = tid + 512 * i;
+                if (idx < LY::io_rows * NCL) {
+                    const int fr = idx % LY::io_rows, j = idx / LY::io_rows, kf = kf_of(T, fr);
+                    const int F = cf_idx[kf];
+                    if (F >= 0) state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / cf_fac[kf];
+                }
             }
         }
         if (slice == 0) {
