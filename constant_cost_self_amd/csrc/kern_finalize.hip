@@ -169,6 +169,10 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + (bh * a.n + t0) * DK;
     const uint16_t* k = static_cast<const uint16_t*>(a.k) + (bh * a.n + t0) * DK;
     const uint16_t* v = static_cast<const uint16_t*>(a.v) + (bh * a.n + t0) * DV;
+    // the head's value scale (the matrix-core scan's v' = v 2^-s_v): the fp16 [v | 1] table
+    // holds v', whatever the magnitude of v
+    const int s_v = a.maxbits ? prep_scale_exp(a.maxbits[bh * 4 + 2]) : 0;
+    const float vsc = ldexpf(1.0f, -s_v);
 
     for (int idx = tid; idx < L * DK / 8; idx += 256) {
         const int t = idx / (DK / 8), s8 = idx % (DK / 8);
@@ -193,8 +197,8 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
             const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vt[(8 * c8 + 2 * e) * TS + t] = (_Float16)__uint_as_float(xw[e] << 16);
-                vt[(8 * c8 + 2 * e + 1) * TS + t] = (_Float16)__uint_as_float(xw[e] & 0xffff0000u);
+                vt[(8 * c8 + 2 * e) * TS + t] = (_Float16)(__uint_as_float(xw[e] << 16) * vsc);
+                vt[(8 * c8 + 2 * e + 1) * TS + t] = (_Float16)(__uint_as_float(xw[e] & 0xffff0000u) * vsc);
             }
         }
         if (tid < L) vt[DV * TS + tid] = (_Float16)(tid < nvk ? 1.0f : 0.0f);
@@ -204,11 +208,15 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
 
     __syncthreads();
 
-    // wave w: query tile w, over the key chunks of the window (the last one causal)
+    // wave w: query tile w, over the key chunks of the window (the last one causal).  The
+    // weights enter the fp16 contraction as w 2^-e, with e a running power of two per query
+    // (lane column li): a key chunk whose largest |w| needs a larger e rescales the fp32
+    // accumulators first, so no weight of any magnitude overflows fp16.
     const int iq = 16 * w + li;                 // this lane's query token
     f32x4_t O[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) O[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    int e_cur = -200;                           // no weight yet
     for (int kc = cw; kc <= c; ++kc) {
         if (kc > cw) {
             __syncthreads();                    // the previous key chunk is consumed
@@ -216,7 +224,8 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
             __syncthreads();
         }
         // S^T tiles over the 4 key tiles, then the weights
-        f16x8_t Wb[2];                          // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
+        float wv[4][4];                         // keys 16 kt + 4 g + r of query iq
+        float wmax = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -232,8 +241,30 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
                 const float wgt = taylor_weight(st[r], a.alpha, a.P);
                 // earlier chunks of the window are whole; chunk c is causal
                 const bool live = iq < nvalid && (kc < c || j <= iq);
-                Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)(live ? wgt : 0.0f);
+                wv[kt][r] = live ? wgt : 0.0f;
+                wmax = fmaxf(wmax, fabsf(wv[kt][r]));
             }
+        }
+        // the query's largest |w| in this key chunk (its keys lie in lane groups g = 0..3)
+        wmax = fmaxf(wmax, __shfl_xor(wmax, 16, 64));
+        wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
+        if (wmax > 0.0f) {
+            int e = (int)((__float_as_uint(wmax) >> 23) & 0xffu) - 127 - 13;   // |w| 2^-e < 2^14
+            e = e < -120 ? -120 : (e > 120 ? 120 : e);
+            if (e > e_cur) {
+                const float f = ldexpf(1.0f, e_cur - e);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) O[ct] *= f;
+                e_cur = e;
+            }
+        }
+        f16x8_t Wb[2];                          // B operands: keys {32 ks + 4 g + r, 32 ks + 16 + 4 g + r}
+        {
+            const float f = e_cur > -200 ? ldexpf(1.0f, -e_cur) : 0.0f;   // all weights 0 so far
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Wb[kt >> 1][4 * (kt & 1) + r] = (_Float16)(wv[kt][r] * f);
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -259,45 +290,57 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
         const float* part = a.partial + ((bh * nch + cl) * (int64_t)a.nslices) * stride;
         if constexpr (TILED) {
             // items of 8 fp16: [token tile][tile pair][lane (li, g)], tokens 16 tile + 4 g + r,
-            // columns 32 pair + li (halves r) and 32 pair + 16 + li (halves 4 + r)
-            constexpr int NVP = DV / 32, NI = L * DV / 8 / 256, SB = 16 / NI;
+            // columns 32 pair + li (halves r) and 32 pair + 16 + li (halves 4 + r); each slice's
+            // items of token tile tt and column group G carry the scale at [L d_V / 2 + L +
+            // tt NG + G], and the sum is in units of 2^s_v (the head's value scale)
+            constexpr int NVP = DV / 32, NG = DV / 64, NI = L * DV / 8 / 256, SB = 16 / NI;
             static_assert(NI * 256 * 8 == L * DV && SB * NI == 16, "whole items per thread");
             const float* p[NI];
+            const float* ps[NI];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) p[i] = part + 4 * (tid + 256 * i);
+            for (int i = 0; i < NI; ++i) {
+                const int item = tid + 256 * i, pr = (item / 64) % NVP, tt = item / 64 / NVP;
+                p[i] = part + 4 * item;
+                ps[i] = part + L * DV / 2 + L + tt * NG + pr / 2;
+            }
             f32x4_t acc[NI][2];
 #pragma unroll
             for (int i = 0; i < NI; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            auto add = [&](f32x4_t* ac, f32x4_t raw) {
+            auto add = [&](f32x4_t* ac, f32x4_t raw, float sc) {
                 const f16x8_t h = __builtin_bit_cast(f16x8_t, raw);
-                ac[0] += f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-                ac[1] += f32x4_t{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+                ac[0] += f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * sc;
+                ac[1] += f32x4_t{(float)h[4], (float)h[5], (float)h[6], (float)h[7]} * sc;
             };
             int sl = 0;
             for (; sl + SB <= a.nslices; sl += SB) {
                 f32x4_t x[SB][NI];
+                float sc[SB][NI];
 #pragma unroll
                 for (int u = 0; u < SB; ++u)
 #pragma unroll
-                    for (int i = 0; i < NI; ++i)
+                    for (int i = 0; i < NI; ++i) {
                         x[u][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + (sl + u) * stride));
+                        sc[u][i] = ps[i][(sl + u) * stride];
+                    }
 #pragma unroll
                 for (int u = 0; u < SB; ++u)
 #pragma unroll
-                    for (int i = 0; i < NI; ++i) add(acc[i], x[u][i]);
+                    for (int i = 0; i < NI; ++i) add(acc[i], x[u][i], sc[u][i]);
             }
             for (; sl < a.nslices; ++sl)
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
-                    add(acc[i], __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride)));
+                    add(acc[i], __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p[i] + sl * stride)),
+                        ps[i][sl * stride]);
+            const float vs = ldexpf(1.0f, prep_scale_exp(a.maxbits[bh * 4 + 2]));
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int item = tid + 256 * i, ln = item % 64, pr = (item / 64) % NVP, tt = item / 64 / NVP;
                 const int col = 32 * pr + (ln & 15), t0 = 16 * tt + 4 * (ln >> 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    num[(t0 + e) * NS + col] = acc[i][0][e] * (1.0f / kPartialScale);
-                    num[(t0 + e) * NS + col + 16] = acc[i][1][e] * (1.0f / kPartialScale);
+                    num[(t0 + e) * NS + col] = acc[i][0][e] * vs;
+                    num[(t0 + e) * NS + col + 16] = acc[i][1][e] * vs;
                 }
             }
         } else {
@@ -353,13 +396,16 @@ __global__ __launch_bounds__(256) void finalize_mfma_kernel(PrefillSegArgs a) {
         }
     }
     __syncthreads();
+    {   // the direct part in true units: 2^e_cur, and 2^s_v for the value columns
+        const float fz = ldexpf(1.0f, e_cur), fv = ldexpf(1.0f, e_cur + s_v);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int col = 16 * ct + 4 * g + r;
-            if (col < COLS) num[iq * NS + col] += O[ct][r];
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int col = 16 * ct + 4 * g + r;
+                if (col < COLS) num[iq * NS + col] += O[ct][r] * (col < DV ? fv : fz);
+            }
+    }
     __syncthreads();
     float* y = a.y + (bh * a.n + t0) * DV;
     for (int idx = tid; idx < nvalid * DV; idx += 256) {

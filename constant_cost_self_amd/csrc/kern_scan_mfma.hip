@@ -4,131 +4,113 @@
 // attention": the state recurrence, evaluated chunk by chunk):
 //     readout   part[t][j] = sum_f qw_f phi_f(q_t) S[f][j]      (S before the window)
 //     update    S[f][j]   += sum_t phi_f(k_t) u_t[j],   u_t = [v_t | 1]
-// The readout is taken once per window of NSUB chunks of L = 64 tokens (R = 256
-// tokens at d_K = 64, 128 at d_K = 128) against the state before the window; the
-// finalize adds the direct part of the window's earlier chunks.  The update runs
-// chunk by chunk.  Both are dense contractions over tokens and a slice of the
-// feature axis, run as v_mfma_f32_16x16x32_f16 with fp32 accumulation:
+// The readout is taken once per window of R tokens (256 at d_K = 64, 128 at d_K = 128)
+// against the state before the window; the finalize adds the direct part of the window's
+// earlier chunks.  The update runs per 128-token sub-chunk.  Both are dense contractions
+// over tokens and a slice of the feature axis, run as v_mfma_f32_16x16x32_f16 with fp32
+// accumulation:
 //     readout  (16 tokens x 32 features) x (32 features x 16 columns)
 //     update   (16 features x 32 tokens) x (32 tokens x 16 columns)
 //
-// Operands are fp16, not bf16: gfx950 multiplies fp16 pairs in one VALU
-// instruction (bf16 only one value at a time) and converts two fp32 values to fp16
-// in one, and operand building competes with the matrix pipe for issue slots; the
-// matrix rate of the two types is the same, and fp16 keeps 3 more mantissa bits.
-// Exact powers of two keep every operand inside fp16's range: the [v | 1] operand
-// carries 2^-8 (the internal state is S' = 2^-8 c S, with c the key-side factor
-// below), the query operand 2^12, and the readout is scaled back by 2^-4.
+// Operands are fp16, built from the operand images of the prep kernels (kern_prep.hip):
+// q' = q 2^-s_q, k' = k 2^-s_k, v' = v 2^-s_v with per-head powers of two that put each
+// input's maximum in [1, 2).  gfx950 multiplies fp16 pairs in one VALU instruction (bf16 only
+// one value at a time), and operand building competes with the matrix pipe for issue slots;
+// the matrix rate of the two types is the same.  The scales are folded back exactly:
+//   query operand  (W'_a q'_a) q'_l with W'_a = W_a 2^(p (s_q + s_k) - e_q), p the degree
+//                  and e_q per head, so that every operand stays below 2^14;
+//   state          S'' = c 2^(-p s_k) [S 2^-s_v | Z] in fp32 registers (c the key factor);
+//   readout copy   S'' 2^-e_w in fp16, e_w per window from the slice's largest entry;
+// so the readout accumulates (q~ . S) 2^-(e_q + e_w) (value columns also 2^-s_v), and each
+// 16-token tile of the stored partials gets its own power-of-two scale.  No finite input
+// overflows fp16 anywhere; precision is that of the fp16 operands (2^-11 relative).
 //
-// Work split.  The columns of [v | 1] are cut into groups of 64 value columns;
-// group 0 also carries the normaliser column (65 columns, 5 tiles of 16), the
-// others 4 tiles.  One workgroup of 8 waves (two per SIMD, so that one wave's
-// waits overlap the other's matrix work) owns one slice of 64 rows = 512 kernel
-// features of one head for one column group, and walks all chunks of the segment
-// in order.  Wave w owns rows 8w .. 8w+7: kernel features (parent a, l = 8b + e),
-// e = 0..7, with one l-block b per wave (see mfma_rows.cpp); its fp32 state never
-// leaves the registers (4 update tiles x 5 column tiles x 4 = 80 registers).
-// Feature tiles are never written to HBM: per chunk the operands are built as
-//     query side  q^(a, l)[t] = (W_a q_a[t]) * q_l[t]        (W_a = alpha_p C(a) p)
-//     key side    k^(a, l)[t] = kpar_a[t] * k_l[t] * c_(a,l)  (c: 0 / 1/(1+m) / 1)
-// directly in the MFMA operand layout (q_a, kpar_a: parent products).
+// Work split.  The columns of [v | 1] are cut into groups of 64 value columns; group 0
+// also carries the normaliser column (65 columns, 5 tiles of 16), the others 4 tiles.  One
+// workgroup of 8 waves (two per SIMD, so that one wave's waits overlap the other's matrix
+// work) owns one slice of 64 rows = 512 kernel features of one head for one column group,
+// and walks all chunks of the segment in order.  Wave w owns rows 8w .. 8w+7: kernel
+// features (parent a, l = 8b + e), e = 0..7, with one l-block b per wave (mfma_rows.cpp);
+// its fp32 state never leaves the registers (4 update tiles x 5 column tiles x 4 = 80
+// registers).  Feature tiles are never written to HBM: per contraction step the operands
+// are built as
+//     query side  q^(a, l)[t] = (W'_a q'_a[t]) * q'_l[t]
+//     key side    k^(a, l)[t] = kpar_a[t] * k'_l[t] * c_(a,l)    (c: 0 / 1/(1+m) / 1)
+// directly in the MFMA operand layout (q'_a, kpar_a: parent products).
 //
-// The readout is split by tokens, not by features: wave w computes R / 8 tokens of
-// the window (two or one 16-token tiles) over all 512 features of the slice, so the
-// slice's partial readout leaves the registers straight to HBM with no exchange
-// between waves.  Its B operand, the state packed to fp16 after the previous
-// window's last update, is shared through LDS and read once per window: the
-// update's accumulator layout (lane = column, 4 rows each) over two tiles is a
-// 32-deep B operand when the query operand uses the same feature order.  A larger
-// window gives each B byte more tokens (R / 8 per wave) without more registers.
+// The readout is split by tokens: wave w computes R / 8 tokens of the window over all 512
+// features of the slice, so the slice's partial readout leaves the registers straight to
+// HBM with no exchange between waves.  Its B operand, the state packed to fp16 after the
+// previous window's last update, is shared through LDS: the update's accumulator layout
+// (lane = column, 4 rows each) over two tiles is a 32-deep B operand when the query operand
+// uses the same feature order.
 //
-// Per window: the window's q arrives in LDS (bf16) by direct-to-LDS loads issued
-// during the previous window and is converted to fp16 in place; readout.  Per chunk:
-// k and v arrive by direct-to-LDS loads a chunk ahead; v (transposed, scaled) and
-// all key coordinates go to fp16 token-major tables; update.  After the window's last
-// update the fp16 state goes to LDS.
+// Per window (the images arrive by direct-to-LDS loads, 1 KiB per wave instruction):
+//     B1  q rows of the window landed; fp16 state copy written
+//         readout, partial stores
+//     B2  readout done (state copy and q rows free); tables of update 0 landed
+//         load: tables of update 1 (over the state copy), next window's q rows
+//         update 0
+//     B3  update 0 done; tables of update 1 landed      (d_K = 64: two updates per window)
+//         load: next window's tables of update 0
+//         update 1
+//     B4  updates done; per-wave state maxima posted
+//         fp16 state copy of the next window
+// so the barriers wait for LDS work only; every image load is issued a phase ahead.
 #include "scan_mfma.h"
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 namespace sata {
 
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kWavesPerSlice;      // 8 waves, 8 rows each
 constexpr int kL = 64;                      // chunk length (partials, finalize)
-constexpr int kLU = 128;                    // tokens per state update
-constexpr float kVScale = 1.0f / 256.0f;    // on the [v | 1] operand of the update
-constexpr float kQScale = 4096.0f;          // on the query operand of the readout
-constexpr float kUScale = 1.0f / 16.0f;     // 1 / (kQScale kVScale): readout back to S's units
+constexpr int kLU = kImgLU;                 // tokens per state update
 
 template <int D, int NCT>
 struct Layout {
-    static constexpr int L = kL;                     // chunk (partials)
-    static constexpr int LU = kLU;                   // update sub-chunk
-    static constexpr int R = D == 64 ? 256 : 128;    // readout window (tokens)
+    static constexpr int L = kL;
+    static constexpr int LU = kLU;
+    static constexpr int R = img_window(D);          // readout window (tokens)
     static constexpr int NSUB = R / L;               // chunks per window
+    static constexpr int NUPD = R / LU;              // updates per window
     static constexpr int TW = R / kWaves;            // readout tokens per wave (32 or 16)
     static constexpr int MTW = TW / 16;              // readout token tiles per wave
     static constexpr int KS = kRowsPerSlice / 4;     // readout K-steps (32 features each)
-    static constexpr int XR = D + 8;                 // raw q/k row: D coords, 1, then 7 zeros
-    static constexpr int XSLOTS = XR / 8;            // 16-byte slots per raw row
-    static constexpr int TS = LU + 8;                // fp16 token-major row stride of the tables
-    static constexpr int VROWS = NCT == 5 ? 65 : 64;
-    static constexpr int sb = 0;                                    // [4 ct][KS][64 lanes] x 16 B
+    static constexpr int XR = img_xr(D);             // q/k row: D coords, the constant 1, 7 zeros
+    static constexpr int TS = img_ts();              // token-major row stride of the tables
+    static constexpr int KTB = img_kt_bytes(D), VTB = img_vt_bytes(), TABB = KTB + VTB;
+    static constexpr int QB = img_q_bytes(D);
+    // LDS
+    static constexpr int t1 = 0;                                    // update tables 1: keys, values
+    static constexpr int sb = TABB;                                 // fp16 state: [4 ct][KS][64 lanes] x 16 B
     static constexpr int sb4 = sb + 4 * KS * 64 * 16;               // normaliser tile: [KS][4 g] x 16 B
-    // the update's tables alias the fp16 state: they live between the window's readout
-    // and the next window's state copy
-    static constexpr int vt = 0;                                    // [VROWS][TS]
-    static constexpr int kT = vt + VROWS * TS * 2;                  // [XR coordinates][TS] fp16 keys
-    static constexpr int tables_end = kT + XR * TS * 2;
     static constexpr int sb_end = sb4 + (NCT == 5 ? KS * 4 * 16 : 0);
-    static constexpr int qt = ((tables_end > sb_end ? tables_end : sb_end) + 15) / 16 * 16;  // window's q rows
-    static constexpr int rawk = qt + R * XR * 2;                    // one sub-chunk of raw k
-    static constexpr int rawv = rawk + LU * XR * 2;                 // one sub-chunk of raw v (64 columns)
-    static constexpr int ri = rawv + LU * 64 * 2;                   // [64 rows] readout row constants
-    static constexpr int bytes = ri + kRowsPerSlice * 8;
-    // state load/store staging (outside the chunk loop) aliases the fp16 state area
+    static constexpr int t2 = sb;                                   // update tables 2, over the state copy
+    static constexpr int qt = sb_end;                               // the window's q rows [R][XR]
+    static constexpr int ri = qt + QB;                              // [64 rows] readout row constants
+    static constexpr int wmx = ri + kRowsPerSlice * 8;              // [8] per-wave state maxima
+    static constexpr int bytes = wmx + kWaves * 4;
+    // state load/store staging at the segment's ends (over the state copy)
     static constexpr int IO = 68;                                   // floats per feature row
     static constexpr int io_rows = kWaves * 16;                     // one tile per wave per phase
     static constexpr int cf = sb + io_rows * IO * 4;                // [512] canonical index, [512] factor
-    static_assert(cf + kRowsPerSlice * 8 * 8 <= 4 * KS * 64 * 16, "state staging size");
-    static_assert(qt % 16 == 0 && rawk % 16 == 0 && rawv % 16 == 0 && kT % 16 == 0 && ri % 16 == 0,
-                  "16-byte alignment of LDS regions");
-    static_assert((R * XSLOTS) % 64 == 0 && (LU * XSLOTS) % 64 == 0, "whole DMA blocks per raw chunk");
-    static_assert(TW % 16 == 0 && L % TW == 0 && KS == 16 && R % LU == 0, "readout tiling");
+    static_assert(cf + kRowsPerSlice * 8 * 8 <= sb + 4 * KS * 64 * 16, "state staging size");
+    static_assert(NUPD == 1 || TABB <= 4 * KS * 64 * 16, "second table buffer inside the state copy");
+    // the second buffer is addressed from the first one's lane bases: its largest constant
+    // offset must fit the 16-bit offset field of ds_read
+    static_assert(NUPD == 1 || t2 - t1 + (3 * 16 * TS + 96) * 2 < 65536, "table offsets");
+    static_assert(QB % 1024 == 0 && TABB % 1024 == 0 && KTB % 1024 == 0 && qt % 16 == 0 && ri % 16 == 0,
+                  "whole DMA blocks, 16-byte alignment");
+    static_assert(TW % 16 == 0 && L % TW == 0 && KS == 16 && R % LU == 0 && (NUPD == 1 || NUPD == 2), "tiling");
 };
-
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// 8 bf16 values (one 16-byte slot) to fp16; exact for |x| in fp16's normal range
-__device__ inline f16x8 bf16x8_to_f16(const uint4& r) {
-    f16x8 o;
-    o[0] = (_Float16)bf16_lo(r.x); o[1] = (_Float16)bf16_hi(r.x);
-    o[2] = (_Float16)bf16_lo(r.y); o[3] = (_Float16)bf16_hi(r.y);
-    o[4] = (_Float16)bf16_lo(r.z); o[5] = (_Float16)bf16_hi(r.z);
-    o[6] = (_Float16)bf16_lo(r.w); o[7] = (_Float16)bf16_hi(r.w);
-    return o;
-}
-
-__device__ inline f16x8 pack_tiles(const f32x4v& lo, const f32x4v& hi) {
-    f16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = (_Float16)lo[e];
-        r[4 + e] = (_Float16)hi[e];
-    }
-    return r;
-}
-
-// the key-side factor as the update applies it (rounded to fp16)
-__device__ inline float kfactor(float c) { return (float)(_Float16)c; }
 
 // An LDS byte address the compiler may not re-derive: the constant parts of the
 // accesses made from it then fit the 16-bit offset field of ds_read/ds_write, and one
@@ -142,10 +124,10 @@ __device__ inline const T& lds_at(const unsigned char* lds, uint32_t base, uint3
     return *reinterpret_cast<const T*>(lds + base + off);
 }
 
-// Workgroup barrier for the chunk loop: this wave's LDS accesses have completed and
+// Workgroup barrier for the window loop: this wave's LDS accesses have completed and
 // at most VM of its vector-memory operations are still outstanding (63: no wait).
-// Unlike __syncthreads() it does not wait for outstanding global stores unless VM
-// asks for it (they retire in order with the loads on this architecture).
+// Unlike __syncthreads() it does not wait for outstanding loads or stores unless VM asks
+// for it (they complete in order on this architecture).
 template <int VM>
 __device__ inline void lds_barrier() {
     static_assert(VM >= 0 && VM <= 63, "vmcnt range");
@@ -155,45 +137,43 @@ __device__ inline void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Direct-to-LDS copy of NB KiB blocks: wave w moves blocks w, w + 8, ...; lane i fills
+// bytes [16 i, 16 i + 16) of its block.  Source and destination are whole blocks.
+template <int NB>
+__device__ inline void dma_blocks(const uint16_t* src, unsigned char* dst, int w, int lane) {
+    for (int blk = w; blk < NB; blk += kWaves)
+        __builtin_amdgcn_global_load_lds((const void*)(src + blk * 512 + lane * 8),
+                                         (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
+}
+// the fewest blocks any wave moves in dma_blocks<NB> (for counted waits)
+template <int NB>
+constexpr int dma_min_per_wave() { return NB / kWaves; }
+
+// the key-side factor as the update applies it (rounded to fp16)
+__device__ inline float kfactor(float c) { return (float)(_Float16)c; }
+
+// largest value over a wave (non-negative inputs)
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+// floor(log2 x) of a positive normal float from its bits; clamped to [lo, hi]
+__device__ inline int exp2_of(float x, int lo, int hi) {
+    const int e = (int)((__float_as_uint(x) >> 23) & 0xffu) - 127;
+    return e < lo ? lo : (e > hi ? hi : e);
+}
+
 struct RowPtrs {
     const uint32_t* parent;
     const float* weight;
     const float* kscale;
     const int32_t* canon;
     const int32_t* wave_lblock;
+    const int8_t* degree;
+    int wlog[8];
 };
-
-// Direct-to-LDS copies of ROWS rows of q or k.  A wave instruction moves 64 lanes x
-// 16 bytes into a contiguous 1 KiB block; lane i fills bytes [16 i, 16 i + 16).  The
-// slot after each row's D coordinates holds the constant coordinates (1, 0, ..., 0),
-// written once: its lanes are masked off.  Rows past n read row 0 of the chunk
-// instead (masked later).  Addresses are a uniform base plus 32-bit lane offsets.
-template <int D, int ROWS>
-__device__ inline void prefetch_x(const uint16_t* x0, int nvalid, unsigned char* dst, int w, int lane) {
-    constexpr int XSLOTS = (D + 8) / 8;
-    constexpr int NBLK = ROWS * XSLOTS / 64;
-    for (int blk = w; blk < NBLK; blk += kWaves) {
-        const int sl = blk * 64 + lane;
-        const int t = sl / XSLOTS, cs = sl % XSLOTS;
-        if (cs != D / 8)
-            __builtin_amdgcn_global_load_lds((const void*)(x0 + ((t < nvalid ? t : 0) * D + 8 * cs)),
-                                             (void __attribute__((address_space(3)))*)(dst + blk * 1024), 16, 0, 0);
-    }
-}
-
-// The 64 value columns [col0, col0 + 64) of a sub-chunk's v rows (row length d_V), v0
-// at its first row and column col0, stored column-group major per 64 tokens: wave w
-// moves columns 8w .. 8w+7 of tokens 64 h + lane into 1 KiB block 8 h + w.  Rows past
-// nvalid read row 0 instead (masked later).
-template <int ROWS>
-__device__ inline void prefetch_v(const uint16_t* v0, int nvalid, int d_V, unsigned char* dst, int w, int lane) {
-#pragma unroll
-    for (int h = 0; h < ROWS / 64; ++h) {
-        const int t = 64 * h + lane;
-        __builtin_amdgcn_global_load_lds((const void*)(v0 + ((t < nvalid ? t : 0) * d_V + 8 * w)),
-                                         (void __attribute__((address_space(3)))*)(dst + (8 * h + w) * 1024), 16, 0, 0);
-    }
-}
 
 template <int D, int DV, int G, int NPC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -202,22 +182,22 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     constexpr int col0 = 64 * G;             // first value column of the group
     constexpr int NCT = ONES ? 5 : 4;        // column tiles of this group
     constexpr int NCL = ONES ? 65 : 64;      // live columns of this group
+    constexpr int NG = DV / 64;              // column groups of the head
     using LY = Layout<D, NCT>;
-    constexpr int L = kL, LU = LY::LU, XR = LY::XR, TS = LY::TS, NSUB = LY::NSUB, R = LY::R, TW = LY::TW;
-    constexpr int MTW = LY::MTW, KS = LY::KS;
+    constexpr int L = kL, LU = LY::LU, TS = LY::TS, NSUB = LY::NSUB, TW = LY::TW;
+    constexpr int XR = LY::XR, MTW = LY::MTW, KS = LY::KS, NUPD = LY::NUPD;
+    constexpr int NB_Q = LY::QB / 1024;
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    const uint16_t* rk = reinterpret_cast<const uint16_t*>(lds_raw + LY::rawk);
-    _Float16* vt = reinterpret_cast<_Float16*>(lds_raw + LY::vt);
-    _Float16* kT = reinterpret_cast<_Float16*>(lds_raw + LY::kT);
     f16x8* sb = reinterpret_cast<f16x8*>(lds_raw + LY::sb);
     f16x8* sb4 = reinterpret_cast<f16x8*>(lds_raw + LY::sb4);
+    float* wmx = reinterpret_cast<float*>(lds_raw + LY::wmx);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y / a.nsub;
     const int sub = blockIdx.y % a.nsub;
-    constexpr int d_V = DV, cols = DV + 1;
+    constexpr int d_V = DV;
     const int nch = a.c_end - a.c_begin;       // chunks of the partial buffer
     // the chunks this block scans: its sub-segment (the whole range when nsub = 1)
     const int cb = a.c_begin + sub * a.sub_chunks;
@@ -226,51 +206,47 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const int lb_w = rt.wave_lblock[slice * kWaves + w];     // l-block of this wave's update rows
     // global column of local column j of this group (local 64 is the normaliser)
     auto gcol = [&](int j) { return (ONES && j == 64) ? d_V : col0 + j; };
+    float* state = a.state ? a.state + (bh * a.nsub + sub) * (int64_t)(DV + 1) * a.M_pad : nullptr;
 
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + bh * (int64_t)a.n * D;
-    const uint16_t* k = static_cast<const uint16_t*>(a.k) + bh * (int64_t)a.n * D;
-    const uint16_t* v = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.n * d_V;
-    float* state = a.state ? a.state + (bh * a.nsub + sub) * (int64_t)cols * a.M_pad : nullptr;
-
-    // tokens of [c L, c L + len) that exist
-    auto nvalid_of = [&](int c, int len) {
-        const int64_t r = a.n - (int64_t)c * L;
-        return (int)(r < len ? r : len);
-    };
-    // tokens of [c L, c L + LU) that belong to the segment (the update stops at its end)
-    const int64_t seg_end = (int64_t)ce * L < a.n ? (int64_t)ce * L : a.n;
-    auto nupd_of = [&](int c) {
-        const int64_t r = seg_end - (int64_t)c * L;
-        return (int)(r < LU ? r : LU);
-    };
-    auto prefetch_q = [&](int cw) {
-        prefetch_x<D, R>(q + (int64_t)cw * L * D, nvalid_of(cw, R), lds_raw + LY::qt, w, lane);
-    };
-    auto prefetch_kv = [&](int c) {        // the update sub-chunk starting at chunk c
-        const int64_t t0 = (int64_t)c * L;
-        const int nv = nupd_of(c);
-        prefetch_x<D, LU>(k + t0 * D, nv, lds_raw + LY::rawk, w, lane);
-        prefetch_v<LU>(v + t0 * d_V + col0, nv, d_V, lds_raw + LY::rawv, w, lane);
-    };
-    // the constant coordinate slot of every raw q and k row, for good
-    for (int t = tid; t < R + LU; t += 512) {
-        uint16_t* row = reinterpret_cast<uint16_t*>(lds_raw + (t < R ? LY::qt : LY::rawk)) + (t < R ? t : t - R) * XR + D;
-        *reinterpret_cast<uint4*>(row) = uint4{0x3f80u, 0u, 0u, 0u};
+    // per-head exponents of the input scales and of the query weights
+    const int s_q = prep_scale_exp(a.maxbits[bh * 4 + 0]);
+    const int s_k = prep_scale_exp(a.maxbits[bh * 4 + 1]);
+    const int s_v = prep_scale_exp(a.maxbits[bh * 4 + 2]);
+    int e_q = -1000;
+    for (int p = 0; p < a.P; ++p) {
+        const int e = rt.wlog[p] + p * (s_q + s_k + 1);
+        e_q = e > e_q ? e : e_q;
     }
-    // the first window's q and first sub-chunk's k, v in flight while the state is set up
-    if (!a.update_only) prefetch_q(cb);
-    prefetch_kv(cb);
+    e_q -= 14;
+
+    // operand images of this head (windows and sub-chunks relative to the images' first)
+    const uint16_t* qimg = a.qimg + bh * (int64_t)a.img_nwin * (LY::QB / 2);
+    const uint16_t* kimg = a.kimg + bh * (int64_t)a.img_nsub * (LY::KTB / 2);
+    const uint16_t* vimg = a.vimg + (bh * NG + G) * (int64_t)a.img_nsub * (LY::VTB / 2);
+    auto dma_q = [&](int cw) {               // q rows of the window starting at chunk cw
+        dma_blocks<NB_Q>(qimg + (int64_t)(cw / NSUB - a.img_w0) * (LY::QB / 2), lds_raw + LY::qt, w, lane);
+    };
+    auto dma_tables = [&](int cu, int buf) {  // tables of the update sub-chunk starting at chunk cu
+        const int64_t u = (int64_t)cu * L / LU - a.img_u0;
+        unsigned char* dst = lds_raw + (buf == 0 ? LY::t1 : LY::t2);
+        dma_blocks<LY::KTB / 1024>(kimg + u * (LY::KTB / 2), dst, w, lane);
+        dma_blocks<LY::VTB / 1024>(vimg + u * (LY::VTB / 2), dst + LY::KTB, w, lane);
+    };
+    // the first window's q rows and first tables in flight while the state is set up
+    if (!a.update_only) dma_q(cb);
+    dma_tables(cb, 0);
 
     // readout constants of the slice's rows (K-step s covers rows 4 s .. 4 s + 3, lane group
     // g row 4 s + g), in LDS: the parent coordinates as byte offsets in a q row (10 bits
-    // each) and the query weight with the operand scale (fp16 bits)
+    // each) and the query weight W'_a (fp16 bits)
     if (tid < kRowsPerSlice) {
         const int row = row_s + tid;
         const uint32_t p3 = rt.parent[row];
         uint32_t o = 0;
 #pragma unroll
         for (int e = 0; e < NPC; ++e) o |= (((p3 >> (10 * e)) & 1023u) * 2u) << (10 * e);
-        const _Float16 wq = (_Float16)(rt.weight[row] * kQScale);
+        const int p = rt.degree[row];
+        const _Float16 wq = (_Float16)ldexpf(rt.weight[row], p * (s_q + s_k) - e_q);
         reinterpret_cast<uint2*>(lds_raw + LY::ri)[tid] = uint2{o, (uint32_t)__builtin_bit_cast(uint16_t, wq)};
     }
     // l-blocks of the slice's row octets (uniform)
@@ -279,7 +255,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     for (int gi = 0; gi < KS / 2; ++gi) lbg[gi] = __builtin_amdgcn_readfirstlane(rt.wave_lblock[slice * kWaves + gi]);
     // key parents of this lane's update rows 8 w + 4 s + li / 4: byte offsets of their
     // coordinate rows in the key table (a missing parent is the constant coordinate d,
-    // which is 1 for the chunk's tokens and 0 past them)
+    // which is 1 for the tokens that exist and 0 past them)
     constexpr int NPR = NPC > 0 ? NPC : 1;
     uint32_t kpa[2][NPR];
 #pragma unroll
@@ -287,7 +263,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const uint32_t p3 = rt.parent[row_s + 8 * w + 4 * s + (li >> 2)];
 #pragma unroll
         for (int e = 0; e < NPR; ++e)
-            kpa[s][e] = lds_base(LY::kT + (((p3 >> (10 * e)) & 1023u) * TS + 8 * g) * 2);
+            kpa[s][e] = lds_base(LY::t1 + (((p3 >> (10 * e)) & 1023u) * TS + 8 * g) * 2);
     }
     // key-side factor of this lane's feature in update tile T (rows 4 (T / 2) + li / 4)
     _Float16 cK[4];
@@ -295,37 +271,41 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     for (int T = 0; T < 4; ++T)
         cK[T] = (_Float16)rt.kscale[(row_s + 8 * w + 4 * (T >> 1) + (li >> 2)) * 8 + 4 * (T & 1) + (li & 3)];
 
-    // Resident state slice S', update-accumulator layout: lane (column 16 ct + li, g)
+    // Resident state slice S'', update-accumulator layout: lane (column 16 ct + li, g)
     // register r of tile T holds kernel feature (row 8 w + 4 (T / 2) + g, element 4 (T % 2) + r).
     f32x4v S[4][NCT];
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[T][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+
     // State I/O at the segment's ends goes through LDS, one update tile per wave at a time.
-    // The slice's canonical feature index and key-side factor per kernel feature are staged
-    // in LDS first; consecutive threads then take consecutive kernel features of one column
-    // (mostly consecutive canonical features: few cache lines per wave), and every thread
-    // issues all its loads before it writes any of them.
+    // The slice's canonical feature index and the factor S'' / S per kernel feature are
+    // staged in LDS first; consecutive threads then take consecutive kernel features of one
+    // column (mostly consecutive canonical features: few cache lines per wave), and every
+    // thread keeps several loads in flight.
     constexpr int NIO = (LY::io_rows * NCL + 511) / 512, IOB = 6;
     int32_t* cf_idx = reinterpret_cast<int32_t*>(lds_raw + LY::cf);
     float* cf_fac = reinterpret_cast<float*>(lds_raw + LY::cf) + kRowsPerSlice * 8;
+    const float vfac = ldexpf(1.0f, -s_v);
+    // S'' / S of local column j: the value scale (the normaliser has none)
+    auto colfac = [&](int j) { return (ONES && j == 64) ? 1.0f : vfac; };
+    auto stage_canon = [&]() {
+        const int fi = row_s * 8 + tid;
+        cf_idx[tid] = rt.canon[fi];
+        cf_fac[tid] = ldexpf(kfactor(rt.kscale[fi]), -(int)rt.degree[row_s + (tid >> 3)] * s_k);
+    };
     // kernel feature (within the slice) of staging row fr of update tile T
     auto kf_of = [](int T, int fr) {
         const int ww = fr / 16, rho = fr % 16;
         return (8 * ww + 4 * (T >> 1) + (rho >> 2)) * 8 + 4 * (T & 1) + (rho & 3);
     };
     if (a.load_state) {
-        const int fi = row_s * 8 + tid;
-        cf_idx[tid] = rt.canon[fi];
-        cf_fac[tid] = kfactor(rt.kscale[fi]) * kVScale;
-    }
-    if (a.load_state) {
+        stage_canon();
         float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             __syncthreads();
-            // batches of IOB loads in flight per thread
             for (int i0 = 0; i0 < NIO; i0 += IOB) {
                 float vals[IOB];
 #pragma unroll
@@ -335,7 +315,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                     if (idx < LY::io_rows * NCL) {
                         const int j = idx / LY::io_rows, kf = kf_of(T, idx % LY::io_rows);
                         const int F = cf_idx[kf];
-                        if (F >= 0) x = state[(int64_t)gcol(j) * a.M_pad + F] * cf_fac[kf];
+                        if (F >= 0) x = state[(int64_t)gcol(j) * a.M_pad + F] * (cf_fac[kf] * colfac(j));
                     }
                     vals[i] = x;
                 }
@@ -355,107 +335,71 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 }
         }
     }
+    __syncthreads();                         // staging reads done before the area is reused
 
+    // per-lane LDS bases of the contraction's operand tables (byte addresses); the second
+    // table buffer is reached from the first one's bases by a constant offset
+    constexpr uint32_t T2OFF = (uint32_t)(LY::t2 - LY::t1);
+    const uint32_t a_sb = lds_base(LY::sb + lane * 16);                           // [ct][K-step][lane]
+    const uint32_t a_sb4 = lds_base(LY::sb4 + g * 16);                            // [K-step][g]
+    const uint32_t a_vt = lds_base(LY::t1 + LY::KTB + (li * TS + 8 * g) * 2);    // row 16 ct + li
+    const uint32_t a_vt4 = lds_base(LY::t1 + LY::KTB + (64 * TS + 8 * g) * 2);   // the ones row
+    const uint32_t a_kt = lds_base(LY::t1 + ((8 * lb_w + (li & 3)) * TS + 8 * g) * 2);
+    const uint32_t a_q = lds_base(LY::qt + (TW * w + li) * XR * 2);               // token row, tile 0
+    const uint32_t a_ri = lds_base(LY::ri + g * 8);                               // row 4 s + g
+
+    // the slice's largest state entry (over all waves: posted to LDS, read after a barrier)
+    auto post_max = [&]() {
+        float m = 0.0f;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(S[T][ct][r]));
+        m = wave_max(m);
+        if (lane == 0) wmx[w] = m;
+    };
+    // exponent e_w of the readout's fp16 state copy: the copy S'' 2^-e_w stays below 2^15
+    auto copy_exp = [&]() {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) m = fmaxf(m, wmx[i]);
+        return m > 0.0f ? exp2_of(m, -100, 126) - 14 : 0;
+    };
     // fp16 copy of this wave's state for the readout (K-steps 2 w, 2 w + 1)
-    auto store_sb = [&]() {
+    auto store_sb = [&](int e_w) {
+        const float f = ldexpf(1.0f, -e_w);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const f16x8 p = pack_tiles(S[2 * s][ct], S[2 * s + 1][ct]);
+                const f32x4v lo = S[2 * s][ct] * f, hi = S[2 * s + 1][ct] * f;
+                const f16x8 p = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+                                 (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
                 if (ct < 4) sb[(ct * KS + 2 * w + s) * 64 + lane] = p;
                 else if (li == 0) sb4[(2 * w + s) * 4 + g] = p;
             }
     };
-    __syncthreads();                         // staging reads done before the area is reused
 
-    // per-lane LDS bases of the contraction's operand tables (byte addresses)
-    const uint32_t a_sb = lds_base(LY::sb + lane * 16);                           // [ct][K-step][lane]
-    const uint32_t a_sb4 = lds_base(LY::sb4 + g * 16);                            // [K-step][g]
-    const uint32_t a_vt = lds_base(LY::vt + (li * TS + 8 * g) * 2);               // row 16 ct + li
-    const uint32_t a_vt4 = lds_base(LY::vt + (64 * TS + 8 * g) * 2);              // the ones row
-    const uint32_t a_kt = lds_base(LY::kT + ((8 * lb_w + (li & 3)) * TS + 8 * g) * 2);
-    const uint32_t a_q = lds_base(LY::qt + (TW * w + li) * XR * 2);               // token row, tile 0
-    const uint32_t a_ri = lds_base(LY::ri + g * 8);                               // row 4 s + g
-
-    // fp16 tables of the update sub-chunk starting at chunk c from its raw k and v.  A
-    // thread takes two consecutive tokens of one 16-byte slot: both raw rows are read
-    // before any conversion, and each transposed table row gets 4-byte token pairs.
-    auto build_tables = [&](int c) {
-        const int nvalid = nupd_of(c);
-        static_assert(LU == 128, "one token pair per lane");
-        const int t0 = 2 * lane;                                    // this lane's tokens t0, t0 + 1
-        const uint32_t m0 = t0 < nvalid ? 0xffffffffu : 0u, m1 = t0 + 1 < nvalid ? 0xffffffffu : 0u;
-        constexpr int NKS = D / 8 / kWaves;                         // key slots per thread (1 or 2)
-        uint4 kx[NKS][2], vx[2];
-        // raw v: block 8 h + w holds columns 8 w .. 8 w + 7 of tokens 64 h + (0 .. 63)
-        const uint4* rv = reinterpret_cast<const uint4*>(lds_raw + LY::rawv) + (8 * (t0 >> 6) + w) * 64 + (t0 & 63);
-        vx[0] = rv[0];
-        vx[1] = rv[1];
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-            const int cs = w + kWaves * j;
-            kx[j][0] = *reinterpret_cast<const uint4*>(rk + t0 * XR + 8 * cs);
-            kx[j][1] = *reinterpret_cast<const uint4*>(rk + (t0 + 1) * XR + 8 * cs);
-        }
-        auto mask = [&](uint4& x, uint32_t m) { x.x &= m; x.y &= m; x.z &= m; x.w &= m; };
-        mask(vx[0], m0);
-        mask(vx[1], m1);
-        {   // v: [column][token], scaled
-            const uint32_t a0[4] = {vx[0].x, vx[0].y, vx[0].z, vx[0].w};
-            const uint32_t a1[4] = {vx[1].x, vx[1].y, vx[1].z, vx[1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f16x2 lo = __builtin_convertvector(f32x2{bf16_lo(a0[e]), bf16_lo(a1[e])} * kVScale, f16x2);
-                const f16x2 hi = __builtin_convertvector(f32x2{bf16_hi(a0[e]), bf16_hi(a1[e])} * kVScale, f16x2);
-                *reinterpret_cast<f16x2*>(vt + (8 * w + 2 * e) * TS + t0) = lo;
-                *reinterpret_cast<f16x2*>(vt + (8 * w + 2 * e + 1) * TS + t0) = hi;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) {   // keys: every coordinate to [coordinate][token]
-            const int cs = w + kWaves * j;
-            mask(kx[j][0], m0);
-            mask(kx[j][1], m1);
-            const uint32_t a0[4] = {kx[j][0].x, kx[j][0].y, kx[j][0].z, kx[j][0].w};
-            const uint32_t a1[4] = {kx[j][1].x, kx[j][1].y, kx[j][1].z, kx[j][1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f16x2 lo = __builtin_convertvector(f32x2{bf16_lo(a0[e]), bf16_lo(a1[e])}, f16x2);
-                const f16x2 hi = __builtin_convertvector(f32x2{bf16_hi(a0[e]), bf16_hi(a1[e])}, f16x2);
-                *reinterpret_cast<f16x2*>(kT + (8 * cs + 2 * e) * TS + t0) = lo;
-                *reinterpret_cast<f16x2*>(kT + (8 * cs + 2 * e + 1) * TS + t0) = hi;
-            }
-        }
-        {   // the constant key coordinate d (1 for the tokens, 0 past them), then
-            // coordinates d + 1 .. d + 7 (zeros): row d + w, this lane's token pair
-            const _Float16 one0 = (_Float16)(w == 0 && t0 < nvalid ? 1.0f : 0.0f);
-            const _Float16 one1 = (_Float16)(w == 0 && t0 + 1 < nvalid ? 1.0f : 0.0f);
-            *reinterpret_cast<f16x2*>(kT + (D + w) * TS + t0) = f16x2{one0, one1};
-            // the ones row of [v | 1]
-            if (ONES && w == 0)
-                *reinterpret_cast<f16x2*>(vt + 64 * TS + t0) =
-                    f16x2{(_Float16)(t0 < nvalid ? kVScale : 0.0f), (_Float16)(t0 + 1 < nvalid ? kVScale : 0.0f)};
-        }
-    };
-
-    // update S' += K^^T . [v | 1] of this wave's rows over the sub-chunk in the tables
-    auto update = [&]() {
+    // update S'' += K^^T . [v' | 1] of this wave's rows over the sub-chunk in table buffer TB
+    auto update = [&](auto TBc) {
+        constexpr uint32_t TO = decltype(TBc)::value ? T2OFF : 0u;
 #pragma unroll
         for (int kk = 0; kk < LU / 32; ++kk) {
             f16x8 Vop[NCT], kreg[2];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Vop[ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_vt, (16 * ct * TS + 32 * kk) * 2)
-                                 : lds_at<f16x8>(lds_raw, a_vt4, 32 * kk * 2);
+                Vop[ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_vt, TO + (16 * ct * TS + 32 * kk) * 2)
+                                 : lds_at<f16x8>(lds_raw, a_vt4, TO + 32 * kk * 2);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) kreg[hh] = lds_at<f16x8>(lds_raw, a_kt, (4 * hh * TS + 32 * kk) * 2);
+            for (int hh = 0; hh < 2; ++hh) kreg[hh] = lds_at<f16x8>(lds_raw, a_kt, TO + (4 * hh * TS + 32 * kk) * 2);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 // parent product of this lane's row for its 8 tokens
-                f16x8 kp8 = lds_at<f16x8>(lds_raw, kpa[s][0], 32 * kk * 2);
+                f16x8 kp8 = lds_at<f16x8>(lds_raw, kpa[s][0], TO + 32 * kk * 2);
 #pragma unroll
-                for (int e = 1; e < NPR; ++e) kp8 = kp8 * lds_at<f16x8>(lds_raw, kpa[s][e], 32 * kk * 2);
+                for (int e = 1; e < NPR; ++e) kp8 = kp8 * lds_at<f16x8>(lds_raw, kpa[s][e], TO + 32 * kk * 2);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int T = 2 * s + h;
@@ -468,129 +412,147 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         }
     };
 
+    // the fp16 state copy of the first window
+    int e_w = 0;
+    if (!a.update_only) {
+        post_max();
+        __syncthreads();
+        e_w = copy_exp();
+        store_sb(e_w);
+    }
+
     // Windows of NSUB chunks: one readout of the window's R tokens against the state
     // before the window, then the window's updates, LU tokens each.  The finalize adds
     // the direct part of the window's earlier chunks.
     for (int cw = cb; cw < ce; cw += NSUB) {
         const int nchw = ce - cw < NSUB ? ce - cw : NSUB;             // chunks of the window
         const bool next_w = cw + NSUB < ce;
-        lds_barrier<0>();           // the window's q and first k, v landed; the updates are done
+        // B1: the window's q rows landed (only the next tables may still be in flight)
+        lds_barrier<dma_min_per_wave<LY::KTB / 1024>() + dma_min_per_wave<LY::VTB / 1024>()>();
+        int nst = 0;                                                  // partial stores issued
         if (!a.update_only) {
-
-        // ---- fp16 state for the readout (over the previous window's tables); q to fp16 --
-        store_sb();
-        {
-            constexpr int NQ = (R * LY::XSLOTS + 511) / 512;
-            uint4 r[NQ];
+            // ---- readout: window tokens TW w .. TW w + TW - 1 over the slice's K-steps ----
+            f32x4v U[MTW][NCT];
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int sl = tid + 512 * i;
-                if (sl < R * LY::XSLOTS) r[i] = reinterpret_cast<const uint4*>(lds_raw + LY::qt)[sl];
-            }
+            for (int m = 0; m < MTW; ++m)
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int sl = tid + 512 * i;
-                // the constant slot is written as fp16 (1, 0, ..., 0); loads never refill it
-                const f16x8 h = sl % LY::XSLOTS == D / 8 ? f16x8{1, 0, 0, 0, 0, 0, 0, 0} : bf16x8_to_f16(r[i]);
-                if (sl < R * LY::XSLOTS) reinterpret_cast<f16x8*>(lds_raw + LY::qt)[sl] = h;
-            }
-        }
-        lds_barrier<63>();
-
-        // ---- readout: window tokens TW w .. TW w + TW - 1 over the slice's K-steps --------
-        f32x4v U[MTW][NCT];
+                for (int ct = 0; ct < NCT; ++ct) U[m][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+            {
+                // software-pipelined: the B operands of K-step s + 1 are requested before the
+                // MFMAs of step s
+                f16x8 B[2][NCT], qreg[MTW];
 #pragma unroll
-        for (int m = 0; m < MTW; ++m)
+                for (int ct = 0; ct < NCT; ++ct)
+                    B[0][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, ct * KS * 64 * 16) : lds_at<f16x8>(lds_raw, a_sb4, 0);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) U[m][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-        {
-            // software-pipelined: the B operands of K-step s + 1 are requested before the
-            // MFMAs of step s
-            f16x8 B[2][NCT], qreg[MTW];
+                for (int s = 0; s < KS; ++s) {
+                    if (s + 1 < KS) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                B[0][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, ct * KS * 64 * 16) : lds_at<f16x8>(lds_raw, a_sb4, 0);
+                        for (int ct = 0; ct < NCT; ++ct)
+                            B[(s + 1) & 1][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, (ct * KS * 64 + (s + 1) * 64) * 16)
+                                                        : lds_at<f16x8>(lds_raw, a_sb4, (s + 1) * 64);
+                    }
+                    if (s % 2 == 0) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if (s + 1 < KS) {
+                        for (int m = 0; m < MTW; ++m)
+                            qreg[m] = lds_at<f16x8>(lds_raw, a_q + 16u * (uint32_t)lbg[s / 2], m * 16 * XR * 2);
+                    }
+                    const uint2 rc = lds_at<uint2>(lds_raw, a_ri, s * 4 * 8);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        B[(s + 1) & 1][ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_sb, (ct * KS * 64 + (s + 1) * 64) * 16)
-                                                    : lds_at<f16x8>(lds_raw, a_sb4, (s + 1) * 64);
-                }
-                if (s % 2 == 0) {
+                    for (int m = 0; m < MTW; ++m) {
+                        _Float16 qp = __builtin_bit_cast(_Float16, (uint16_t)rc.y);
 #pragma unroll
-                    for (int m = 0; m < MTW; ++m)
-                        qreg[m] = lds_at<f16x8>(lds_raw, a_q + 16u * (uint32_t)lbg[s / 2], m * 16 * XR * 2);
-                }
-                const uint2 rc = lds_at<uint2>(lds_raw, a_ri, s * 4 * 8);
+                        for (int e = 0; e < NPC; ++e)
+                            qp *= lds_at<_Float16>(lds_raw, a_q + ((rc.x >> (10 * e)) & 1023u), m * 16 * XR * 2);
+                        const f16x8 A = qreg[m] * qp;
 #pragma unroll
-                for (int m = 0; m < MTW; ++m) {
-                    _Float16 qp = __builtin_bit_cast(_Float16, (uint16_t)rc.y);
-#pragma unroll
-                    for (int e = 0; e < NPC; ++e)
-                        qp *= lds_at<_Float16>(lds_raw, a_q + ((rc.x >> (10 * e)) & 1023u), m * 16 * XR * 2);
-                    const f16x8 A = qreg[m] * qp;
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        U[m][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[s & 1][ct], U[m][ct], 0, 0, 0);
+                        for (int ct = 0; ct < NCT; ++ct)
+                            U[m][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[s & 1][ct], U[m][ct], 0, 0, 0);
+                    }
                 }
             }
-        }
-        {   // this wave's tokens lie in one chunk.  Partials in HBM, per (chunk, slice), in
-            // the tiled layout (launch.h): a lane's accumulators of two adjacent column tiles
-            // as one 16-byte store of fp16, so that one store instruction writes 1 KiB
-            // contiguously; then the normaliser column in fp32, [token] (its lanes li = 0
-            // write 16 bytes each)
+            // this wave's tokens lie in one chunk.  Partials in HBM, per (chunk, slice), in the
+            // tiled layout (launch.h): per 16-token tile a power-of-two scale from the tile's
+            // largest value; a lane's accumulators of two adjacent column tiles as one 16-byte
+            // store of fp16 (one store instruction writes 1 KiB contiguously); the normaliser
+            // column in fp32, [token]; the tile's scale
             const int cs = (TW * w) / L;
             if (cs < nchw) {
                 const int c = cw + cs;
                 constexpr int NVP = d_V / 32;                       // value column-tile pairs of the head
-                constexpr float ps = kUScale * kPartialScale;
                 float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * tiled_partial_floats(L, d_V);
                 _Float16* ph = reinterpret_cast<_Float16*>(pp);
 #pragma unroll
                 for (int m = 0; m < MTW; ++m) {
                     const int mg = ((TW * w) % L) / 16 + m;         // token tile within the chunk
+                    float mx = 0.0f;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(U[m][ct][r]));
+                    mx = wave_max(mx);
+                    const int ex = mx > 0.0f ? exp2_of(mx, -110, 126) : 0;
+                    const float mul = ldexpf(1.0f, 14 - ex);
 #pragma unroll
                     for (int cp = 0; cp < 2; ++cp) {
-                        const f32x4v lo = U[m][2 * cp] * ps, hi = U[m][2 * cp + 1] * ps;
+                        const f32x4v lo = U[m][2 * cp] * mul, hi = U[m][2 * cp + 1] * mul;
                         const f16x8 h = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
                                          (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
                         *reinterpret_cast<f16x8*>(ph + ((mg * NVP + 2 * G + cp) * 64 + lane) * 8) = h;
                     }
                     if constexpr (ONES) {
-                        if (li == 0) *reinterpret_cast<f32x4v*>(pp + L * d_V / 2 + 16 * mg + 4 * g) = U[m][NCT - 1] * kUScale;
+                        if (li == 0)
+                            *reinterpret_cast<f32x4v*>(pp + L * d_V / 2 + 16 * mg + 4 * g) =
+                                U[m][NCT - 1] * ldexpf(1.0f, e_q + e_w);
                     }
+                    if (lane == 0)
+                        pp[L * d_V / 2 + L + mg * NG + G] = mx > 0.0f ? ldexpf(1.0f, ex - 14 + e_q + e_w) : 0.0f;
                 }
+                nst = 2 * MTW;
             }
         }
-        lds_barrier<63>();          // every readout is done: the state copy and q are free
-        if (next_w) prefetch_q(cw + NSUB);
-        }   // readout
-
-        // ---- the window's updates ----------------------------------------------------------
-        for (int cu = cw; cu < cw + nchw; cu += LU / L) {
-            if (cu > cw) lds_barrier<0>();    // k, v of this sub-chunk landed; the last update is done
-            build_tables(cu);
-            lds_barrier<63>();
-            // next raw k, v: this window's next sub-chunk, or the next window's first
-            if (cu + LU / L < ce) prefetch_kv(cu + LU / L);
-            update();
+        // B2: every readout is done (state copy and q rows free); the first update's tables
+        // landed (only this wave's partial stores, issued after them, may be outstanding)
+        if (nst) lds_barrier<2 * MTW>();
+        else lds_barrier<0>();
+        const int cu1 = cw + LU / L;                                  // the window's second update sub-chunk
+        const bool upd1 = NUPD == 2 && cu1 < cw + nchw;
+        if (upd1) dma_tables(cu1, 1);
+        if (next_w && !a.update_only) dma_q(cw + NSUB);
+        update(std::integral_constant<bool, false>());
+        if constexpr (NUPD == 2) {
+            if (upd1) {
+                // B3: the first update is done (its tables are free); the second's landed
+                // (only the next window's q rows may be outstanding)
+                if (next_w && !a.update_only) lds_barrier<dma_min_per_wave<NB_Q>()>();
+                else lds_barrier<0>();
+                if (next_w) dma_tables(cw + NSUB, 0);
+                update(std::integral_constant<bool, true>());
+            } else if (next_w) {
+                lds_barrier<63>();
+                dma_tables(cw + NSUB, 0);
+            }
+        }
+        // B4: the window's updates are done (the state copy's area is free) and every wave's
+        // state maximum is posted
+        if (!a.update_only && next_w) post_max();
+        lds_barrier<63>();
+        if constexpr (NUPD == 1) {
+            if (next_w) dma_tables(cw + NSUB, 0);
+        }
+        if (!a.update_only && next_w) {
+            e_w = copy_exp();
+            store_sb(e_w);
         }
     }
     __builtin_amdgcn_s_waitcnt(0);
 
     if (a.store_state) {
-        // through LDS as for the load; S = S' / (2^-8 c).  The window loop has reused the
+        // through LDS as for the load; S = S'' / factor.  The window loop has reused the
         // staging area: stage the canonical indices and factors again.
         float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
         __syncthreads();
-        {
-            const int fi = row_s * 8 + tid;
-            cf_idx[tid] = rt.canon[fi];
-            cf_fac[tid] = kfactor(rt.kscale[fi]) * kVScale;
-        }
+        stage_canon();
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             __syncthreads();
@@ -608,7 +570,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 if (idx < LY::io_rows * NCL) {
                     const int fr = idx % LY::io_rows, j = idx / LY::io_rows, kf = kf_of(T, fr);
                     const int F = cf_idx[kf];
-                    if (F >= 0) state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / cf_fac[kf];
+                    if (F >= 0) state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / (cf_fac[kf] * colfac(j));
                 }
             }
         }
@@ -624,7 +586,8 @@ template <int D, int DV, int G, int NPC>
 hipError_t launch_t(const PrefillSegArgs& a, const MfmaTables& m, hipStream_t st) {
     using LY = Layout<D, G == 0 ? 5 : 4>;
     static_assert(LY::bytes <= 160 * 1024, "LDS budget");
-    RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock};
+    RowPtrs rt{m.parent, m.weight, m.kscale, m.canon, m.wave_lblock, m.degree, {0}};
+    for (int p = 0; p < 8; ++p) rt.wlog[p] = m.wlog[p];
     hipError_t e = hipFuncSetAttribute((const void*)scan_mfma_kernel<D, DV, G, NPC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (e != hipSuccess) return e;
@@ -658,7 +621,7 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
     MfmaHostRows r;
     if (!build_mfma_rows(h, r)) return 0;        // not an MFMA shape: the VALU scan is used
     const size_t nr = (size_t)r.nrows, nw = r.wave_lblock.size();
-    const size_t bytes = nr * 4 + nr * 4 + nr * 8 * 4 + nr * 8 * 4 + nw * 4;
+    const size_t bytes = nr * 4 + nr * 4 + nr * 8 * 4 + nr * 8 * 4 + nw * 4 + nr;
     char* base = nullptr;
     if (hipMalloc(&base, bytes) != hipSuccess) {
         (void)hipGetLastError();
@@ -675,8 +638,10 @@ int build_mfma_tables(const HostTables& h, MfmaTables& m) {
     m.kscale = (const float*)put(r.kscale.data(), nr * 8 * 4);
     m.canon = (const int32_t*)put(r.canon.data(), nr * 8 * 4);
     m.wave_lblock = (const int32_t*)put(r.wave_lblock.data(), nw * 4);
+    m.degree = (const int8_t*)put(r.degree.data(), nr);
+    for (int p = 0; p < 8; ++p) m.wlog[p] = r.wlog[p];
     m.d_rows = base;
-    if (!m.parent || !m.weight || !m.kscale || !m.canon || !m.wave_lblock) {
+    if (!m.parent || !m.weight || !m.kscale || !m.canon || !m.wave_lblock || !m.degree) {
         free_mfma_tables(m);
         return -4;
     }

@@ -68,15 +68,40 @@ struct PrefillSegArgs {
     // [BH][d_V+1][M_pad].  update_only: no readout and no partials, only the state updates.
     int nsub = 1, sub_chunks = 0;
     bool update_only = false;
+    // Matrix-core scan only: the fp16 operand images written by the prep kernels
+    // (kern_prep.hip, layouts in scan_mfma.h) for windows [img_w0, img_w0 + img_nwin) and
+    // 128-token update sub-chunks [img_u0, img_u0 + img_nsub) of every head, and the per-head
+    // maxima of |q|, |k|, |v| (float bits, [BH][4]) that set their power-of-two scales.
+    uint16_t* qimg = nullptr;
+    uint16_t* kimg = nullptr;
+    uint16_t* vimg = nullptr;
+    int img_w0 = 0, img_nwin = 0, img_u0 = 0, img_nsub = 0;
+    const uint32_t* maxbits = nullptr;
 };
 
 // Slice partials of the matrix-core scan, one block per (head, chunk, slice): the d_V value
-// columns as fp16 times kPartialScale, in tile-pair order [token tile][pair of 16-column
-// tiles][lane] x 16 bytes (lane (li, g): tokens 16 tile + 4 g .. + 3, halves 0-3 column
-// 32 pair + li, halves 4-7 column 32 pair + 16 + li), then the normaliser column as L fp32
-// values.  The power-of-two scale keeps partials up to 65504 / kPartialScale in range.
-constexpr float kPartialScale = 1.0f / 256.0f;
-__host__ __device__ constexpr int64_t tiled_partial_floats(int L, int d_V) { return (int64_t)L * d_V / 2 + L; }
+// columns as fp16 in tile-pair order [token tile][pair of 16-column tiles][lane] x 16 bytes
+// (lane (li, g): tokens 16 tile + 4 g .. + 3, halves 0-3 column 32 pair + li, halves 4-7
+// column 32 pair + 16 + li), then the normaliser column as L fp32 values, then one fp32
+// scale per 16-token tile: value column j of token t is (q~_t . S)_j = stored x scale[tile]
+// x 2^s_v, with s_v the head's value scale (prep_scale_exp of its max |v|); the normaliser
+// is stored as is.  Each tile's scale is a power of two chosen from the tile's largest
+// value, so every finite partial fits fp16; there is one per tile and column group of 64
+// ([tile][group]).
+__host__ __device__ constexpr int64_t tiled_partial_floats(int L, int d_V) {
+    return (int64_t)L * d_V / 2 + L + (L / 16) * (d_V / 64);
+}
+
+// Per-head power-of-two input scale of the matrix-core path: for a maximum |x| with float
+// bits mb, the exponent s with max |x| 2^-s in [1, 2) (0 for an all-zero input), clamped.
+__host__ __device__ inline int prep_scale_exp(uint32_t mb) {
+    if (mb == 0u) return 0;
+    int e = (int)((mb >> 23) & 0xffu) - 127;
+    return e < -60 ? -60 : (e > 60 ? 60 : e);
+}
+// Prep kernels of the matrix-core scan (kern_prep.hip): the maxima, then the fp16 images.
+hipError_t launch_prep_max(const PrefillSegArgs& a, uint32_t* maxbits, hipStream_t st);
+hipError_t launch_prep_images(const PrefillSegArgs& a, int u_begin, int u_end, hipStream_t st);
 
 // Two-level prefill: replaces the nsub local states of every head, [BH][nsub][per_state],
 // by the state each sub-segment starts from (exclusive prefix sums, starting from init, which

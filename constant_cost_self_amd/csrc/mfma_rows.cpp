@@ -18,6 +18,7 @@
 // inside the scan is therefore S'[f] = S[f] / (1+m_f); it is converted back to
 // the unweighted state when it is written out.
 #include <algorithm>
+#include <cmath>
 
 #include "scan_mfma.h"
 
@@ -58,6 +59,7 @@ bool build_mfma_rows(const HostTables& h, MfmaHostRows& r) {
     auto push_dead = [&](int b) {
         r.parent.push_back(sentinel | (sentinel << 10) | (sentinel << 20));
         r.weight.push_back(0.0f);
+        r.degree.push_back(0);
         for (int e = 0; e < 8; ++e) {
             r.kscale.push_back(0.0f);
             r.canon.push_back(-1);
@@ -73,6 +75,7 @@ bool build_mfma_rows(const HostTables& h, MfmaHostRows& r) {
             if (row.a < 0) {                    // phi_0 = 1: coordinate d, weight alpha_0
                 r.parent.push_back(sentinel | (sentinel << 10) | (sentinel << 20));
                 r.weight.push_back((float)h.alpha[0]);
+                r.degree.push_back(0);
                 for (int e = 0; e < 8; ++e) {
                     r.kscale.push_back(e == 0 ? 1.0f : 0.0f);
                     r.canon.push_back(e == 0 ? 0 : -1);
@@ -90,6 +93,7 @@ bool build_mfma_rows(const HostTables& h, MfmaHostRows& r) {
             r.parent.push_back(pc);
             const double Ca = (double)h.Cp[dp][a - h.off[dp]];
             r.weight.push_back((float)(h.alpha[p] * Ca * p));
+            r.degree.push_back((int8_t)p);
             const int start = dp == 0 ? 0 : h.last[a];
             for (int e = 0; e < 8; ++e) {
                 const int l = 8 * row.b + e;
@@ -115,6 +119,15 @@ bool build_mfma_rows(const HostTables& h, MfmaHostRows& r) {
         r.wave_lblock.push_back(0);
     }
     r.nrows = (int)r.parent.size();
+    // per degree, the binary exponent bounding the rows' query weights: |w| <= 2^wlog[p]
+    for (int p = 0; p < 8; ++p) r.wlog[p] = -126;
+    for (int i = 0; i < r.nrows; ++i) {
+        if (r.weight[i] == 0.0f) continue;
+        int e = 0;
+        const double m = std::frexp((double)std::fabs(r.weight[i]), &e);   // |w| = m 2^e, m in [0.5, 1)
+        (void)m;
+        if (e > r.wlog[r.degree[i]]) r.wlog[r.degree[i]] = e;
+    }
 
     // every canonical feature must appear exactly once with a nonzero key factor
     std::vector<int> seen(h.M, 0);

@@ -168,21 +168,29 @@ struct PrefillPlan {
     int win = 1;                 // chunks per readout window
     int nslices = 0, slice_feats = 0;
     int nchunks = 0;
-    int64_t per_chunk = 0;       // slice-partial bytes of one chunk of every head
+    int64_t part_chunk = 0;      // slice-partial bytes of one chunk of every head
+    int64_t img_chunk = 0;       // operand-image bytes of one chunk of every head (matrix cores)
+    int64_t per_chunk = 0;       // part_chunk + img_chunk
+    int64_t fixed = 0;           // per-head input maxima (matrix cores)
     int64_t state_b = 0;         // bytes of one state per head, all heads
     int nsub = 1, sub_chunks = 0; // two-level form when nsub >= 2
     int seg = 0, nseg = 1;       // one-level form: segments of seg chunks
     int64_t ws_bytes = 0;
+    // workspace layout (byte offsets): partials, carried state, operand images, maxima
+    int64_t off_carrier = 0, off_img = 0, off_max = 0;
 };
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 // Segment length of the one-level form: whole readout windows (a segment starts a new
 // window, so results do not depend on the segmentation), at least one window, segments of
 // nearly equal length (each boundary stores and reloads the state of every slice), and
-// per_chunk * seg + carrier <= limit whenever one window fits.
+// per_chunk * seg + carrier + fixed <= limit whenever one window fits.  `whole` is the
+// need of a single segment over all nchunks chunks (no carrier).
 int64_t segment_chunks(int64_t nchunks, int64_t win, int64_t per_chunk, int64_t carrier,
-                       int64_t limit) {
-    if (per_chunk * nchunks <= limit) return nchunks;
-    int64_t seg = (limit - carrier) / per_chunk;
+                       int64_t fixed, int64_t whole, int64_t limit) {
+    if (whole <= limit) return nchunks;
+    int64_t seg = (limit - carrier - fixed) / per_chunk;
     seg -= seg % win;
     if (seg < win) seg = win;                          // one window even above the cap
     if (seg >= nchunks) return nchunks;
@@ -208,10 +216,25 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
         if (pl.slice_feats == 0) return fail(SATA_ERR_UNSUPPORTED, "no fp32 scan slice fits LDS");
         pl.nslices = (int)((t->h.M + pl.slice_feats - 1) / pl.slice_feats);
     }
-    pl.per_chunk = BH * pl.nslices * 4 *
-                   (pl.mfma ? sata::tiled_partial_floats(L, d_V) : (int64_t)L * cols);
+    pl.part_chunk = BH * pl.nslices * 4 *
+                    (pl.mfma ? sata::tiled_partial_floats(L, d_V) : (int64_t)L * cols);
+    if (pl.mfma) {
+        // images of whole windows: q rows per window, tables per 128-token sub-chunk
+        const int64_t win_bytes = sata::img_head_bytes(d_K, d_V, 1, sata::img_window(d_K) / sata::kImgLU);
+        pl.img_chunk = BH * win_bytes / pl.win;
+        pl.fixed = BH * 16 + 3 * 256;
+    }
+    pl.per_chunk = pl.part_chunk + pl.img_chunk;
     pl.state_b = BH * cols * t->h.M_pad * 4;
     const int64_t limit = t->ws_limit;
+    // the layout for segments of `chunks` chunks (images rounded up to whole windows)
+    auto layout = [&](int64_t chunks, int64_t carrier_b) {
+        const int64_t img_chunks = (chunks + pl.win - 1) / pl.win * pl.win;
+        pl.off_carrier = round256(pl.part_chunk * chunks);
+        pl.off_img = pl.off_carrier + round256(carrier_b);
+        pl.off_max = pl.off_img + round256(pl.img_chunk * img_chunks);
+        pl.ws_bytes = pl.off_max + (pl.mfma ? BH * 16 : 0);
+    };
 
     // Two-level form: when the slices of all heads leave compute units idle, the sequence
     // is cut into nsub sub-segments of whole readout windows (at least 4 windows each).
@@ -232,21 +255,24 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
             sub_chunks = (nwin + nsub - 1) / nsub * pl.win;
             nsub = (pl.nchunks + sub_chunks - 1) / sub_chunks;     // no empty sub-segment
         }
-        const int64_t need = pl.per_chunk * pl.nchunks + pl.state_b * nsub;
+        const int64_t need = pl.part_chunk * pl.nchunks + pl.state_b * nsub + pl.fixed +
+                             pl.img_chunk * ((pl.nchunks + pl.win - 1) / pl.win * pl.win) + 256;
         if (nsub >= 2 && BH * nsub <= 65535 && need <= limit) {
             pl.nsub = (int)nsub;
             pl.sub_chunks = (int)sub_chunks;
             pl.seg = pl.nchunks;
             pl.nseg = 1;
-            pl.ws_bytes = need;
+            layout(pl.nchunks, pl.state_b * nsub);
             return SATA_OK;
         }
     }
     (void)cont;
     const int64_t carrier = has_state ? 0 : pl.state_b;
-    pl.seg = (int)segment_chunks(pl.nchunks, pl.win, pl.per_chunk, carrier, limit);
+    const int64_t whole = pl.part_chunk * pl.nchunks +
+                          pl.img_chunk * ((pl.nchunks + pl.win - 1) / pl.win * pl.win) + pl.fixed;
+    pl.seg = (int)segment_chunks(pl.nchunks, pl.win, pl.per_chunk, carrier, pl.fixed, whole, limit);
     pl.nseg = (pl.nchunks + pl.seg - 1) / pl.seg;
-    pl.ws_bytes = pl.per_chunk * pl.seg + (!has_state && pl.nseg > 1 ? pl.state_b : 0);
+    layout(pl.seg, !has_state && pl.nseg > 1 ? pl.state_b : 0);
     return SATA_OK;
 }
 
@@ -422,7 +448,7 @@ int sata_set_workspace_limit(sata_tables* t, int64_t bytes) {
 
 int sata_prefill_workspace(const sata_tables* t, int B, int H, int n, int d_K, int d_V, int P,
                            int chunk, sata_dtype in_dtype, int flags, int with_state,
-                           int64_t* bytes, int* segments, int* subsegments) {
+                           int64_t* bytes, int* segments, int* segment_chunks_out, int* subsegments) {
     clear_err();
     if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
     if (!bytes) return fail(SATA_ERR_ARG, "bytes is NULL");
@@ -438,6 +464,7 @@ int sata_prefill_workspace(const sata_tables* t, int B, int H, int n, int d_K, i
     if (rc) return rc;
     *bytes = pl.ws_bytes;
     if (segments) *segments = pl.nseg;
+    if (segment_chunks_out) *segment_chunks_out = pl.seg;
     if (subsegments) *subsegments = pl.nsub;
     return SATA_OK;
 }
@@ -505,6 +532,34 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     hipStream_t st = (hipStream_t)stream;
     rc = ensure_ws(t, (size_t)pl.ws_bytes, st);
     if (rc) return rc;
+    char* ws = (char*)t->ws;
+    a.partial = (float*)ws;
+
+    // Matrix-core path: the per-head maxima of |q|, |k|, |v| over the whole sequence (they
+    // fix the power-of-two scales of the fp16 operands), then, per segment, the operand
+    // images of its whole windows (kern_prep.hip).
+    const int R = sata::img_window(d_K);
+    auto prep_images = [&](int c0, int c1, int nwin_stride) -> hipError_t {
+        const int QB = sata::img_q_bytes(d_K), KTB = sata::img_kt_bytes(d_K);
+        a.img_w0 = c0 / pl.win;
+        a.img_nwin = nwin_stride;
+        a.img_u0 = (int)((int64_t)c0 * L / sata::kImgLU);
+        a.img_nsub = nwin_stride * (R / sata::kImgLU);
+        char* img = ws + pl.off_img;
+        a.qimg = (uint16_t*)img;
+        a.kimg = (uint16_t*)(img + (int64_t)BH * a.img_nwin * QB);
+        a.vimg = (uint16_t*)(img + (int64_t)BH * a.img_nwin * QB + (int64_t)BH * a.img_nsub * KTB);
+        const int c1w = (c1 + pl.win - 1) / pl.win * pl.win;
+        return sata::launch_prep_images(a, a.img_u0, (int)((int64_t)c1w * L / sata::kImgLU), st);
+    };
+    if (pl.mfma) {
+        uint32_t* maxbits = (uint32_t*)(ws + pl.off_max);
+        a.maxbits = maxbits;
+        hipEvent_t ev = t->timer.begin(st);
+        const hipError_t e = sata::launch_prep_max(a, maxbits, st);
+        t->timer.end(SATA_KERNEL_PREP, ev, st);
+        if (e != hipSuccess) return fail(SATA_ERR_HIP, "prep launch failed: %s", hipGetErrorString(e));
+    }
 
     if (pl.nsub >= 2) {
         // Two-level form (the state recurrence as a prefix over segments, [TA] "Hardware
@@ -512,18 +567,20 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         // parallel (update-only scan), turned into each sub-segment's starting state by a
         // prefix sum, and the sub-segments are then scanned in parallel from those states.
         // Same sums as one segment, in another order.
-        a.partial = (float*)t->ws;
-        float* starts = (float*)((char*)t->ws + pl.per_chunk * pl.nchunks);
+        float* starts = (float*)(ws + pl.off_carrier);
         a.c_begin = 0;
         a.c_end = pl.nchunks;
         a.nsub = pl.nsub;
         a.sub_chunks = pl.sub_chunks;
         a.state = starts;
         hipEvent_t ev = t->timer.begin(st);
+        hipError_t e = prep_images(0, pl.nchunks, (pl.nchunks + pl.win - 1) / pl.win);
+        t->timer.end(SATA_KERNEL_PREP, ev, st);
+        ev = t->timer.begin(st);
         a.update_only = true;                   // local states from zero
         a.load_state = 0;
         a.store_state = 1;
-        hipError_t e = sata::launch_scan_mfma(a, t->mfma, st);
+        if (e == hipSuccess) e = sata::launch_scan_mfma(a, t->mfma, st);
         if (e == hipSuccess)
             e = sata::launch_state_prefix(starts, cont ? state : nullptr, state, BH, pl.nsub,
                                           (int64_t)cols * t->h.M_pad, st);
@@ -542,18 +599,23 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         return SATA_OK;
     }
 
-    a.partial = (float*)t->ws;
     float* carrier = state;
-    if (!carrier && pl.nseg > 1) carrier = (float*)((char*)t->ws + pl.per_chunk * pl.seg);
+    if (!carrier && pl.nseg > 1) carrier = (float*)(ws + pl.off_carrier);
     a.state = carrier;
     for (int s = 0; s < pl.nseg; ++s) {
         a.c_begin = s * pl.seg;
         a.c_end = (s + 1) * pl.seg < pl.nchunks ? (s + 1) * pl.seg : pl.nchunks;
         a.load_state = (s > 0 || cont) ? 1 : 0;
         a.store_state = (s < pl.nseg - 1 || state) ? 1 : 0;
+        hipError_t e = hipSuccess;
+        if (pl.mfma) {
+            hipEvent_t ev = t->timer.begin(st);
+            e = prep_images(a.c_begin, a.c_end, (pl.seg + pl.win - 1) / pl.win);
+            t->timer.end(SATA_KERNEL_PREP, ev, st);
+            if (e != hipSuccess) return fail(SATA_ERR_HIP, "prep launch failed: %s", hipGetErrorString(e));
+        }
         hipEvent_t ev = t->timer.begin(st);
-        hipError_t e = pl.mfma ? sata::launch_scan_mfma(a, t->mfma, st)
-                               : sata::launch_scan_valu(a, st);
+        e = pl.mfma ? sata::launch_scan_mfma(a, t->mfma, st) : sata::launch_scan_valu(a, st);
         t->timer.end(SATA_KERNEL_SCAN, ev, st);
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));

@@ -25,7 +25,31 @@ struct MfmaHostRows {
     std::vector<float> kscale;           // [nrows*8] key-side factor: 0 masked, 1/(m+1) diag, 1
     std::vector<int32_t> canon;          // [nrows*8] canonical feature index, -1 if none
     std::vector<int32_t> wave_lblock;    // [nrows/16] l-block of each wave
+    std::vector<int8_t> degree;          // [nrows] degree p of the row's features
+    int wlog[8] = {0};                   // per degree p: ceil(log2 max |weight|) over its rows
 };
+
+// fp16 operand images of the matrix-core scan, written by the prep kernels and copied as is
+// into LDS (whole 1 KiB blocks per direct-to-LDS wave instruction):
+//   q window image   [R][XR]: token rows q' = q 2^-s_q (d_K coordinates), then the constant
+//                    slot (1, 0, ..., 0); R = 256 at d_K = 64, 128 at d_K = 128
+//   key table        [XR][TS] per 128-token update sub-chunk: coordinate rows over tokens,
+//                    k' = k 2^-s_k, then row d_K = 1 for the tokens that exist (0 past n),
+//                    rows d_K + 1 .. d_K + 7 zero; 8 padding tokens per row
+//   value table      [rows][TS] per sub-chunk and group of 64 value columns: v' = v 2^-s_v,
+//                    then (group 0) the row of ones for the normaliser (0 past n)
+constexpr int kImgLU = 128;
+__host__ __device__ constexpr int img_pad1k(int b) { return (b + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int img_xr(int d_K) { return d_K + 8; }
+__host__ __device__ constexpr int img_ts() { return kImgLU + 8; }
+__host__ __device__ constexpr int img_window(int d_K) { return d_K == 64 ? 256 : 128; }
+__host__ __device__ constexpr int img_q_bytes(int d_K) { return img_window(d_K) * img_xr(d_K) * 2; }
+__host__ __device__ constexpr int img_kt_bytes(int d_K) { return img_pad1k(img_xr(d_K) * img_ts() * 2); }
+__host__ __device__ constexpr int img_vt_bytes() { return img_pad1k(65 * img_ts() * 2); }
+// bytes of the images of one head for nwin windows and nsub sub-chunks
+inline int64_t img_head_bytes(int d_K, int d_V, int64_t nwin, int64_t nsub) {
+    return nwin * img_q_bytes(d_K) + nsub * img_kt_bytes(d_K) + nsub * (d_V / 64) * img_vt_bytes();
+}
 
 constexpr int kRowsPerWave = 8;
 constexpr int kWavesPerSlice = 8;
@@ -43,6 +67,8 @@ struct MfmaTables {
     const float* kscale = nullptr;
     const int32_t* canon = nullptr;
     const int32_t* wave_lblock = nullptr;
+    const int8_t* degree = nullptr;
+    int wlog[8] = {0};
     bool ok = false;
 };
 

@@ -30,7 +30,7 @@ EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "s
             "sata_last_error", "sata_set_workspace_limit", "sata_set_prefill_split", "sata_set_timing",
             "sata_read_timing", "sata_prefill_workspace", "sata_decode_workspace",
             "sata_reserve_workspace", "sata_decode_step_noalloc")
-KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward")
+KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward", "prep")
 
 _lib = None
 
@@ -90,7 +90,7 @@ def load():
     lib.sata_prefill_workspace.restype = i32
     lib.sata_prefill_workspace.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.POINTER(i64), ctypes.POINTER(i32),
-                                           ctypes.POINTER(i32)]
+                                           ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.sata_decode_workspace.restype = i32
     lib.sata_decode_workspace.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i64)]
     lib.sata_reserve_workspace.restype = i32
@@ -194,15 +194,19 @@ class Tables:
 
     def prefill_workspace(self, B: int, H: int, n: int, d_V: int, *, chunk: int = 64,
                           dtype: int = SATA_BF16, continue_state: bool = False,
-                          with_state: bool = True):
-        """(workspace bytes, one-level segments, two-level sub-segments) of a prefill."""
+                          with_state: bool = True, segment_chunks: bool = False):
+        """(workspace bytes, one-level segments, two-level sub-segments) of a prefill;
+        with segment_chunks=True also the segments' length in chunks (a 4-tuple)."""
         nb = ctypes.c_int64()
         seg = ctypes.c_int()
+        segc = ctypes.c_int()
         sub = ctypes.c_int()
         _check(load().sata_prefill_workspace(self.handle, B, H, n, self.d_K, d_V, self.P, chunk,
                                              dtype, SATA_PREFILL_CONTINUE if continue_state else 0,
                                              1 if with_state else 0, ctypes.byref(nb),
-                                             ctypes.byref(seg), ctypes.byref(sub)))
+                                             ctypes.byref(seg), ctypes.byref(segc), ctypes.byref(sub)))
+        if segment_chunks:
+            return nb.value, seg.value, sub.value, segc.value
         return nb.value, seg.value, sub.value
 
     def decode_workspace(self, B: int, H: int, d_V: int) -> int:

@@ -141,14 +141,14 @@ int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
  * stream hipStream_t (NULL = default stream)
  *
  * Precision: bf16 inputs with d_K, d_V in {64, 128}, P >= 2 and chunk 64 take the
- * matrix-core path: contractions with fp16 operands (the bf16 values converted exactly,
- * power-of-two scales) and fp32 accumulation, the state in fp32, and the per-slice partial
- * readouts of the value columns stored in fp16 (times 2^-8; the normaliser's in fp32).  Its
- * per-row error against the exact attention is about 1e-3 on the benchmark shapes.  Its range
- * limits: |sum_t phi_f(k_t) [v_t | 1]| < 1.6e7 for every feature and column (e.g. n max|v|
- * for the constant feature), |q_i| up to about 16, and one slice's share of a numerator
- * below 1.7e7; beyond them y becomes NaN rather than silently wrong.  All other cases take
- * the fp32 path (errors of fp32 rounding, no such limits).
+ * matrix-core path: contractions with fp16 operands and fp32 accumulation, the state in
+ * fp32.  q, k and v enter as q 2^-s_q, k 2^-s_k, v 2^-s_v, with per-head powers of two that
+ * put each one's maximum in [1, 2); the readout's fp16 copy of the state and the per-slice
+ * partial readouts (fp16) carry power-of-two exponents chosen from their own largest
+ * entries, so no finite input overflows, whatever the magnitude of q, k or v or the length
+ * of the context (a continued prefill included).  Per-row error against the exact attention
+ * about 1e-3 (the fp16 operand rounding).  All other cases take the fp32 path (errors of
+ * fp32 rounding).
  *
  * Two-level form (bf16 matrix-core path only): when the slices of all B x H heads
  * leave compute units idle (few heads), the sequence is cut into sub-segments of
@@ -255,13 +255,15 @@ int sata_set_workspace_limit(sata_tables *t, int64_t bytes);
  * Workspace that sata_prefill with these arguments would use under the handle's
  * current cap, and how it would cut the sequence; no device work, so a host-only
  * handle serves too.  with_state: nonzero if the call passes a state buffer.
- * *bytes receives the workspace bytes; *segments (nullable) the number of segments
- * of the one-level scan; *subsegments (nullable) the sub-segments of the two-level
- * form (1 when it is not used).  Errors: those of sata_prefill's size checks.
+ * *bytes receives the workspace bytes; the nullable outputs: *segments the number of
+ * segments of the one-level scan, *segment_chunks their length in chunks (the last may
+ * be shorter), *subsegments the sub-segments of the two-level form (1 when it is not
+ * used).  Errors: those of sata_prefill's size checks.
  */
 int sata_prefill_workspace(const sata_tables *t, int B, int H, int n, int d_K, int d_V,
                            int P, int chunk, sata_dtype in_dtype, int flags, int with_state,
-                           int64_t *bytes, int *segments, int *subsegments);
+                           int64_t *bytes, int *segments, int *segment_chunks,
+                           int *subsegments);
 
 /* Workspace bytes of sata_decode_step (or the pool form with count = B) for B x H heads. */
 int sata_decode_workspace(const sata_tables *t, int B, int H, int d_V, int64_t *bytes);
@@ -300,7 +302,8 @@ enum {
     SATA_KERNEL_DECODE = 2,        /* decode state read-modify-write             */
     SATA_KERNEL_DECODE_REDUCE = 3, /* decode per-head reduction, y               */
     SATA_KERNEL_BACKWARD = 4,      /* one sata_prefill_backward call, all kernels */
-    SATA_NUM_KERNELS = 5
+    SATA_KERNEL_PREP = 5,          /* operand images of the matrix-core scan      */
+    SATA_NUM_KERNELS = 6
 };
 int sata_set_timing(sata_tables *t, int enable);
 int sata_read_timing(sata_tables *t, double *ms, int64_t *count);

@@ -20,33 +20,38 @@ def handles():
         t.close()
 
 
+def _plan(t, B, H, n, dV, chunk, dtype, with_state=True):
+    return t.prefill_workspace(B, H, n, dV, chunk=chunk, dtype=dtype, with_state=with_state,
+                               segment_chunks=True)
+
+
 @pytest.mark.parametrize("dK,dV,chunk,dtype,win", PATHS)
 def test_segments_cover_whole_windows_under_every_cap(handles, dK, dV, chunk, dtype, win):
     t = handles[dK]
     t.set_prefill_split(1)                       # the one-level form only
     B, H = 1, 2
     t.set_workspace_limit(1 << 62)
-    per_chunk = t.prefill_workspace(B, H, chunk, dV, chunk=chunk, dtype=dtype)[0]
-    assert per_chunk > 0
+    one_window = _plan(t, B, H, win * chunk, dV, chunk, dtype)[0]
+    per_chunk = (_plan(t, B, H, 2 * win * chunk, dV, chunk, dtype)[0] - one_window) // win
+    assert per_chunk > 0 and one_window > 0
     try:
         for nch in range(1, 65):
             n = nch * chunk - (chunk // 3 if nch > 1 else 0)      # ragged last chunk
             for cap_chunks in range(1, nch + 2):
                 for extra in (0, per_chunk // 2):
-                    cap = cap_chunks * per_chunk + extra
+                    cap = one_window + (cap_chunks - 1) * per_chunk + extra
                     t.set_workspace_limit(cap)
-                    nbytes, nseg, nsub = t.prefill_workspace(B, H, n, dV, chunk=chunk, dtype=dtype)
+                    nbytes, nseg, nsub, seg = _plan(t, B, H, n, dV, chunk, dtype)
                     assert nsub == 1
-                    assert nbytes % per_chunk == 0
-                    seg = nbytes // per_chunk
                     assert nseg >= 1 and seg >= 1
                     assert (nseg - 1) * seg < nch <= nseg * seg, (nch, cap_chunks, seg, nseg)
                     if nseg > 1:
                         assert seg % win == 0, (nch, cap_chunks, seg)
-                    if cap >= win * per_chunk:
-                        assert nbytes <= cap, (nch, cap_chunks, seg)
-                    else:
-                        assert seg == min(win, nch) or nseg == 1
+                    assert nbytes <= cap, (nch, cap_chunks, seg, nbytes, cap)
+            # a cap below one window: single windows, above the cap
+            t.set_workspace_limit(one_window // 2)
+            nbytes, nseg, nsub, seg = _plan(t, B, H, nch * chunk, dV, chunk, dtype)
+            assert seg == min(win, nch) or nseg == 1
     finally:
         t.set_workspace_limit(0)
         t.set_prefill_split(0)
@@ -57,26 +62,26 @@ def test_advisor_shapes_do_not_crash(handles):
     and B=128, H=64, n=560 under the default cap."""
     t = handles[64]
     t.set_workspace_limit(4 << 20)
-    nbytes, nseg, nsub = t.prefill_workspace(1, 1, 560, 64)
-    assert nseg >= 1 and nbytes > 0
+    nbytes, nseg, nsub, seg = _plan(t, 1, 1, 560, 64, 64, sata.SATA_BF16)
+    assert nseg >= 1 and nbytes > 0 and seg >= 4
     t.set_workspace_limit(0)
-    nbytes, nseg, nsub = t.prefill_workspace(128, 64, 560, 64)
+    nbytes, nseg, nsub, seg = _plan(t, 128, 64, 560, 64, 64, sata.SATA_BF16)
     # 9 chunks of 8192 heads: one readout window (4 chunks) fits the 32 GiB cap, two do not,
     # so the segments are single windows
-    per_chunk = nbytes // 4
-    assert nseg == 3 and nbytes == 4 * per_chunk and 8 * per_chunk > 32 << 30
+    assert nseg == 3 and seg == 4 and nbytes <= 32 << 30
 
 
 def test_carrier_counted_without_caller_state(handles):
     """Without a caller state, several segments carry the state in the workspace."""
     t = handles[64]
     t.set_prefill_split(1)
-    one = t.prefill_workspace(1, 1, 64 * 64, 64)[0] // 64
-    t.set_workspace_limit(one * 16 + sata.sata_state_bytes(1, 1, 64, 64, 4))
-    with_state = t.prefill_workspace(1, 1, 64 * 64, 64, with_state=True)
-    without = t.prefill_workspace(1, 1, 64 * 64, 64, with_state=False)
+    t.set_workspace_limit(1 << 62)
+    full = t.prefill_workspace(1, 1, 64 * 64, 64)[0]
+    t.set_workspace_limit(full // 3)
+    with_state = _plan(t, 1, 1, 64 * 64, 64, 64, sata.SATA_BF16, with_state=True)
+    without = _plan(t, 1, 1, 64 * 64, 64, 64, sata.SATA_BF16, with_state=False)
     assert with_state[1] > 1 and without[1] > 1
-    assert without[0] - sata.sata_state_bytes(1, 1, 64, 64, 4) <= with_state[0]
+    assert without[3] <= with_state[3]
     t.set_workspace_limit(0)
     t.set_prefill_split(0)
 
