@@ -149,9 +149,6 @@ __device__ inline void dma_blocks(const uint16_t* src, unsigned char* dst, int w
 template <int NB>
 constexpr int dma_min_per_wave() { return NB / kWaves; }
 
-// the key-side factor as the update applies it (rounded to fp16)
-__device__ inline float kfactor(float c) { return (float)(_Float16)c; }
-
 // largest value over a wave (non-negative inputs)
 __device__ inline float wave_max(float x) {
 #pragma unroll
@@ -265,11 +262,14 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         for (int e = 0; e < NPR; ++e)
             kpa[s][e] = lds_base(LY::t1 + (((p3 >> (10 * e)) & 1023u) * TS + 8 * g) * 2);
     }
-    // key-side factor of this lane's feature in update tile T (rows 4 (T / 2) + li / 4)
-    _Float16 cK[4];
+    // key-side factors c (0 / 1/(1+m) / 1) of the 8 features of this lane's rows 8 w + 4 s + g,
+    // in the order of its fp16 state copy (the update accumulates the plain products; the
+    // factor enters once per window, with the copy)
+    f16x8 cf8[2];
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
-        cK[T] = (_Float16)rt.kscale[(row_s + 8 * w + 4 * (T >> 1) + (li >> 2)) * 8 + 4 * (T & 1) + (li & 3)];
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cf8[s][e] = (_Float16)rt.kscale[(row_s + 8 * w + 4 * s + g) * 8 + e];
 
     // Resident state slice S'', update-accumulator layout: lane (column 16 ct + li, g)
     // register r of tile T holds kernel feature (row 8 w + 4 (T / 2) + g, element 4 (T % 2) + r).
@@ -293,7 +293,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     auto stage_canon = [&]() {
         const int fi = row_s * 8 + tid;
         cf_idx[tid] = rt.canon[fi];
-        cf_fac[tid] = ldexpf(kfactor(rt.kscale[fi]), -(int)rt.degree[row_s + (tid >> 3)] * s_k);
+        cf_fac[tid] = ldexpf(1.0f, -(int)rt.degree[row_s + (tid >> 3)] * s_k);
     };
     // kernel feature (within the slice) of staging row fr of update tile T
     auto kf_of = [](int T, int fr) {
@@ -348,26 +348,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint32_t a_q = lds_base(LY::qt + (TW * w + li) * XR * 2);               // token row, tile 0
     const uint32_t a_ri = lds_base(LY::ri + g * 8);                               // row 4 s + g
 
-    // the slice's largest state entry (over all waves: posted to LDS, read after a barrier)
-    auto post_max = [&]() {
-        float m = 0.0f;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(S[T][ct][r]));
-        m = wave_max(m);
-        if (lane == 0) wmx[w] = m;
-    };
-    // exponent e_w of the readout's fp16 state copy: the copy S'' 2^-e_w stays below 2^15
-    auto copy_exp = [&]() {
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) m = fmaxf(m, wmx[i]);
-        return m > 0.0f ? exp2_of(m, -100, 126) - 14 : 0;
-    };
-    // fp16 copy of this wave's state for the readout (K-steps 2 w, 2 w + 1)
+    // fp16 copy c S'' 2^-e_w of this wave's state for the readout (K-steps 2 w, 2 w + 1)
     auto store_sb = [&](int e_w) {
         const float f = ldexpf(1.0f, -e_w);
 #pragma unroll
@@ -375,15 +356,16 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const f32x4v lo = S[2 * s][ct] * f, hi = S[2 * s + 1][ct] * f;
-                const f16x8 p = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
-                                 (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+                const f16x8 p = f16x8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+                                      (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]} * cf8[s];
                 if (ct < 4) sb[(ct * KS + 2 * w + s) * 64 + lane] = p;
                 else if (li == 0) sb4[(2 * w + s) * 4 + g] = p;
             }
     };
 
-    // update S'' += K^^T . [v' | 1] of this wave's rows over the sub-chunk in table buffer TB
-    auto update = [&](auto TBc) {
+    // update S'' += K^^T . [v' | 1] of this wave's rows over the sub-chunk in table buffer TB;
+    // after each 32-token step, hook(kk) (other work to interleave with the matrix pipe)
+    auto update = [&](auto TBc, auto hook) {
         constexpr uint32_t TO = decltype(TBc)::value ? T2OFF : 0u;
 #pragma unroll
         for (int kk = 0; kk < LU / 32; ++kk) {
@@ -403,21 +385,47 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int T = 2 * s + h;
-                    const f16x8 Au = kp8 * kreg[h] * cK[T];
+                    const f16x8 Au = kp8 * kreg[h];
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
                         S[T][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Au, Vop[ct], S[T][ct], 0, 0, 0);
                 }
             }
+            hook(kk);
         }
     };
 
-    // the fp16 state copy of the first window
-    int e_w = 0;
+    // largest |S''| over the slice: every wave posts its own, read after the next barrier
+    auto post_max = [&]() {
+        float m = 0.0f;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(S[T][ct][r]));
+        m = wave_max(m);
+        if (lane == 0) wmx[w] = m;
+    };
+    auto slice_max = [&]() {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) m = fmaxf(m, wmx[i]);
+        return m;
+    };
+    // exponent of the readout's fp16 state copy: c S'' 2^-e stays below 2^15 for |S''| <= bound
+    auto copy_exp = [](float bound) { return bound > 0.0f ? exp2_of(bound, -100, 126) - 14 : 0; };
+    // One window's updates add at most R 2^P to any |S''| (|k'|, |v'| < 2, products of P - 1
+    // key coordinates), so the next copy's exponent is fixed from the state before the window
+    // (measured during the readout, off the path between the updates and the next readout).
+    constexpr float kGrowth = (float)LY::R * 32.0f;      // R 2^P for P <= 5
+
+    // the fp16 state copy of the first window: exponent from the exact maximum
+    int e_w = 0, e_next = 0;
     if (!a.update_only) {
         post_max();
         __syncthreads();
-        e_w = copy_exp();
+        e_w = copy_exp(slice_max());
         store_sb(e_w);
     }
 
@@ -429,10 +437,11 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         const bool next_w = cw + NSUB < ce;
         // B1: the window's q rows landed (only the next tables may still be in flight)
         lds_barrier<dma_min_per_wave<LY::KTB / 1024>() + dma_min_per_wave<LY::VTB / 1024>()>();
-        int nst = 0;                                                  // partial stores issued
+        f32x4v U[MTW][NCT];
+        const int cs = (TW * w) / L;                                  // this wave's chunk in the window
+        const bool stores = !a.update_only && cs < nchw;
         if (!a.update_only) {
             // ---- readout: window tokens TW w .. TW w + TW - 1 over the slice's K-steps ----
-            f32x4v U[MTW][NCT];
 #pragma unroll
             for (int m = 0; m < MTW; ++m)
 #pragma unroll
@@ -471,77 +480,83 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                     }
                 }
             }
-            // this wave's tokens lie in one chunk.  Partials in HBM, per (chunk, slice), in the
-            // tiled layout (launch.h): per 16-token tile a power-of-two scale from the tile's
-            // largest value; a lane's accumulators of two adjacent column tiles as one 16-byte
-            // store of fp16 (one store instruction writes 1 KiB contiguously); the normaliser
-            // column in fp32, [token]; the tile's scale
-            const int cs = (TW * w) / L;
-            if (cs < nchw) {
-                const int c = cw + cs;
-                constexpr int NVP = d_V / 32;                       // value column-tile pairs of the head
-                float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * tiled_partial_floats(L, d_V);
-                _Float16* ph = reinterpret_cast<_Float16*>(pp);
-#pragma unroll
-                for (int m = 0; m < MTW; ++m) {
-                    const int mg = ((TW * w) % L) / 16 + m;         // token tile within the chunk
-                    float mx = 0.0f;
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(U[m][ct][r]));
-                    mx = wave_max(mx);
-                    const int ex = mx > 0.0f ? exp2_of(mx, -110, 126) : 0;
-                    const float mul = ldexpf(1.0f, 14 - ex);
-#pragma unroll
-                    for (int cp = 0; cp < 2; ++cp) {
-                        const f32x4v lo = U[m][2 * cp] * mul, hi = U[m][2 * cp + 1] * mul;
-                        const f16x8 h = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
-                                         (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
-                        *reinterpret_cast<f16x8*>(ph + ((mg * NVP + 2 * G + cp) * 64 + lane) * 8) = h;
-                    }
-                    if constexpr (ONES) {
-                        if (li == 0)
-                            *reinterpret_cast<f32x4v*>(pp + L * d_V / 2 + 16 * mg + 4 * g) =
-                                U[m][NCT - 1] * ldexpf(1.0f, e_q + e_w);
-                    }
-                    if (lane == 0)
-                        pp[L * d_V / 2 + L + mg * NG + G] = mx > 0.0f ? ldexpf(1.0f, ex - 14 + e_q + e_w) : 0.0f;
-                }
-                nst = 2 * MTW;
-            }
+            // the state before this window, for the next copy's exponent (behind the MFMAs)
+            if (next_w) post_max();
         }
         // B2: every readout is done (state copy and q rows free); the first update's tables
-        // landed (only this wave's partial stores, issued after them, may be outstanding)
-        if (nst) lds_barrier<2 * MTW>();
-        else lds_barrier<0>();
+        // landed; every wave's state maximum is posted
+        lds_barrier<0>();
+        if (!a.update_only && next_w) e_next = copy_exp(slice_max() + kGrowth);
         const int cu1 = cw + LU / L;                                  // the window's second update sub-chunk
         const bool upd1 = NUPD == 2 && cu1 < cw + nchw;
         if (upd1) dma_tables(cu1, 1);
         if (next_w && !a.update_only) dma_q(cw + NSUB);
-        update(std::integral_constant<bool, false>());
+
+        // Partials in HBM, per (chunk, slice), in the tiled layout (launch.h), written while
+        // the first update runs: per 16-token tile a power-of-two scale from the tile's largest
+        // value; a lane's accumulators of two adjacent column tiles as one 16-byte store of fp16
+        // (one store instruction writes 1 KiB contiguously); the normaliser column in fp32,
+        // [token]; the tile's scale.  This wave's tokens lie in one chunk.
+        auto store_tile = [&](int m) {
+            constexpr int NVP = d_V / 32;                       // value column-tile pairs of the head
+            const int c = cw + cs;
+            float* pp = a.partial + ((bh * nch + (c - a.c_begin)) * a.nslices + slice) * tiled_partial_floats(L, d_V);
+            _Float16* ph = reinterpret_cast<_Float16*>(pp);
+            const int mg = ((TW * w) % L) / 16 + m;             // token tile within the chunk
+            float mx = 0.0f;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(U[m][ct][r]));
+            mx = wave_max(mx);
+            const int ex = mx > 0.0f ? exp2_of(mx, -110, 126) : 0;
+            const float mul = ldexpf(1.0f, 14 - ex);
+#pragma unroll
+            for (int cp = 0; cp < 2; ++cp) {
+                const f32x4v lo = U[m][2 * cp] * mul, hi = U[m][2 * cp + 1] * mul;
+                const f16x8 h = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+                                 (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+                *reinterpret_cast<f16x8*>(ph + ((mg * NVP + 2 * G + cp) * 64 + lane) * 8) = h;
+            }
+            if constexpr (ONES) {
+                if (li == 0)
+                    *reinterpret_cast<f32x4v*>(pp + L * d_V / 2 + 16 * mg + 4 * g) = U[m][NCT - 1] * ldexpf(1.0f, e_q + e_w);
+            }
+            if (lane == 0) pp[L * d_V / 2 + L + mg * NG + G] = mx > 0.0f ? ldexpf(1.0f, ex - 14 + e_q + e_w) : 0.0f;
+        };
+        update(std::integral_constant<bool, false>(), [&](int kk) {
+            // token tile m's stores after 32-token step 2 m + 1 of the first update
+            if (stores && (kk & 1) && kk / 2 < MTW) store_tile(kk / 2);
+        });
+        if constexpr (MTW > LU / 64) {
+            if (stores)
+#pragma unroll
+                for (int m = LU / 64; m < MTW; ++m) store_tile(m);
+        }
         if constexpr (NUPD == 2) {
             if (upd1) {
-                // B3: the first update is done (its tables are free); the second's landed
-                // (only the next window's q rows may be outstanding)
-                if (next_w && !a.update_only) lds_barrier<dma_min_per_wave<NB_Q>()>();
+                // B3: the first update is done (its tables are free); the second's landed:
+                // only the next window's q rows and this wave's partial stores, issued after
+                // them, may be outstanding
+                const bool q_out = next_w && !a.update_only;
+                if (q_out && stores) lds_barrier<dma_min_per_wave<NB_Q>() + 2 * MTW>();
+                else if (q_out) lds_barrier<dma_min_per_wave<NB_Q>()>();
+                else if (stores) lds_barrier<2 * MTW>();
                 else lds_barrier<0>();
                 if (next_w) dma_tables(cw + NSUB, 0);
-                update(std::integral_constant<bool, true>());
+                update(std::integral_constant<bool, true>(), [](int) {});
             } else if (next_w) {
                 lds_barrier<63>();
                 dma_tables(cw + NSUB, 0);
             }
         }
-        // B4: the window's updates are done (the state copy's area is free) and every wave's
-        // state maximum is posted
-        if (!a.update_only && next_w) post_max();
+        // B4: the window's updates are done (the state copy's area is free)
         lds_barrier<63>();
         if constexpr (NUPD == 1) {
             if (next_w) dma_tables(cw + NSUB, 0);
         }
         if (!a.update_only && next_w) {
-            e_w = copy_exp();
+            e_w = e_next;
             store_sb(e_w);
         }
     }

@@ -115,3 +115,20 @@ def test_decode_workspace(handles):
     nb = t.decode_workspace(16, 32, 64)
     assert nb > 0 and nb % 4 == 0
     assert t.decode_workspace(32, 32, 64) == 2 * nb
+
+
+@pytest.mark.parametrize("d,P", [(64, 2), (64, 3), (64, 4), (64, 5), (128, 2), (128, 3), (128, 4)])
+def test_matrix_core_rows_build_for_every_supported_shape(d, P):
+    """The row tables of the matrix-core scan (every monomial of the basis in exactly one
+    8-slot row, checked when they are built) exist for every bf16 shape it serves: its plan
+    cuts a long sequence under a small cap into whole readout windows (4 chunks at d = 64,
+    2 at d = 128), where the fp32 scan would cut single chunks."""
+    t = sata.sata_tables_build_host(d, P)
+    try:
+        t.set_prefill_split(1)
+        one = _plan(t, 1, 1, 64, d, 64, sata.SATA_BF16)[0]
+        t.set_workspace_limit(3 * one)
+        nbytes, nseg, nsub, seg = _plan(t, 1, 1, 64 * 40, d, 64, sata.SATA_BF16)
+        assert nseg > 1 and seg % (4 if d == 64 else 2) == 0 and seg > 1
+    finally:
+        t.close()
