@@ -149,11 +149,22 @@ __device__ inline void dma_blocks(const uint16_t* src, unsigned char* dst, int w
 template <int NB>
 constexpr int dma_min_per_wave() { return NB / kWaves; }
 
-// largest value over a wave (non-negative inputs)
+// DPP lane exchange of a float (CTRL is the DPP control word)
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// largest value over a wave (non-negative inputs), in every lane: DPP within rows of 16
+// lanes (quad swaps, then the half-row and row mirrors), then the four row results read
+// out to scalars (no LDS round trip)
 __device__ inline float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
+    x = fmaxf(x, dpp_f<0xB1>(x));      // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));      // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));     // row_half_mirror
+    x = fmaxf(x, dpp_f<0x140>(x));     // row_mirror
+    const int b = __float_as_int(x);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 // floor(log2 x) of a positive normal float from its bits; clamped to [lo, hi]
@@ -191,6 +202,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
+    const int wu = __builtin_amdgcn_readfirstlane(w);        // the wave index, known uniform
     const int slice = blockIdx.x;
     const int64_t bh = blockIdx.y / a.nsub;
     const int sub = blockIdx.y % a.nsub;
@@ -221,13 +233,13 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint16_t* kimg = a.kimg + bh * (int64_t)a.img_nsub * (LY::KTB / 2);
     const uint16_t* vimg = a.vimg + (bh * NG + G) * (int64_t)a.img_nsub * (LY::VTB / 2);
     auto dma_q = [&](int cw) {               // q rows of the window starting at chunk cw
-        dma_blocks<NB_Q>(qimg + (int64_t)(cw / NSUB - a.img_w0) * (LY::QB / 2), lds_raw + LY::qt, w, lane);
+        dma_blocks<NB_Q>(qimg + (int64_t)(cw / NSUB - a.img_w0) * (LY::QB / 2), lds_raw + LY::qt, wu, lane);
     };
     auto dma_tables = [&](int cu, int buf) {  // tables of the update sub-chunk starting at chunk cu
         const int64_t u = (int64_t)cu * L / LU - a.img_u0;
         unsigned char* dst = lds_raw + (buf == 0 ? LY::t1 : LY::t2);
-        dma_blocks<LY::KTB / 1024>(kimg + u * (LY::KTB / 2), dst, w, lane);
-        dma_blocks<LY::VTB / 1024>(vimg + u * (LY::VTB / 2), dst + LY::KTB, w, lane);
+        dma_blocks<LY::KTB / 1024>(kimg + u * (LY::KTB / 2), dst, wu, lane);
+        dma_blocks<LY::VTB / 1024>(vimg + u * (LY::VTB / 2), dst + LY::KTB, wu, lane);
     };
     // the first window's q rows and first tables in flight while the state is set up
     if (!a.update_only) dma_q(cb);
@@ -489,8 +501,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         if (!a.update_only && next_w) e_next = copy_exp(slice_max() + kGrowth);
         const int cu1 = cw + LU / L;                                  // the window's second update sub-chunk
         const bool upd1 = NUPD == 2 && cu1 < cw + nchw;
-        if (upd1) dma_tables(cu1, 1);
-        if (next_w && !a.update_only) dma_q(cw + NSUB);
+        // the second update's tables and the next window's q rows are requested from inside
+        // the first update (steps 0 and 2), behind its matrix work
 
         // Partials in HBM, per (chunk, slice), in the tiled layout (launch.h), written while
         // the first update runs: per 16-token tile a power-of-two scale from the tile's largest
@@ -525,6 +537,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             if (lane == 0) pp[L * d_V / 2 + L + mg * NG + G] = mx > 0.0f ? ldexpf(1.0f, ex - 14 + e_q + e_w) : 0.0f;
         };
         update(std::integral_constant<bool, false>(), [&](int kk) {
+            if (kk == 0 && upd1) dma_tables(cu1, 1);
+            if (kk == 2 && next_w && !a.update_only) dma_q(cw + NSUB);
             // token tile m's stores after 32-token step 2 m + 1 of the first update
             if (stores && (kk & 1) && kk / 2 < MTW) store_tile(kk / 2);
         });
@@ -536,8 +550,8 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
         if constexpr (NUPD == 2) {
             if (upd1) {
                 // B3: the first update is done (its tables are free); the second's landed:
-                // only the next window's q rows and this wave's partial stores, issued after
-                // them, may be outstanding
+                // only this wave's partial stores and the next window's q rows, both issued
+                // after them, may be outstanding
                 const bool q_out = next_w && !a.update_only;
                 if (q_out && stores) lds_barrier<dma_min_per_wave<NB_Q>() + 2 * MTW>();
                 else if (q_out) lds_barrier<dma_min_per_wave<NB_Q>()>();
