@@ -18,6 +18,9 @@ its own stream: achieved = algorithmic work per launch / mean launch time.
                 (the forward FLOPs/token closed form of the method), peak = bf16 MFMA
                 2.5 PFLOP/s.
   decode:       bytes = 8 (d_V + 1) M per head (fp32 state read + write), peak 8 TB/s.
+  decode_f16:   the same decode steps on half-precision states (fp16 value columns, fp32
+                normaliser): bytes = (4 d_V + 8) M per head, peak 8 TB/s; likewise
+                wide_decode_f16.
   decode_pool:  the same step in its serving form: 16 of a pool of 24 prefilled sequences,
                 at seeded scattered slots; bytes and peak as for decode (active heads only).
   two_level:    one head of 65536 tokens (too few slices to fill the CUs): the automatic
@@ -150,12 +153,14 @@ def prefill_record(w, steps, wall, tim, ceil_tflops):
     }
 
 
-def decode_record(w, steps, wall, tim, nbytes, ceil_gbs, label):
+def decode_record(w, steps, wall, tim, nbytes, ceil_gbs, label, state16=False):
     dk_ms, dk_n = tim["decode"]
     kern_gbs = nbytes / (dk_ms / dk_n * 1e-3) / 1e9
+    form = "half-precision states (fp16 values, fp32 normaliser)" if state16 else "fp32 states"
+    traffic_key = ("decode16_step" if state16 else "decode_step") + ("" if w.d_K == 64 else "_" + w.name)
     return {
-        "workload": "%s: %d sequences x %d heads, d_K=%d d_V=%d, P=%d, fp32 states (%.3f GB) "
-                    "prefilled with %d tokens, %s q,k,v" % (label, w.B, w.H, w.d_K, w.d_V, w.P,
+        "workload": "%s: %d sequences x %d heads, d_K=%d d_V=%d, P=%d, %s (%.3f GB) "
+                    "prefilled with %d tokens, %s q,k,v" % (label, w.B, w.H, w.d_K, w.d_V, w.P, form,
                                                           nbytes / 2e9, w.n, w.dtype),
         "value": nbytes * steps / wall / 1e9, "unit": "GB/s", "steps": steps,
         "ms_per_step": wall / steps * 1e3,
@@ -163,7 +168,7 @@ def decode_record(w, steps, wall, tim, nbytes, ceil_gbs, label):
         "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kern_gbs / HBM_PEAK_GBS,
                      "frac_of_measured_ceiling": kern_gbs / ceil_gbs if ceil_gbs else None,
-                     "traffic": traffic_from_profiles("decode_step" if w.d_K == 64 else "decode_step_" + w.name),
+                     "traffic": traffic_from_profiles(traffic_key),
                      "kernel": "decode state read-modify-write",
                      "ms_per_launch": dk_ms / dk_n, "algorithmic_bytes_per_launch": nbytes},
         "reduce_ms_per_step": tim["decode_reduce"][0] / max(tim["decode_reduce"][1], 1),
@@ -223,19 +228,27 @@ def measure_ceilings(rmw_bytes):
                                   "v_mfma_f32_16x16x32_f16 x %d per wave" % (blocks, iters)}}
 
 
-def bench_decode(w, steps, warmup, prefill_chunk=64):
-    """Decode steps over all B x H heads of workload w, states prefilled with its w.n tokens."""
+def bench_decode(w, steps, warmup, prefill_chunk=64, state16=False):
+    """Decode steps over all B x H heads of workload w, states prefilled with its w.n tokens
+    (fp32 states, or half-precision ones with state16)."""
     import torch
     from constant_cost_self_amd import inputs, sata
 
-    log("decode %s: prefilling %d tokens for %dx%d heads" % (w.name, w.n, w.B, w.H))
+    log("decode %s%s: prefilling %d tokens for %dx%d heads" % (w.name, " (fp16 states)" if state16 else "",
+                                                              w.n, w.B, w.H))
     x = inputs.prefill_inputs(w)
     q, k, v = (to_dev(x[s], w.dtype) for s in ("q", "k", "v"))
     t = sata.sata_tables_build(w.d_K, w.P)
-    Mp = sata.sata_state_stride(w.d_K, w.P)
-    state = torch.zeros((w.B, w.H, w.d_V + 1, Mp), device="cuda:0", dtype=torch.float32)
+    if state16:
+        state = torch.zeros((w.B, w.H, sata.sata_state16_bytes(1, 1, w.d_K, w.d_V, w.P)),
+                            device="cuda:0", dtype=torch.uint8)
+        step = sata.sata_decode_step_f16
+    else:
+        Mp = sata.sata_state_stride(w.d_K, w.P)
+        state = torch.zeros((w.B, w.H, w.d_V + 1, Mp), device="cuda:0", dtype=torch.float32)
+        step = sata.sata_decode_step
     y = torch.empty((w.B, w.H, w.n, w.d_V), device="cuda:0", dtype=torch.float32)
-    sata.sata_prefill(t, q, k, v, y, state, chunk=prefill_chunk)
+    sata.sata_prefill(t, q, k, v, y, state, chunk=prefill_chunk, state16=state16)
     del q, k, v, y, x
     s = inputs.decode_inputs(w, warmup + steps, seed=1)
     qs, ks, vs = (to_dev(s[c], w.dtype) for c in ("q", "k", "v"))
@@ -243,12 +256,12 @@ def bench_decode(w, steps, warmup, prefill_chunk=64):
     torch.cuda.synchronize()
     t.set_timing(True)
     for i in range(warmup):
-        sata.sata_decode_step(t, state, qs[i], ks[i], vs[i], yd)
+        step(t, state, qs[i], ks[i], vs[i], yd)
     torch.cuda.synchronize()
     t.read_timing()
     t0 = time.perf_counter()
     for i in range(warmup, warmup + steps):
-        sata.sata_decode_step(t, state, qs[i], ks[i], vs[i], yd)
+        step(t, state, qs[i], ks[i], vs[i], yd)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tim = t.read_timing()
@@ -257,7 +270,10 @@ def bench_decode(w, steps, warmup, prefill_chunk=64):
     del state
     torch.cuda.empty_cache()
     M = math.comb(w.d_K + w.P - 1, w.P - 1)
-    bytes_per_step = 8.0 * (w.d_V + 1) * M * w.B * w.H
+    # read + write of every entry: 4-byte fp32 entries, or 2-byte value entries and the
+    # 4-byte normaliser column of the half-precision state
+    per_entry = (4.0 * w.d_V + 8.0) if state16 else 8.0 * (w.d_V + 1)
+    bytes_per_step = per_entry * M * w.B * w.H
     return wall, tim, bytes_per_step
 
 
@@ -443,7 +459,7 @@ def main():
     ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-two-level", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decode16", "backward"], default=None,
                     help="time one part only (for profiler runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB, 3 times (calibrates the "
@@ -480,9 +496,10 @@ def main():
         print(json.dumps({"backward_ms": btim["backward"][0] / btim["backward"][1],
                           "backward_step_ms": bwall / args.backward_steps * 1e3}))
         return
-    if args.only == "decode":
+    if args.only in ("decode", "decode16"):
         dw = inputs.DECODE if w.d_K == 64 else inputs.WIDE
-        dwall, dtim, dbytes = bench_decode(dw, args.decode_steps, args.decode_warmup)
+        dwall, dtim, dbytes = bench_decode(dw, args.decode_steps, args.decode_warmup,
+                                           state16=args.only == "decode16")
         dk_ms, dk_n = dtim["decode"]
         print(json.dumps({"decode_kernel_gbs": dbytes / (dk_ms / dk_n * 1e-3) / 1e9,
                           "decode_step_ms": dwall / args.decode_steps * 1e3}))
@@ -535,6 +552,14 @@ def main():
         wwall, wtim, wbytes = bench_decode(inputs.WIDE, wsteps, args.decode_warmup)
         out["wide_decode"] = decode_record(inputs.WIDE, wsteps, wwall, wtim, wbytes, ceil_gbs,
                                            "wide-head decode step")
+        hwall, htim, hbytes = bench_decode(inputs.DECODE, args.decode_steps, args.decode_warmup, state16=True)
+        out["decode_f16"] = decode_record(inputs.DECODE, args.decode_steps, hwall, htim, hbytes, ceil_gbs,
+                                          "decode step", state16=True)
+        out["decode_f16"]["speedup_vs_fp32_state"] = dwall / hwall
+        hwall, htim, hbytes = bench_decode(inputs.WIDE, wsteps, args.decode_warmup, state16=True)
+        out["wide_decode_f16"] = decode_record(inputs.WIDE, wsteps, hwall, htim, hbytes, ceil_gbs,
+                                               "wide-head decode step", state16=True)
+        out["wide_decode_f16"]["speedup_vs_fp32_state"] = wwall / hwall
 
     if not args.no_decode and args.only is None:
         pwall, ptim, pbytes, pw, pslots = bench_decode_pool(args.decode_steps, args.decode_warmup)

@@ -66,26 +66,6 @@ constexpr int kDecFeatPerBlock = kThreads * 4 * kDecVec; // 2048 features
 constexpr int kDecWaves = kThreads / 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// DPP lane exchange of a float (CTRL is the DPP control word)
-template <int CTRL>
-__device__ inline float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// sum over the 64 lanes of a wave: DPP within rows of 16 lanes (quad swaps, then the
-// half-row and row mirrors), then the four row sums read out to scalars
-__device__ inline float wave_sum(float x) {
-    x += dpp_f<0xB1>(x);      // quad_perm [1,0,3,2]
-    x += dpp_f<0x4E>(x);      // quad_perm [2,3,0,1]
-    x += dpp_f<0x141>(x);     // row_half_mirror
-    x += dpp_f<0x140>(x);     // row_mirror
-    const int b = __float_as_int(x);
-    return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
-            __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
-            __int_as_float(__builtin_amdgcn_readlane(b, 48)));
-}
-
 // grid (ceil(cols / kDecCols) * nblk, BH): x = column group * nblk + feature block
 template <typename In>
 __global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
@@ -182,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
     }
 #pragma unroll
     for (int c = 0; c < kDecCols; ++c) {
-        const float a = wave_sum(acc[c]);
+        const float a = wave_sum64(acc[c]);
         if (lane == 0 && j0 + c < cols) pw[c * pstride] = a;
     }
 }

@@ -38,6 +38,54 @@ constexpr int64_t kNoAllocScratchBytes = 16LL << 20;
 hipError_t noalloc_scratch(int device, float** ptr);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);  // partials -> y
 
+// The state in half precision (kern_state16.hip).  Compact layout of one head, each part
+// starting on a multiple of 256 bytes:
+//   header  int32 expo[P][d_V], float bound[P][d_V]
+//   Z       fp32 [Mh]            the normaliser column
+//   V       fp16 [d_V][Mh]       the value columns
+// Feature rows are those of the fp32 state with degree block p moved to start at hoff[p] (a
+// multiple of 64); rows past m_p of a block are zero.  Value entry (row r of degree p,
+// column j) = V[j][hoff[p] + r] 2^expo[p][j]; bound[p][j] is the largest |entry| of that
+// block when it was written.
+struct State16Geom {
+    int64_t M, M_pad;                 // fp32 layout
+    int64_t Mh;                       // rows of the compact layout
+    int64_t head_bytes, z_off, v_off; // compact layout of one head
+    int64_t off[kMaxP], hoff[kMaxP], m[kMaxP];
+    int d_K, d_V, P;
+};
+inline int64_t state16_header_bytes(int d_V, int P) { return ((int64_t)8 * P * d_V + 255) / 256 * 256; }
+inline int64_t state16_head_bytes(int64_t Mh, int d_V, int P) {
+    return (state16_header_bytes(d_V, P) + 4 * Mh + 2 * (int64_t)d_V * Mh + 255) / 256 * 256;
+}
+
+struct Decode16Args {
+    uint8_t* state;                   // compact states (pool slots with `slots`)
+    const void* q;
+    const void* k;
+    const void* v;
+    float* y;
+    const uint32_t* fidx_h;           // packed indices in compact row order [Mh]
+    const float* qw_h;                // alpha_p C_p in compact row order [Mh]
+    float* partial;                   // decode16_partial_floats(BH, d_V, P, Mh) floats: the partial
+                                      // readouts, then the per-wave block maxima
+    State16Geom g;
+    int BH, nblk;
+    bool bf16;
+    const int32_t* slots;
+    int64_t pool;
+    int H;
+};
+int decode16_blocks(int64_t Mh);
+int64_t decode16_partial_floats(int BH, int d_V, int P, int64_t Mh);
+hipError_t launch_decode16(const Decode16Args& a, hipStream_t st);
+hipError_t launch_decode16_reduce(const Decode16Args& a, hipStream_t st);
+// fp32 states [count][d_V + 1][M_pad] <-> compact states [count][head_bytes]
+hipError_t launch_state16_pack(const float* src, uint8_t* dst, const State16Geom& g, int count,
+                               hipStream_t st);
+hipError_t launch_state16_unpack(const uint8_t* src, float* dst, const State16Geom& g, int count,
+                                 hipStream_t st);
+
 // One segment [c_begin, c_end) of chunks of a chunked prefill.
 struct PrefillSegArgs {
     const void* q;

@@ -95,6 +95,8 @@ struct sata_tables {
     int device = -1;
     uint32_t* d_fidx = nullptr;
     float* d_qw = nullptr;
+    uint32_t* d_fidx_h = nullptr;     // the same in the row order of the half-precision state
+    float* d_qw_h = nullptr;
     sata::MfmaTables mfma;            // slice tables of the MFMA scan (may be empty)
     std::mutex mu;
     void* ws = nullptr;
@@ -173,11 +175,13 @@ struct PrefillPlan {
     int64_t per_chunk = 0;       // part_chunk + img_chunk
     int64_t fixed = 0;           // per-head input maxima (matrix cores)
     int64_t state_b = 0;         // bytes of one state per head, all heads
+    int64_t s32_b = 0;           // fp32 working state of a call with a half-precision state
     int nsub = 1, sub_chunks = 0; // two-level form when nsub >= 2
     int seg = 0, nseg = 1;       // one-level form: segments of seg chunks
     int64_t ws_bytes = 0;
-    // workspace layout (byte offsets): partials, carried state, operand images, maxima
-    int64_t off_carrier = 0, off_img = 0, off_max = 0;
+    // workspace layout (byte offsets): partials, carried state, operand images, maxima,
+    // fp32 working state
+    int64_t off_carrier = 0, off_img = 0, off_max = 0, off_s32 = 0;
 };
 
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
@@ -200,7 +204,7 @@ int64_t segment_chunks(int64_t nchunks, int64_t win, int64_t per_chunk, int64_t 
 }
 
 int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, bool bf16,
-                 bool has_state, bool cont, PrefillPlan& pl) {
+                 bool has_state, bool cont, bool f16state, PrefillPlan& pl) {
     const int d_K = t->h.d_K, P = t->h.P, L = chunk, cols = d_V + 1;
     const int64_t BH = (int64_t)B * H;
     pl = PrefillPlan();
@@ -222,10 +226,11 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
         // images of whole windows: q rows per window, tables per 128-token sub-chunk
         const int64_t win_bytes = sata::img_head_bytes(d_K, d_V, 1, sata::img_window(d_K) / sata::kImgLU);
         pl.img_chunk = BH * win_bytes / pl.win;
-        pl.fixed = BH * 16 + 3 * 256;
+        pl.fixed = BH * 16 + 4 * 256;
     }
     pl.per_chunk = pl.part_chunk + pl.img_chunk;
     pl.state_b = BH * cols * t->h.M_pad * 4;
+    pl.s32_b = f16state ? round256(pl.state_b) : 0;
     const int64_t limit = t->ws_limit;
     // the layout for segments of `chunks` chunks (images rounded up to whole windows)
     auto layout = [&](int64_t chunks, int64_t carrier_b) {
@@ -233,7 +238,8 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
         pl.off_carrier = round256(pl.part_chunk * chunks);
         pl.off_img = pl.off_carrier + round256(carrier_b);
         pl.off_max = pl.off_img + round256(pl.img_chunk * img_chunks);
-        pl.ws_bytes = pl.off_max + (pl.mfma ? BH * 16 : 0);
+        pl.off_s32 = pl.off_max + round256(pl.mfma ? BH * 16 : 0);
+        pl.ws_bytes = pl.off_s32 + pl.s32_b;
     };
 
     // Two-level form: when the slices of all heads leave compute units idle, the sequence
@@ -255,7 +261,7 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
             sub_chunks = (nwin + nsub - 1) / nsub * pl.win;
             nsub = (pl.nchunks + sub_chunks - 1) / sub_chunks;     // no empty sub-segment
         }
-        const int64_t need = pl.part_chunk * pl.nchunks + pl.state_b * nsub + pl.fixed +
+        const int64_t need = pl.part_chunk * pl.nchunks + pl.state_b * nsub + pl.fixed + pl.s32_b +
                              pl.img_chunk * ((pl.nchunks + pl.win - 1) / pl.win * pl.win) + 256;
         if (nsub >= 2 && BH * nsub <= 65535 && need <= limit) {
             pl.nsub = (int)nsub;
@@ -269,8 +275,9 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
     (void)cont;
     const int64_t carrier = has_state ? 0 : pl.state_b;
     const int64_t whole = pl.part_chunk * pl.nchunks +
-                          pl.img_chunk * ((pl.nchunks + pl.win - 1) / pl.win * pl.win) + pl.fixed;
-    pl.seg = (int)segment_chunks(pl.nchunks, pl.win, pl.per_chunk, carrier, pl.fixed, whole, limit);
+                          pl.img_chunk * ((pl.nchunks + pl.win - 1) / pl.win * pl.win) + pl.fixed + pl.s32_b;
+    pl.seg = (int)segment_chunks(pl.nchunks, pl.win, pl.per_chunk, carrier, pl.fixed + pl.s32_b,
+                                 whole, limit);
     pl.nseg = (pl.nchunks + pl.seg - 1) / pl.seg;
     layout(pl.seg, !has_state && pl.nseg > 1 ? pl.state_b : 0);
     return SATA_OK;
@@ -295,6 +302,39 @@ int check_prefill_sizes(const sata_tables* t, int B, int H, int n, int d_K, int 
     if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
     return SATA_OK;
 }
+
+// Compact (half-precision) state layout of one head of this handle's d_K, P for d_V.
+sata::State16Geom state16_geom(const sata_tables* t, int d_V) {
+    sata::State16Geom g{};
+    g.M = t->h.M;
+    g.M_pad = t->h.M_pad;
+    g.Mh = t->h.Mh;
+    g.d_K = t->h.d_K;
+    g.d_V = d_V;
+    g.P = t->h.P;
+    for (int p = 0; p < g.P; ++p) {
+        g.off[p] = t->h.off[p];
+        g.hoff[p] = t->h.hoff[p];
+        g.m[p] = t->h.m[p];
+    }
+    g.z_off = sata::state16_header_bytes(d_V, g.P);
+    g.v_off = g.z_off + 4 * g.Mh;
+    g.head_bytes = sata::state16_head_bytes(g.Mh, d_V, g.P);
+    return g;
+}
+
+constexpr int kPrefillFlags = SATA_PREFILL_CONTINUE | SATA_STATE_F16;
+
+// Checks of the state conversions: count heads of d_V value columns.
+int convert_args(const sata_tables* t, const void* a, const void* b, int count, int d_V) {
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!a || !b) return fail(SATA_ERR_ARG, "state pointers must be non-NULL");
+    if (count < 1 || count > 65535) return fail(SATA_ERR_ARG, "count must be in 1..65535 (got %d)", count);
+    if (d_V < 1 || d_V > sata::kMaxD) return fail(SATA_ERR_UNSUPPORTED, "d_V=%d outside 1..128", d_V);
+    if (!aligned16(a) || !aligned16(b)) return fail(SATA_ERR_ALIGN, "state pointers must be 16-byte aligned");
+    return check_device(t);
+}
+
 
 }  // namespace
 
@@ -336,14 +376,17 @@ int sata_tables_build(int d_K, int P, sata_tables** out) {
         delete t;
         return fail(SATA_ERR_HIP, "hipGetDevice failed");
     }
-    const size_t n = (size_t)t->h.M_pad;
-    if (hipMalloc(&t->d_fidx, n * 4) != hipSuccess || hipMalloc(&t->d_qw, n * 4) != hipSuccess) {
+    const size_t n = (size_t)t->h.M_pad, nh = (size_t)t->h.Mh;
+    if (hipMalloc(&t->d_fidx, n * 4) != hipSuccess || hipMalloc(&t->d_qw, n * 4) != hipSuccess ||
+        hipMalloc(&t->d_fidx_h, nh * 4) != hipSuccess || hipMalloc(&t->d_qw_h, nh * 4) != hipSuccess) {
         (void)hipGetLastError();
         sata_tables_free(t);
         return fail(SATA_ERR_OOM, "device allocation of the tables failed");
     }
     if (hipMemcpy(t->d_fidx, t->h.fidx.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(t->d_qw, t->h.qw.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess) {
+        hipMemcpy(t->d_qw, t->h.qw.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(t->d_fidx_h, t->h.fidx_h.data(), nh * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(t->d_qw_h, t->h.qw_h.data(), nh * 4, hipMemcpyHostToDevice) != hipSuccess) {
         sata_tables_free(t);
         return fail(SATA_ERR_HIP, "copy of the tables to the device failed");
     }
@@ -390,6 +433,8 @@ void sata_tables_free(sata_tables* t) {
     if (!t) return;
     if (t->d_fidx) (void)hipFree(t->d_fidx);
     if (t->d_qw) (void)hipFree(t->d_qw);
+    if (t->d_fidx_h) (void)hipFree(t->d_fidx_h);
+    if (t->d_qw_h) (void)hipFree(t->d_qw_h);
     sata::free_mfma_tables(t->mfma);
     if (t->ws) (void)hipFree(t->ws);
     t->timer.destroy();
@@ -454,13 +499,14 @@ int sata_prefill_workspace(const sata_tables* t, int B, int H, int n, int d_K, i
     if (!bytes) return fail(SATA_ERR_ARG, "bytes is NULL");
     int rc = check_prefill_sizes(t, B, H, n, d_K, d_V, P, chunk, in_dtype);
     if (rc) return rc;
-    if (flags & ~SATA_PREFILL_CONTINUE) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
-    const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0;
+    if (flags & ~kPrefillFlags) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
+    const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0, f16 = (flags & SATA_STATE_F16) != 0;
     if (cont && !with_state) return fail(SATA_ERR_ARG, "SATA_PREFILL_CONTINUE needs a state buffer");
+    if (f16 && !with_state) return fail(SATA_ERR_ARG, "SATA_STATE_F16 needs a state buffer");
     sata_tables* tm = const_cast<sata_tables*>(t);
     std::lock_guard<std::mutex> lock(tm->mu);
     PrefillPlan pl;
-    rc = plan_prefill(t, B, H, n, d_V, chunk, in_dtype == SATA_BF16, with_state != 0, cont, pl);
+    rc = plan_prefill(t, B, H, n, d_V, chunk, in_dtype == SATA_BF16, with_state != 0, cont, f16, pl);
     if (rc) return rc;
     *bytes = pl.ws_bytes;
     if (segments) *segments = pl.nseg;
@@ -475,7 +521,9 @@ int sata_decode_workspace(const sata_tables* t, int B, int H, int d_V, int64_t* 
     if (!bytes) return fail(SATA_ERR_ARG, "bytes is NULL");
     if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
     if (d_V < 1 || d_V > sata::kMaxD) return fail(SATA_ERR_UNSUPPORTED, "d_V=%d outside 1..128", d_V);
-    *bytes = sata::decode_partial_floats(B * H, d_V, t->h.M_pad) * 4;
+    const int64_t f32 = sata::decode_partial_floats(B * H, d_V, t->h.M_pad) * 4;
+    const int64_t f16 = sata::decode16_partial_floats(B * H, d_V, t->h.P, t->h.Mh) * 4;
+    *bytes = f32 > f16 ? f32 : f16;
     return SATA_OK;
 }
 
@@ -490,7 +538,7 @@ int sata_reserve_workspace(sata_tables* t, int64_t bytes, void* stream) {
 }
 
 int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void* v, float* y,
-                 float* state, int B, int H, int n, int d_K, int d_V, int P, int chunk,
+                 void* state_arg, int B, int H, int n, int d_K, int d_V, int P, int chunk,
                  sata_dtype in_dtype, int flags, void* stream) {
     clear_err();
     sata_tables* t = const_cast<sata_tables*>(tc);
@@ -498,18 +546,19 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     if (!q || !k || !v || !y) return fail(SATA_ERR_ARG, "q, k, v and y must be non-NULL");
     int rc = check_prefill_sizes(t, B, H, n, d_K, d_V, P, chunk, in_dtype);
     if (rc) return rc;
-    if (flags & ~SATA_PREFILL_CONTINUE) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
-    const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0;
-    if (cont && !state) return fail(SATA_ERR_ARG, "SATA_PREFILL_CONTINUE needs a state buffer");
+    if (flags & ~kPrefillFlags) return fail(SATA_ERR_ARG, "unknown flags 0x%x", flags);
+    const bool cont = (flags & SATA_PREFILL_CONTINUE) != 0, f16 = (flags & SATA_STATE_F16) != 0;
+    if (cont && !state_arg) return fail(SATA_ERR_ARG, "SATA_PREFILL_CONTINUE needs a state buffer");
+    if (f16 && !state_arg) return fail(SATA_ERR_ARG, "SATA_STATE_F16 needs a state buffer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
-        (state && !aligned16(state)))
+        (state_arg && !aligned16(state_arg)))
         return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     rc = check_device(t);
     if (rc) return rc;
 
     std::lock_guard<std::mutex> lock(t->mu);
     PrefillPlan pl;
-    rc = plan_prefill(t, B, H, n, d_V, chunk, in_dtype == SATA_BF16, state != nullptr, cont, pl);
+    rc = plan_prefill(t, B, H, n, d_V, chunk, in_dtype == SATA_BF16, state_arg != nullptr, cont, f16, pl);
     if (rc) return rc;
     const bool bf16 = in_dtype == SATA_BF16;
     const int BH = B * H, L = chunk, cols = d_V + 1;
@@ -534,6 +583,25 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     if (rc) return rc;
     char* ws = (char*)t->ws;
     a.partial = (float*)ws;
+
+    // With a half-precision state the scans run on an fp32 working copy in the workspace:
+    // unpacked from the caller's state first when it holds a prefix, packed into it at the end.
+    const sata::State16Geom g16 = state16_geom(t, d_V);
+    float* state = f16 ? (float*)(ws + pl.off_s32) : (float*)state_arg;
+    if (f16 && cont) {
+        hipEvent_t ev = t->timer.begin(st);
+        const hipError_t e = sata::launch_state16_unpack((const uint8_t*)state_arg, state, g16, BH, st);
+        t->timer.end(SATA_KERNEL_CONVERT, ev, st);
+        if (e != hipSuccess) return fail(SATA_ERR_HIP, "state conversion failed: %s", hipGetErrorString(e));
+    }
+    auto finish = [&]() -> int {
+        if (!f16) return SATA_OK;
+        hipEvent_t ev = t->timer.begin(st);
+        const hipError_t e = sata::launch_state16_pack(state, (uint8_t*)state_arg, g16, BH, st);
+        t->timer.end(SATA_KERNEL_CONVERT, ev, st);
+        if (e != hipSuccess) return fail(SATA_ERR_HIP, "state conversion failed: %s", hipGetErrorString(e));
+        return SATA_OK;
+    };
 
     // Matrix-core path: the per-head maxima of |q|, |k|, |v| over the whole sequence (they
     // fix the power-of-two scales of the fp16 operands), then, per segment, the operand
@@ -596,7 +664,7 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         t->timer.end(SATA_KERNEL_FINALIZE, ev, st);
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
-        return SATA_OK;
+        return finish();
     }
 
     float* carrier = state;
@@ -625,7 +693,7 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
         if (e != hipSuccess)
             return fail(SATA_ERR_HIP, "finalize launch failed: %s", hipGetErrorString(e));
     }
-    return SATA_OK;
+    return finish();
 }
 
 int sata_prefill_backward(const sata_tables* tc, const void* q, const void* k, const void* v,
@@ -767,10 +835,11 @@ namespace {
 
 // Decode step shared by the dense, the pool and the allocation-free forms: BH = batch
 // entries x H heads; slots == NULL for the dense forms; noalloc: the partial readouts go to
-// the fixed device scratch, and nothing is allocated (no workspace, no timing events).
-int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool, const void* q,
+// the fixed device scratch, and nothing is allocated (no workspace, no timing events);
+// f16: the states are compact half-precision states.
+int decode_impl(sata_tables* t, void* state, const int32_t* slots, int64_t pool, const void* q,
                 const void* k, const void* v, float* y, int B, int H, int d_K, int d_V, int P,
-                sata_dtype in_dtype, void* stream, bool noalloc = false) {
+                sata_dtype in_dtype, void* stream, bool noalloc = false, bool f16 = false) {
     int rc = check_sizes(d_K, d_V, P);
     if (rc) return rc;
     if (d_K != t->h.d_K || P != t->h.P)
@@ -781,7 +850,8 @@ int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool
     if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
         return fail(SATA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     if ((int64_t)B * H > 65535) return fail(SATA_ERR_UNSUPPORTED, "B*H must be <= 65535");
-    const int64_t part_bytes = sata::decode_partial_floats(B * H, d_V, t->h.M_pad) * 4;
+    const int64_t part_bytes = f16 ? sata::decode16_partial_floats(B * H, d_V, P, t->h.Mh) * 4
+                                   : sata::decode_partial_floats(B * H, d_V, t->h.M_pad) * 4;
     if (noalloc && part_bytes > sata::kNoAllocScratchBytes)
         return fail(SATA_ERR_UNSUPPORTED,
                     "the allocation-free decode step holds %lld bytes of partials; B=%d H=%d "
@@ -789,9 +859,38 @@ int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool
                     (long long)part_bytes);
     rc = check_device(t);
     if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (f16) {
+        sata::Decode16Args a{};
+        a.state = (uint8_t*)state; a.q = q; a.k = k; a.v = v; a.y = y;
+        a.fidx_h = t->d_fidx_h;
+        a.qw_h = t->d_qw_h;
+        a.g = state16_geom(t, d_V);
+        a.BH = B * H;
+        a.nblk = sata::decode16_blocks(t->h.Mh);
+        a.bf16 = in_dtype == SATA_BF16;
+        a.slots = slots;
+        a.pool = pool;
+        a.H = H;
+        std::lock_guard<std::mutex> lock(t->mu);
+        rc = ensure_ws(t, (size_t)part_bytes, st);
+        if (rc) return rc;
+        a.partial = (float*)t->ws;
+        hipEvent_t ev = t->timer.begin(st);
+        hipError_t e = sata::launch_decode16(a, st);
+        t->timer.end(SATA_KERNEL_DECODE, ev, st);
+        if (e != hipSuccess) return fail(SATA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+        ev = t->timer.begin(st);
+        e = sata::launch_decode16_reduce(a, st);
+        t->timer.end(SATA_KERNEL_DECODE_REDUCE, ev, st);
+        if (e != hipSuccess)
+            return fail(SATA_ERR_HIP, "decode reduction launch failed: %s", hipGetErrorString(e));
+        return SATA_OK;
+    }
 
     sata::DecodeArgs a{};
-    a.state = state; a.q = q; a.k = k; a.v = v; a.y = y;
+    a.state = (float*)state; a.q = q; a.k = k; a.v = v; a.y = y;
     a.fidx = t->d_fidx;
     a.qw = t->d_qw;
     a.M = t->h.M;
@@ -803,7 +902,6 @@ int decode_impl(sata_tables* t, float* state, const int32_t* slots, int64_t pool
     a.pool = pool;
     a.H = H;
 
-    hipStream_t st = (hipStream_t)stream;
     if (noalloc) {
         hipError_t e = sata::noalloc_scratch(t->device, &a.partial);
         if (e != hipSuccess)
@@ -872,6 +970,70 @@ int sata_decode_step_pool(const sata_tables* tc, float* state_pool, int64_t pool
     if (((uintptr_t)slots & 3) != 0) return fail(SATA_ERR_ALIGN, "slots must be 4-byte aligned");
     return decode_impl(t, state_pool, slots, pool_size, q, k, v, y, count, H, d_K, d_V, P,
                        in_dtype, stream);
+}
+
+int sata_decode_step_f16(const sata_tables* tc, void* state16, const void* q, const void* k,
+                         const void* v, float* y, int B, int H, int d_K, int d_V, int P,
+                         sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!state16 || !q || !k || !v || !y)
+        return fail(SATA_ERR_ARG, "state16, q, k, v and y must be non-NULL");
+    if (B < 1 || H < 1) return fail(SATA_ERR_ARG, "need B, H >= 1 (got %d %d)", B, H);
+    return decode_impl(t, state16, nullptr, 0, q, k, v, y, B, H, d_K, d_V, P, in_dtype, stream,
+                       false, true);
+}
+
+int sata_decode_step_pool_f16(const sata_tables* tc, void* state16_pool, int64_t pool_size,
+                              const int32_t* slots, int count, const void* q, const void* k,
+                              const void* v, float* y, int H, int d_K, int d_V, int P,
+                              sata_dtype in_dtype, void* stream) {
+    clear_err();
+    sata_tables* t = const_cast<sata_tables*>(tc);
+    if (!t) return fail(SATA_ERR_ARG, "handle is NULL");
+    if (!state16_pool || !slots || !q || !k || !v || !y)
+        return fail(SATA_ERR_ARG, "state16_pool, slots, q, k, v and y must be non-NULL");
+    if (count < 1 || H < 1 || pool_size < 1)
+        return fail(SATA_ERR_ARG, "need count, H, pool_size >= 1 (got %d %d %lld)", count, H,
+                    (long long)pool_size);
+    if (((uintptr_t)slots & 3) != 0) return fail(SATA_ERR_ALIGN, "slots must be 4-byte aligned");
+    return decode_impl(t, state16_pool, slots, pool_size, q, k, v, y, count, H, d_K, d_V, P,
+                       in_dtype, stream, false, true);
+}
+
+int64_t sata_state16_stride(int d_K, int P) {
+    if (d_K < 1 || d_K > sata::kMaxD || P < 1 || P > sata::kMaxP) return -1;
+    return sata::state16_stride(d_K, P);
+}
+
+int64_t sata_state16_bytes(int B, int H, int d_K, int d_V, int P) {
+    if (B < 1 || H < 1 || d_V < 1 || d_V > sata::kMaxD) return -1;
+    const int64_t Mh = sata_state16_stride(d_K, P);
+    if (Mh < 0) return -1;
+    return (int64_t)B * H * sata::state16_head_bytes(Mh, d_V, P);
+}
+
+int sata_state_pack_f16(const sata_tables* t, const float* state, void* state16, int count, int d_V,
+                        void* stream) {
+    clear_err();
+    int rc = convert_args(t, state, state16, count, d_V);
+    if (rc) return rc;
+    const hipError_t e = sata::launch_state16_pack(state, (uint8_t*)state16, state16_geom(t, d_V), count,
+                                                   (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SATA_ERR_HIP, "state conversion failed: %s", hipGetErrorString(e));
+    return SATA_OK;
+}
+
+int sata_state_unpack_f16(const sata_tables* t, const void* state16, float* state, int count, int d_V,
+                          void* stream) {
+    clear_err();
+    int rc = convert_args(t, state16, state, count, d_V);
+    if (rc) return rc;
+    const hipError_t e = sata::launch_state16_unpack((const uint8_t*)state16, state, state16_geom(t, d_V),
+                                                     count, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SATA_ERR_HIP, "state conversion failed: %s", hipGetErrorString(e));
+    return SATA_OK;
 }
 
 }  // extern "C"

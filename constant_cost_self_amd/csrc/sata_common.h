@@ -56,6 +56,38 @@ __device__ inline float taylor_weight(float x, const Alpha& al, int P) {
     return w;
 }
 
+// DPP lane exchange of a float within rows of 16 lanes (CTRL is the DPP control word)
+template <int CTRL>
+__device__ inline float dpp_row(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum and maximum over the 64 lanes of a wave, returned in every lane: DPP within rows of
+// 16 lanes (quad swaps, then the half-row and row mirrors), then the four row results read
+// out to scalars.
+__device__ inline float wave_sum64(float x) {
+    x += dpp_row<0xB1>(x);      // quad_perm [1,0,3,2]
+    x += dpp_row<0x4E>(x);      // quad_perm [2,3,0,1]
+    x += dpp_row<0x141>(x);     // row_half_mirror
+    x += dpp_row<0x140>(x);     // row_mirror
+    const int b = __float_as_int(x);
+    return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+__device__ inline float wave_max64(float x) {
+    x = fmaxf(x, dpp_row<0xB1>(x));
+    x = fmaxf(x, dpp_row<0x4E>(x));
+    x = fmaxf(x, dpp_row<0x141>(x));
+    x = fmaxf(x, dpp_row<0x140>(x));
+    const int b = __float_as_int(x);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
 __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kScanThreads = 512;    // block size of the fp32 scan kernels (2 waves per SIMD)

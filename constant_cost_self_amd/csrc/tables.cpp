@@ -39,6 +39,17 @@ int64_t state_stride(int d_K, int P) {
     return (M + 63) / 64 * 64;
 }
 
+int64_t state16_stride(int d_K, int P) {
+    if (d_K < 1 || P < 1) return -1;
+    int64_t total = 0;
+    for (int p = 0; p < P; ++p) {
+        const int64_t m = binom_i64((int64_t)d_K + p - 1, p);
+        if (m < 0) return -1;
+        total += (m + 63) / 64 * 64;
+    }
+    return total;
+}
+
 static int64_t multinomial(const int32_t* row, int p) {
     // p! / prod over runs of equal indices of (run length)!   (rows are sorted)
     int64_t num = 1;
@@ -126,6 +137,22 @@ bool build_host_tables(int d_K, int P, HostTables& t) {
         }
     }
     for (int64_t f = t.M; f < t.M_pad; ++f) t.fidx[f] = all_sentinel;
+
+    // the same rows with every degree block starting on a multiple of 64
+    t.hoff.resize(P);
+    t.Mh = 0;
+    for (int p = 0; p < P; ++p) {
+        t.hoff[p] = t.Mh;
+        t.Mh += (t.m[p] + 63) / 64 * 64;
+    }
+    t.fidx_h.assign(t.Mh, all_sentinel);
+    t.qw_h.assign(t.Mh, 0.0f);
+    for (int p = 0; p < P; ++p) {
+        for (int64_t r = 0; r < t.m[p]; ++r) {
+            t.fidx_h[t.hoff[p] + r] = t.fidx[t.off[p] + r];
+            t.qw_h[t.hoff[p] + r] = t.qw[t.off[p] + r];
+        }
+    }
     return (int64_t)t.M == feature_dim(d_K, P);
 }
 

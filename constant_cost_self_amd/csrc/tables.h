@@ -23,11 +23,19 @@ struct HostTables {
     std::vector<uint32_t> fidx;
     std::vector<float> qw;
     std::vector<double> alpha;               // alpha_p, fp64
+    // Half-precision state order: degree block p starts at hoff[p], a multiple of 64, and
+    // Mh = sum_p roundup(m_p, 64); fidx_h and qw_h are fidx and qw in that order (size Mh),
+    // the rows past m_p of a block holding the sentinel indices and weight 0.
+    int64_t Mh = 0;
+    std::vector<int64_t> hoff;
+    std::vector<uint32_t> fidx_h;
+    std::vector<float> qw_h;
 };
 
 int64_t binom_i64(int64_t n, int64_t k);     // -1 on overflow
 int64_t feature_dim(int d_K, int P);
 int64_t state_stride(int d_K, int P);        // M rounded up to a multiple of 64
+int64_t state16_stride(int d_K, int P);      // Mh of the half-precision state order
 bool build_host_tables(int d_K, int P, HostTables& t);
 
 }  // namespace sata

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libsata.so")
 SATA_F32 = 0
 SATA_BF16 = 1
 SATA_PREFILL_CONTINUE = 1
+SATA_STATE_F16 = 2
 SATA_OK = 0
 SATA_ERR_ARG = -1
 SATA_ERR_UNSUPPORTED = -2
@@ -29,8 +30,10 @@ EXPORTED = ("sata_tables_build", "sata_tables_build_host", "sata_tables_get", "s
             "sata_decode_step_pool", "sata_prefill_backward",
             "sata_last_error", "sata_set_workspace_limit", "sata_set_prefill_split", "sata_set_timing",
             "sata_read_timing", "sata_prefill_workspace", "sata_decode_workspace",
-            "sata_reserve_workspace", "sata_decode_step_noalloc")
-KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward", "prep")
+            "sata_reserve_workspace", "sata_decode_step_noalloc", "sata_state16_stride",
+            "sata_state16_bytes", "sata_state_pack_f16", "sata_state_unpack_f16",
+            "sata_decode_step_f16", "sata_decode_step_pool_f16")
+KERNELS = ("scan", "finalize", "decode", "decode_reduce", "backward", "prep", "convert")
 
 _lib = None
 
@@ -95,6 +98,19 @@ def load():
     lib.sata_decode_workspace.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i64)]
     lib.sata_reserve_workspace.restype = i32
     lib.sata_reserve_workspace.argtypes = [vp, i64, vp]
+    lib.sata_state16_stride.restype = i64
+    lib.sata_state16_stride.argtypes = [i32, i32]
+    lib.sata_state16_bytes.restype = i64
+    lib.sata_state16_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.sata_state_pack_f16.restype = i32
+    lib.sata_state_pack_f16.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.sata_state_unpack_f16.restype = i32
+    lib.sata_state_unpack_f16.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.sata_decode_step_f16.restype = i32
+    lib.sata_decode_step_f16.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.sata_decode_step_pool_f16.restype = i32
+    lib.sata_decode_step_pool_f16.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, i32, i32, i32,
+                                              i32, i32, vp]
     lib.sata_read_timing.restype = i32
     lib.sata_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
@@ -159,6 +175,15 @@ def sata_state_bytes(B: int, H: int, d_K: int, d_V: int, P: int) -> int:
     return int(load().sata_state_bytes(B, H, d_K, d_V, P))
 
 
+def sata_state16_stride(d_K: int, P: int) -> int:
+    """Rows Mh of the half-precision state (degree blocks starting on multiples of 64)."""
+    return int(load().sata_state16_stride(d_K, P))
+
+
+def sata_state16_bytes(B: int, H: int, d_K: int, d_V: int, P: int) -> int:
+    return int(load().sata_state16_bytes(B, H, d_K, d_V, P))
+
+
 # --------------------------------------------------------------------------
 # Tables
 # --------------------------------------------------------------------------
@@ -194,16 +219,17 @@ class Tables:
 
     def prefill_workspace(self, B: int, H: int, n: int, d_V: int, *, chunk: int = 64,
                           dtype: int = SATA_BF16, continue_state: bool = False,
-                          with_state: bool = True, segment_chunks: bool = False):
+                          with_state: bool = True, segment_chunks: bool = False,
+                          state16: bool = False):
         """(workspace bytes, one-level segments, two-level sub-segments) of a prefill;
         with segment_chunks=True also the segments' length in chunks (a 4-tuple)."""
         nb = ctypes.c_int64()
         seg = ctypes.c_int()
         segc = ctypes.c_int()
         sub = ctypes.c_int()
+        flags = (SATA_PREFILL_CONTINUE if continue_state else 0) | (SATA_STATE_F16 if state16 else 0)
         _check(load().sata_prefill_workspace(self.handle, B, H, n, self.d_K, d_V, self.P, chunk,
-                                             dtype, SATA_PREFILL_CONTINUE if continue_state else 0,
-                                             1 if with_state else 0, ctypes.byref(nb),
+                                             dtype, flags, 1 if with_state else 0, ctypes.byref(nb),
                                              ctypes.byref(seg), ctypes.byref(segc), ctypes.byref(sub)))
         if segment_chunks:
             return nb.value, seg.value, sub.value, segc.value
@@ -258,14 +284,15 @@ def sata_tables_build_host(d_K: int, P: int) -> Tables:
 # --------------------------------------------------------------------------
 
 def sata_prefill(t: Tables, q, k, v, y, state=None, *, chunk: int = 64,
-                 continue_state: bool = False, stream=None):
+                 continue_state: bool = False, state16: bool = False, stream=None):
     """Chunked causal prefill.  q, k: [B, H, n, d_K]; v: [B, H, n, d_V] (fp32 or
     bf16, contiguous, on the GPU); y: fp32 [B, H, n, d_V]; state: optional fp32
-    [B, H, d_V + 1, M_pad]."""
+    [B, H, d_V + 1, M_pad], or with state16=True a half-precision state (uint8
+    [B, H, sata_state16_bytes(1, 1, ...)])."""
     _need(q, k, v, y, state)
     B, H, n, d_K = q.shape
     d_V = v.shape[-1]
-    flags = SATA_PREFILL_CONTINUE if continue_state else 0
+    flags = (SATA_PREFILL_CONTINUE if continue_state else 0) | (SATA_STATE_F16 if state16 else 0)
     _check(load().sata_prefill(t.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(state),
                                B, H, n, d_K, d_V, t.P, chunk, _dtype_code(q), flags,
                                _stream(stream)))
@@ -313,6 +340,39 @@ def sata_decode_step_pool(t: Tables, pool, slots, q, k, v, y, *, stream=None):
     _check(load().sata_decode_step_pool(t.handle, _ptr(pool), pool.shape[0], _ptr(slots), count,
                                         _ptr(q), _ptr(k), _ptr(v), _ptr(y), H, d_K, d_V, t.P,
                                         _dtype_code(q), _stream(stream)))
+
+
+def sata_decode_step_f16(t: Tables, state16, q, k, v, y, *, stream=None):
+    """One decode step on half-precision states (uint8 [B, H, sata_state16_bytes(1, 1, ...)])."""
+    _need(state16, q, k, v, y)
+    B, H, d_K = q.shape
+    d_V = v.shape[-1]
+    _check(load().sata_decode_step_f16(t.handle, _ptr(state16), _ptr(q), _ptr(k), _ptr(v), _ptr(y),
+                                       B, H, d_K, d_V, t.P, _dtype_code(q), _stream(stream)))
+
+
+def sata_decode_step_pool_f16(t: Tables, pool16, slots, q, k, v, y, *, stream=None):
+    """Decode step over a pool of half-precision states (uint8 [pool_size, H, head bytes])."""
+    _need(pool16, slots, q, k, v, y)
+    count, H, d_K = q.shape
+    d_V = v.shape[-1]
+    _check(load().sata_decode_step_pool_f16(t.handle, _ptr(pool16), pool16.shape[0], _ptr(slots),
+                                            count, _ptr(q), _ptr(k), _ptr(v), _ptr(y), H, d_K, d_V,
+                                            t.P, _dtype_code(q), _stream(stream)))
+
+
+def sata_state_pack_f16(t: Tables, state, state16, d_V: int, *, stream=None):
+    """fp32 states [..., d_V + 1, M_pad] -> half-precision states (same leading shape)."""
+    _need(state, state16)
+    count = state.numel() // ((d_V + 1) * sata_state_stride(t.d_K, t.P))
+    _check(load().sata_state_pack_f16(t.handle, _ptr(state), _ptr(state16), count, d_V, _stream(stream)))
+
+
+def sata_state_unpack_f16(t: Tables, state16, state, d_V: int, *, stream=None):
+    """Half-precision states -> fp32 states [..., d_V + 1, M_pad] (exact)."""
+    _need(state16, state)
+    count = state.numel() // ((d_V + 1) * sata_state_stride(t.d_K, t.P))
+    _check(load().sata_state_unpack_f16(t.handle, _ptr(state16), _ptr(state), count, d_V, _stream(stream)))
 
 
 def sata_last_error() -> str:

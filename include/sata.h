@@ -84,6 +84,8 @@ enum {
 
 /* Prefill flag: `state` holds the prefix on entry and is advanced in place. */
 #define SATA_PREFILL_CONTINUE 1
+/* Prefill flag: `state` is a half-precision state (layout below), not an fp32 one. */
+#define SATA_STATE_F16 2
 
 /*
  * Build the tables M_p, C_p (p = 0..P-1) for key dimension d_K on the host, plus
@@ -126,6 +128,40 @@ int64_t sata_state_stride(int d_K, int P);
 int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
 
 /*
+ * Half-precision state.  [TA] "Hidden-state size and compute analysis" sizes a head's state
+ * in Float16 (about 6.2 MB at d_K = d_V = 64, P = 4).  In this form the d_V value columns are
+ * stored as IEEE fp16 and the normaliser column stays fp32 (its degree-0 entry counts the
+ * tokens, which fp16 cannot past 2048); the decode step moves about half the bytes of the
+ * fp32 state.  Layout of one head, sata_state16_bytes(1, 1, ...) bytes, each part starting
+ * on a multiple of 256 bytes:
+ *   header  int32 expo[P][d_V], then float bound[P][d_V]
+ *   Z       fp32 [Mh]              the normaliser column
+ *   V       fp16 [d_V][Mh]         the value columns
+ * Rows follow the feature order of the fp32 state, but the block of degree p starts at row
+ * hoff[p] = sum_{p' < p} roundup(m_p', 64), and Mh = sata_state16_stride = sum_p
+ * roundup(m_p, 64); rows past m_p in a block are zero.  Entry (row r of M_p, column j < d_V)
+ * = V[j][hoff[p] + r] x 2^expo[p][j]; Z[hoff[p] + r] is the normaliser entry.  Each degree
+ * block of each column has its own power-of-two exponent, chosen from the largest entry of the
+ * block so that every finite state fits fp16's range; bound[p][j] holds that largest |entry|.
+ * An all-zero block of bytes is the empty prefix.
+ * Arithmetic is fp32; each write rounds a value entry to fp16 (to nearest even, relative
+ * error at most 2^-11 of the entry).  Caller-owned, 16-byte aligned, like the fp32 state.
+ */
+int64_t sata_state16_stride(int d_K, int P);
+int64_t sata_state16_bytes(int B, int H, int d_K, int d_V, int P);
+
+/*
+ * Conversions between the two state forms for `count` heads (1..65535): fp32 states
+ * [count][d_V + 1][M_pad] and half-precision states [count][sata_state16_bytes(1, 1, ...)]
+ * (pack rounds each value entry to fp16 and sets the exponents; unpack is exact).  Enqueued on
+ * `stream`.  Errors: SATA_ERR_ARG (NULL, count), SATA_ERR_UNSUPPORTED (d_V), SATA_ERR_ALIGN.
+ */
+int sata_state_pack_f16(const sata_tables *t, const float *state, void *state16, int count,
+                        int d_V, void *stream);
+int sata_state_unpack_f16(const sata_tables *t, const void *state16, float *state, int count,
+                          int d_V, void *stream);
+
+/*
  * Causal prefill of n tokens per head: y for every row, by a chunked scan
  * ([TA] "Feature maps and linear attention": the state recurrence, evaluated by
  * chunks).  Within a chunk of `chunk` tokens the weights w(q_T, k_t) are formed
@@ -134,7 +170,10 @@ int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
  * t      handle built for (d_K, P) on the current device
  * q,k,v  inputs, in_dtype, layouts above
  * y      fp32 output [B][H][n][d_V]
- * state  nullable.  If non-NULL the state after the n tokens is written to it.
+ * state  nullable.  If non-NULL the state after the n tokens is written to it: an fp32
+ *        state, or with flags & SATA_STATE_F16 a half-precision state (the scan then runs
+ *        on an fp32 copy in the workspace, converted from and to the caller's state; y is
+ *        the same either way).
  *        With flags & SATA_PREFILL_CONTINUE it must be non-NULL and on entry holds
  *        the state of a prefix that precedes these n tokens; y then attends to
  *        that prefix too.  Without the flag the prefix is empty.
@@ -159,7 +198,7 @@ int64_t sata_state_bytes(int B, int H, int d_K, int d_V, int P);
  * sata_set_prefill_split chooses when it is used.
  */
 int sata_prefill(const sata_tables *t, const void *q, const void *k, const void *v,
-                 float *y, float *state, int B, int H, int n, int d_K, int d_V,
+                 float *y, void *state, int B, int H, int n, int d_K, int d_V,
                  int P, int chunk, sata_dtype in_dtype, int flags, void *stream);
 
 /*
@@ -211,6 +250,22 @@ int sata_decode_step_pool(const sata_tables *t, float *state_pool, int64_t pool_
 int sata_decode_step_noalloc(const sata_tables *t, float *state, const void *q,
                              const void *k, const void *v, float *y, int B, int H,
                              int d_K, int d_V, int P, sata_dtype in_dtype, void *stream);
+
+/*
+ * The decode step on half-precision states (layout above), dense and pool forms; otherwise as
+ * sata_decode_step and sata_decode_step_pool.  The readout uses the fp32 entries before they
+ * are rounded to fp16 for storage.  Each step sets the exponent of every degree block of every
+ * column from the bound bound (1 + 2^-10) + kinf^p |u_j| on its new entries (kinf = max_i
+ * |k_i|, u = [v | 1]; fp16 rounding of an entry is below 2^-11 of it) and records the blocks'
+ * new largest entries as the next bounds.
+ */
+int sata_decode_step_f16(const sata_tables *t, void *state16, const void *q, const void *k,
+                         const void *v, float *y, int B, int H, int d_K, int d_V, int P,
+                         sata_dtype in_dtype, void *stream);
+int sata_decode_step_pool_f16(const sata_tables *t, void *state16_pool, int64_t pool_size,
+                              const int32_t *slots, int count, const void *q, const void *k,
+                              const void *v, float *y, int H, int d_K, int d_V, int P,
+                              sata_dtype in_dtype, void *stream);
 
 /*
  * Gradients of the causal prefill: for a loss with dL/dy = dy, the gradients dq, dk, dv
@@ -265,7 +320,8 @@ int sata_prefill_workspace(const sata_tables *t, int B, int H, int n, int d_K, i
                            int64_t *bytes, int *segments, int *segment_chunks,
                            int *subsegments);
 
-/* Workspace bytes of sata_decode_step (or the pool form with count = B) for B x H heads. */
+/* Workspace bytes of the decode step (either state form, dense or pool with count = B) for
+ * B x H heads. */
 int sata_decode_workspace(const sata_tables *t, int B, int H, int d_V, int64_t *bytes);
 
 /*
@@ -303,7 +359,8 @@ enum {
     SATA_KERNEL_DECODE_REDUCE = 3, /* decode per-head reduction, y               */
     SATA_KERNEL_BACKWARD = 4,      /* one sata_prefill_backward call, all kernels */
     SATA_KERNEL_PREP = 5,          /* operand images of the matrix-core scan      */
-    SATA_NUM_KERNELS = 6
+    SATA_KERNEL_CONVERT = 6,       /* state conversions of a half-precision prefill */
+    SATA_NUM_KERNELS = 7
 };
 int sata_set_timing(sata_tables *t, int enable);
 int sata_read_timing(sata_tables *t, double *ms, int64_t *count);
