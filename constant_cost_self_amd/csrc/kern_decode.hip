@@ -20,8 +20,8 @@
 // workgroup recomputes the features 65 times and reaches about 3.5-4.6 TB/s, one
 // thread walking all 65 columns about 5.1 TB/s, four columns about 5.6 TB/s.  Each
 // wave writes its partial readout of each column.
-// Kernel 2 (decode_finalize_kernel): one workgroup per head sums the partials of
-// every column and divides by the normaliser column.
+// Kernel 2 (decode_finalize_kernel): per head, one workgroup per 16 value columns sums
+// their partials and the normaliser column's, and divides.
 // Pool form ([HW] "The fixed-size hidden state of SATA attention": the state's memory
 // is allocated up front and requests share the device in turns): batch entry b uses
 // the state in slot slots[b] of a preallocated pool instead of state b.
@@ -167,25 +167,30 @@ __global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
     }
 }
 
-// one workgroup per head: wave w sums the partials of columns w, w + 4, ... (lanes
-// over the feature blocks and waves of the column), then y = num / normaliser
+// grid (BH, ceil(d_V / 16)): workgroup (h, c) writes y of head h for value columns 16 c ..
+// 16 c + 15: each wave sums the partials of one of those columns (lanes over the feature
+// blocks and waves of the column) and of the normaliser column, then y = num / normaliser
+constexpr int kFinCols = 16;
+
 __global__ __launch_bounds__(kThreads) void decode_finalize_kernel(
     const float* __restrict__ partial, float* __restrict__ y, int d_V, int nblk) {
     const int64_t bh = blockIdx.x;
     const int cols = d_V + 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int per_col = nblk * kDecWaves;
-    __shared__ float num[kMaxD + 1];
-    for (int j = wave; j < cols; j += kDecWaves) {
+    const int j0 = blockIdx.y * kFinCols;
+    const int nc = min(kFinCols, d_V - j0);
+    __shared__ float num[kFinCols + 1];
+    for (int c = wave; c <= nc; c += kDecWaves) {
+        const int j = c < nc ? j0 + c : d_V;
         const float* pc = partial + (bh * cols + j) * per_col;
         float s = 0.0f;
         for (int i = lane; i < per_col; i += 64) s += pc[i];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-        if (lane == 0) num[j] = s;
+        s = wave_sum64(s);
+        if (lane == 0) num[c < nc ? c : kFinCols] = s;
     }
     __syncthreads();
-    for (int j = threadIdx.x; j < d_V; j += kThreads) y[bh * d_V + j] = num[j] / num[d_V];
+    if ((int)threadIdx.x < nc) y[bh * d_V + j0 + threadIdx.x] = num[threadIdx.x] / num[kFinCols];
 }
 
 template <typename In>
@@ -212,8 +217,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(decode_finalize_kernel, dim3(a.BH), dim3(kThreads), 0, st, a.partial,
-                       a.y, a.d_V, a.nblk);
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3(a.BH, (a.d_V + kFinCols - 1) / kFinCols),
+                       dim3(kThreads), 0, st, a.partial, a.y, a.d_V, a.nblk);
     return hipGetLastError();
 }
 
