@@ -30,8 +30,10 @@ namespace {
 
 constexpr int kH16Feat = 8;                         // rows per thread (one 16-byte fp16 load)
 constexpr int kH16Cols = 8;                         // value columns per workgroup
-constexpr int kH16Block = kThreads * kH16Feat;      // 2048 rows per workgroup
-constexpr int kH16Waves = kThreads / 64;
+constexpr int kSweepThreads = 256;                  // block size of the sweep
+constexpr int kH16Block = kSweepThreads * kH16Feat; // rows per sweep workgroup
+constexpr int kH16Waves = kSweepThreads / 64;       // waves per sweep workgroup
+constexpr int kFinWaves = kThreads / 64;            // waves of the other kernels' blocks
 constexpr int kH16WaveRows = 64 * kH16Feat;         // rows of one wave: one slot of block maxima
 static_assert(kH16Cols == 8, "the wave reductions take 8 values per lane");
 constexpr float kGrow = 1.0009765625f;              // 1 + 2^-10
@@ -122,7 +124,7 @@ __device__ inline float head_kinf(const typename In::T* k, int64_t bh, int d_K, 
 // step: batch entry b uses slot slots[b]; an entry whose slot is outside the pool leaves the
 // pool alone and reads out NaN.
 template <typename In, int NIDX>
-__global__ __launch_bounds__(kThreads) void decode16_sweep_kernel(const Decode16Args a) {
+__global__ __launch_bounds__(kSweepThreads) void decode16_sweep_kernel(const Decode16Args a) {
     using T = typename In::T;
     const State16Geom& g = a.g;
     const int d_K = g.d_K, d_V = g.d_V, P = g.P, cols = d_V + 1, nblk = a.nblk;
@@ -160,26 +162,36 @@ __global__ __launch_bounds__(kThreads) void decode16_sweep_kernel(const Decode16
     const int64_t f0 = (int64_t)fb * kH16Block + tid * kH16Feat;
     const bool live = f0 < Mh;
 
-    // The small inputs are loaded first, so that waiting for them does not wait for the state
-    // (loads complete in order).  The loads are unconditional, from valid places (indices past
-    // the end clamped; rows past Mh and columns past the group's last read the last ones), so
-    // that no wait comes before the state loads are all issued; only live rows and columns
-    // are used and stored.
-    const int ti = tid < d_K ? tid : d_K - 1;
-    const float xqv = In::load(q, bh * d_K + ti), xkv = In::load(k, bh * d_K + ti);
-    const float ka = fabsf(In::load(k, bh * d_K + min(lane, d_K - 1)));
-    const float kb = fabsf(In::load(k, bh * d_K + min(lane + 64, d_K - 1)));
-    float u[kH16Cols];
+    // degree block of this thread's rows, its first row and its row count
+    int p = 0;
+    int64_t hstart = 0, mcount = g.m[0];
 #pragma unroll
-    for (int c = 0; c < kH16Cols; ++c) u[c] = In::load(v, bh * d_V + min(j0 + c, d_V - 1));
-    // thread p * 8 + c reads the header entry of block (p, j0 + c)
-    const bool hdr = tid < P * kH16Cols && (tid % kH16Cols) < ncol;
-    const int hp = min(tid / kH16Cols, P - 1), hc = min(tid % kH16Cols, ncol - 1);
-    const int hidx = hp * d_V + j0 + hc;
-    const int h_e = hd.expo[hidx];
-    const float h_b = hd.bound[hidx];
-    const float h_ua = fabsf(In::load(v, bh * d_V + j0 + hc));
-
+    for (int s = 1; s < kMaxP; ++s) {
+        if (s < P && f0 >= g.hoff[s]) {
+            p = s;
+            hstart = g.hoff[s];
+            mcount = g.m[s];
+        }
+    }
+    // The small inputs (q, k, v, this lane's header entries) are loaded first, so that waiting
+    // for them does not wait for the state (loads complete in order).  Every load is
+    // unconditional, from a valid place (indices past the end clamped; rows past Mh and columns
+    // past the group's last read the last ones), so that no wait comes before the state loads
+    // are all issued; only live rows and columns are used and stored.  Each wave stages its own
+    // q and k and takes its own exponents: the sweep has no workgroup barrier.
+    const int ti0 = min(lane, d_K - 1), ti1 = min(lane + 64, d_K - 1);
+    const float q0 = In::load(q, bh * d_K + ti0), q1 = In::load(q, bh * d_K + ti1);
+    const float k0 = In::load(k, bh * d_K + ti0), k1 = In::load(k, bh * d_K + ti1);
+    float u[kH16Cols];
+    int h_e[kH16Cols];
+    float h_b[kH16Cols];
+#pragma unroll
+    for (int c = 0; c < kH16Cols; ++c) {
+        const int j = j0 + min(c, ncol - 1);
+        u[c] = In::load(v, bh * d_V + j);
+        h_e[c] = hd.expo[p * d_V + j];
+        h_b[c] = hd.bound[p * d_V + j];
+    }
     const int64_t fl = live ? f0 : Mh - kH16Feat;
     u32x4 hv[kH16Cols];
 #pragma unroll
@@ -196,35 +208,19 @@ __global__ __launch_bounds__(kThreads) void decode16_sweep_kernel(const Decode16
                          *reinterpret_cast<const u32x4*>(a.fidx_h + fl + 4)};
     const f32x4 wq[2] = {*reinterpret_cast<const f32x4*>(a.qw_h + fl),
                          *reinterpret_cast<const f32x4*>(a.qw_h + fl + 4)};
-
-    // kinf = max_i |k_i| (every wave from all d_K coordinates) and ek = floor(log2 kinf); q and
-    // k 2^-ek (and the constant 1 at index d_K) into LDS, so that a degree-p feature of k comes
-    // out as phi_f(k) 2^-(p ek), below 2^p, whatever the magnitude of k
-    const float kinf = wave_max64(fmaxf(ka, kb));
+    const float kinf = wave_max64(fmaxf(fabsf(k0), fabsf(k1)));
     const int ek = kinf > 0.0f ? (int)((__float_as_uint(kinf) >> 23) & 0xffu) - 127 : 0;
-    __shared__ float xq[kMaxD + 1], xk[kMaxD + 1];
-    __shared__ int s_ein[kMaxP][kH16Cols], s_eout[kMaxP][kH16Cols];
-    if (tid <= d_K) {
-        xq[tid] = tid < d_K ? xqv : 1.0f;
-        xk[tid] = tid < d_K ? ldexpf(xkv, -ek) : 1.0f;
-    }
-    if (hdr) {
-        s_ein[hp][hc] = h_e;
-        s_eout[hp][hc] = s16_exp(s16_bound(h_b, kinf, hp, h_ua));
-    }
-    __syncthreads();
+    // this wave's copy of q and k 2^-ek, the constant 1 at index d_K
+    __shared__ float xs[kH16Waves][2][kMaxD + 1];
+    float* xq = xs[wave][0];
+    float* xk = xs[wave][1];
+    if (lane < d_K) { xq[lane] = q0; xk[lane] = ldexpf(k0, -ek); }
+    if (lane + 64 < d_K) { xq[lane + 64] = q1; xk[lane + 64] = ldexpf(k1, -ek); }
+    if (lane == 0) { xq[d_K] = 1.0f; xk[d_K] = 1.0f; }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // degree block of this thread's rows, its first row and its row count
-    int p = 0;
-    int64_t hstart = 0, mcount = g.m[0];
-#pragma unroll
-    for (int s = 1; s < kMaxP; ++s) {
-        if (s < P && f0 >= g.hoff[s]) {
-            p = s;
-            hstart = g.hoff[s];
-            mcount = g.m[s];
-        }
-    }
     // Features of the 8 rows: phi'_f = phi_f(k) 2^-kp (kp = p ek) from the scaled k; with
     // u_j 2^(kp - e_out) their product is the increment in units of 2^e_out, and neither factor
     // overflows (2^e_out is at least 2^-15 kinf^p |u_j|).
@@ -248,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode16_sweep_kernel(const Decode16
     for (int c = 0; c < kH16Cols; ++c) {
         float a = 0.0f, m = 0.0f;
         if (live && c < ncol) {
-                const int ein = s_ein[p][c], eout = s_eout[p][c];
+                const int ein = h_e[c], eout = s16_exp(s16_bound(h_b[c], kinf, p, fabsf(u[c])));
                 const float uc = ldexpf(u[c], kp - eout);
                 const u32x4 h = hv[c];
                 float sv[kH16Feat];
@@ -342,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void decode16_finalize_kernel(const Decod
         __shared__ float num[kFinCols + 1];
         const int j0 = blockIdx.y * kFinCols;
         const int nc = min(kFinCols, d_V - j0);
-        for (int c = wave; c <= nc; c += kH16Waves) {
+        for (int c = wave; c <= nc; c += kFinWaves) {
             const int j = c < nc ? j0 + c : d_V;
             const float* pc = a.partial + (bh * cols + j) * nslot;
             float s = 0.0f;
@@ -365,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void decode16_finalize_kernel(const Decod
     const float* pmax = a.partial + (int64_t)a.BH * cols * nslot + bh * g.P * d_V * nslot;
     const int b0 = (blockIdx.y - ny) * kFinBlocks;
     const int b1 = min(b0 + kFinBlocks, g.P * d_V);
-    for (int idx = b0 + wave; idx < b1; idx += kH16Waves) {
+    for (int idx = b0 + wave; idx < b1; idx += kFinWaves) {
         const int p = idx / d_V;
         const int j = idx - p * d_V;
         int64_t r0 = g.hoff[0], r1 = g.Mh;
@@ -398,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void state16_pack_kernel(const float* __r
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* s = src + (h * cols + j) * g.M_pad;
     const Head16 hd = head16(dst + h * g.head_bytes, g);
-    __shared__ float red[kH16Waves];
+    __shared__ float red[kFinWaves];
     for (int p = 0; p < g.P; ++p) {
         const int64_t off = g.off[p], hoff = g.hoff[p], m = g.m[p], mr = (m + 63) / 64 * 64;
         if (j == d_V) {
@@ -458,9 +454,9 @@ __global__ __launch_bounds__(kThreads) void state16_unpack_kernel(const uint8_t*
 template <int NIDX>
 hipError_t launch_sweep16(const Decode16Args& a, dim3 grid, hipStream_t st) {
     if (a.bf16)
-        hipLaunchKernelGGL((decode16_sweep_kernel<InBF16, NIDX>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((decode16_sweep_kernel<InBF16, NIDX>), grid, dim3(kSweepThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((decode16_sweep_kernel<InF32, NIDX>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((decode16_sweep_kernel<InF32, NIDX>), grid, dim3(kSweepThreads), 0, st, a);
     return hipGetLastError();
 }
 
