@@ -215,6 +215,50 @@ def test_decode_state16_matches_fp32_state(torch_cuda):
     t.close()
 
 
+@pytest.mark.parametrize("d_K,d_V,P,seed", [(7, 20, 5, 361), (64, 64, 2, 362), (16, 3, 3, 363)])
+def test_decode_state16_fp32_inputs_odd_sizes(torch_cuda, d_K, d_V, P, seed):
+    """fp32 inputs and odd sizes (a partial group of value columns, several degree blocks inside
+    one wave's rows, P from 2 to 5): a prefill into the half-precision state and decode steps
+    on it, against the oracle (the bar of the half-precision state) and against the same steps
+    on the fp32 state (which meets the fp32 bar)."""
+    torch = torch_cuda
+    n1, steps = 150, 6
+    say("state16 decode, fp32 inputs: d_K=%d d_V=%d P=%d" % (d_K, d_V, P))
+    x = inputs.draw((2, 3, n1 + steps, d_K), (2, 3, n1 + steps, d_V), "f32", 0.7, 1.0, seed)
+    q, k, v = upload(x, "f32")
+    t = sata.sata_tables_build(d_K, P)
+    S32 = new_state(2, 3, d_K, d_V, P)
+    S16 = new_state16(2, 3, d_K, d_V, P)
+    qa, ka, va = (z[:, :, :n1].contiguous() for z in (q, k, v))
+    prefill(t, qa, ka, va, 64, S32)
+    _prefill16(t, qa, ka, va, S16)
+    y32, y16 = [], []
+    for T in range(n1, n1 + steps):
+        a = torch.empty((2, 3, d_V), device="cuda:0")
+        b = torch.empty((2, 3, d_V), device="cuda:0")
+        qs, ks, vs = q[:, :, T].contiguous(), k[:, :, T].contiguous(), v[:, :, T].contiguous()
+        sata.sata_decode_step(t, S32, qs, ks, vs, a)
+        sata.sata_decode_step_f16(t, S16, qs, ks, vs, b)
+        y32.append(a.cpu().numpy())
+        y16.append(b.cpu().numpy())
+    torch.cuda.synchronize()
+    ref = oracle.direct(x["q"], x["k"], x["v"], P)[:, :, n1:]
+    e32 = max_row_err(np.stack(y32, axis=2), ref)
+    e16 = max_row_err(np.stack(y16, axis=2), ref)
+    say("  fp32 state %.3e, half-precision state %.3e" % (e32, e16))
+    assert e32 <= TOL_F32 and e16 <= TOL_BF16
+    raw = S16.cpu().numpy()
+    for b_, h in ((0, 0), (1, 2)):
+        Sd, expo, bound, pads_zero = state16_read(raw[b_, h], d_K, d_V, P)
+        assert pads_zero and Sd[d_V, 0] == n1 + steps
+        cat_k = x["k"][b_, h]
+        cat_v = x["v"][b_, h]
+        serr = _oracle_state_err(Sd, cat_k, cat_v, d_K, P, seed, joint_values=True)
+        say("  state (%d,%d) err %.3e" % (b_, h, serr))
+        assert serr <= TOL_BF16
+    t.close()
+
+
 def test_decode_state16_pool_equals_dense(torch_cuda):
     """The pool form on half-precision states: bit-identical y and state bytes to the dense
     step; an entry with a slot outside the pool reads out NaN and leaves the pool alone."""
