@@ -99,8 +99,14 @@ struct sata_tables {
     float* d_qw_h = nullptr;
     sata::MfmaTables mfma;            // slice tables of the MFMA scan (may be empty)
     std::mutex mu;
-    void* ws = nullptr;
-    size_t ws_bytes = 0;
+    // one workspace per stream the handle is used on: calls on one stream run in order, and
+    // calls on different streams never share workspace memory
+    struct Workspace {
+        hipStream_t stream;
+        void* ptr;
+        size_t bytes;
+    };
+    std::vector<Workspace> ws;
     int64_t ws_limit = kDefaultWorkspace;
     int cus = 0;                      // compute units of the device (256 assumed host-only)
     int split = 0;                    // two-level prefill: 0 automatic, 1 never, k >= 2 forced
@@ -133,24 +139,33 @@ int check_device(const sata_tables* t) {
     return SATA_OK;
 }
 
-// Grow the handle's workspace to at least `bytes`.  Growth waits for `st` (calls
-// on one handle are issued on one stream), frees the old buffer and allocates.
-int ensure_ws(sata_tables* t, size_t bytes, hipStream_t st) {
-    if (bytes <= t->ws_bytes) return SATA_OK;
-    if (t->ws) {
-        if (hipStreamSynchronize(st) != hipSuccess)
-            return fail(SATA_ERR_HIP, "hipStreamSynchronize failed while growing the workspace");
-        (void)hipFree(t->ws);
-        t->ws = nullptr;
-        t->ws_bytes = 0;
+// The workspace of stream `st`, grown to at least `bytes` (*out receives it).  Growth waits
+// for `st` (the only user of that buffer), frees the old buffer and allocates.
+int ensure_ws(sata_tables* t, size_t bytes, hipStream_t st, char** out) {
+    sata_tables::Workspace* w = nullptr;
+    for (auto& e : t->ws)
+        if (e.stream == st) w = &e;
+    if (!w) {
+        t->ws.push_back(sata_tables::Workspace{st, nullptr, 0});
+        w = &t->ws.back();
     }
-    const size_t rounded = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
-    if (hipMalloc(&t->ws, rounded) != hipSuccess) {
-        (void)hipGetLastError();
-        t->ws = nullptr;
-        return fail(SATA_ERR_OOM, "cannot allocate a %zu-byte workspace", rounded);
+    if (bytes > w->bytes) {
+        if (w->ptr) {
+            if (hipStreamSynchronize(st) != hipSuccess)
+                return fail(SATA_ERR_HIP, "hipStreamSynchronize failed while growing the workspace");
+            (void)hipFree(w->ptr);
+            w->ptr = nullptr;
+            w->bytes = 0;
+        }
+        const size_t rounded = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+        if (hipMalloc(&w->ptr, rounded) != hipSuccess) {
+            (void)hipGetLastError();
+            w->ptr = nullptr;
+            return fail(SATA_ERR_OOM, "cannot allocate a %zu-byte workspace", rounded);
+        }
+        w->bytes = rounded;
     }
-    t->ws_bytes = rounded;
+    if (out) *out = (char*)w->ptr;
     return SATA_OK;
 }
 
@@ -436,7 +451,8 @@ void sata_tables_free(sata_tables* t) {
     if (t->d_fidx_h) (void)hipFree(t->d_fidx_h);
     if (t->d_qw_h) (void)hipFree(t->d_qw_h);
     sata::free_mfma_tables(t->mfma);
-    if (t->ws) (void)hipFree(t->ws);
+    for (auto& e : t->ws)
+        if (e.ptr) (void)hipFree(e.ptr);
     t->timer.destroy();
     delete t;
 }
@@ -534,7 +550,7 @@ int sata_reserve_workspace(sata_tables* t, int64_t bytes, void* stream) {
     int rc = check_device(t);
     if (rc) return rc;
     std::lock_guard<std::mutex> lock(t->mu);
-    return ensure_ws(t, (size_t)bytes, (hipStream_t)stream);
+    return ensure_ws(t, (size_t)bytes, (hipStream_t)stream, nullptr);
 }
 
 int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void* v, float* y,
@@ -579,9 +595,9 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
     a.mfma_rows = pl.mfma ? t->mfma.d_rows : nullptr;
 
     hipStream_t st = (hipStream_t)stream;
-    rc = ensure_ws(t, (size_t)pl.ws_bytes, st);
+    char* ws = nullptr;
+    rc = ensure_ws(t, (size_t)pl.ws_bytes, st, &ws);
     if (rc) return rc;
-    char* ws = (char*)t->ws;
     a.partial = (float*)ws;
 
     // With a half-precision state the scans run on an fp32 working copy in the workspace:
@@ -753,9 +769,9 @@ int sata_prefill_backward(const sata_tables* tc, const void* q, const void* k, c
 
     std::lock_guard<std::mutex> lock(t->mu);
     hipStream_t st = (hipStream_t)stream;
-    rc = ensure_ws(t, (size_t)(fixed + per_chunk * seg), st);
+    char* base = nullptr;
+    rc = ensure_ws(t, (size_t)(fixed + per_chunk * seg), st, &base);
     if (rc) return rc;
-    char* base = (char*)t->ws;
     float* y_ws = (float*)base;
     float* den_ws = (float*)(base + y_b);
     float* u_ws = (float*)(base + y_b + den_b);
@@ -874,9 +890,10 @@ int decode_impl(sata_tables* t, void* state, const int32_t* slots, int64_t pool,
         a.pool = pool;
         a.H = H;
         std::lock_guard<std::mutex> lock(t->mu);
-        rc = ensure_ws(t, (size_t)part_bytes, st);
+        char* ws = nullptr;
+        rc = ensure_ws(t, (size_t)part_bytes, st, &ws);
         if (rc) return rc;
-        a.partial = (float*)t->ws;
+        a.partial = (float*)ws;
         hipEvent_t ev = t->timer.begin(st);
         hipError_t e = sata::launch_decode16(a, st);
         t->timer.end(SATA_KERNEL_DECODE, ev, st);
@@ -912,9 +929,10 @@ int decode_impl(sata_tables* t, void* state, const int32_t* slots, int64_t pool,
         return SATA_OK;
     }
     std::lock_guard<std::mutex> lock(t->mu);
-    rc = ensure_ws(t, (size_t)part_bytes, st);
+    char* ws = nullptr;
+    rc = ensure_ws(t, (size_t)part_bytes, st, &ws);
     if (rc) return rc;
-    a.partial = (float*)t->ws;
+    a.partial = (float*)ws;
     hipEvent_t ev = t->timer.begin(st);
     hipError_t e = sata::launch_decode(a, st);
     t->timer.end(SATA_KERNEL_DECODE, ev, st);

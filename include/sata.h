@@ -43,13 +43,14 @@
  *     and returns without waiting; apart from workspace growth (below) no call
  *     synchronises the host.
  *   Ownership.  The caller owns q, k, v, y and the state.  The library owns the
- *     tables handle (host and device copies) and a scratch workspace held by the
- *     handle, grown on demand and released by sata_tables_free.  Calls that share
- *     one handle must not overlap in time (issue them on one stream, or use one
- *     handle per stream): they share that workspace.
- *   Workspace growth.  A call that needs more workspace than the handle holds waits
- *     for its stream (hipStreamSynchronize), frees the old buffer and allocates a
- *     larger one; that is the only host synchronisation of the compute calls.  Size
+ *     tables handle (host and device copies) and scratch workspaces held by the
+ *     handle, one per stream the handle is used on, grown on demand and released by
+ *     sata_tables_free.  A handle is safe across threads (its host state is locked
+ *     during each call) and streams (calls on different streams never share workspace
+ *     memory, so they may overlap on the device).
+ *   Workspace growth.  A call that needs more workspace than its stream's buffer holds
+ *     waits for that stream (hipStreamSynchronize), frees the old buffer and allocates
+ *     a larger one; that is the only host synchronisation of the compute calls.  Size
  *     it beforehand with sata_prefill_workspace / sata_decode_workspace and
  *     sata_reserve_workspace to keep every later call free of it.
  *   Errors.  Every int-returning call returns SATA_OK (0) or a negative code and
@@ -114,7 +115,7 @@ int sata_tables_build_host(int d_K, int P, sata_tables **out);
 int sata_tables_get(const sata_tables *t, int p, const int32_t **M_p,
                     const int32_t **C_p, int64_t *m_p);
 
-/* Release a handle, its device tables and its workspace.  NULL-safe. */
+/* Release a handle, its device tables and its workspaces.  NULL-safe. */
 void sata_tables_free(sata_tables *t);
 
 /* M = binom(d_K + P - 1, P - 1) ([TA] "Hidden-state size and compute analysis"),
@@ -297,7 +298,7 @@ int sata_prefill_backward(const sata_tables *t, const void *q, const void *k, co
 const char *sata_last_error(void);
 
 /*
- * Optional: cap (bytes) on the workspace a handle may hold; prefill splits the
+ * Optional: cap (bytes) on the workspace a handle may hold per stream; prefill splits the
  * sequence into segments of whole readout windows to stay under it (a segment holds
  * at least one window: 4 chunks at d_K = 64, 2 at d_K = 128 on the bf16 matrix-core
  * path, 1 otherwise, even when one window alone exceeds the cap).  0 restores the
@@ -325,9 +326,9 @@ int sata_prefill_workspace(const sata_tables *t, int B, int H, int n, int d_K, i
 int sata_decode_workspace(const sata_tables *t, int B, int H, int d_V, int64_t *bytes);
 
 /*
- * Grow the handle's workspace to at least `bytes` now (growth waits for `stream`,
- * see "Workspace growth"), so that later calls needing at most that much neither
- * allocate nor synchronise.  SATA_ERR_OOM if the allocation fails.
+ * Grow the handle's workspace of `stream` to at least `bytes` now (growth waits for
+ * `stream`, see "Workspace growth"), so that later calls on that stream needing at most
+ * that much neither allocate nor synchronise.  SATA_ERR_OOM if the allocation fails.
  */
 int sata_reserve_workspace(sata_tables *t, int64_t bytes, void *stream);
 
