@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kH16Feat = 8;                         // rows per thread (one 16-byte fp16 load)
 constexpr int kH16Cols = 8;                         // value columns per workgroup
-constexpr int kSweepThreads = 256;                  // block size of the sweep
+constexpr int kSweepThreads = 128;                  // block size of the sweep
 constexpr int kH16Block = kSweepThreads * kH16Feat; // rows per sweep workgroup
 constexpr int kH16Waves = kSweepThreads / 64;       // waves per sweep workgroup
 constexpr int kFinWaves = kThreads / 64;            // waves of the other kernels' blocks
@@ -122,7 +122,8 @@ __device__ inline float head_kinf(const typename In::T* k, int64_t bh, int d_K, 
 //     partial readout  sum_f alpha_p C_p[f] phi_f(q) S[f][j]  per wave,
 // with the readout taken from the fp32 entries before their rounding.  Pool form as the fp32
 // step: batch entry b uses slot slots[b]; an entry whose slot is outside the pool leaves the
-// pool alone and reads out NaN.
+// pool alone and reads out NaN.  Row blocks of 1024 leave little of a head's last block idle
+// (48000 rows at d = 64: 47 blocks, the last 7/8 full).
 template <typename In, int NIDX>
 __global__ __launch_bounds__(kSweepThreads) void decode16_sweep_kernel(const Decode16Args a) {
     using T = typename In::T;
@@ -173,8 +174,9 @@ __global__ __launch_bounds__(kSweepThreads) void decode16_sweep_kernel(const Dec
             mcount = g.m[s];
         }
     }
-    // The small inputs (q, k, v, this lane's header entries) are loaded first, so that waiting
-    // for them does not wait for the state (loads complete in order).  Every load is
+    // The small inputs (q, k, v, this lane's header entries, the rows' feature indices and
+    // query weights) are loaded before the state, so that the features are computed while the
+    // state is still in flight (loads complete in order).  Every load is
     // unconditional, from a valid place (indices past the end clamped; rows past Mh and columns
     // past the group's last read the last ones), so that no wait comes before the state loads
     // are all issued; only live rows and columns are used and stored.  Each wave stages its own
@@ -193,6 +195,10 @@ __global__ __launch_bounds__(kSweepThreads) void decode16_sweep_kernel(const Dec
         h_b[c] = hd.bound[p * d_V + j];
     }
     const int64_t fl = live ? f0 : Mh - kH16Feat;
+    const u32x4 pk[2] = {*reinterpret_cast<const u32x4*>(a.fidx_h + fl),
+                         *reinterpret_cast<const u32x4*>(a.fidx_h + fl + 4)};
+    const f32x4 wq[2] = {*reinterpret_cast<const f32x4*>(a.qw_h + fl),
+                         *reinterpret_cast<const f32x4*>(a.qw_h + fl + 4)};
     u32x4 hv[kH16Cols];
 #pragma unroll
     for (int c = 0; c < kH16Cols; ++c) {
@@ -204,10 +210,6 @@ __global__ __launch_bounds__(kSweepThreads) void decode16_sweep_kernel(const Dec
         zv[0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hd.Z + fl));
         zv[1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hd.Z + fl + 4));
     }
-    const u32x4 pk[2] = {*reinterpret_cast<const u32x4*>(a.fidx_h + fl),
-                         *reinterpret_cast<const u32x4*>(a.fidx_h + fl + 4)};
-    const f32x4 wq[2] = {*reinterpret_cast<const f32x4*>(a.qw_h + fl),
-                         *reinterpret_cast<const f32x4*>(a.qw_h + fl + 4)};
     const float kinf = wave_max64(fmaxf(fabsf(k0), fabsf(k1)));
     const int ek = kinf > 0.0f ? (int)((__float_as_uint(kinf) >> 23) & 0xffu) - 127 : 0;
     // this wave's copy of q and k 2^-ek, the constant 1 at index d_K
