@@ -10,7 +10,7 @@
 // streaming read-modify-write and is bound by HBM bandwidth (8 bytes of traffic
 // per state entry for 4 flops).
 //
-// Kernel 1 (decode_sweep_kernel): workgroup (g, b) of head h updates 2048 features of
+// Kernel 1 (decode_sweep_kernel): workgroup (g, b) of head h updates 1024 features of
 // four columns of the state, two 16-byte non-temporal loads and stores per thread and
 // column, all loads issued before any arithmetic.  Consecutive workgroups take
 // consecutive feature blocks of the same four columns, so the workgroups in flight
@@ -60,24 +60,26 @@ hipError_t noalloc_scratch(int device, float** ptr) {
 
 namespace {
 
+constexpr int kDecThreads = 128;                         // block size of the sweep
 constexpr int kDecVec = 2;                               // 16-byte groups per thread
 constexpr int kDecCols = 4;                              // state columns per workgroup
-constexpr int kDecFeatPerBlock = kThreads * 4 * kDecVec; // 2048 features
-constexpr int kDecWaves = kThreads / 64;
+constexpr int kDecFeatPerBlock = kDecThreads * 4 * kDecVec;
+constexpr int kDecWaves = kDecThreads / 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // grid (ceil(cols / kDecCols) * nblk, BH): x = column group * nblk + feature block
-template <typename In>
-__global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
+template <typename In, int NIDX>
+__global__ __launch_bounds__(kDecThreads) void decode_sweep_kernel(
     float* __restrict__ state, const typename In::T* __restrict__ q,
     const typename In::T* __restrict__ k, const typename In::T* __restrict__ v,
     const uint32_t* __restrict__ fidx, const float* __restrict__ qw,
-    float* __restrict__ partial, int64_t M, int64_t M_pad, int d_K, int d_V, int P,
+    float* __restrict__ partial, int64_t M, int64_t M_pad, int d_K, int d_V,
     int nblk, const int32_t* __restrict__ slots, int64_t pool, int H) {
     const int cols = d_V + 1;
     const int64_t bh = blockIdx.y;
     const int fb = (int)(blockIdx.x % nblk);
     const int j0 = (int)(blockIdx.x / nblk) * kDecCols;
+    const int ncol = min(kDecCols, cols - j0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // partial readouts: [BH][cols][nblk][kDecWaves]
     const int64_t pstride = (int64_t)nblk * kDecWaves;
@@ -90,43 +92,50 @@ __global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
         const int64_t s = slots[bh / H];
         if (s < 0 || s >= pool) {
             if (lane == 0)
-                for (int c = 0; c < kDecCols && j0 + c < cols; ++c) pw[c * pstride] = __builtin_nanf("");
+                for (int c = 0; c < ncol; ++c) pw[c * pstride] = __builtin_nanf("");
             return;
         }
         sh = s * H + bh % H;
     }
 
-    // issue every state load first; the tables are M_pad long (padding rows have weight 0
-    // and an all-sentinel index row)
-    float* __restrict__ base = state + (sh * cols + j0) * M_pad;
+    // The small inputs (q, k, v, the features' index rows and query weights) are loaded
+    // before the state, so that the features are computed while the state is in flight
+    // (loads complete in order).  Every load is unconditional, from a valid place (indices
+    // past the end clamped), so that no wait comes before the state loads are all issued;
+    // only live features and columns are used and stored.  The tables are M_pad long
+    // (padding rows have weight 0 and an all-sentinel index row).
+    const int ti0 = min(lane, d_K - 1), ti1 = min(lane + 64, d_K - 1);
+    const float q0 = In::load(q, bh * d_K + ti0), q1 = In::load(q, bh * d_K + ti1);
+    const float k0 = In::load(k, bh * d_K + ti0), k1 = In::load(k, bh * d_K + ti1);
+    float u[kDecCols];
+#pragma unroll
+    for (int c = 0; c < kDecCols; ++c) u[c] = In::load(v, bh * d_V + min(j0 + c, d_V - 1));
     const int64_t f0 = (int64_t)fb * kDecFeatPerBlock + tid * 4;
-    f32x4 s[kDecVec][kDecCols];
+    int64_t fl[kDecVec];
     u32x4 packed[kDecVec];
     f32x4 w[kDecVec];
 #pragma unroll
     for (int g = 0; g < kDecVec; ++g) {
-        const int64_t f = f0 + g * kThreads * 4;
-        if (f < M_pad) {
-#pragma unroll
-            for (int c = 0; c < kDecCols; ++c)
-                if (j0 + c < cols)
-                    s[g][c] = __builtin_nontemporal_load(reinterpret_cast<f32x4*>(base + c * M_pad + f));
-            packed[g] = *reinterpret_cast<const u32x4*>(fidx + f);
-            w[g] = *reinterpret_cast<const f32x4*>(qw + f);
-        }
+        fl[g] = min(f0 + g * kDecThreads * 4, M_pad - 4);
+        packed[g] = *reinterpret_cast<const u32x4*>(fidx + fl[g]);
+        w[g] = *reinterpret_cast<const f32x4*>(qw + fl[g]);
     }
+    float* __restrict__ base = state + (sh * cols + j0) * M_pad;
+    f32x4 s[kDecVec][kDecCols];
+#pragma unroll
+    for (int g = 0; g < kDecVec; ++g)
+#pragma unroll
+        for (int c = 0; c < kDecCols; ++c)
+            s[g][c] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(base + min(c, ncol - 1) * M_pad + fl[g]));
 
     // this wave's copy of the head's q and k coordinates and the constant 1 (index d_K)
     __shared__ float xs[kDecWaves][2][kMaxD + 1];
     float* xq = xs[wave][0];
     float* xk = xs[wave][1];
-    for (int i = lane; i <= d_K; i += 64) {
-        xq[i] = i < d_K ? In::load(q, bh * d_K + i) : 1.0f;
-        xk[i] = i < d_K ? In::load(k, bh * d_K + i) : 1.0f;
-    }
-    float u[kDecCols];
-#pragma unroll
-    for (int c = 0; c < kDecCols; ++c) u[c] = j0 + c < d_V ? In::load(v, bh * d_V + j0 + c) : 1.0f;
+    if (lane < d_K) { xq[lane] = q0; xk[lane] = k0; }
+    if (lane + 64 < d_K) { xq[lane + 64] = q1; xk[lane + 64] = k1; }
+    if (lane == 0) { xq[d_K] = 1.0f; xk[d_K] = 1.0f; }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -134,26 +143,26 @@ __global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
     float acc[kDecCols];
 #pragma unroll
     for (int c = 0; c < kDecCols; ++c) acc[c] = 0.0f;
-    const int nidx = P - 1;
 #pragma unroll
     for (int g = 0; g < kDecVec; ++g) {
-        const int64_t f = f0 + g * kThreads * 4;
-        if (f < M_pad) {
-            // phi(k) masked to f < M keeps the padding of S at zero
-            float pk[4], pq[4];
+        const int64_t f = f0 + g * kDecThreads * 4;
+        // phi(k) masked to f < M keeps the padding of S at zero
+        float pk[4], pq[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pk[e] = f + e < M ? feature_value(xk, packed[g][e], nidx) : 0.0f;
-                pq[e] = w[g][e] * feature_value(xq, packed[g][e], nidx);
-            }
+        for (int e = 0; e < 4; ++e) {
+            pk[e] = f + e < M ? feature_value_n<NIDX>(xk, packed[g][e]) : 0.0f;
+            pq[e] = w[g][e] * feature_value_n<NIDX>(xq, packed[g][e]);
+        }
+        if (f < M_pad) {
 #pragma unroll
             for (int c = 0; c < kDecCols; ++c) {
-                if (j0 + c < cols) {
+                if (c < ncol) {
+                    const float uc = j0 + c < d_V ? u[c] : 1.0f;
                     f32x4 t = s[g][c];
-                    t.x = fmaf(pk[0], u[c], t.x);
-                    t.y = fmaf(pk[1], u[c], t.y);
-                    t.z = fmaf(pk[2], u[c], t.z);
-                    t.w = fmaf(pk[3], u[c], t.w);
+                    t.x = fmaf(pk[0], uc, t.x);
+                    t.y = fmaf(pk[1], uc, t.y);
+                    t.z = fmaf(pk[2], uc, t.z);
+                    t.w = fmaf(pk[3], uc, t.w);
                     __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(base + c * M_pad + f));
                     acc[c] = fmaf(pq[0], t.x, fmaf(pq[1], t.y, fmaf(pq[2], t.z, fmaf(pq[3], t.w, acc[c]))));
                 }
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void decode_sweep_kernel(
 #pragma unroll
     for (int c = 0; c < kDecCols; ++c) {
         const float a = wave_sum64(acc[c]);
-        if (lane == 0 && j0 + c < cols) pw[c * pstride] = a;
+        if (lane == 0 && c < ncol) pw[c * pstride] = a;
     }
 }
 
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void decode_finalize_kernel(
     const int j0 = blockIdx.y * kFinCols;
     const int nc = min(kFinCols, d_V - j0);
     __shared__ float num[kFinCols + 1];
-    for (int c = wave; c <= nc; c += kDecWaves) {
+    for (int c = wave; c <= nc; c += kThreads / 64) {
         const int j = c < nc ? j0 + c : d_V;
         const float* pc = partial + (bh * cols + j) * per_col;
         float s = 0.0f;
@@ -193,15 +202,26 @@ __global__ __launch_bounds__(kThreads) void decode_finalize_kernel(
     if ((int)threadIdx.x < nc) y[bh * d_V + j0 + threadIdx.x] = num[threadIdx.x] / num[kFinCols];
 }
 
-template <typename In>
-hipError_t launch_decode_in(const DecodeArgs& a, hipStream_t st) {
+template <typename In, int NIDX>
+hipError_t launch_decode_n(const DecodeArgs& a, hipStream_t st) {
     const unsigned per_head = (unsigned)((a.d_V + kDecCols) / kDecCols * a.nblk);
-    hipLaunchKernelGGL((decode_sweep_kernel<In>), dim3(per_head, a.BH), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((decode_sweep_kernel<In, NIDX>), dim3(per_head, a.BH), dim3(kDecThreads), 0, st,
                        a.state, static_cast<const typename In::T*>(a.q),
                        static_cast<const typename In::T*>(a.k),
                        static_cast<const typename In::T*>(a.v), a.fidx, a.qw, a.partial, a.M,
-                       a.M_pad, a.d_K, a.d_V, a.P, a.nblk, a.slots, a.pool, a.H);
+                       a.M_pad, a.d_K, a.d_V, a.nblk, a.slots, a.pool, a.H);
     return hipGetLastError();
+}
+
+template <typename In>
+hipError_t launch_decode_in(const DecodeArgs& a, hipStream_t st) {
+    switch (a.P) {
+        case 1: return launch_decode_n<In, 0>(a, st);
+        case 2: return launch_decode_n<In, 1>(a, st);
+        case 3: return launch_decode_n<In, 2>(a, st);
+        case 4: return launch_decode_n<In, 3>(a, st);
+        default: return launch_decode_n<In, 4>(a, st);
+    }
 }
 
 }  // namespace

@@ -33,14 +33,7 @@ struct Alpha {
 // A feature f of degree p is the product of p coordinates; its indices are
 // packed one per byte (low byte first) in fidx[f].  Unused bytes hold the
 // sentinel index d_K, which the kernels map to a stored coordinate equal to 1,
-// so every feature is a product of exactly P-1 gathered values.
-__device__ inline float feature_value(const float* x, uint32_t packed, int nidx) {
-    float prod = 1.0f;
-    for (int s = 0; s < nidx; ++s) prod *= x[(packed >> (8 * s)) & 0xffu];
-    return prod;
-}
-
-// feature_value with the slot count known at compile time (fully unrolled gathers)
+// so every feature is a product of exactly NIDX = P-1 gathered values.
 template <int NIDX>
 __device__ inline float feature_value_n(const float* x, uint32_t packed) {
     float prod = 1.0f;

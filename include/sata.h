@@ -242,7 +242,7 @@ int sata_decode_step_pool(const sata_tables *t, float *state_pool, int64_t pool_
  * kernels as sata_decode_step, but the partial readouts go to a fixed device array of
  * 16 MiB that the library holds on each GPU it runs on until the process ends, instead of
  * the handle's workspace.  The call allocates nothing (no workspace, no timing events).
- * Limit: B x H x (d_V + 1) x ceil(M_pad / 2048) x 16 bytes <= 16 MiB (e.g. 512 heads at
+ * Limit: B x H x (d_V + 1) x ceil(M_pad / 1024) x 8 bytes <= 16 MiB (e.g. 512 heads at
  * d_K = d_V = 64, P = 4; 32 heads at d_K = d_V = 128, P = 4); larger batches return
  * SATA_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU shares that
  * array, so calls that overlap in time on one GPU (several streams, threads or handles)

@@ -81,7 +81,7 @@ def test_decode_workspace_covers_both_forms():
             # readout partials of d + 1 columns and block maxima of P x d blocks, per wave of
             # 512 rows (two waves per 1024-row block)
             need16 = 16 * 32 * (d + 1 + P * d) * ((rows + 1023) // 1024) * 2 * 4
-            need32 = 16 * 32 * (d + 1) * ((sata.sata_state_stride(d, P) + 2047) // 2048) * 4 * 4
+            need32 = 16 * 32 * (d + 1) * ((sata.sata_state_stride(d, P) + 1023) // 1024) * 2 * 4
             assert t.decode_workspace(16, 32, d) == max(need16, need32)
         finally:
             t.close()
