@@ -355,7 +355,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     const uint32_t a_sb = lds_base(LY::sb + lane * 16);                           // [ct][K-step][lane]
     const uint32_t a_sb4 = lds_base(LY::sb4 + g * 16);                            // [K-step][g]
     const uint32_t a_vt = lds_base(LY::t1 + LY::KTB + (li * TS + 8 * g) * 2);    // row 16 ct + li
-    const uint32_t a_vt4 = lds_base(LY::t1 + LY::KTB + (64 * TS + 8 * g) * 2);   // the ones row
+    // B operand of the normaliser's tile: u = 1 in column 0 for every token (the key operand is
+    // zero for tokens past the sequence)
+    const _Float16 one_h = li == 0 ? (_Float16)1.0f : (_Float16)0.0f;
+    const f16x8 ones_op = {one_h, one_h, one_h, one_h, one_h, one_h, one_h, one_h};
     const uint32_t a_kt = lds_base(LY::t1 + ((8 * lb_w + (li & 3)) * TS + 8 * g) * 2);
     const uint32_t a_q = lds_base(LY::qt + (TW * w + li) * XR * 2);               // token row, tile 0
     const uint32_t a_ri = lds_base(LY::ri + g * 8);                               // row 4 s + g
@@ -384,8 +387,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
             f16x8 Vop[NCT], kreg[2];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Vop[ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_vt, TO + (16 * ct * TS + 32 * kk) * 2)
-                                 : lds_at<f16x8>(lds_raw, a_vt4, TO + 32 * kk * 2);
+                Vop[ct] = ct < 4 ? lds_at<f16x8>(lds_raw, a_vt, TO + (16 * ct * TS + 32 * kk) * 2) : ones_op;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) kreg[hh] = lds_at<f16x8>(lds_raw, a_kt, TO + (4 * hh * TS + 32 * kk) * 2);
 #pragma unroll
