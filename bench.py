@@ -65,9 +65,10 @@ def flops_per_token(d_K, d_V, P):
     return (4 * d_V + 2 * (P * d_K + 1) / (d_K + 1) + 2) * math.comb(d_K + P - 1, P - 1)
 
 
-def traffic_from_profiles(kernel_key):
+def traffic_from_profiles(kernel_key, chunks_per_launch=None):
     """Measured HBM bytes per launch from profiles/traffic.json, if the kernel's
-    source has not changed since the counters were taken; else None."""
+    source has not changed since the counters were taken and (for a prefill kernel) the
+    launches cover as many chunks as the measured ones; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -81,6 +82,8 @@ def traffic_from_profiles(kernel_key):
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if sha != rec["source_sha256"]:
         return None
+    if chunks_per_launch is not None and rec.get("chunks_per_launch") != chunks_per_launch:
+        return None
     return rec["bytes_per_launch"]
 
 
@@ -91,7 +94,8 @@ def to_dev(a, dtype):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-WORKSPACE_CAP = 0          # bytes; 0 = the library's default (--workspace-gib)
+WORKSPACE_CAP = 0          # bytes; 0 = the library's default (set from --workspace-gib)
+PLANS = {}                 # per workload: how the prefill was cut (segments, workspace)
 
 
 def bench_prefill(w, steps, warmup):
@@ -110,6 +114,7 @@ def bench_prefill(w, steps, warmup):
     nbytes, nseg, nsub = t.prefill_workspace(w.B, w.H, w.n, w.d_V, chunk=w.chunk,
                                              dtype=sata.SATA_BF16 if w.dtype == "bf16" else sata.SATA_F32)
     log("  plan: %d segment(s), %d sub-segment(s), workspace %.2f GB" % (nseg, nsub, nbytes / 1e9))
+    PLANS[w.name] = {"segments": nseg, "sub_segments": nsub, "workspace_gb": nbytes / 1e9}
     t.set_timing(True)
     for i in range(warmup):
         sata.sata_prefill(t, q, k, v, y, state, chunk=w.chunk)
@@ -129,6 +134,15 @@ def bench_prefill(w, steps, warmup):
     return wall, tim
 
 
+def chunks_per_launch(w):
+    """Chunks one scan launch of this workload's prefill covers (the first segment's)."""
+    plan = PLANS.get(w.name)
+    if not plan or plan["sub_segments"] > 1:
+        return None
+    nchunks = (w.n + w.chunk - 1) // w.chunk
+    return -(-nchunks // plan["segments"])
+
+
 def prefill_record(w, steps, wall, tim, ceil_tflops):
     """The JSON object of one prefill leg: tokens/s and the scan kernel's roofline."""
     F = flops_per_token(w.d_K, w.d_V, w.P)
@@ -145,11 +159,12 @@ def prefill_record(w, steps, wall, tim, ceil_tflops):
         "roofline": {"bound": "mfma", "achieved": scan_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": scan_tflops / MFMA_BF16_PEAK_TFLOPS,
                      "frac_of_measured_ceiling": scan_tflops / ceil_tflops if ceil_tflops else None,
-                     "traffic": traffic_from_profiles("prefill_scan_" + w.name),
+                     "traffic": traffic_from_profiles("prefill_scan_" + w.name, chunks_per_launch(w)),
                      "kernel": "prefill scan", "launches": scan_n, "ms_per_launch": scan_ms / scan_n,
                      "algorithmic_flops_per_launch": alg_total / scan_n},
         "step": {"tflops": step_tflops, "frac_mfma": step_tflops / MFMA_BF16_PEAK_TFLOPS,
                  "kernels_ms_per_step": {k: v[0] / steps for k, v in tim.items() if v[1]}},
+        "plan": PLANS.get(w.name),
     }
 
 
@@ -452,7 +467,9 @@ def main():
                     help="skip the prefill legs of the workloads other than --workload")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--workspace-gib", type=float, default=0.0,
-                    help="workspace cap of the prefill legs (0: the library's default)")
+                    help="workspace cap of the prefill legs (0: the library's default, 32 GiB; "
+                         "64 runs the Long prefill as one segment of 1024 chunks instead of two "
+                         "of 512, which measured the same within the boxes' spread)")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--softmax-rows", type=int, default=512)
     ap.add_argument("--no-cpu", action="store_true")
@@ -531,7 +548,7 @@ def main():
                    "B": w.B, "H": w.H, "n": w.n, "d_K": w.d_K, "d_V": w.d_V, "P": w.P,
                    "chunk": w.chunk},
         "roofline": rec["roofline"],
-        "prefill_step": dict(rec["step"], token_heads_per_s=rec["token_heads_per_s"]),
+        "prefill_step": dict(rec["step"], token_heads_per_s=rec["token_heads_per_s"], plan=rec["plan"]),
     }
     if ceil:
         out["ceilings"] = ceil
