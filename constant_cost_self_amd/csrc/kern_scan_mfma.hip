@@ -216,6 +216,10 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     // global column of local column j of this group (local 64 is the normaliser)
     auto gcol = [&](int j) { return (ONES && j == 64) ? d_V : col0 + j; };
     float* state = a.state ? a.state + (bh * a.nsub + sub) * (int64_t)(DV + 1) * a.M_pad : nullptr;
+    // where the end state goes: this block's own slot, or (final_state) the final state from
+    // the blocks of the last sub-segment alone
+    float* sdst = a.final_state ? (sub == a.nsub - 1 ? a.final_state + bh * (int64_t)(DV + 1) * a.M_pad : nullptr)
+                                : state;
 
     // per-head exponents of the input scales and of the query weights
     const int s_q = prep_scale_exp(a.maxbits[bh * 4 + 0]);
@@ -578,7 +582,7 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
     }
     __builtin_amdgcn_s_waitcnt(0);
 
-    if (a.store_state) {
+    if (a.store_state && sdst) {
         // through LDS as for the load; S = S'' / factor.  The window loop has reused the
         // staging area: stage the canonical indices and factors again.
         float* io = reinterpret_cast<float*>(lds_raw + LY::sb);
@@ -601,14 +605,14 @@ void scan_mfma_kernel(PrefillSegArgs a, RowPtrs rt) {
                 if (idx < LY::io_rows * NCL) {
                     const int fr = idx % LY::io_rows, j = idx / LY::io_rows, kf = kf_of(T, fr);
                     const int F = cf_idx[kf];
-                    if (F >= 0) state[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / (cf_fac[kf] * colfac(j));
+                    if (F >= 0) sdst[(int64_t)gcol(j) * a.M_pad + F] = io[fr * LY::IO + j] / (cf_fac[kf] * colfac(j));
                 }
             }
         }
         if (slice == 0) {
             const int64_t padn = a.M_pad - a.M;
             for (int64_t idx = tid; idx < NCL * padn; idx += 512)
-                state[(int64_t)gcol((int)(idx / padn)) * a.M_pad + a.M + idx % padn] = 0.0f;
+                sdst[(int64_t)gcol((int)(idx / padn)) * a.M_pad + a.M + idx % padn] = 0.0f;
         }
     }
 }
@@ -690,26 +694,29 @@ void free_mfma_tables(MfmaTables& m) {
 }
 
 namespace {
-__global__ __launch_bounds__(kThreads) void state_prefix_kernel(float* __restrict__ states, const float* __restrict__ init,
-                                                                float* __restrict__ final, int nsub, int64_t per_state) {
+__global__ __launch_bounds__(kThreads) void state_starts_kernel(const float* __restrict__ pieces,
+                                                                const float* __restrict__ init,
+                                                                float* __restrict__ starts, int nsub,
+                                                                int pps, int64_t per_state) {
     const int64_t bh = blockIdx.y;
     const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (e >= per_state) return;
     float acc = init ? init[bh * per_state + e] : 0.0f;
-    float* s = states + bh * nsub * per_state + e;
+    const float* p = pieces + bh * (int64_t)(nsub - 1) * pps * per_state + e;
+    float* s = starts + bh * nsub * per_state + e;
     for (int i = 0; i < nsub; ++i) {
-        const float x = s[i * per_state];
         s[i * per_state] = acc;
-        acc += x;
+        if (i + 1 < nsub)
+            for (int j = 0; j < pps; ++j) acc += p[(int64_t)(i * pps + j) * per_state];
     }
-    if (final) final[bh * per_state + e] = acc;
 }
 }  // namespace
 
-hipError_t launch_state_prefix(float* states, const float* init, float* final, int BH, int nsub,
-                               int64_t per_state, hipStream_t st) {
+hipError_t launch_state_starts(const float* pieces, const float* init, float* starts, int BH, int nsub,
+                               int pieces_per_sub, int64_t per_state, hipStream_t st) {
     dim3 grid((unsigned)((per_state + kThreads - 1) / kThreads), (unsigned)BH);
-    hipLaunchKernelGGL(state_prefix_kernel, grid, dim3(kThreads), 0, st, states, init, final, nsub, per_state);
+    hipLaunchKernelGGL(state_starts_kernel, grid, dim3(kThreads), 0, st, pieces, init, starts, nsub,
+                       pieces_per_sub, per_state);
     return hipGetLastError();
 }
 

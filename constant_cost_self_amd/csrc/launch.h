@@ -114,8 +114,11 @@ struct PrefillSegArgs {
     // sub-segments of sub_chunks chunks (a multiple of win), scanned in parallel, each from
     // its own state: state holds [BH][nsub][d_V+1][M_pad].  nsub = 1: one segment, state
     // [BH][d_V+1][M_pad].  update_only: no readout and no partials, only the state updates.
+    // final_state (two-level only, nullable): with store_state, the blocks of the last
+    // sub-segment store their end state there ([BH][d_V+1][M_pad]) and the others store none.
     int nsub = 1, sub_chunks = 0;
     bool update_only = false;
+    float* final_state = nullptr;
     // Matrix-core scan only: the fp16 operand images written by the prep kernels
     // (kern_prep.hip, layouts in scan_mfma.h) for windows [img_w0, img_w0 + img_nwin) and
     // 128-token update sub-chunks [img_u0, img_u0 + img_nsub) of every head, and the per-head
@@ -151,12 +154,12 @@ __host__ __device__ inline int prep_scale_exp(uint32_t mb) {
 hipError_t launch_prep_max(const PrefillSegArgs& a, uint32_t* maxbits, hipStream_t st);
 hipError_t launch_prep_images(const PrefillSegArgs& a, int u_begin, int u_end, hipStream_t st);
 
-// Two-level prefill: replaces the nsub local states of every head, [BH][nsub][per_state],
-// by the state each sub-segment starts from (exclusive prefix sums, starting from init, which
-// is [BH][per_state] or zero when null), and writes the total to final when non-null (final
-// may equal init).
-hipError_t launch_state_prefix(float* states, const float* init, float* final, int BH, int nsub,
-                               int64_t per_state, hipStream_t st);
+// Two-level prefill: from the local states of the pieces of the first nsub - 1 sub-segments,
+// pieces [BH][(nsub - 1) pieces_per_sub][per_state] in order, the state each of the nsub
+// sub-segments starts from, starts [BH][nsub][per_state]: init ([BH][per_state], zero when
+// null) plus the pieces before the sub-segment, added in order.
+hipError_t launch_state_starts(const float* pieces, const float* init, float* starts, int BH, int nsub,
+                               int pieces_per_sub, int64_t per_state, hipStream_t st);
 
 // fp32 scan: slice_feats features per block, chosen by valu_slice_feats().
 int valu_slice_feats(int d_K, int d_V, int L);

@@ -192,6 +192,7 @@ struct PrefillPlan {
     int64_t state_b = 0;         // bytes of one state per head, all heads
     int64_t s32_b = 0;           // fp32 working state of a call with a half-precision state
     int nsub = 1, sub_chunks = 0; // two-level form when nsub >= 2
+    int pps = 1;                 // two-level: pieces per sub-segment in the update-only pass
     int seg = 0, nseg = 1;       // one-level form: segments of seg chunks
     int64_t ws_bytes = 0;
     // workspace layout (byte offsets): partials, carried state, operand images, maxima,
@@ -271,19 +272,36 @@ int plan_prefill(const sata_tables* t, int B, int H, int n, int d_V, int chunk, 
             if (nsub > nwin / 4) nsub = nwin / 4;
         }
         if (nsub > nwin) nsub = nwin;
-        int64_t sub_chunks = pl.nchunks;
+        int64_t sub_chunks = pl.nchunks, pps = 1;
         if (nsub >= 2) {
             sub_chunks = (nwin + nsub - 1) / nsub * pl.win;
             nsub = (pl.nchunks + sub_chunks - 1) / sub_chunks;     // no empty sub-segment
         }
-        const int64_t need = pl.part_chunk * pl.nchunks + pl.state_b * nsub + pl.fixed + pl.s32_b +
+        if (nsub >= 2) {
+            // The update-only pass needs the local states of the first nsub - 1 sub-segments
+            // alone (the last one's end state comes from the second pass); each is cut into
+            // pps pieces of whole windows, as many as the idle compute units take.
+            const int64_t cus = t->cus > 0 ? t->cus : 256;
+            const int64_t sub_win = sub_chunks / pl.win;
+            int64_t kmax = cus / (BH * pl.nslices * (nsub - 1));
+            if (kmax > sub_win) kmax = sub_win;
+            for (int64_t k = kmax; k >= 1; --k)
+                if (sub_win % k == 0) {
+                    pps = k;
+                    break;
+                }
+            if (BH * (nsub - 1) * pps > 65535) pps = 1;
+        }
+        const int64_t carrier_b = pl.state_b * (nsub + (nsub - 1) * pps);   // starts, then pieces
+        const int64_t need = pl.part_chunk * pl.nchunks + carrier_b + pl.fixed + pl.s32_b +
                              pl.img_chunk * ((pl.nchunks + pl.win - 1) / pl.win * pl.win) + 256;
         if (nsub >= 2 && BH * nsub <= 65535 && need <= limit) {
             pl.nsub = (int)nsub;
             pl.sub_chunks = (int)sub_chunks;
+            pl.pps = (int)pps;
             pl.seg = pl.nchunks;
             pl.nseg = 1;
-            layout(pl.nchunks, pl.state_b * nsub);
+            layout(pl.nchunks, carrier_b);
             return SATA_OK;
         }
     }
@@ -647,30 +665,39 @@ int sata_prefill(const sata_tables* tc, const void* q, const void* k, const void
 
     if (pl.nsub >= 2) {
         // Two-level form (the state recurrence as a prefix over segments, [TA] "Hardware
-        // optimisation path"): the local states of the sub-segments are accumulated in
-        // parallel (update-only scan), turned into each sub-segment's starting state by a
-        // prefix sum, and the sub-segments are then scanned in parallel from those states.
-        // Same sums as one segment, in another order.
+        // optimisation path"): the local states of the pieces of the first nsub - 1
+        // sub-segments are accumulated in parallel (update-only scan), summed in order into
+        // each sub-segment's starting state, and the sub-segments are then scanned in parallel
+        // from those states; the last one's blocks store the final state.  Same sums as one
+        // segment, in another order.
+        const int64_t per_state = (int64_t)cols * t->h.M_pad;
         float* starts = (float*)(ws + pl.off_carrier);
-        a.c_begin = 0;
-        a.c_end = pl.nchunks;
-        a.nsub = pl.nsub;
-        a.sub_chunks = pl.sub_chunks;
-        a.state = starts;
+        float* pieces = starts + (int64_t)BH * pl.nsub * per_state;
         hipEvent_t ev = t->timer.begin(st);
         hipError_t e = prep_images(0, pl.nchunks, (pl.nchunks + pl.win - 1) / pl.win);
         t->timer.end(SATA_KERNEL_PREP, ev, st);
         ev = t->timer.begin(st);
-        a.update_only = true;                   // local states from zero
+        a.c_begin = 0;                          // local states of the pieces, from zero
+        a.c_end = (pl.nsub - 1) * pl.sub_chunks;
+        a.nsub = (pl.nsub - 1) * pl.pps;
+        a.sub_chunks = pl.sub_chunks / pl.pps;
+        a.state = pieces;
+        a.update_only = true;
         a.load_state = 0;
         a.store_state = 1;
+        a.final_state = nullptr;
         if (e == hipSuccess) e = sata::launch_scan_mfma(a, t->mfma, st);
         if (e == hipSuccess)
-            e = sata::launch_state_prefix(starts, cont ? state : nullptr, state, BH, pl.nsub,
-                                          (int64_t)cols * t->h.M_pad, st);
-        a.update_only = false;                  // readouts and partials from the starts
+            e = sata::launch_state_starts(pieces, cont ? state : nullptr, starts, BH, pl.nsub, pl.pps,
+                                          per_state, st);
+        a.c_end = pl.nchunks;                   // readouts and partials from the starts
+        a.nsub = pl.nsub;
+        a.sub_chunks = pl.sub_chunks;
+        a.state = starts;
+        a.update_only = false;
         a.load_state = 1;
-        a.store_state = 0;
+        a.store_state = state ? 1 : 0;
+        a.final_state = state;
         if (e == hipSuccess) e = sata::launch_scan_mfma(a, t->mfma, st);
         t->timer.end(SATA_KERNEL_SCAN, ev, st);
         if (e != hipSuccess)

@@ -192,10 +192,11 @@ int sata_state_unpack_f16(const sata_tables *t, const void *state16, float *stat
  *
  * Two-level form (bf16 matrix-core path only): when the slices of all B x H heads
  * leave compute units idle (few heads), the sequence is cut into sub-segments of
- * whole readout windows whose local states are summed in parallel, turned into
- * each sub-segment's starting state by a prefix sum, and then scanned in parallel
- * from those states ([TA] "Hardware optimisation path": the recurrence as a
- * parallel prefix).  The results equal the one-segment scan up to rounding.
+ * whole readout windows; the local states of the first sub-segments (in pieces of
+ * whole windows) are summed in parallel, added in order into each sub-segment's
+ * starting state, and the sub-segments are then scanned in parallel from those
+ * states ([TA] "Hardware optimisation path": the recurrence as a parallel prefix).
+ * The results equal the one-segment scan up to rounding.
  * sata_set_prefill_split chooses when it is used.
  */
 int sata_prefill(const sata_tables *t, const void *q, const void *k, const void *v,
@@ -338,7 +339,8 @@ int sata_reserve_workspace(sata_tables *t, int64_t bytes, void *stream);
  * compute units, with at least 4 readout windows per sub-segment; 1: never;
  * k >= 2: k sub-segments (fewer when the sequence has fewer readout windows)
  * whenever the matrix-core path runs.  The two-level form needs workspace for
- * the partials of the whole sequence plus one state per sub-segment; beyond the
+ * the partials of the whole sequence plus one state per sub-segment and one per
+ * piece of the update pass (sata_prefill_workspace reports it); beyond the
  * workspace cap the one-level form runs.  Errors: SATA_ERR_ARG for a NULL handle
  * or k outside [0, 4096].
  */
